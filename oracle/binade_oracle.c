@@ -1,0 +1,456 @@
+/*
+ * Binade oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU statement of what the Binade hot path
+ * computes. Only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg may load this file's library. It shares no code, header, table or helper
+ * with the HIP library under decode_gemv_tensor_amd/csrc, and it never calls it.
+ *
+ * Sources (the pages):
+ *   [P1] "Binade" package page, pypi.org/project/binade: intro paragraph
+ *        (sign and mantissa kept as one raw byte; exponent replaced by its
+ *        frequency rank in a per-tensor table; Rice codes on disk; a 4-bit
+ *        runtime layout at load) and section "How it works" (one table per
+ *        tensor; format 2 = Rice codes; runtime layout R4 = every rank in
+ *        4 bits with rare escapes; exactness by a fixed summation order).
+ *   [P5] "Lossless BF16 weight compression" page, intro (only the exponent
+ *        field is entropy coded; sign and mantissa stay raw).
+ *
+ * Where the pages are silent the oracle takes the readings listed at the top
+ * of each function (they are the same readings the library documents).
+ *
+ * Arithmetic: integer work is exact. Floating point uses explicit fmaf() and
+ * is compiled with -ffp-contract=off so no other contraction happens.
+ *
+ * Parity status by function:
+ *   table, rice pack/decode, r4 make/unpack, gemv replay, gemv fp64,
+ *   moe replay, bf16 rounding        -- pinned by tests/test_oracle_*.py
+ *   gemm replay                       -- see the comment on oracle_gemm_replay
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+
+#define OR_OK 0
+#define OR_EINVAL (-1)
+#define OR_ECORRUPT (-2)
+#define OR_ENOSPACE (-5)
+
+/* Weights per row-chunk: the unit that carries one unary-bit anchor and one
+ * escape prefix in format 2, and one escape prefix in R4. Reading of the
+ * pages' unspecified index granularity. */
+#define OR_CHUNK 2048
+
+/* ------------------------------------------------------------------ */
+/* bf16 fields ([P1] intro: sign + mantissa in one byte, exponent ranked) */
+
+static unsigned exponent_field(uint16_t b) { return (b >> 7) & 0xFFu; }
+static unsigned sign_field(uint16_t b) { return (b >> 15) & 1u; }
+static unsigned mantissa_field(uint16_t b) { return b & 0x7Fu; }
+
+/* sign+mantissa byte: sign in bit 7, the 7 mantissa bits below it. */
+static uint8_t sm_byte(uint16_t b) {
+  return (uint8_t)((sign_field(b) << 7) | mantissa_field(b));
+}
+
+static uint16_t bf16_from_parts(uint8_t sm, unsigned exponent) {
+  unsigned sign = (sm >> 7) & 1u;
+  unsigned mant = sm & 0x7Fu;
+  return (uint16_t)((sign << 15) | ((exponent & 0xFFu) << 7) | mant);
+}
+
+/* ------------------------------------------------------------------ */
+/* Per-tensor frequency-rank table ([P1] intro, "How it works").
+ * Reading: only exponents that occur get a rank; rank 0 is the most frequent
+ * exponent; equal counts are ordered by the smaller exponent value first. */
+
+int oracle_build_table(const uint16_t *w, int64_t n, uint32_t *n_present,
+                       uint8_t *exp_of_rank /*256*/,
+                       uint64_t *count_of_rank /*256*/) {
+  uint64_t count[256];
+  int taken[256];
+  int64_t i;
+  int e;
+  uint32_t m = 0;
+  if (!w || n <= 0 || !n_present || !exp_of_rank || !count_of_rank)
+    return OR_EINVAL;
+  memset(count, 0, sizeof count);
+  memset(taken, 0, sizeof taken);
+  for (i = 0; i < n; ++i) count[exponent_field(w[i])] += 1;
+  /* selection: pick the untaken present exponent with the largest count;
+   * scanning e upwards with a strict '>' keeps the smaller exponent on ties */
+  for (;;) {
+    int best = -1;
+    for (e = 0; e < 256; ++e) {
+      if (count[e] == 0 || taken[e]) continue;
+      if (best < 0 || count[e] > count[best]) best = e;
+    }
+    if (best < 0) break;
+    taken[best] = 1;
+    exp_of_rank[m] = (uint8_t)best;
+    count_of_rank[m] = count[best];
+    ++m;
+  }
+  for (e = (int)m; e < 256; ++e) {
+    exp_of_rank[e] = 0;
+    count_of_rank[e] = 0;
+  }
+  *n_present = m;
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Rice code lengths ([P1] "How it works": format 2 uses Rice codes).
+ * A Rice(k) code of rank r is q = r >> k in unary plus the k low bits. */
+
+uint64_t oracle_rice_code_bits(const uint64_t *count_of_rank, uint32_t n,
+                               int k) {
+  uint64_t bits = 0;
+  uint32_t r;
+  for (r = 0; r < n; ++r)
+    bits += count_of_rank[r] * (uint64_t)((r >> k) + 1u + (unsigned)k);
+  return bits;
+}
+
+/* Reading: one k per tensor, the k in 0..7 with the fewest total bits, ties
+ * to the smaller k. */
+int oracle_rice_k(const uint64_t *count_of_rank, uint32_t n) {
+  int k, best = 0;
+  uint64_t best_bits = oracle_rice_code_bits(count_of_rank, n, 0);
+  for (k = 1; k <= 7; ++k) {
+    uint64_t b = oracle_rice_code_bits(count_of_rank, n, k);
+    if (b < best_bits) {
+      best_bits = b;
+      best = k;
+    }
+  }
+  return best;
+}
+
+/* ------------------------------------------------------------------ */
+/* Bit planes: bit p of a plane is bit (p mod 32) of 32-bit word p / 32. */
+
+static void set_bit(uint32_t *words, uint64_t p) {
+  words[p >> 5] |= (uint32_t)1u << (p & 31u);
+}
+
+static unsigned get_bit(const uint32_t *words, uint64_t p) {
+  return (words[p >> 5] >> (p & 31u)) & 1u;
+}
+
+static int64_t chunks_per_row(int64_t cols) {
+  return (cols + OR_CHUNK - 1) / OR_CHUNK;
+}
+
+/* Format 2 pack. Readings (the pages give no byte layout):
+ *  - symbols in row-major order;
+ *  - unary plane: for each symbol, q zero bits and then one 1 bit;
+ *  - remainder plane: the k low bits of symbol i at bits i*k .. i*k+k-1,
+ *    least significant bit first;
+ *  - for each row-chunk c of OR_CHUNK columns (the last chunk of a row may be
+ *    shorter): anchor[c] = unary bit position of its first symbol and
+ *    esc_pre[c] = number of symbols before it whose rank is 15 or more;
+ *    the entry after the last chunk holds the totals.
+ * The caller provides zero-capacity-checked buffers; they are cleared here. */
+int oracle_pack_rice(const uint16_t *w, int64_t rows, int64_t cols,
+                     const uint8_t *exp_of_rank, uint32_t n, int k,
+                     uint8_t *sm, uint32_t *unary, int64_t unary_words,
+                     uint32_t *rem, int64_t rem_words, uint64_t *anchor,
+                     uint32_t *esc_pre, uint64_t *unary_bits_out) {
+  int rank_of_exp[256];
+  int64_t row, col, cpr, nchunks;
+  uint64_t pos = 0, nesc = 0;
+  uint32_t r;
+  if (!w || rows <= 0 || cols <= 0 || !exp_of_rank || n == 0 || n > 256 ||
+      k < 0 || k > 7 || !sm || !unary || !anchor || !esc_pre)
+    return OR_EINVAL;
+  if (k > 0 && !rem) return OR_EINVAL;
+  for (r = 0; r < 256; ++r) rank_of_exp[r] = -1;
+  for (r = 0; r < n; ++r) rank_of_exp[exp_of_rank[r]] = (int)r;
+  memset(unary, 0, (size_t)unary_words * 4);
+  if (k > 0) memset(rem, 0, (size_t)rem_words * 4);
+  cpr = chunks_per_row(cols);
+  nchunks = rows * cpr;
+  for (row = 0; row < rows; ++row) {
+    for (col = 0; col < cols; ++col) {
+      int64_t i = row * cols + col;
+      uint16_t b = w[i];
+      int rank = rank_of_exp[exponent_field(b)];
+      unsigned q, t;
+      int j;
+      if (col % OR_CHUNK == 0) {
+        int64_t c = row * cpr + col / OR_CHUNK;
+        anchor[c] = pos;
+        esc_pre[c] = (uint32_t)nesc;
+      }
+      if (rank < 0) return OR_EINVAL; /* exponent not in the table */
+      sm[i] = sm_byte(b);
+      q = (unsigned)rank >> k;
+      for (t = 0; t < q; ++t) ++pos; /* q zero bits */
+      if ((int64_t)(pos >> 5) >= unary_words) return OR_ENOSPACE;
+      set_bit(unary, pos);
+      ++pos;
+      for (j = 0; j < k; ++j) {
+        uint64_t p = (uint64_t)i * (uint64_t)k + (uint64_t)j;
+        if ((int64_t)(p >> 5) >= rem_words) return OR_ENOSPACE;
+        if ((rank >> j) & 1) set_bit(rem, p);
+      }
+      if (rank >= 15) ++nesc;
+    }
+  }
+  anchor[nchunks] = pos;
+  esc_pre[nchunks] = (uint32_t)nesc;
+  if (unary_bits_out) *unary_bits_out = pos;
+  return OR_OK;
+}
+
+/* Format 2 decode, bit by bit, back to bf16. Any inconsistency between the
+ * stream, the anchors, the escape prefixes and the table is ECORRUPT. */
+int oracle_rice_decode(int64_t rows, int64_t cols, int k,
+                       const uint8_t *exp_of_rank, uint32_t n,
+                       const uint8_t *sm, const uint32_t *unary,
+                       uint64_t unary_bits, const uint32_t *rem,
+                       const uint64_t *anchor, const uint32_t *esc_pre,
+                       uint16_t *out) {
+  int64_t row, col, cpr, nchunks;
+  uint64_t pos = 0, nesc = 0;
+  if (rows <= 0 || cols <= 0 || k < 0 || k > 7 || n == 0 || n > 256 ||
+      !exp_of_rank || !sm || !unary || !anchor || !esc_pre || !out)
+    return OR_EINVAL;
+  if (k > 0 && !rem) return OR_EINVAL;
+  cpr = chunks_per_row(cols);
+  nchunks = rows * cpr;
+  for (row = 0; row < rows; ++row) {
+    for (col = 0; col < cols; ++col) {
+      int64_t i = row * cols + col;
+      unsigned q = 0, remainder = 0, rank;
+      int j;
+      if (col % OR_CHUNK == 0) {
+        int64_t c = row * cpr + col / OR_CHUNK;
+        if (anchor[c] != pos || esc_pre[c] != nesc) return OR_ECORRUPT;
+      }
+      for (;;) {
+        unsigned bit;
+        if (pos >= unary_bits) return OR_ECORRUPT;
+        bit = get_bit(unary, pos);
+        ++pos;
+        if (bit) break;
+        ++q;
+        if (q > 255) return OR_ECORRUPT;
+      }
+      for (j = 0; j < k; ++j)
+        remainder |= get_bit(rem, (uint64_t)i * (uint64_t)k + (uint64_t)j)
+                     << j;
+      rank = (q << k) | remainder;
+      if (rank >= n) return OR_ECORRUPT;
+      if (rank >= 15) ++nesc;
+      out[i] = bf16_from_parts(sm[i], exp_of_rank[rank]);
+    }
+  }
+  if (pos != unary_bits || anchor[nchunks] != pos ||
+      esc_pre[nchunks] != nesc)
+    return OR_ECORRUPT;
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* R4 runtime layout ([P1] "How it works": every rank in 4 bits with rare
+ * escapes). Readings:
+ *  - nibble = rank for ranks 0..14; nibble 15 marks an escape;
+ *  - lut[r] = exponent of rank r for r < 15 (0 where the table has no such
+ *    rank), lut[15] = 0;
+ *  - nibble placement: inside each row, columns are taken in groups of 8;
+ *    group g of row i owns the 4 bytes starting at i*cols/2 + 4*g; byte b of
+ *    those 4 holds column 8g+b in its low nibble and column 8g+4+b in its
+ *    high nibble;
+ *  - escapes: a side list of 32-bit entries in row-major order, each
+ *    (exponent << 16) | (column - 2048 * chunk), i.e. the exponent byte and
+ *    the position inside its row-chunk;
+ *  - esc_pre[c]: entries before row-chunk c (same values as format 2's). */
+
+static int64_t nib_byte_index(int64_t row, int64_t col, int64_t cols) {
+  int64_t g = col / 8, within = col % 8;
+  return row * (cols / 2) + 4 * g + (within % 4);
+}
+
+static unsigned nib_shift(int64_t col) { return (unsigned)(((col % 8) / 4) * 4); }
+
+int oracle_make_r4(const uint16_t *w, int64_t rows, int64_t cols,
+                   const uint8_t *exp_of_rank, uint32_t n, uint8_t *lut16,
+                   uint8_t *nib, uint32_t *esc_pre, uint32_t *esc,
+                   int64_t esc_cap, int64_t *n_esc_out) {
+  int rank_of_exp[256];
+  int64_t row, col, cpr, nchunks, nesc = 0;
+  uint32_t r;
+  if (!w || rows <= 0 || cols <= 0 || cols % 8 != 0 || !exp_of_rank ||
+      n == 0 || n > 256 || !lut16 || !nib || !esc_pre || !n_esc_out)
+    return OR_EINVAL;
+  for (r = 0; r < 256; ++r) rank_of_exp[r] = -1;
+  for (r = 0; r < n; ++r) rank_of_exp[exp_of_rank[r]] = (int)r;
+  for (r = 0; r < 16; ++r) lut16[r] = (r < 15 && r < n) ? exp_of_rank[r] : 0;
+  memset(nib, 0, (size_t)(rows * cols / 2));
+  cpr = chunks_per_row(cols);
+  nchunks = rows * cpr;
+  for (row = 0; row < rows; ++row) {
+    for (col = 0; col < cols; ++col) {
+      uint16_t b = w[row * cols + col];
+      unsigned e = exponent_field(b);
+      int rank = rank_of_exp[e];
+      unsigned v;
+      if (col % OR_CHUNK == 0) esc_pre[row * cpr + col / OR_CHUNK] = (uint32_t)nesc;
+      if (rank < 0) return OR_EINVAL;
+      v = rank < 15 ? (unsigned)rank : 15u;
+      nib[nib_byte_index(row, col, cols)] |= (uint8_t)(v << nib_shift(col));
+      if (rank >= 15) {
+        if (nesc >= esc_cap) return OR_ENOSPACE;
+        esc[nesc] = (uint32_t)((e << 16) | (uint32_t)(col % OR_CHUNK));
+        ++nesc;
+      }
+    }
+  }
+  esc_pre[nchunks] = (uint32_t)nesc;
+  *n_esc_out = nesc;
+  return OR_OK;
+}
+
+/* R4 back to bf16. */
+int oracle_r4_unpack(int64_t rows, int64_t cols, const uint8_t *lut16,
+                     const uint8_t *sm, const uint8_t *nib,
+                     const uint32_t *esc_pre, const uint32_t *esc,
+                     int64_t n_esc, uint16_t *out) {
+  int64_t row, col, cpr, nchunks, next = 0;
+  if (rows <= 0 || cols <= 0 || cols % 8 != 0 || !lut16 || !sm || !nib ||
+      !esc_pre || !out)
+    return OR_EINVAL;
+  cpr = chunks_per_row(cols);
+  nchunks = rows * cpr;
+  for (row = 0; row < rows; ++row) {
+    for (col = 0; col < cols; ++col) {
+      int64_t i = row * cols + col;
+      unsigned v = (nib[nib_byte_index(row, col, cols)] >> nib_shift(col)) & 0xFu;
+      unsigned e;
+      if (col % OR_CHUNK == 0 && esc_pre[row * cpr + col / OR_CHUNK] != (uint32_t)next)
+        return OR_ECORRUPT;
+      if (v < 15) {
+        e = lut16[v];
+      } else {
+        if (next >= n_esc) return OR_ECORRUPT;
+        if ((esc[next] & 0xFFFFu) != (uint32_t)(col % OR_CHUNK)) return OR_ECORRUPT;
+        e = (esc[next] >> 16) & 0xFFu;
+        ++next;
+      }
+      out[i] = bf16_from_parts(sm[i], e);
+    }
+  }
+  if (esc_pre[nchunks] != (uint32_t)next || next != n_esc) return OR_ECORRUPT;
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Matrix-vector product. [P1] intro and "How it works": the outputs are
+ * exact because the kernels add the products in one fixed order. The pages'
+ * order (MLX's) is not available, so the order is this library's own:
+ *
+ *   The K inputs are cut into tiles of 32 (K must be a multiple of 32).
+ *   Tile j belongs to slot j mod 64. Each slot keeps two fp32 partial sums,
+ *   both starting at +0.0; for each of its tiles in increasing j and for
+ *   i = 0..15 it does  a0 = fma(w[32j+2i],   x[32j+2i],   a0)
+ *                      a1 = fma(w[32j+2i+1], x[32j+2i+1], a1).
+ *   The slot's value is a0 + a1 (a slot with no tile gives +0.0).
+ *   Then for s = 32, 16, 8, 4, 2, 1: p[l] = p[l] + p[l+s] for every l < s.
+ *   The output is p[0]. */
+
+static float bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+static float gemv_row_replay(const uint16_t *wrow, const uint16_t *x,
+                             int64_t K) {
+  float p[64];
+  int64_t J = K / 32, j;
+  int l, i, s;
+  for (l = 0; l < 64; ++l) {
+    float a0 = 0.0f, a1 = 0.0f;
+    for (j = l; j < J; j += 64) {
+      for (i = 0; i < 16; ++i) {
+        int64_t k0 = 32 * j + 2 * i, k1 = k0 + 1;
+        a0 = fmaf(bf16_value(wrow[k0]), bf16_value(x[k0]), a0);
+        a1 = fmaf(bf16_value(wrow[k1]), bf16_value(x[k1]), a1);
+      }
+    }
+    p[l] = a0 + a1;
+  }
+  for (s = 32; s >= 1; s /= 2)
+    for (l = 0; l < s; ++l) p[l] = p[l] + p[l + s];
+  return p[0];
+}
+
+int oracle_gemv_replay(const uint16_t *w, int64_t rows, int64_t cols,
+                       const uint16_t *x, float *y) {
+  int64_t r;
+  if (!w || !x || !y || rows < 0 || cols <= 0 || cols % 32 != 0)
+    return OR_EINVAL;
+  for (r = 0; r < rows; ++r) y[r] = gemv_row_replay(w + r * cols, x, cols);
+  return OR_OK;
+}
+
+/* The plain definition y = W x, summed in double. bf16 products are exact in
+ * double; the sum of K of them differs from the exact value by far less than
+ * the 1e-2 relative bound it is used for. */
+int oracle_gemv_f64(const uint16_t *w, int64_t rows, int64_t cols,
+                    const uint16_t *x, double *y) {
+  int64_t r, c;
+  if (!w || !x || !y || rows < 0 || cols <= 0) return OR_EINVAL;
+  for (r = 0; r < rows; ++r) {
+    double acc = 0.0;
+    for (c = 0; c < cols; ++c)
+      acc += (double)bf16_value(w[r * cols + c]) * (double)bf16_value(x[c]);
+    y[r] = acc;
+  }
+  return OR_OK;
+}
+
+/* Expert-gather GEMV ([P1] "How it works": the MoE expert gather adds in the
+ * same fixed order as the matvec). experts is a stack of n_experts matrices
+ * [N, K]; for token t and slot j the expert is idx[t*top_k + j] and the input
+ * is x[t] (x_per_slot = 0) or x[t*top_k + j] (x_per_slot = 1); the output row
+ * is y[(t*top_k + j) * N ...]. */
+int oracle_moe_replay(const uint16_t *experts, int64_t n_experts, int64_t N,
+                      int64_t K, const uint16_t *x, int x_per_slot,
+                      const int32_t *idx, int64_t n_tokens, int64_t top_k,
+                      float *y) {
+  int64_t t, j, r;
+  if (!experts || !x || !idx || !y || N < 0 || K <= 0 || K % 32 != 0 ||
+      n_tokens < 0 || top_k <= 0)
+    return OR_EINVAL;
+  for (t = 0; t < n_tokens; ++t) {
+    for (j = 0; j < top_k; ++j) {
+      int64_t pair = t * top_k + j;
+      int32_t e = idx[pair];
+      const uint16_t *xv = x + (x_per_slot ? pair : t) * K;
+      if (e < 0 || e >= n_experts) return OR_EINVAL;
+      for (r = 0; r < N; ++r)
+        y[pair * N + r] = gemv_row_replay(experts + ((int64_t)e * N + r) * K, xv, K);
+    }
+  }
+  return OR_OK;
+}
+
+/* fp32 -> bf16, round to nearest even; NaN keeps its top bits and is made
+ * quiet. */
+uint16_t oracle_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)
+    return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+void oracle_f32_to_bf16_array(const float *in, int64_t n, uint16_t *out) {
+  int64_t i;
+  for (i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(in[i]);
+}

@@ -1,0 +1,305 @@
+"""Pins of the oracle's format code (table, format 2 / Rice, R4, unpack)
+against what the pages and the mathematics fix, independent of the oracle:
+hand-derived fixtures, closed forms, brute force and library routines.
+
+Pages: "Binade" package page (pypi.org/project/binade), intro and "How it
+works"; "Lossless BF16 weight compression" page, intro (2.65-bit exponent
+entropy, sign and mantissa near full entropy).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_gemv_tensor_amd import synth
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+def _words_from_positions(positions, nbits):
+    words = np.zeros((nbits + 31) // 32 if nbits else 0, np.uint32)
+    for p in positions:
+        words[p // 32] |= np.uint32(1 << (p % 32))
+    return words
+
+
+def _bf16_from(exps, sm):
+    exps = np.asarray(exps, np.uint16)
+    sm = np.asarray(sm, np.uint16)
+    return (((sm >> 7) & 1) << 15 | (exps << 7) | (sm & 0x7F)).astype(np.uint16)
+
+
+def _rand_bits(rows, cols, sigma=0.02, seed=0, frac=1e-3, scale=20.0):
+    spec = synth.TensorSpec("t", rows, cols, sigma, seed, outlier_frac=frac,
+                            outlier_scale=scale)
+    return synth.bits(synth.normal_bf16(spec)).numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------ golden: rice
+def test_golden_table_and_rice_k0(golden_dir):
+    g = _load(golden_dir, "rice_tiny_8.json")
+    w = np.array([int(h, 16) for h in g["bf16_hex"]], np.uint16).reshape(1, 8)
+    t = oracle.build_table(w)
+    assert t["n"] == g["n"]
+    assert list(t["exp_of_rank"][: t["n"]]) == g["exp_of_rank"]
+    assert list(t["count_of_rank"][: t["n"]]) == g["count_of_rank"]
+    for k, bits in g["code_bits_by_k"].items():
+        assert oracle.rice_code_bits(t["count_of_rank"], t["n"], int(k)) == bits
+    assert oracle.rice_k(t["count_of_rank"], t["n"]) == g["k"]
+    pk = oracle.pack_rice(w, t)
+    assert pk["k"] == 0
+    assert [int(b) for b in pk["sm"].reshape(-1)] == [int(h, 16) for h in g["sm_hex"]]
+    assert pk["unary_bits"] == g["k0"]["unary_bits"]
+    want = _words_from_positions(g["k0"]["unary_one_positions"], g["k0"]["unary_bits"])
+    assert np.array_equal(pk["unary"], want)
+    assert int(pk["unary"][0]) == g["k0"]["unary_word0"]
+    assert list(pk["anchor"]) == g["anchor"]
+    assert list(pk["esc_pre"]) == g["esc_pre"]
+    assert np.array_equal(oracle.rice_decode(pk), w)
+
+
+def test_golden_rice_k1_remainder_plane(golden_dir):
+    g = _load(golden_dir, "rice_tiny_8.json")
+    w = np.array([int(h, 16) for h in g["bf16_hex"]], np.uint16).reshape(1, 8)
+    t = oracle.build_table(w)
+    pk = oracle.pack_rice(w, t, k=1)
+    assert pk["unary_bits"] == g["k1"]["unary_bits"]
+    assert int(pk["unary"][0]) == g["k1"]["unary_word0"]
+    assert int(pk["rem"][0]) == g["k1"]["rem_word0"]
+    assert pk["unary_bits"] + 8 * 1 == g["code_bits_by_k"]["1"]
+    assert np.array_equal(oracle.rice_decode(pk), w)
+
+
+def test_golden_r4_escape_and_tie_rule(golden_dir):
+    g = _load(golden_dir, "r4_escape_32.json")
+    cols = np.arange(32)
+    exps = np.full(32, 120)
+    for m in range(15):
+        exps[2 * m + 1] = 100 + m
+    w = _bf16_from(exps, cols).reshape(1, 32)
+    t = oracle.build_table(w)
+    assert t["n"] == g["n"]
+    assert list(t["exp_of_rank"][:16]) == g["exp_of_rank_first16"]
+    for k, bits in g["code_bits_by_k"].items():
+        assert oracle.rice_code_bits(t["count_of_rank"], t["n"], int(k)) == bits
+    assert oracle.rice_k(t["count_of_rank"], t["n"]) == g["k"]
+    pk = oracle.pack_rice(w, t)
+    assert pk["unary_bits"] == g["unary_bits"]
+    assert np.array_equal(pk["unary"], _words_from_positions(g["unary_one_positions"], 88))
+    assert np.array_equal(pk["rem"], _words_from_positions(g["rem_one_positions"], 32))
+    r4 = oracle.make_r4(w, t)
+    assert list(r4["lut"]) == g["lut"]
+    assert [int(b) for b in r4["nib"].reshape(-1)] == [int(h, 16) for h in g["nib_hex"]]
+    assert list(r4["esc"]) == g["esc"]
+    assert list(r4["esc_pre"]) == g["esc_pre"]
+    assert np.array_equal(oracle.r4_unpack(r4), w)
+
+
+def test_golden_r4_escapes_across_chunks(golden_dir):
+    g = _load(golden_dir, "r4_escape_chunks.json")
+    rows, cols = g["rows"], g["cols"]
+    exps = np.full((rows, cols), 120)
+    for m in range(14):
+        exps[0, 100 + m] = 90 + m
+    for r, c, e in g["escapes"]:
+        exps[r, c] = e
+    sm = np.tile(np.arange(cols) % 128, (rows, 1))
+    w = _bf16_from(exps, sm)
+    t = oracle.build_table(w)
+    assert list(t["exp_of_rank"][: t["n"]]) == g["exp_of_rank"]
+    r4 = oracle.make_r4(w, t)
+    assert list(r4["esc"]) == g["esc"]
+    assert list(r4["esc_pre"]) == g["esc_pre"]
+    pk = oracle.pack_rice(w, t)
+    assert list(pk["esc_pre"]) == g["esc_pre"]
+    assert np.array_equal(oracle.r4_unpack(r4), w)
+    assert np.array_equal(oracle.rice_decode(pk), w)
+
+
+# ------------------------------------------------------------ table
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_table_is_frequency_sorted_permutation(seed):
+    w = _rand_bits(64, 96, seed=seed)
+    t = oracle.build_table(w)
+    e = ((w >> 7) & 0xFF).reshape(-1)
+    vals, counts = np.unique(e, return_counts=True)   # library routine
+    n = t["n"]
+    assert n == len(vals)
+    assert sorted(t["exp_of_rank"][:n].tolist()) == vals.tolist()
+    want = sorted(zip(vals.tolist(), counts.tolist()), key=lambda p: (-p[1], p[0]))
+    assert t["exp_of_rank"][:n].tolist() == [p[0] for p in want]
+    assert t["count_of_rank"][:n].tolist() == [p[1] for p in want]
+    assert int(t["count_of_rank"][:n].sum()) == w.size
+
+
+def test_frequency_order_minimises_rice_bits_bruteforce():
+    """Rice lengths are non-decreasing in the rank, so giving the most
+    frequent exponent rank 0 and so on is optimal for every k: check every
+    assignment of ranks on small alphabets."""
+    rng = np.random.default_rng(7)
+    for trial in range(6):
+        m = rng.integers(2, 7)
+        counts_by_exp = rng.integers(1, 30, size=m)
+        exps = rng.choice(np.arange(60, 140), size=m, replace=False)
+        w = np.repeat(exps, counts_by_exp).astype(np.uint16) << 7
+        w = w.reshape(1, -1)
+        t = oracle.build_table(w)
+        for k in range(0, 4):
+            best = oracle.rice_code_bits(t["count_of_rank"], t["n"], k)
+            for perm in itertools.permutations(range(m)):
+                bits = sum(int(counts_by_exp[i]) * ((perm[i] >> k) + 1 + k)
+                           for i in range(m))
+                assert best <= bits
+
+
+def test_exhaustive_all_bf16_patterns_round_trip():
+    """All 65,536 bit patterns (signed zeros, subnormals, infinities, every
+    NaN payload): table -> format 2 -> decode and table -> R4 -> unpack give
+    the same bits back ("Binade" package page: every weight restored bit for
+    bit)."""
+    w = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(64, 1024)
+    t = oracle.build_table(w)
+    assert t["n"] == 256
+    assert set(t["count_of_rank"][:256].tolist()) == {256}
+    # all counts equal: ties go to the smaller exponent
+    assert t["exp_of_rank"].tolist() == list(range(256))
+    pk = oracle.pack_rice(w, t)
+    assert np.array_equal(oracle.rice_decode(pk), w)
+    r4 = oracle.make_r4(w, t)
+    assert r4["n_esc"] == 241 * 256
+    assert np.array_equal(oracle.r4_unpack(r4), w)
+
+
+# ------------------------------------------------------------ rice
+@pytest.mark.parametrize("shape", [(1, 32), (3, 2048), (2, 2080), (5, 4160),
+                                   (7, 96)])
+def test_rice_bits_match_closed_form_and_round_trip(shape):
+    w = _rand_bits(*shape, seed=sum(shape))
+    t = oracle.build_table(w)
+    for k in range(8):
+        pk = oracle.pack_rice(w, t, k=k)
+        # closed form: sum over ranks of count * (q + 1 + k), q = r >> k
+        closed = sum(int(c) * ((r >> k) + 1 + k)
+                     for r, c in enumerate(t["count_of_rank"][: t["n"]]))
+        assert pk["unary_bits"] + k * w.size == closed
+        assert np.array_equal(oracle.rice_decode(pk), w)
+        # escapes: symbols with rank >= 15
+        assert pk["n_esc"] == int(t["count_of_rank"][15: t["n"]].sum())
+
+
+def test_rice_k_is_bruteforce_argmin():
+    for seed in range(4):
+        w = _rand_bits(16, 256, sigma=[0.02, 1.0, 1e-4, 3.0][seed], seed=seed)
+        t = oracle.build_table(w)
+        emitted = []
+        for k in range(8):
+            pk = oracle.pack_rice(w, t, k=k)
+            emitted.append(pk["unary_bits"] + k * w.size)
+        assert oracle.rice_k(t["count_of_rank"], t["n"]) == int(np.argmin(emitted))
+
+
+def test_rice_anchors_point_at_chunk_starts():
+    w = _rand_bits(3, 4160, seed=11)
+    t = oracle.build_table(w)
+    pk = oracle.pack_rice(w, t)
+    # decode every chunk on its own from its anchor: count terminators
+    bits = np.unpackbits(pk["unary"].view(np.uint8), bitorder="little")
+    ones = np.flatnonzero(bits)
+    cpr = 3
+    sizes = [2048, 2048, 64]
+    start_sym = 0
+    for row in range(3):
+        for j in range(cpr):
+            c = row * cpr + j
+            # the symbol before the chunk ends one bit before the anchor
+            if start_sym:
+                assert ones[start_sym - 1] + 1 == pk["anchor"][c]
+            else:
+                assert pk["anchor"][c] == 0
+            start_sym += sizes[j]
+    assert pk["anchor"][-1] == pk["unary_bits"] == ones[-1] + 1
+
+
+def test_rice_decode_rejects_corruption():
+    w = _rand_bits(2, 2080, seed=3)
+    t = oracle.build_table(w)
+    pk = oracle.pack_rice(w, t)
+    bad = dict(pk, anchor=pk["anchor"].copy())
+    bad["anchor"][1] += 1
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.rice_decode(bad)
+    assert e.value.code == -2
+    bad = dict(pk, unary=pk["unary"].copy())
+    bad["unary"][3] ^= np.uint32(1 << 5)
+    with pytest.raises(oracle.OracleError):
+        oracle.rice_decode(bad)
+    bad = dict(pk, esc_pre=pk["esc_pre"].copy())
+    bad["esc_pre"][-1] += 1
+    with pytest.raises(oracle.OracleError):
+        oracle.rice_decode(bad)
+
+
+def test_bits_per_weight_near_exponent_entropy_plus_8():
+    """"Lossless BF16 weight compression" page, intro: all the headroom is in
+    the exponent, whose entropy is about 2.65 of 8 bits. Rice coding of the
+    ranks stays within 0.2 bit of the empirical entropy on N(0, sigma)
+    weights, and the whole format stays near 8 + that."""
+    w = _rand_bits(512, 2048, sigma=0.02, seed=5)
+    t = oracle.build_table(w)
+    c = t["count_of_rank"][: t["n"]].astype(np.float64)
+    p = c / c.sum()
+    H = float(-(p * np.log2(p)).sum())
+    pk = oracle.pack_rice(w, t)
+    per_exp = (pk["unary_bits"] + pk["k"] * w.size) / w.size
+    assert H <= per_exp <= H + 0.2
+    assert 2.3 < H < 2.8
+    index_bits = 96 * (len(pk["anchor"]) - 1) / w.size
+    bpw = 8 + per_exp + index_bits
+    assert 10.5 < bpw < 10.9
+
+
+# ------------------------------------------------------------ r4
+@pytest.mark.parametrize("shape", [(1, 32), (4, 2048), (3, 2080), (2, 8192)])
+def test_r4_round_trip_and_counts(shape):
+    w = _rand_bits(*shape, sigma=0.02, seed=shape[1], frac=5e-3, scale=1e4)
+    t = oracle.build_table(w)
+    r4 = oracle.make_r4(w, t)
+    assert np.array_equal(oracle.r4_unpack(r4), w)
+    nib = r4["nib"].reshape(-1)
+    n15 = int(((nib & 0xF) == 15).sum() + ((nib >> 4) == 15).sum())
+    assert n15 == r4["n_esc"] == int(t["count_of_rank"][15: t["n"]].sum())
+    # the escape entries carry the weights' own exponents, in row-major order
+    e = ((w >> 7) & 0xFF)
+    rank_of = {int(x): r for r, x in enumerate(t["exp_of_rank"][: t["n"]])}
+    esc_pos = [(i, j) for i in range(w.shape[0]) for j in range(w.shape[1])
+               if rank_of[int(e[i, j])] >= 15]
+    assert [int(v) >> 16 for v in r4["esc"]] == [int(e[i, j]) for i, j in esc_pos]
+    assert [int(v) & 0xFFFF for v in r4["esc"]] == [j % 2048 for _, j in esc_pos]
+
+
+def test_r4_unpack_rejects_corruption():
+    w = _rand_bits(2, 2080, sigma=0.02, seed=9, frac=5e-3, scale=1e4)
+    t = oracle.build_table(w)
+    r4 = oracle.make_r4(w, t)
+    assert r4["n_esc"] > 0
+    bad = dict(r4, esc_pre=r4["esc_pre"].copy())
+    bad["esc_pre"][1] += 1
+    with pytest.raises(oracle.OracleError):
+        oracle.r4_unpack(bad)
+    bad = dict(r4, esc=r4["esc"].copy())
+    bad["esc"][0] ^= np.uint32(1)
+    with pytest.raises(oracle.OracleError):
+        oracle.r4_unpack(bad)
+
+
+def test_build_table_rejects_empty():
+    with pytest.raises(oracle.OracleError):
+        oracle.build_table(np.zeros(0, np.uint16))
