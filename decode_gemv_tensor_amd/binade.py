@@ -1,0 +1,400 @@
+"""Python binding of libbinade (include/binade.h): argument marshalling only.
+
+Every step of the path runs in the library: the table and the format 2 pack
+in its host C++, the format 2 -> R4 conversion, the products and the unpack in
+its HIP kernels. PyTorch provides device memory (tensors) and streams. If the
+built library is missing this module raises on first use; there is no other
+implementation behind it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass, field
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libbinade.so")
+CHUNK = 2048
+
+OK, EINVAL, ECORRUPT, EUNSUPPORTED, EHIP, ENOSPACE = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+DEV_CORRUPT_STREAM, DEV_BAD_INDEX, DEV_CORRUPT_ESC = 0x1, 0x2, 0x4
+
+EXPORTS = ["binade_status_str", "binade_last_hip_error", "binade_build_table",
+           "binade_sizes_of", "binade_pack_rice", "binade_rice_to_r4",
+           "binade_unpack", "binade_r4_gemv", "binade_bf16_gemv",
+           "binade_r4_gemm", "binade_bf16_gemm", "binade_r4_moe_gemv",
+           "binade_bf16_moe_gemv"]
+
+
+class Table(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_uint32), ("k", ctypes.c_uint32),
+                ("exp_of_rank", ctypes.c_uint8 * 256),
+                ("rank_of_exp", ctypes.c_uint16 * 256),
+                ("count_of_rank", ctypes.c_uint64 * 256)]
+
+
+class Sizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in
+                ("n_weights", "n_chunks", "unary_bits", "unary_words",
+                 "rem_words", "n_esc", "nib_bytes")]
+
+
+class RiceDesc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("k", ctypes.c_uint32), ("n", ctypes.c_uint32),
+                ("exp_of_rank", ctypes.c_uint8 * 256),
+                ("sm", ctypes.c_void_p), ("unary", ctypes.c_void_p),
+                ("unary_bits", ctypes.c_uint64), ("unary_words", ctypes.c_uint64),
+                ("rem", ctypes.c_void_p), ("rem_words", ctypes.c_uint64),
+                ("anchor", ctypes.c_void_p), ("esc_pre", ctypes.c_void_p),
+                ("n_esc", ctypes.c_uint64)]
+
+
+class R4Desc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("lut", ctypes.c_uint8 * 16),
+                ("sm", ctypes.c_void_p), ("nib", ctypes.c_void_p),
+                ("esc_pre", ctypes.c_void_p), ("esc", ctypes.c_void_p),
+                ("n_esc", ctypes.c_uint64)]
+
+
+class BinadeError(RuntimeError):
+    def __init__(self, fn: str, code: int, hip: int = 0):
+        lib = _lib_or_none()
+        text = lib.binade_status_str(code).decode() if lib else str(code)
+        super().__init__(f"{fn}: {text} ({code})" + (f", hip error {hip}" if hip else ""))
+        self.code = code
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def _lib_or_none():
+    return _lib
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is not built; run "
+                    "`python -m decode_gemv_tensor_amd.build` (hipcc, gfx950)")
+            L = ctypes.CDLL(LIB_PATH)
+            P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+            L.binade_status_str.argtypes = [I32]
+            L.binade_status_str.restype = ctypes.c_char_p
+            L.binade_last_hip_error.restype = I32
+            sig = {
+                "binade_build_table": [P, I64, P],
+                "binade_sizes_of": [P, I64, I64, P],
+                "binade_pack_rice": [P, I64, I64, P, P],
+                "binade_rice_to_r4": [P, P, P, P],
+                "binade_unpack": [P, P, P],
+                "binade_r4_gemv": [P, P, P, I32, P],
+                "binade_bf16_gemv": [P, I64, I64, P, P, I32, P],
+                "binade_r4_gemm": [P, P, I64, I64, P, I64, I32, P],
+                "binade_bf16_gemm": [P, I64, I64, P, I64, I64, P, I64, I32, P],
+                "binade_r4_moe_gemv": [P, I32, P, I32, P, I64, I32, P, I32, P, P],
+                "binade_bf16_moe_gemv": [P, I32, I64, I64, P, I32, P, I64, I32,
+                                         P, I32, P, P],
+            }
+            for name, args in sig.items():
+                if hasattr(L, name):
+                    fn = getattr(L, name)
+                    fn.argtypes = args
+                    fn.restype = I32
+            _lib = L
+    return _lib
+
+
+def _call(name: str, *args):
+    rc = getattr(lib(), name)(*args)
+    if rc != OK:
+        raise BinadeError(name, rc, lib().binade_last_hip_error() if rc == EHIP else 0)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _bits16(t: torch.Tensor) -> torch.Tensor:
+    """bf16 / int16 / uint16 tensor -> contiguous view of its 16-bit patterns"""
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16, torch.float16):
+        raise TypeError(f"expected 16-bit weights, got {t.dtype}")
+    return t.contiguous()
+
+
+# ------------------------------------------------------------------ host
+def build_table(w: torch.Tensor) -> Table:
+    """binade_build_table on a host bf16 tensor."""
+    w = _bits16(w)
+    if w.is_cuda:
+        raise ValueError("build_table runs on host memory")
+    t = Table()
+    _call("binade_build_table", _ptr(w), w.numel(), ctypes.byref(t))
+    return t
+
+
+def sizes_of(table: Table, rows: int, cols: int) -> Sizes:
+    s = Sizes()
+    _call("binade_sizes_of", ctypes.byref(table), rows, cols, ctypes.byref(s))
+    return s
+
+
+@dataclass
+class RicePlanes:
+    """Format 2 planes of one tensor (host or device tensors) + descriptor."""
+    rows: int
+    cols: int
+    table: Table
+    sm: torch.Tensor
+    unary: torch.Tensor
+    rem: torch.Tensor | None
+    anchor: torch.Tensor
+    esc_pre: torch.Tensor
+    unary_bits: int
+    n_esc: int
+
+    @property
+    def k(self) -> int:
+        return int(self.table.k)
+
+    def desc(self) -> RiceDesc:
+        d = RiceDesc()
+        d.rows, d.cols = self.rows, self.cols
+        d.k, d.n = self.table.k, self.table.n
+        ctypes.memmove(d.exp_of_rank, self.table.exp_of_rank, 256)
+        d.sm = self.sm.data_ptr()
+        d.unary = self.unary.data_ptr()
+        d.unary_bits = self.unary_bits
+        d.unary_words = self.unary.numel()
+        d.rem = self.rem.data_ptr() if self.rem is not None else None
+        d.rem_words = self.rem.numel() if self.rem is not None else 0
+        d.anchor = self.anchor.data_ptr()
+        d.esc_pre = self.esc_pre.data_ptr()
+        d.n_esc = self.n_esc
+        return d
+
+    def to(self, device) -> "RicePlanes":
+        mv = lambda t: None if t is None else t.to(device, non_blocking=False)
+        return RicePlanes(self.rows, self.cols, self.table, mv(self.sm),
+                          mv(self.unary), mv(self.rem), mv(self.anchor),
+                          mv(self.esc_pre), self.unary_bits, self.n_esc)
+
+    def nbytes(self) -> dict:
+        """Bytes of each plane as stored (padding words included)."""
+        return {"sm": self.sm.numel(), "unary": 4 * self.unary.numel(),
+                "rem": 0 if self.rem is None else 4 * self.rem.numel(),
+                "anchor": 8 * self.anchor.numel(),
+                "esc_pre": 4 * self.esc_pre.numel()}
+
+    def bits_per_weight(self) -> float:
+        n = self.rows * self.cols
+        bits = 8 * n + self.unary_bits + self.k * n + 96 * (self.anchor.numel() - 1)
+        return bits / n
+
+
+def pack_rice(w: torch.Tensor, table: Table | None = None) -> RicePlanes:
+    """binade_pack_rice: host bf16 [rows, cols] -> host format 2 planes."""
+    w = _bits16(w)
+    if w.is_cuda or w.dim() != 2:
+        raise ValueError("pack_rice takes a 2-D host tensor")
+    rows, cols = w.shape
+    if table is None:
+        table = build_table(w)
+    s = sizes_of(table, rows, cols)
+    sm = torch.empty(rows, cols, dtype=torch.uint8)
+    unary = torch.empty(int(s.unary_words), dtype=torch.int32)
+    rem = torch.empty(int(s.rem_words), dtype=torch.int32) if table.k > 0 else None
+    anchor = torch.empty(int(s.n_chunks) + 1, dtype=torch.int64)
+    esc_pre = torch.empty(int(s.n_chunks) + 1, dtype=torch.int32)
+    planes = RicePlanes(rows, cols, table, sm, unary, rem, anchor, esc_pre, 0, 0)
+    d = planes.desc()
+    _call("binade_pack_rice", _ptr(w), rows, cols, ctypes.byref(table), ctypes.byref(d))
+    planes.unary_bits = int(d.unary_bits)
+    planes.n_esc = int(d.n_esc)
+    return planes
+
+
+# ------------------------------------------------------------------ device
+@dataclass
+class R4Tensor:
+    """R4 weights on the device. sm and esc_pre are the format 2 planes'."""
+    rows: int
+    cols: int
+    lut: bytes
+    sm: torch.Tensor
+    nib: torch.Tensor
+    esc_pre: torch.Tensor
+    esc: torch.Tensor
+    n_esc: int
+    _keep: list = field(default_factory=list, repr=False)
+
+    def desc(self) -> R4Desc:
+        d = R4Desc()
+        d.rows, d.cols = self.rows, self.cols
+        ctypes.memmove(d.lut, self.lut, 16)
+        d.sm = self.sm.data_ptr()
+        d.nib = self.nib.data_ptr()
+        d.esc_pre = self.esc_pre.data_ptr()
+        d.esc = self.esc.data_ptr() if self.n_esc > 0 else None
+        d.n_esc = self.n_esc
+        return d
+
+    def nbytes(self) -> int:
+        return (self.sm.numel() + self.nib.numel() + 4 * self.esc_pre.numel()
+                + 4 * self.n_esc)
+
+    def bits_per_weight(self) -> float:
+        return 8.0 * self.nbytes() / (self.rows * self.cols)
+
+
+def r4_from_planes(rows, cols, lut, sm, nib, esc_pre, esc) -> R4Tensor:
+    """Wrap R4 planes that are already on the device."""
+    return R4Tensor(rows, cols, bytes(bytearray(lut)), sm, nib, esc_pre, esc,
+                    int(esc.numel()))
+
+
+def rice_to_r4(planes: RicePlanes, status: torch.Tensor | None = None,
+               stream=None, out: R4Tensor | None = None) -> R4Tensor:
+    """binade_rice_to_r4 on device planes; allocates nib / esc unless `out`."""
+    if not planes.sm.is_cuda:
+        raise ValueError("rice_to_r4 takes device planes (RicePlanes.to('cuda'))")
+    dev = planes.sm.device
+    if out is None:
+        nib = torch.empty(planes.rows * planes.cols // 2, dtype=torch.uint8, device=dev)
+        esc = torch.empty(max(planes.n_esc, 1), dtype=torch.int32, device=dev)
+    else:
+        nib, esc = out.nib, out.esc
+    d_in = planes.desc()
+    d_out = R4Desc()
+    d_out.nib = nib.data_ptr()
+    d_out.esc = esc.data_ptr()
+    _call("binade_rice_to_r4", ctypes.byref(d_in), ctypes.byref(d_out),
+          _ptr(status), _stream(stream))
+    lut = bytes(d_out.lut)
+    if out is not None:
+        out.lut = lut
+        return out
+    return R4Tensor(planes.rows, planes.cols, lut, planes.sm, nib,
+                    planes.esc_pre, esc, planes.n_esc)
+
+
+def _y(rows_shape, y_dtype, device, y):
+    if y is not None:
+        return y
+    dt = torch.float32 if y_dtype == F32 else torch.bfloat16
+    return torch.empty(rows_shape, dtype=dt, device=device)
+
+
+def _dtype_code(out_dtype) -> int:
+    if out_dtype in (torch.float32, F32, "f32"):
+        return F32
+    if out_dtype in (torch.bfloat16, BF16, "bf16"):
+        return BF16
+    raise ValueError(out_dtype)
+
+
+def r4_gemv(w: R4Tensor, x: torch.Tensor, out_dtype=torch.float32,
+            y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    code = _dtype_code(out_dtype)
+    x = _bits16(x)
+    y = _y((w.rows,), code, x.device, y)
+    d = w.desc()
+    _call("binade_r4_gemv", ctypes.byref(d), _ptr(x), _ptr(y), code, _stream(stream))
+    return y
+
+
+def bf16_gemv(w: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32,
+              y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    code = _dtype_code(out_dtype)
+    w = _bits16(w)
+    x = _bits16(x)
+    rows, cols = w.shape
+    y = _y((rows,), code, x.device, y)
+    _call("binade_bf16_gemv", _ptr(w), rows, cols, _ptr(x), _ptr(y), code,
+          _stream(stream))
+    return y
+
+
+def unpack(w: R4Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device=w.nib.device)
+    d = w.desc()
+    _call("binade_unpack", ctypes.byref(d), _ptr(out), _stream(stream))
+    return out
+
+
+def r4_gemm(w: R4Tensor, x: torch.Tensor, out_dtype=torch.float32,
+            y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    code = _dtype_code(out_dtype)
+    x = _bits16(x)
+    m = x.shape[0]
+    y = _y((m, w.rows), code, x.device, y)
+    d = w.desc()
+    _call("binade_r4_gemm", ctypes.byref(d), _ptr(x), m, x.stride(0), _ptr(y),
+          y.stride(0), code, _stream(stream))
+    return y
+
+
+def bf16_gemm(w: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32,
+              y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    code = _dtype_code(out_dtype)
+    w = _bits16(w)
+    x = _bits16(x)
+    rows, cols = w.shape
+    m = x.shape[0]
+    y = _y((m, rows), code, x.device, y)
+    _call("binade_bf16_gemm", _ptr(w), rows, cols, _ptr(x), m, x.stride(0),
+          _ptr(y), y.stride(0), code, _stream(stream))
+    return y
+
+
+def r4_moe_gemv(experts: R4Tensor, n_experts: int, x: torch.Tensor,
+                idx: torch.Tensor, x_per_slot: bool = False,
+                out_dtype=torch.float32, y: torch.Tensor | None = None,
+                status: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    code = _dtype_code(out_dtype)
+    x = _bits16(x)
+    idx = idx.contiguous()
+    n_tokens, top_k = idx.shape
+    N = experts.rows // n_experts
+    y = _y((n_tokens * top_k, N), code, x.device, y)
+    d = experts.desc()
+    _call("binade_r4_moe_gemv", ctypes.byref(d), n_experts, _ptr(x),
+          1 if x_per_slot else 0, _ptr(idx), n_tokens, top_k, _ptr(y), code,
+          _ptr(status), _stream(stream))
+    return y
+
+
+def bf16_moe_gemv(experts: torch.Tensor, n_experts: int, x: torch.Tensor,
+                  idx: torch.Tensor, x_per_slot: bool = False,
+                  out_dtype=torch.float32, y: torch.Tensor | None = None,
+                  status: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    code = _dtype_code(out_dtype)
+    experts = _bits16(experts)
+    x = _bits16(x)
+    idx = idx.contiguous()
+    rows, cols = experts.shape
+    N = rows // n_experts
+    n_tokens, top_k = idx.shape
+    y = _y((n_tokens * top_k, N), code, x.device, y)
+    _call("binade_bf16_moe_gemv", _ptr(experts), n_experts, N, cols, _ptr(x),
+          1 if x_per_slot else 0, _ptr(idx), n_tokens, top_k, _ptr(y), code,
+          _ptr(status), _stream(stream))
+    return y

@@ -1,0 +1,337 @@
+// Batch-1 matrix-vector product on R4 weights, its bf16-weight twin, and the
+// R4 -> bf16 unpack.
+//
+// "Binade" package page (pypi.org/project/binade), "Results": the batch-1
+// matvec on R4 runs at BF16's bandwidth efficiency, so it is faster per
+// token by the byte ratio; "How it works": R4 keeps every rank in 4 bits
+// with rare escapes, and the matvec adds its products in one fixed order so
+// its outputs equal the BF16 computation's bit for bit.
+//
+// Order (shared with the twin, independent of the launch shape): K is cut
+// into lane tiles of 32 columns; tile j belongs to slot j mod 64; slot l's
+// two fp32 sums (even / odd columns) start at +0.0 and take its tiles in
+// increasing j with one fma per column; then slot values a0 + a1 are reduced
+// by p[l] += p[l+s] for s = 32..1. One wave of 64 lanes is exactly one slot
+// per lane, so a wave pass over 2048 columns is one row-chunk.
+//
+// Mapping on gfx950: a wave owns R rows and walks their chunks; lane l reads
+// its tile's 32 sign/mantissa bytes (two 16-byte loads) and 16 nibble bytes
+// (one 16-byte load) per row, rebuilds the 32 fp32 weights in registers with
+// v_perm_b32 lookups into the 16-byte table, and shares one x tile (four
+// 16-byte loads, converted once) across the R rows. Escapes are patched from
+// the chunk's side list by a uniform scalar loop before the weights are
+// assembled. The slot tree is five xor shuffles after the last chunk.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+
+#include "binade.h"
+#include "device_common.h"
+
+namespace binade {
+namespace {
+
+using namespace dev;
+
+struct GemvArgs {
+  const uint8_t* sm;       // R4 sign/mantissa plane (or bf16 weights, twin)
+  const uint8_t* nib;
+  const uint32_t* esc_pre;
+  const uint32_t* esc;
+  const uint16_t* x;
+  void* y;
+  int64_t rows;
+  int32_t cols;
+  int32_t y_bf16;
+  uint32_t n_esc;
+  uint32_t lut0, lut1, lut2, lut3;
+};
+
+// fma 4 weights of one split group into the two running sums, columns
+// 4d .. 4d+3 of the tile (4d is even).
+__device__ __forceinline__ void fma_group(uint32_t H, uint32_t Lo,
+                                          const float* xg, float& a0,
+                                          float& a1) {
+  a0 = __builtin_fmaf(weight_f32<0>(H, Lo), xg[0], a0);
+  a1 = __builtin_fmaf(weight_f32<1>(H, Lo), xg[1], a1);
+  a0 = __builtin_fmaf(weight_f32<2>(H, Lo), xg[2], a0);
+  a1 = __builtin_fmaf(weight_f32<3>(H, Lo), xg[3], a1);
+}
+
+__device__ __forceinline__ void store_y(const GemvArgs& a, int64_t row,
+                                        float v) {
+  if (a.y_bf16)
+    static_cast<uint16_t*>(a.y)[row] = to_bf16_rne(v);
+  else
+    static_cast<float*>(a.y)[row] = v;
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void r4_gemv_kernel(GemvArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 =
+      uniform64((static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) +
+                 (threadIdx.x >> 6)) * R);
+  if (row0 >= a.rows) return;
+  const int J = a.cols >> 5;
+  const int C = (J + 63) >> 6;
+  const Lut L{a.lut0, a.lut1, a.lut2, a.lut3};
+
+  float acc0[R], acc1[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc0[r] = acc1[r] = 0.0f;
+
+  for (int j = 0; j < C; ++j) {
+    const int t = j * 64 + lane;
+    const bool active = t < J;
+    uint4 s0[R], s1[R], nb[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = row0 + r;
+      if (active && row < a.rows) {
+        const uint4* ps = reinterpret_cast<const uint4*>(a.sm + row * a.cols + 32 * t);
+        s0[r] = ps[0];
+        s1[r] = ps[1];
+        nb[r] = *reinterpret_cast<const uint4*>(a.nib + row * (a.cols >> 1) + 16 * t);
+      } else {
+        s0[r] = s1[r] = nb[r] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    float xf[32];
+    if (active) load_x_tile(a.x, t, xf);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = row0 + r;
+      if (row >= a.rows) continue;  // uniform
+      uint32_t E[8];
+      tile_exponents(nb[r], L, a.esc_pre, a.esc, a.n_esc, row * C + j, lane, E);
+      if (active) {
+        const uint32_t S[8] = {s0[r].x, s0[r].y, s0[r].z, s0[r].w,
+                               s1[r].x, s1[r].y, s1[r].z, s1[r].w};
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          uint32_t H, Lo;
+          split4(S[d], E[d], H, Lo);
+          fma_group(H, Lo, xf + 4 * d, acc0[r], acc1[r]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + r;
+    const float p = slot_tree(acc0[r] + acc1[r]);
+    if (lane == 0 && row < a.rows) store_y(a, row, p);
+  }
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void bf16_gemv_kernel(GemvArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 =
+      uniform64((static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) +
+                 (threadIdx.x >> 6)) * R);
+  if (row0 >= a.rows) return;
+  const int J = a.cols >> 5;
+  const int C = (J + 63) >> 6;
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.sm);
+
+  float acc0[R], acc1[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc0[r] = acc1[r] = 0.0f;
+
+  for (int j = 0; j < C; ++j) {
+    const int t = j * 64 + lane;
+    if (t >= J) continue;  // only in the last chunk
+    uint4 wv[R][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = row0 + r;
+      const uint4* p = reinterpret_cast<const uint4*>(W + row * a.cols + 32 * t);
+      if (row < a.rows) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) wv[r][v] = p[v];
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) wv[r][v] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    float xf[32];
+    load_x_tile(a.x, t, xf);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t w[4] = {wv[r][v].x, wv[r][v].y, wv[r][v].z, wv[r][v].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc0[r] = __builtin_fmaf(bf16_lo(w[e]), xf[8 * v + 2 * e], acc0[r]);
+          acc1[r] = __builtin_fmaf(bf16_hi(w[e]), xf[8 * v + 2 * e + 1], acc1[r]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + r;
+    const float p = slot_tree(acc0[r] + acc1[r]);
+    if (lane == 0 && row < a.rows) store_y(a, row, p);
+  }
+}
+
+// One wave per row-chunk; lane l rebuilds its tile's 32 bf16 patterns.
+__global__ __launch_bounds__(256) void r4_unpack_kernel(GemvArgs a,
+                                                        uint16_t* out) {
+  const int lane = threadIdx.x & 63;
+  const int J = a.cols >> 5;
+  const int C = (J + 63) >> 6;
+  const int64_t c = uniform64(static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) +
+                              (threadIdx.x >> 6));
+  if (c >= a.rows * C) return;
+  const int64_t row = c / C;
+  const int j = static_cast<int>(c - row * C);
+  const int t = j * 64 + lane;
+  const bool active = t < J;
+  const Lut L{a.lut0, a.lut1, a.lut2, a.lut3};
+  uint4 s0 = make_uint4(0, 0, 0, 0), s1 = s0, nb = s0;
+  if (active) {
+    const uint4* ps = reinterpret_cast<const uint4*>(a.sm + row * a.cols + 32 * t);
+    s0 = ps[0];
+    s1 = ps[1];
+    nb = *reinterpret_cast<const uint4*>(a.nib + row * (a.cols >> 1) + 16 * t);
+  }
+  uint32_t E[8];
+  tile_exponents(nb, L, a.esc_pre, a.esc, a.n_esc, c, lane, E);
+  if (!active) return;
+  const uint32_t S[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  uint32_t o[16];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    uint32_t H, Lo;
+    split4(S[d], E[d], H, Lo);
+    o[2 * d] = weight_pair_bf16<0>(H, Lo);
+    o[2 * d + 1] = weight_pair_bf16<2>(H, Lo);
+  }
+  uint4* po = reinterpret_cast<uint4*>(out + row * a.cols + 32 * t);
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    po[v] = make_uint4(o[4 * v], o[4 * v + 1], o[4 * v + 2], o[4 * v + 3]);
+}
+
+uint32_t pack_lut(const uint8_t* l, int q) {
+  return uint32_t(l[4 * q]) | (uint32_t(l[4 * q + 1]) << 8) |
+         (uint32_t(l[4 * q + 2]) << 16) | (uint32_t(l[4 * q + 3]) << 24);
+}
+
+int32_t check_r4(const binade_r4* w) {
+  if (w == nullptr || w->rows < 0 || w->cols <= 0) return BINADE_EINVAL;
+  if (w->cols % 32 != 0) return BINADE_EUNSUPPORTED;
+  if (w->cols > (1 << 30)) return BINADE_EUNSUPPORTED;
+  if (w->rows == 0) return BINADE_OK;
+  if (w->sm == nullptr || w->nib == nullptr || w->esc_pre == nullptr ||
+      (w->n_esc > 0 && w->esc == nullptr))
+    return BINADE_EINVAL;
+  if (!aligned16(w->sm) || !aligned16(w->nib)) return BINADE_EUNSUPPORTED;
+  if (w->n_esc > 0xFFFFFFFFull) return BINADE_EUNSUPPORTED;
+  return BINADE_OK;
+}
+
+GemvArgs args_from_r4(const binade_r4* w) {
+  GemvArgs a{};
+  a.sm = w->sm;
+  a.nib = w->nib;
+  a.esc_pre = w->esc_pre;
+  a.esc = w->esc;
+  a.rows = w->rows;
+  a.cols = static_cast<int32_t>(w->cols);
+  a.n_esc = static_cast<uint32_t>(w->n_esc);
+  a.lut0 = pack_lut(w->lut, 0);
+  a.lut1 = pack_lut(w->lut, 1);
+  a.lut2 = pack_lut(w->lut, 2);
+  a.lut3 = pack_lut(w->lut, 3);
+  return a;
+}
+
+// Rows per wave: enough waves to cover the CUs, more rows per wave (x reuse,
+// more loads in flight) when the matrix is tall.
+int rows_per_wave(int64_t rows) {
+  const char* env = getenv("BINADE_GEMV_ROWS_PER_WAVE");
+  if (env != nullptr) {
+    const int r = atoi(env);
+    if (r == 1 || r == 2 || r == 4) return r;
+  }
+  if (rows >= 8192) return 4;
+  if (rows >= 4096) return 2;
+  return 1;
+}
+
+int32_t launch_gemv(const GemvArgs& a, bool r4, hipStream_t stream) {
+  const int R = rows_per_wave(a.rows);
+  const int64_t waves = (a.rows + R - 1) / R;
+  const dim3 grid(static_cast<uint32_t>((waves + 3) / 4));
+  const dim3 block(256);
+  if (r4) {
+    if (R == 4) hipLaunchKernelGGL(r4_gemv_kernel<4>, grid, block, 0, stream, a);
+    else if (R == 2) hipLaunchKernelGGL(r4_gemv_kernel<2>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(r4_gemv_kernel<1>, grid, block, 0, stream, a);
+  } else {
+    if (R == 4) hipLaunchKernelGGL(bf16_gemv_kernel<4>, grid, block, 0, stream, a);
+    else if (R == 2) hipLaunchKernelGGL(bf16_gemv_kernel<2>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(bf16_gemv_kernel<1>, grid, block, 0, stream, a);
+  }
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace binade
+
+using namespace binade;
+
+extern "C" int32_t binade_r4_gemv(const binade_r4* w, const uint16_t* x,
+                                  void* y, int32_t y_dtype, void* stream) {
+  int32_t s = check_r4(w);
+  if (s != BINADE_OK) return s;
+  if (y_dtype != BINADE_F32 && y_dtype != BINADE_BF16) return BINADE_EINVAL;
+  if (w->rows == 0) return BINADE_OK;
+  if (x == nullptr || y == nullptr) return BINADE_EINVAL;
+  if (!aligned16(x)) return BINADE_EUNSUPPORTED;
+  GemvArgs a = args_from_r4(w);
+  a.x = x;
+  a.y = y;
+  a.y_bf16 = y_dtype == BINADE_BF16;
+  return launch_gemv(a, true, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t binade_bf16_gemv(const uint16_t* w, int64_t rows,
+                                    int64_t cols, const uint16_t* x, void* y,
+                                    int32_t y_dtype, void* stream) {
+  if (rows < 0 || cols <= 0) return BINADE_EINVAL;
+  if (cols % 32 != 0 || cols > (1 << 30)) return BINADE_EUNSUPPORTED;
+  if (y_dtype != BINADE_F32 && y_dtype != BINADE_BF16) return BINADE_EINVAL;
+  if (rows == 0) return BINADE_OK;
+  if (w == nullptr || x == nullptr || y == nullptr) return BINADE_EINVAL;
+  if (!aligned16(w) || !aligned16(x)) return BINADE_EUNSUPPORTED;
+  GemvArgs a{};
+  a.sm = reinterpret_cast<const uint8_t*>(w);
+  a.rows = rows;
+  a.cols = static_cast<int32_t>(cols);
+  a.x = x;
+  a.y = y;
+  a.y_bf16 = y_dtype == BINADE_BF16;
+  return launch_gemv(a, false, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t binade_unpack(const binade_r4* w, uint16_t* out,
+                                 void* stream) {
+  int32_t s = check_r4(w);
+  if (s != BINADE_OK) return s;
+  if (w->rows == 0) return BINADE_OK;
+  if (out == nullptr) return BINADE_EINVAL;
+  if (!aligned16(out)) return BINADE_EUNSUPPORTED;
+  GemvArgs a = args_from_r4(w);
+  const int64_t chunks = w->rows * ((w->cols / 32 + 63) / 64);
+  const dim3 grid(static_cast<uint32_t>((chunks + 3) / 4));
+  hipLaunchKernelGGL(r4_unpack_kernel, grid, dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a, out);
+  return launch_status();
+}

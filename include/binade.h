@@ -1,0 +1,243 @@
+/*
+ * binade.h -- C ABI of libbinade, the Binade hot path on MI355X (gfx950).
+ *
+ * What it computes (the pages):
+ *   "Binade" package page (pypi.org/project/binade), intro: a BF16 weight
+ *   keeps its sign and mantissa as one raw byte; its 8-bit exponent is
+ *   replaced by its frequency rank in a per-tensor table, stored on disk in
+ *   Rice codes; at load the ranks become a 4-bit runtime layout that the
+ *   kernels read during inference, and outputs are bit-identical.
+ *   Same page, "How it works": one table per tensor (no exponent locality);
+ *   format 2 = Rice codes; runtime layout R4 = every rank in 4 bits with rare
+ *   escapes, converted by a GPU kernel at load; matvec, MoE expert gather and
+ *   GEMM add their products in one fixed order.
+ *
+ * Conventions
+ *   - Every function returns a binade_status (0 = OK). Nothing aborts or
+ *     throws across this ABI.
+ *   - The caller owns every buffer. Host functions take host pointers;
+ *     device functions take device pointers (e.g. torch tensors' data_ptr())
+ *     inside the descriptors and never allocate device memory.
+ *   - Device functions check their arguments on the host, enqueue kernels on
+ *     the given hipStream_t (NULL = the default stream) and return; results
+ *     and the device status word are valid after the stream is synchronised.
+ *   - Matrices are row-major [rows = N outputs, cols = K inputs], like a
+ *     linear layer's weight. The device paths require cols % 32 == 0 and
+ *     16-byte aligned planes, else BINADE_EUNSUPPORTED.
+ *   - Row-chunks: each row is cut into chunks of BINADE_CHUNK columns (the
+ *     last one of a row may be shorter); chunk c of row i has flat index
+ *     i * ceil(cols / BINADE_CHUNK) + c. Format 2 stores one unary-bit anchor
+ *     and one escape prefix per row-chunk; R4 reuses the escape prefix.
+ *
+ * Format 2 (on-disk layout, readings of the pages stated in the design doc):
+ *   sm      u8[rows*cols]   (sign << 7) | mantissa
+ *   unary   u32 words       per weight in row-major order: q = rank >> k zero
+ *                           bits, then a one; bit p is bit p%32 of word p/32
+ *   rem     u32 words       the k low bits of the rank of weight i at bits
+ *                           i*k .. i*k+k-1, least significant first
+ *   anchor  u64[chunks+1]   unary bit position of each row-chunk's first
+ *                           weight; the last entry = total unary bits
+ *   esc_pre u32[chunks+1]   weights with rank >= 15 before each row-chunk;
+ *                           the last entry = total
+ * R4 (runtime layout):
+ *   sm      the same plane as format 2 (shared, never copied)
+ *   nib     u8[rows*cols/2] min(rank, 15); in each row the columns go in
+ *                           groups of 8; group g owns bytes 4g..4g+3 of the
+ *                           row, byte b = col 8g+b (low nibble) | col 8g+4+b
+ *                           (high nibble) << 4
+ *   lut     u8[16]          exponent of ranks 0..14; lut[15] unused
+ *   esc     u32[n_esc]      one entry per weight of rank >= 15, row-major:
+ *                           (exponent << 16) | (column - BINADE_CHUNK*chunk)
+ *   esc_pre the same array as format 2's
+ */
+#ifndef BINADE_H
+#define BINADE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BINADE_CHUNK 2048
+
+typedef enum binade_status {
+  BINADE_OK = 0,
+  BINADE_EINVAL = -1,       /* bad argument: null pointer, size, shape */
+  BINADE_ECORRUPT = -2,     /* inconsistent planes found on the host */
+  BINADE_EUNSUPPORTED = -3, /* shape or alignment the kernels do not take */
+  BINADE_EHIP = -4,         /* a HIP runtime call failed */
+  BINADE_ENOSPACE = -5      /* an output buffer is smaller than needed */
+} binade_status;
+
+/* Output element type of the products. */
+typedef enum binade_dtype {
+  BINADE_F32 = 0,     /* fp32 as accumulated */
+  BINADE_BF16 = 1     /* the fp32 result rounded to bf16, nearest-even */
+} binade_dtype;
+
+/* Device status word bits (set with atomic OR by the kernels; the caller
+ * clears the word before the call and reads it after synchronising). */
+#define BINADE_DEV_CORRUPT_STREAM 0x1u  /* a chunk's unary bits do not hold
+                                            its weight count, or a rank is not
+                                            in the table */
+#define BINADE_DEV_BAD_INDEX 0x2u       /* an expert index is out of range */
+#define BINADE_DEV_CORRUPT_ESC 0x4u     /* escape prefix / entries disagree */
+
+/* Per-tensor exponent table. */
+typedef struct binade_table {
+  uint32_t n;                /* distinct exponents present, 1..256 */
+  uint32_t k;                /* Rice parameter for this table, 0..7 */
+  uint8_t exp_of_rank[256];  /* exponent of rank r (r < n); 0 beyond n */
+  uint16_t rank_of_exp[256]; /* rank of exponent e; 0xFFFF if absent */
+  uint64_t count_of_rank[256];
+} binade_table;
+
+/* Format 2 descriptor. Pointers are host memory for binade_pack_rice and
+ * device memory for binade_rice_to_r4. */
+typedef struct binade_rice {
+  int64_t rows, cols;
+  uint32_t k, n;
+  uint8_t exp_of_rank[256];
+  uint8_t *sm;
+  uint32_t *unary;
+  uint64_t unary_bits;
+  uint64_t unary_words;   /* words the buffer holds (>= binade_rice_sizes) */
+  uint32_t *rem;
+  uint64_t rem_words;
+  uint64_t *anchor;       /* chunks + 1 */
+  uint32_t *esc_pre;      /* chunks + 1 */
+  uint64_t n_esc;
+} binade_rice;
+
+/* Sizes a caller allocates for format 2 and R4. */
+typedef struct binade_sizes {
+  uint64_t n_weights;     /* rows * cols */
+  uint64_t n_chunks;      /* rows * ceil(cols / BINADE_CHUNK) */
+  uint64_t unary_bits;    /* sum over ranks of count * ((r >> k) + 1) */
+  uint64_t unary_words;   /* u32 words to allocate (bits rounded up + 2) */
+  uint64_t rem_words;     /* u32 words to allocate (rows*cols*k bits + 2) */
+  uint64_t n_esc;         /* weights with rank >= 15 */
+  uint64_t nib_bytes;     /* rows * cols / 2 */
+} binade_sizes;
+
+/* R4 descriptor (device pointers). */
+typedef struct binade_r4 {
+  int64_t rows, cols;
+  uint8_t lut[16];
+  const uint8_t *sm;
+  uint8_t *nib;
+  const uint32_t *esc_pre;
+  uint32_t *esc;
+  uint64_t n_esc;
+} binade_r4;
+
+/* Text for a status code (static storage). */
+const char *binade_status_str(int32_t status);
+/* The last HIP error code seen by a device call on this thread (0 if none). */
+int32_t binade_last_hip_error(void);
+
+/* ---------------------------------------------------------------- host */
+
+/* Histogram of the exponent field of n bf16 values (host), ranks ordered by
+ * count descending and exponent ascending on ties, and the Rice k with the
+ * fewest bits (ties to the smaller k). "Binade" package page, intro and
+ * "How it works" (one frequency-rank table per tensor).
+ * EINVAL: w or out null, n <= 0. */
+int32_t binade_build_table(const uint16_t *w, int64_t n, binade_table *out);
+
+/* Buffer sizes for a rows x cols tensor under table t (host, closed form).
+ * EINVAL: null pointers, rows/cols <= 0, table n or k out of range. */
+int32_t binade_sizes_of(const binade_table *t, int64_t rows, int64_t cols,
+                        binade_sizes *out);
+
+/* Format 2 pack of the bf16 matrix w [rows, cols] (host). out->sm, unary,
+ * rem (if t->k > 0), anchor and esc_pre point at caller buffers of at least
+ * binade_sizes_of() entries, with out->unary_words / rem_words giving their
+ * capacity; fills the scalar fields. Byte-identical to the oracle's pack.
+ * "Binade" package page, intro and "How it works" (format 2 = Rice codes).
+ * EINVAL: bad pointers or shape, or a weight whose exponent is not in t.
+ * ENOSPACE: a plane's capacity is too small. */
+int32_t binade_pack_rice(const uint16_t *w, int64_t rows, int64_t cols,
+                         const binade_table *t, binade_rice *out);
+
+/* -------------------------------------------------------------- device */
+
+/* Format 2 -> R4 on the GPU ("Binade" package page, "How it works": a GPU
+ * kernel turns the file format into R4 at load). in: device planes of a
+ * format 2 tensor (all of in's fields filled as binade_pack_rice leaves
+ * them, unary/rem buffers at least binade_sizes_of() words). out: rows, cols
+ * are set from in; out->sm and out->esc_pre are set to in->sm and
+ * in->esc_pre; lut is filled; the kernel writes out->nib (nib_bytes) and
+ * out->esc (n_esc entries), which the caller allocates. dev_status: device
+ * u32 or NULL; the kernel ORs BINADE_DEV_CORRUPT_* into it when a chunk's
+ * bits are inconsistent (its outputs are then unspecified).
+ * EUNSUPPORTED: cols % 32 != 0 or misaligned planes. */
+int32_t binade_rice_to_r4(const binade_rice *in, binade_r4 *out,
+                          uint32_t *dev_status, void *stream);
+
+/* R4 -> bf16 bits [rows, cols] on the GPU (the rebuild path; "Binade"
+ * package page, "Use": unpack restores the original BF16 bit for bit). */
+int32_t binade_unpack(const binade_r4 *w, uint16_t *out, void *stream);
+
+/* Batch-1 product y[N] = W[N,K] x[K] with W in R4, every weight rebuilt in
+ * registers ("Binade" package page, "Results" and "How it works": the R4
+ * matvec). x: device bf16[K]. y: device fp32[N] or bf16[N] per y_dtype.
+ * Summation order (fixed, independent of launch shape): K is cut into tiles
+ * of 32; tile j goes to slot j mod 64; each slot keeps fp32 sums a0 (even
+ * columns) and a1 (odd columns) from +0.0, fused multiply-adding its tiles
+ * in increasing j and columns in increasing order; slot value a0 + a1; then
+ * p[l] += p[l+s] for s = 32, 16, 8, 4, 2, 1; y = p[0]. */
+int32_t binade_r4_gemv(const binade_r4 *w, const uint16_t *x, void *y,
+                       int32_t y_dtype, void *stream);
+
+/* The same product and order with W given as plain bf16 [N, K] (device):
+ * the exactness twin and the speed reference. */
+int32_t binade_bf16_gemv(const uint16_t *w, int64_t rows, int64_t cols,
+                         const uint16_t *x, void *y, int32_t y_dtype,
+                         void *stream);
+
+/* Prompt GEMM Y[M,N] = X[M,K] W[N,K]^T with W in R4, tiles decoded into LDS
+ * and multiplied on bf16 MFMA with fp32 accumulation ("Binade" package page,
+ * "Results" and "Limitations": prompt processing with fused GEMM). X: device
+ * bf16 with row stride ldx (elements); Y: fp32 or bf16 with row stride ldy.
+ * Order: per output, one fp32 accumulator, K taken in blocks of 32 in
+ * increasing order, each block one bf16 MFMA step. */
+int32_t binade_r4_gemm(const binade_r4 *w, const uint16_t *x, int64_t m,
+                       int64_t ldx, void *y, int64_t ldy, int32_t y_dtype,
+                       void *stream);
+
+/* The same GEMM with plain bf16 W [N, K] (device). */
+int32_t binade_bf16_gemm(const uint16_t *w, int64_t rows, int64_t cols,
+                         const uint16_t *x, int64_t m, int64_t ldx, void *y,
+                         int64_t ldy, int32_t y_dtype, void *stream);
+
+/* MoE expert-gather GEMV ("Binade" package page, "How it works": the MoE
+ * expert gather in the matvec's order; "Limitations": fused kernels cover
+ * every expert product). experts: R4 stack of n_experts matrices [N, K]
+ * stored as one [n_experts*N, K] tensor with one table. idx: device
+ * int32[n_tokens*top_k]. x: device bf16 [n_tokens, K] (x_per_slot = 0) or
+ * [n_tokens*top_k, K] (x_per_slot = 1). y: [n_tokens*top_k, N], row p =
+ * expert idx[p] times its input, in the binade_r4_gemv order. Experts chosen
+ * by several pairs are read from HBM once per launch. An index outside
+ * [0, n_experts) sets BINADE_DEV_BAD_INDEX in dev_status (if not NULL) and
+ * leaves that output row as zeros. */
+int32_t binade_r4_moe_gemv(const binade_r4 *experts, int32_t n_experts,
+                           const uint16_t *x, int32_t x_per_slot,
+                           const int32_t *idx, int64_t n_tokens,
+                           int32_t top_k, void *y, int32_t y_dtype,
+                           uint32_t *dev_status, void *stream);
+
+/* The same gather with plain bf16 experts [n_experts*N, K] (device). */
+int32_t binade_bf16_moe_gemv(const uint16_t *experts, int32_t n_experts,
+                             int64_t rows_per_expert, int64_t cols,
+                             const uint16_t *x, int32_t x_per_slot,
+                             const int32_t *idx, int64_t n_tokens,
+                             int32_t top_k, void *y, int32_t y_dtype,
+                             uint32_t *dev_status, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BINADE_H */

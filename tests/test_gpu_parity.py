@@ -1,0 +1,273 @@
+"""GPU parity: every device entry point through the C-ABI against the oracle
+(and against its bf16 twin), on seeded inputs at sizes the oracle finishes
+in seconds, spanning several tiles, chunks and ragged tails.
+
+Bars: bit-exact for R4 / escapes / unpacked bits; matvec and expert gather
+bit-identical to the oracle's replay of the fixed fp32 order and to the
+bf16-weight twin, and within 1e-2 (relative to sum |w x|) of the fp64 sum.
+NaN outputs compare as NaN (payload not compared)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_gemv_tensor_amd import binade as B
+from decode_gemv_tensor_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def bits_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def spec(rows, cols, sigma=0.02, seed=0, frac=1e-3, scale=20.0, count=0):
+    return synth.TensorSpec("t", rows, cols, sigma, seed, outlier_frac=frac,
+                            outlier_scale=scale, outlier_count=count)
+
+
+def to_r4(w_cpu: torch.Tensor, status=None):
+    planes = B.pack_rice(w_cpu).to(DEV)
+    r4 = B.rice_to_r4(planes, status=status)
+    return planes, r4
+
+
+def same_f32(a: np.ndarray, b: np.ndarray) -> bool:
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    na, nb = np.isnan(a), np.isnan(b)
+    return bool(np.array_equal(na, nb) and
+                np.array_equal(a[~na].view(np.uint32), b[~nb].view(np.uint32)))
+
+
+def within_f64(y, w_bits, x_bits):
+    y64 = oracle.gemv_f64(w_bits, x_bits)
+    wf = (w_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    xf = (x_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    scale = np.abs(wf) @ np.abs(xf)
+    return bool(np.all(np.abs(np.asarray(y, np.float64) - y64) <= 1e-2 * scale + 1e-30))
+
+
+GEMV_SHAPES = [(1024, 1024, 0.02, 0, 0.0, 1.0, 16, 50.0),   # single 1024 tensor
+               (37, 96, 0.02, 1, 1e-2, 1e4, 0, 1.0),          # ragged rows, 3 tiles
+               (5, 4160, 0.02, 2, 5e-3, 1e4, 0, 1.0),         # ragged chunk 4096+64
+               (300, 3072, 0.02, 3, 1e-3, 20.0, 0, 1.0),      # Llama q/o width
+               (64, 8192, 0.02, 4, 1e-3, 20.0, 0, 1.0),       # down width
+               (19, 15360, 0.015, 5, 0.0, 1.0, 0, 1.0),       # 12B down width
+               (4100, 256, 0.015, 6, 0.0, 1.0, 0, 1.0)]       # short rows, many
+
+
+@pytest.mark.parametrize("shape", GEMV_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_rice_to_r4_is_byte_exact_and_unpacks(shape):
+    rows, cols, sigma, seed, frac, scale, count, cscale = shape
+    sp = spec(rows, cols, sigma, seed, frac, scale if count == 0 else cscale, count)
+    w = synth.normal_bf16(sp)
+    wn = bits_np(w)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    planes, r4 = to_r4(w, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ref = oracle.make_r4(wn, oracle.build_table(wn))
+    assert bytes(bytearray(r4.lut)) == bytes(ref["lut"])
+    assert np.array_equal(r4.nib.cpu().numpy(), ref["nib"].reshape(-1))
+    assert r4.n_esc == ref["n_esc"]
+    if r4.n_esc:
+        assert np.array_equal(r4.esc[: r4.n_esc].cpu().numpy().view(np.uint32), ref["esc"])
+    assert np.array_equal(r4.esc_pre.cpu().numpy().view(np.uint32), ref["esc_pre"])
+    assert np.array_equal(bits_np(B.unpack(r4)), wn)
+
+
+@pytest.mark.parametrize("shape", GEMV_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_r4_gemv_matches_oracle_twin_and_f64(shape):
+    rows, cols, sigma, seed, frac, scale, count, cscale = shape
+    sp = spec(rows, cols, sigma, seed, frac, scale if count == 0 else cscale, count)
+    w = synth.normal_bf16(sp)
+    wn = bits_np(w)
+    x = synth.vector_bf16(cols, 100 + seed)
+    xn = bits_np(x)
+    _, r4 = to_r4(w)
+    xd = x.to(DEV)
+    y = B.r4_gemv(r4, xd).cpu().numpy()
+    y_twin = B.bf16_gemv(w.to(DEV), xd).cpu().numpy()
+    y_ref = oracle.gemv_replay(wn, xn)
+    assert same_f32(y, y_ref)
+    assert same_f32(y_twin, y_ref)
+    assert within_f64(y, wn, xn)
+    yb = bits_np(B.r4_gemv(r4, xd, out_dtype=torch.bfloat16))
+    assert np.array_equal(yb, oracle.f32_to_bf16(y_ref))
+
+
+@pytest.mark.parametrize("rpw", ["1", "2", "4"])
+def test_gemv_bits_do_not_depend_on_launch_shape(rpw, monkeypatch):
+    monkeypatch.setenv("BINADE_GEMV_ROWS_PER_WAVE", rpw)
+    w = synth.normal_bf16(spec(203, 3072, seed=9))
+    x = synth.vector_bf16(3072, 10)
+    _, r4 = to_r4(w)
+    y = B.r4_gemv(r4, x.to(DEV)).cpu().numpy()
+    assert same_f32(y, oracle.gemv_replay(bits_np(w), bits_np(x)))
+    y2 = B.bf16_gemv(w.to(DEV), x.to(DEV)).cpu().numpy()
+    assert same_f32(y2, y)
+
+
+def test_exhaustive_bit_patterns_through_the_device():
+    """All 65,536 bf16 patterns in one tensor (241 of 256 exponents escape):
+    Rice -> R4 on the device, unpack back bit for bit, matvec = oracle."""
+    w = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).reshape(64, 1024)
+    wn = bits_np(w)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    _, r4 = to_r4(w, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert r4.n_esc == 241 * 256
+    ref = oracle.make_r4(wn, oracle.build_table(wn))
+    assert np.array_equal(r4.nib.cpu().numpy(), ref["nib"].reshape(-1))
+    assert np.array_equal(r4.esc.cpu().numpy().view(np.uint32), ref["esc"])
+    assert np.array_equal(bits_np(B.unpack(r4)), wn)
+    x = synth.vector_bf16(1024, 11)
+    y = B.r4_gemv(r4, x.to(DEV)).cpu().numpy()
+    assert same_f32(y, oracle.gemv_replay(wn, bits_np(x)))
+
+
+@pytest.mark.parametrize("sigma,frac,scale", [(1.0, 0.0, 1.0), (1e-30, 0.01, 1e30),
+                                              (3e4, 0.0, 1.0), (0.02, 0.2, 1e6)])
+def test_other_rice_parameters(sigma, frac, scale):
+    """Tables whose best k is not 1 (wide or bimodal exponent spreads)."""
+    w = synth.normal_bf16(spec(48, 2080, sigma, 21, frac, scale))
+    wn = bits_np(w)
+    planes, r4 = to_r4(w)
+    ref = oracle.make_r4(wn, oracle.build_table(wn))
+    assert np.array_equal(r4.nib.cpu().numpy(), ref["nib"].reshape(-1))
+    assert np.array_equal(bits_np(B.unpack(r4)), wn)
+
+
+def test_corrupt_stream_sets_status():
+    w = synth.normal_bf16(spec(8, 2080, seed=12))
+    planes = B.pack_rice(w)
+    # flip a unary bit: the affected chunk holds one weight too many or few
+    bad_unary = planes.unary.clone()
+    bad_unary[5] ^= 1 << 7
+    bad = B.RicePlanes(planes.rows, planes.cols, planes.table, planes.sm,
+                       bad_unary, planes.rem, planes.anchor, planes.esc_pre,
+                       planes.unary_bits, planes.n_esc).to(DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.rice_to_r4(bad, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & B.DEV_CORRUPT_STREAM
+    # inconsistent escape prefix
+    esc_pre = planes.esc_pre.clone()
+    esc_pre[1] += 1
+    bad2 = B.RicePlanes(planes.rows, planes.cols, planes.table, planes.sm,
+                        planes.unary, planes.rem, planes.anchor, esc_pre,
+                        planes.unary_bits, planes.n_esc).to(DEV)
+    status.zero_()
+    B.rice_to_r4(bad2, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & B.DEV_CORRUPT_ESC
+
+
+# ---------------------------------------------------------- order pins on GPU
+BIG = 4096.0
+
+
+def _pin(K, terms):
+    w = np.zeros(K, np.float32)
+    x = np.zeros(K, np.float32)
+    for i, wi, xi in terms:
+        w[i], x[i] = wi, xi
+    wt = torch.tensor(w).to(torch.bfloat16).reshape(1, K)
+    xt = torch.tensor(x).to(torch.bfloat16)
+    _, r4 = to_r4(wt)
+    return (B.r4_gemv(r4, xt.to(DEV)).item(), B.bf16_gemv(wt.to(DEV), xt.to(DEV)).item())
+
+
+def test_order_pins_hold_on_the_device():
+    # same hand-derived cases as the oracle's pins
+    assert _pin(32, [(0, BIG, BIG), (2, 1, 1), (4, -BIG, BIG)]) == (0.0, 0.0)
+    assert _pin(32, [(1, BIG, BIG), (2, 1, 1), (4, -BIG, BIG)]) == (1.0, 1.0)
+    assert _pin(4096, [(0, BIG, BIG), (2050, 1, 1), (2052, -BIG, BIG)]) == (0.0, 0.0)
+    assert _pin(2048, [(0, BIG, BIG), (1024, 1, 1), (512, -BIG, BIG)]) == (0.0, 0.0)
+    w = -torch.ones(3, 64, dtype=torch.bfloat16)
+    x = torch.zeros(64, dtype=torch.bfloat16)
+    _, r4 = to_r4(w)
+    y = B.r4_gemv(r4, x.to(DEV)).cpu()
+    assert y.view(torch.int32).tolist() == [0, 0, 0]
+
+
+# ---------------------------------------------------------- MoE
+def _moe_case(E, N, K, n_tokens, top_k, seed, x_per_slot):
+    w = synth.normal_bf16(spec(E * N, K, 0.02, seed, 1e-3, 20.0))
+    idx = synth.topk_indices(n_tokens, top_k, E, seed + 1)
+    nx = n_tokens * top_k if x_per_slot else n_tokens
+    x = synth.vector_bf16(K, seed + 2, count=nx)
+    return w, idx, x
+
+
+@pytest.mark.parametrize("case", [(16, 40, 96, 3, 4, False), (128, 704, 2816, 8, 8, False),
+                                  (128, 2816, 704, 8, 8, True), (6, 33, 4160, 5, 2, True)],
+                         ids=["small", "gate_up", "down", "ragged"])
+def test_moe_matches_oracle_and_twin(case):
+    E, N, K, T, k, per_slot = case
+    w, idx, x = _moe_case(E, N, K, T, k, 40 + E, per_slot)
+    _, r4 = to_r4(w)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    y = B.r4_moe_gemv(r4, E, x.to(DEV), idx.to(DEV), x_per_slot=per_slot,
+                      status=status).cpu().numpy()
+    y2 = B.bf16_moe_gemv(w.to(DEV), E, x.to(DEV), idx.to(DEV),
+                         x_per_slot=per_slot).cpu().numpy()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ref = oracle.moe_replay(bits_np(w).reshape(E, N, K), bits_np(x), idx.numpy(), per_slot)
+    assert same_f32(y, ref)
+    assert same_f32(y2, ref)
+
+
+def test_moe_shared_experts_and_bad_index():
+    E, N, K = 8, 24, 64
+    w, _, x = _moe_case(E, N, K, 6, 2, 77, False)
+    idx = torch.tensor([[3, 3], [3, 1], [3, 0], [3, 3], [3, 5], [3, 3]], dtype=torch.int32)
+    _, r4 = to_r4(w)
+    y = B.r4_moe_gemv(r4, E, x.to(DEV), idx.to(DEV)).cpu().numpy()
+    ref = oracle.moe_replay(bits_np(w).reshape(E, N, K), bits_np(x), idx.numpy(), False)
+    assert same_f32(y, ref)
+    idx_bad = idx.clone()
+    idx_bad[2, 1] = E + 4
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    y = B.r4_moe_gemv(r4, E, x.to(DEV), idx_bad.to(DEV), status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & B.DEV_BAD_INDEX
+    assert torch.count_nonzero(y[5]).item() == 0
+
+
+# ---------------------------------------------------------- GEMM
+@pytest.mark.parametrize("mnk", [(16, 64, 64), (33, 200, 96), (128, 384, 3840), (5, 70, 4160)])
+def test_gemm_small_integers_exact_and_twin(mnk):
+    M, N, K = mnk
+    g = torch.Generator().manual_seed(M * N)
+    W = torch.randint(-4, 5, (N, K), generator=g).to(torch.bfloat16)
+    X = torch.randint(-4, 5, (M, K), generator=g).to(torch.bfloat16)
+    _, r4 = to_r4(W)
+    Y = B.r4_gemm(r4, X.to(DEV)).cpu()
+    Y2 = B.bf16_gemm(W.to(DEV), X.to(DEV)).cpu()
+    exact = X.to(torch.int64) @ W.to(torch.int64).T
+    assert torch.equal(Y.to(torch.int64), exact)
+    assert torch.equal(Y.view(torch.int32), Y2.view(torch.int32))
+
+
+@pytest.mark.parametrize("mnk", [(16, 128, 3840), (32, 96, 15360), (130, 64, 3840)])
+def test_gemm_random_twin_and_f64(mnk):
+    M, N, K = mnk
+    W = synth.normal_bf16(spec(N, K, 0.015, M, 1e-3, 20.0))
+    X = synth.vector_bf16(K, M + 1, count=M)
+    _, r4 = to_r4(W)
+    Y = B.r4_gemm(r4, X.to(DEV)).cpu()
+    Y2 = B.bf16_gemm(W.to(DEV), X.to(DEV)).cpu()
+    assert torch.equal(Y.view(torch.int32), Y2.view(torch.int32))
+    ref = X.double() @ W.double().T
+    scale = X.double().abs() @ W.double().abs().T
+    assert torch.all((Y.double() - ref).abs() <= 1e-2 * scale)
+    Yb = B.r4_gemm(r4, X.to(DEV), out_dtype=torch.bfloat16).cpu()
+    assert np.array_equal(bits_np(Yb), oracle.f32_to_bf16(Y.numpy()))

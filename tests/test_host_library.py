@@ -1,0 +1,147 @@
+"""CPU tests of libbinade's host half and of the ABI surface: the library
+loads, exports every symbol include/binade.h declares, its table and format 2
+pack are byte-identical to the oracle's, and bad arguments give the declared
+status codes. No device call is made here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_gemv_tensor_amd import binade as B
+from decode_gemv_tensor_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "binade.h")).read()
+    pat = r"^(?:int32_t|const char \*)\s*(binade_\w+)\("
+    return sorted(set(re.findall(pat, text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    declared = _header_functions()
+    assert len(declared) >= 13
+    L = B.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(B.EXPORTS) == declared
+
+
+def test_struct_layouts_match_header_sizes():
+    # natural alignment on x86-64 / gfx950: the ctypes mirrors must agree
+    assert ctypes.sizeof(B.Table) == 8 + 256 + 512 + 2048
+    assert ctypes.sizeof(B.RiceDesc) == 352
+    assert ctypes.sizeof(B.R4Desc) == 72
+    assert ctypes.sizeof(B.Sizes) == 56
+
+
+def _tensor(rows, cols, sigma=0.02, seed=0, frac=1e-3, scale=20.0):
+    spec = synth.TensorSpec("t", rows, cols, sigma, seed, outlier_frac=frac,
+                            outlier_scale=scale)
+    return synth.normal_bf16(spec)
+
+
+def _np(t):
+    return synth.bits(t).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("shape,sigma,frac,scale", [
+    ((1, 32), 0.02, 0.0, 1.0), ((64, 1024), 0.02, 1e-3, 20.0),
+    ((3, 2080), 0.02, 5e-3, 1e4), ((16, 4096 + 64), 1.0, 0.0, 1.0),
+    ((8, 256), 1e-30, 0.01, 1e30)])
+def test_table_and_pack_match_oracle_bytes(shape, sigma, frac, scale):
+    w = _tensor(*shape, sigma=sigma, seed=shape[1], frac=frac, scale=scale)
+    wn = _np(w)
+    t = B.build_table(w)
+    to = oracle.build_table(wn)
+    assert t.n == to["n"]
+    assert bytes(t.exp_of_rank)[: t.n] == bytes(to["exp_of_rank"][: t.n])
+    assert list(t.count_of_rank)[: t.n] == to["count_of_rank"][: t.n].tolist()
+    assert t.k == oracle.rice_k(to["count_of_rank"], to["n"])
+    for e in range(256):
+        r = t.rank_of_exp[e]
+        if r != 0xFFFF:
+            assert t.exp_of_rank[r] == e
+    p = B.pack_rice(w, t)
+    po = oracle.pack_rice(wn, to)
+    assert p.unary_bits == po["unary_bits"]
+    assert p.n_esc == po["n_esc"]
+    assert np.array_equal(p.sm.numpy(), po["sm"])
+    nu = po["unary"].size
+    assert np.array_equal(p.unary.numpy().view(np.uint32)[:nu], po["unary"])
+    assert not p.unary.numpy()[nu:].any()          # padding words are zero
+    if p.k:
+        nr = po["rem"].size
+        assert np.array_equal(p.rem.numpy().view(np.uint32)[:nr], po["rem"])
+        assert not p.rem.numpy()[nr:].any()
+    assert np.array_equal(p.anchor.numpy().view(np.uint64), po["anchor"])
+    assert np.array_equal(p.esc_pre.numpy().view(np.uint32), po["esc_pre"])
+    s = B.sizes_of(t, *shape)
+    assert s.unary_bits == p.unary_bits and s.n_esc == p.n_esc
+
+
+def test_exhaustive_patterns_pack_matches_oracle():
+    w = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).reshape(64, 1024)
+    wn = _np(w)
+    p = B.pack_rice(w)
+    po = oracle.pack_rice(wn, oracle.build_table(wn))
+    assert p.table.n == 256 and p.k == po["k"]
+    assert np.array_equal(p.unary.numpy().view(np.uint32)[: po["unary"].size], po["unary"])
+    assert np.array_equal(p.anchor.numpy().view(np.uint64), po["anchor"])
+
+
+def test_bits_per_weight_matches_pages_order_of_magnitude():
+    """"Binade" package page, "How it works": format 2 ~10.75 bits/weight.
+    Synthetic N(0, 0.02) weights land within a few hundredths of that."""
+    p = B.pack_rice(_tensor(256, 3072, seed=3))
+    assert 10.6 < p.bits_per_weight() < 10.85
+
+
+def test_status_codes():
+    L = B.lib()
+    t = B.Table()
+    assert L.binade_build_table(None, 10, ctypes.byref(t)) == B.EINVAL
+    w = torch.zeros(4, dtype=torch.bfloat16)
+    assert L.binade_build_table(ctypes.c_void_p(w.data_ptr()), 0, ctypes.byref(t)) == B.EINVAL
+    assert L.binade_status_str(B.EUNSUPPORTED) == b"unsupported shape or alignment"
+    # table from another tensor: sizes refuse
+    t = B.build_table(_tensor(4, 64))
+    s = B.Sizes()
+    assert L.binade_sizes_of(ctypes.byref(t), 4, 32, ctypes.byref(s)) == B.EINVAL
+    # weights with an exponent the table does not hold
+    w1 = _tensor(2, 64, sigma=0.02)
+    w2 = _tensor(2, 64, sigma=100.0)
+    with pytest.raises(B.BinadeError) as e:
+        B.pack_rice(w2, B.build_table(w1))
+    assert e.value.code in (B.EINVAL,)
+    # too small a unary plane
+    p = B.pack_rice(w1)
+    d = p.desc()
+    d.unary_words = 1
+    assert L.binade_pack_rice(ctypes.c_void_p(w1.data_ptr()), 2, 64,
+                              ctypes.byref(p.table), ctypes.byref(d)) == B.ENOSPACE
+
+
+def test_device_entry_points_validate_before_touching_the_gpu():
+    """Argument checks run on the host and return before any HIP call."""
+    L = B.lib()
+    d = B.R4Desc()
+    d.rows, d.cols = 4, 48            # cols % 32 != 0
+    assert L.binade_r4_gemv(ctypes.byref(d), None, None, 0, None) == B.EUNSUPPORTED
+    d.cols = -1
+    assert L.binade_r4_gemv(ctypes.byref(d), None, None, 0, None) == B.EINVAL
+    d.cols = 64
+    assert L.binade_r4_gemv(ctypes.byref(d), None, None, 0, None) == B.EINVAL
+    assert L.binade_r4_gemv(None, None, None, 0, None) == B.EINVAL
+    assert L.binade_bf16_gemv(None, 4, 40, None, None, 0, None) == B.EUNSUPPORTED
+    assert L.binade_unpack(None, None, None) == B.EINVAL
+    r = B.RiceDesc()
+    assert L.binade_rice_to_r4(ctypes.byref(r), ctypes.byref(d), None, None) == B.EINVAL
+    # zero rows: a valid no-op that launches nothing
+    d.rows, d.cols = 0, 64
+    assert L.binade_r4_gemv(ctypes.byref(d), None, None, 0, None) == B.OK
