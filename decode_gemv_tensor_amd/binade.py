@@ -246,14 +246,18 @@ class R4Tensor:
     _keep: list = field(default_factory=list, repr=False)
 
     def desc(self) -> R4Desc:
-        d = R4Desc()
-        d.rows, d.cols = self.rows, self.cols
-        ctypes.memmove(d.lut, self.lut, 16)
-        d.sm = self.sm.data_ptr()
-        d.nib = self.nib.data_ptr()
-        d.esc_pre = self.esc_pre.data_ptr()
-        d.esc = self.esc.data_ptr() if self.n_esc > 0 else None
-        d.n_esc = self.n_esc
+        """The C descriptor (built once; the tensors must not be replaced)."""
+        d = getattr(self, "_desc", None)
+        if d is None or d.lut[:] != list(self.lut):
+            d = R4Desc()
+            d.rows, d.cols = self.rows, self.cols
+            ctypes.memmove(d.lut, self.lut, 16)
+            d.sm = self.sm.data_ptr()
+            d.nib = self.nib.data_ptr()
+            d.esc_pre = self.esc_pre.data_ptr()
+            d.esc = self.esc.data_ptr() if self.n_esc > 0 else None
+            d.n_esc = self.n_esc
+            self._desc = d
         return d
 
     def nbytes(self) -> int:

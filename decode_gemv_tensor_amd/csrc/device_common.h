@@ -53,6 +53,22 @@ __device__ __forceinline__ void split4(uint32_t S, uint32_t E, uint32_t& H,
   Lo = (S & 0x7F7F7F7Fu) | ((E << 7) & 0x80808080u);
 }
 
+// The exponent byte rotated right by one: (e >> 1) | (e & 1) << 7. With the
+// table held in this form, both bf16 bytes of four weights are one bit-field
+// insert each (split4_rot).
+__host__ __device__ __forceinline__ uint32_t rot_exponent(uint32_t e) {
+  return ((e >> 1) & 0x7Fu) | ((e & 1u) << 7);
+}
+__host__ __device__ __forceinline__ uint32_t rot_exponents4(uint32_t e4) {
+  return ((e4 >> 1) & 0x7F7F7F7Fu) | ((e4 << 7) & 0x80808080u);
+}
+
+__device__ __forceinline__ void split4_rot(uint32_t S, uint32_t Er, uint32_t& H,
+                                           uint32_t& Lo) {
+  H = (S & 0x80808080u) | (Er & 0x7F7F7F7Fu);
+  Lo = (Er & 0x80808080u) | (S & 0x7F7F7F7Fu);
+}
+
 // fp32 value of weight b (0..3) of a split group: bf16 bits in the top half.
 template <int b>
 __device__ __forceinline__ float weight_f32(uint32_t H, uint32_t Lo) {
@@ -84,14 +100,23 @@ __device__ __forceinline__ uint16_t to_bf16_rne(float f) {
 }
 
 // Escape patch: replace exponent byte `idx & 3` of dword `idx >> 2` of E[8].
+// idx is wave-uniform; a switch keeps every E[q] in its own register (an
+// indexed form would put E in scratch memory).
 __device__ __forceinline__ void patch_exponent(uint32_t (&E)[8], uint32_t idx,
                                                uint32_t expo) {
-  const uint32_t d = idx >> 2;
   const uint32_t sh = (idx & 3u) * 8u;
-  const uint32_t keep = ~(0xFFu << sh);
-#pragma unroll
-  for (uint32_t q = 0; q < 8; ++q)
-    if (q == d) E[q] = (E[q] & keep) | (expo << sh);
+  const uint32_t m = 0xFFu << sh;
+  const uint32_t v = expo << sh;
+  switch (idx >> 2) {
+    case 0: E[0] = (E[0] & ~m) | v; break;
+    case 1: E[1] = (E[1] & ~m) | v; break;
+    case 2: E[2] = (E[2] & ~m) | v; break;
+    case 3: E[3] = (E[3] & ~m) | v; break;
+    case 4: E[4] = (E[4] & ~m) | v; break;
+    case 5: E[5] = (E[5] & ~m) | v; break;
+    case 6: E[6] = (E[6] & ~m) | v; break;
+    default: E[7] = (E[7] & ~m) | v; break;
+  }
 }
 
 template <typename T>
@@ -133,7 +158,9 @@ __device__ __forceinline__ float slot_tree(float p) {
 
 // The 8 exponent dwords of one lane tile: table lookups of its 16 nibble
 // bytes, then the escapes of the row-chunk (uniform loop over the chunk's
-// side-list entries; the lane owning an entry's position patches it).
+// side-list entries; the lane owning an entry's position patches it). With
+// kRot the table L is rotated (rot_exponents4) and so are the patches.
+template <bool kRot = false>
 __device__ __forceinline__ void tile_exponents(uint4 nb, const Lut& L,
                                                const uint32_t* esc_pre,
                                                const uint32_t* esc,
@@ -152,8 +179,9 @@ __device__ __forceinline__ void tile_exponents(uint4 nb, const Lut& L,
   for (uint32_t e = e_beg; e < e_end; ++e) {
     const uint32_t ent = uniform(esc[e]);
     const uint32_t off = ent & 0xFFFFu;
+    const uint32_t ex = (ent >> 16) & 0xFFu;
     if (static_cast<uint32_t>(lane) == (off >> 5))
-      patch_exponent(E, off & 31u, (ent >> 16) & 0xFFu);
+      patch_exponent(E, off & 31u, kRot ? rot_exponent(ex) : ex);
   }
 }
 

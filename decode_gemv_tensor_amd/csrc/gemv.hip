@@ -66,7 +66,64 @@ __device__ __forceinline__ void store_y(const GemvArgs& a, int64_t row,
     static_cast<float*>(a.y)[row] = v;
 }
 
+// Raw loads of one lane tile of R rows plus its x tile.
 template <int R>
+struct TileLoads {
+  uint4 s0[R], s1[R], nb[R];
+  uint4 xq[4];
+};
+
+template <int R>
+__device__ __forceinline__ void load_tiles(TileLoads<R>& b, const GemvArgs& a,
+                                           const int64_t (&row)[R], int t) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint4* ps = reinterpret_cast<const uint4*>(a.sm + row[r] * a.cols + 32 * t);
+    b.s0[r] = ps[0];
+    b.s1[r] = ps[1];
+    b.nb[r] = *reinterpret_cast<const uint4*>(a.nib + row[r] * (a.cols >> 1) + 16 * t);
+  }
+  const uint4* px = reinterpret_cast<const uint4*>(a.x + 32 * t);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) b.xq[v] = px[v];
+}
+
+// Rebuild and multiply one lane tile of R rows (tile t of row-chunk j).
+template <int R>
+__device__ __forceinline__ void fma_tiles(const TileLoads<R>& b, const GemvArgs& a,
+                                          const Lut& Lr, const int64_t (&row)[R],
+                                          int C, int j, int lane, float (&acc0)[R],
+                                          float (&acc1)[R]) {
+  float xf[32];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const uint32_t w[4] = {b.xq[v].x, b.xq[v].y, b.xq[v].z, b.xq[v].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xf[8 * v + 2 * e] = bf16_lo(w[e]);
+      xf[8 * v + 2 * e + 1] = bf16_hi(w[e]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    uint32_t E[8];
+    tile_exponents<true>(b.nb[r], Lr, a.esc_pre, a.esc, a.n_esc, row[r] * C + j, lane, E);
+    const uint32_t S[8] = {b.s0[r].x, b.s0[r].y, b.s0[r].z, b.s0[r].w,
+                           b.s1[r].x, b.s1[r].y, b.s1[r].z, b.s1[r].w};
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      uint32_t H, Lo;
+      split4_rot(S[d], E[d], H, Lo);
+      fma_group(H, Lo, xf + 4 * d, acc0[r], acc1[r]);
+    }
+  }
+}
+
+// One wave owns rows row0 .. row0+R-1 (rows past the end are computed on a
+// clamped row index and not stored). Full row-chunks run with every lane
+// active and the next chunk's loads in flight; a ragged last chunk (K not a
+// multiple of 2048) runs on its first K/32 mod 64 lanes.
+template <int R, bool kPrefetch>
 __global__ __launch_bounds__(256) void r4_gemv_kernel(GemvArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row0 =
@@ -74,54 +131,47 @@ __global__ __launch_bounds__(256) void r4_gemv_kernel(GemvArgs a) {
                  (threadIdx.x >> 6)) * R);
   if (row0 >= a.rows) return;
   const int J = a.cols >> 5;
-  const int C = (J + 63) >> 6;
-  const Lut L{a.lut0, a.lut1, a.lut2, a.lut3};
+  const int Cf = J >> 6;          // full chunks
+  const int tail = J & 63;        // lanes in the ragged chunk
+  const int C = Cf + (tail ? 1 : 0);
+  const Lut Lr{a.lut0, a.lut1, a.lut2, a.lut3};   // rotated table
+  int64_t row[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) row[r] = row0 + r < a.rows ? row0 + r : a.rows - 1;
 
   float acc0[R], acc1[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc0[r] = acc1[r] = 0.0f;
 
-  for (int j = 0; j < C; ++j) {
-    const int t = j * 64 + lane;
-    const bool active = t < J;
-    uint4 s0[R], s1[R], nb[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t row = row0 + r;
-      if (active && row < a.rows) {
-        const uint4* ps = reinterpret_cast<const uint4*>(a.sm + row * a.cols + 32 * t);
-        s0[r] = ps[0];
-        s1[r] = ps[1];
-        nb[r] = *reinterpret_cast<const uint4*>(a.nib + row * (a.cols >> 1) + 16 * t);
-      } else {
-        s0[r] = s1[r] = nb[r] = make_uint4(0, 0, 0, 0);
+  if (kPrefetch) {
+    if (Cf > 0) {
+      TileLoads<R> A, B;
+      load_tiles(A, a, row, lane);
+      int j = 0;
+      for (; j + 2 <= Cf; j += 2) {
+        load_tiles(B, a, row, (j + 1) * 64 + lane);
+        fma_tiles(A, a, Lr, row, C, j, lane, acc0, acc1);
+        if (j + 2 < Cf) load_tiles(A, a, row, (j + 2) * 64 + lane);
+        fma_tiles(B, a, Lr, row, C, j + 1, lane, acc0, acc1);
       }
+      if (j < Cf) fma_tiles(A, a, Lr, row, C, j, lane, acc0, acc1);
     }
-    float xf[32];
-    if (active) load_x_tile(a.x, t, xf);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t row = row0 + r;
-      if (row >= a.rows) continue;  // uniform
-      uint32_t E[8];
-      tile_exponents(nb[r], L, a.esc_pre, a.esc, a.n_esc, row * C + j, lane, E);
-      if (active) {
-        const uint32_t S[8] = {s0[r].x, s0[r].y, s0[r].z, s0[r].w,
-                               s1[r].x, s1[r].y, s1[r].z, s1[r].w};
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          uint32_t H, Lo;
-          split4(S[d], E[d], H, Lo);
-          fma_group(H, Lo, xf + 4 * d, acc0[r], acc1[r]);
-        }
-      }
+  } else {
+    for (int j = 0; j < Cf; ++j) {
+      TileLoads<R> A;
+      load_tiles(A, a, row, j * 64 + lane);
+      fma_tiles(A, a, Lr, row, C, j, lane, acc0, acc1);
     }
+  }
+  if (tail && lane < tail) {
+    TileLoads<R> A;
+    load_tiles(A, a, row, Cf * 64 + lane);
+    fma_tiles(A, a, Lr, row, C, Cf, lane, acc0, acc1);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t row = row0 + r;
     const float p = slot_tree(acc0[r] + acc1[r]);
-    if (lane == 0 && row < a.rows) store_y(a, row, p);
+    if (lane == 0 && row0 + r < a.rows) store_y(a, row0 + r, p);
   }
 }
 
@@ -236,7 +286,7 @@ int32_t check_r4(const binade_r4* w) {
   return BINADE_OK;
 }
 
-GemvArgs args_from_r4(const binade_r4* w) {
+GemvArgs args_from_r4(const binade_r4* w, bool rotated) {
   GemvArgs a{};
   a.sm = w->sm;
   a.nib = w->nib;
@@ -249,31 +299,50 @@ GemvArgs args_from_r4(const binade_r4* w) {
   a.lut1 = pack_lut(w->lut, 1);
   a.lut2 = pack_lut(w->lut, 2);
   a.lut3 = pack_lut(w->lut, 3);
+  if (rotated) {
+    a.lut0 = dev::rot_exponents4(a.lut0);
+    a.lut1 = dev::rot_exponents4(a.lut1);
+    a.lut2 = dev::rot_exponents4(a.lut2);
+    a.lut3 = dev::rot_exponents4(a.lut3);
+  }
   return a;
 }
 
-// Rows per wave: enough waves to cover the CUs, more rows per wave (x reuse,
-// more loads in flight) when the matrix is tall.
-int rows_per_wave(int64_t rows) {
-  const char* env = getenv("BINADE_GEMV_ROWS_PER_WAVE");
-  if (env != nullptr) {
+// Launch shape: rows per wave R and whether a wave prefetches its next
+// chunk. Neither changes the arithmetic. BINADE_GEMV_ROWS_PER_WAVE (1, 2, 4)
+// and BINADE_GEMV_PREFETCH (0, 1) override the defaults.
+struct GemvShape {
+  int rows_per_wave;
+  bool prefetch;
+};
+
+GemvShape gemv_shape(int64_t rows) {
+  GemvShape s{1, false};
+  if (rows >= 8192) s.rows_per_wave = 2;
+  if (const char* env = getenv("BINADE_GEMV_ROWS_PER_WAVE")) {
     const int r = atoi(env);
-    if (r == 1 || r == 2 || r == 4) return r;
+    if (r == 1 || r == 2 || r == 4) s.rows_per_wave = r;
   }
-  if (rows >= 8192) return 4;
-  if (rows >= 4096) return 2;
-  return 1;
+  if (const char* env = getenv("BINADE_GEMV_PREFETCH")) s.prefetch = atoi(env) != 0;
+  return s;
 }
 
 int32_t launch_gemv(const GemvArgs& a, bool r4, hipStream_t stream) {
-  const int R = rows_per_wave(a.rows);
+  const GemvShape sh = gemv_shape(a.rows);
+  const int R = sh.rows_per_wave;
   const int64_t waves = (a.rows + R - 1) / R;
   const dim3 grid(static_cast<uint32_t>((waves + 3) / 4));
   const dim3 block(256);
   if (r4) {
-    if (R == 4) hipLaunchKernelGGL(r4_gemv_kernel<4>, grid, block, 0, stream, a);
-    else if (R == 2) hipLaunchKernelGGL(r4_gemv_kernel<2>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(r4_gemv_kernel<1>, grid, block, 0, stream, a);
+    if (sh.prefetch) {
+      if (R == 4) hipLaunchKernelGGL((r4_gemv_kernel<4, true>), grid, block, 0, stream, a);
+      else if (R == 2) hipLaunchKernelGGL((r4_gemv_kernel<2, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((r4_gemv_kernel<1, true>), grid, block, 0, stream, a);
+    } else {
+      if (R == 4) hipLaunchKernelGGL((r4_gemv_kernel<4, false>), grid, block, 0, stream, a);
+      else if (R == 2) hipLaunchKernelGGL((r4_gemv_kernel<2, false>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((r4_gemv_kernel<1, false>), grid, block, 0, stream, a);
+    }
   } else {
     if (R == 4) hipLaunchKernelGGL(bf16_gemv_kernel<4>, grid, block, 0, stream, a);
     else if (R == 2) hipLaunchKernelGGL(bf16_gemv_kernel<2>, grid, block, 0, stream, a);
@@ -295,7 +364,7 @@ extern "C" int32_t binade_r4_gemv(const binade_r4* w, const uint16_t* x,
   if (w->rows == 0) return BINADE_OK;
   if (x == nullptr || y == nullptr) return BINADE_EINVAL;
   if (!aligned16(x)) return BINADE_EUNSUPPORTED;
-  GemvArgs a = args_from_r4(w);
+  GemvArgs a = args_from_r4(w, true);
   a.x = x;
   a.y = y;
   a.y_bf16 = y_dtype == BINADE_BF16;
@@ -328,7 +397,7 @@ extern "C" int32_t binade_unpack(const binade_r4* w, uint16_t* out,
   if (w->rows == 0) return BINADE_OK;
   if (out == nullptr) return BINADE_EINVAL;
   if (!aligned16(out)) return BINADE_EUNSUPPORTED;
-  GemvArgs a = args_from_r4(w);
+  GemvArgs a = args_from_r4(w, false);
   const int64_t chunks = w->rows * ((w->cols / 32 + 63) / 64);
   const dim3 grid(static_cast<uint32_t>((chunks + 3) / 4));
   hipLaunchKernelGGL(r4_unpack_kernel, grid, dim3(256), 0,
