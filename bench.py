@@ -1,0 +1,362 @@
+"""Benchmark of the Binade hot path on one MI355X.
+
+Workload: the Llama-3.2-3B-shaped linear stack (28 layers x {q, o 3072x3072;
+k, v 1024x3072; gate, up 8192x3072; down 3072x8192}; bf16 N(0, 0.02) with
+0.1% outliers x20; seeds 1000 + tensor index). One step = format 2 -> R4
+decode of all 196 tensors, then the batch-1 R4 GEMV of every tensor with an
+N(0, 1) bf16 input of its width. Inputs and planes are resident in HBM before
+the timed region; every kernel is timed with HIP events on its stream.
+
+Before timing, parity is checked (and the run refuses to time if it fails):
+every tensor's device decode unpacks to its original bits and its R4 GEMV
+equals the bf16-weight twin bit for bit; the first layer's R4 planes equal
+the oracle's byte for byte and sampled GEMV rows equal the oracle's replay.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 2]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import subprocess
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from decode_gemv_tensor_amd import binade as B  # noqa: E402
+from decode_gemv_tensor_amd import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemv_bytes(r4: B.R4Tensor) -> int:
+    """Algorithmic bytes of one R4 GEMV: sign/mantissa + nibbles + escape
+    entries + escape prefixes + x (bf16) + y (fp32)."""
+    n, k = r4.rows, r4.cols
+    return n * k + n * k // 2 + 4 * r4.n_esc + 4 * r4.esc_pre.numel() + 2 * k + 4 * n
+
+
+def twin_bytes(n: int, k: int) -> int:
+    return 2 * n * k + 2 * k + 4 * n
+
+
+def decode_bytes(p: B.RicePlanes) -> int:
+    """Algorithmic bytes of one format 2 -> R4 decode: the unary and
+    remainder bits, anchors and escape prefixes read; nibbles and escape
+    entries written. The sign/mantissa plane is not touched."""
+    n = p.rows * p.cols
+    unary = 4 * ((p.unary_bits + 31) // 32)
+    rem = 4 * ((n * p.k + 31) // 32)
+    chunks = p.anchor.numel()
+    return unary + rem + 12 * chunks + n // 2 + 4 * p.n_esc
+
+
+class Timer:
+    """Pairs of HIP events recorded on one stream."""
+
+    def __init__(self, stream):
+        self.stream = stream
+        self.pairs: dict[str, list] = {}
+
+    def start(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
+
+    def stop(self, key, e0):
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record(self.stream)
+        self.pairs.setdefault(key, []).append((e0, e1))
+
+    def total_ms(self, key):
+        return sum(a.elapsed_time(b) for a, b in self.pairs.get(key, []))
+
+    def count(self, key):
+        return len(self.pairs.get(key, []))
+
+
+def host_cores_used() -> int:
+    return 1
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=synth.LLAMA_3B_LAYERS)
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-twin", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: "
+              "this build runs the single-GPU path only", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream()
+    L = B.lib()
+
+    # ------------------------------------------------------------ inputs
+    t0 = time.time()
+    specs = synth.llama32_3b_stack(args.layers)
+    host_bits = {}
+
+    def prepare(spec):
+        w = synth.normal_bf16(spec, device=dev)
+        wh = w.cpu()
+        planes = B.pack_rice(wh)
+        return spec, w, wh, planes
+
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        prepared = list(ex.map(prepare, specs))
+    tensors = []
+    for spec, w, wh, planes in prepared:
+        dplanes = planes.to(dev)
+        nib = torch.empty(spec.rows * spec.cols // 2, dtype=torch.uint8, device=dev)
+        esc = torch.empty(max(planes.n_esc, 1), dtype=torch.int32, device=dev)
+        r4 = B.R4Tensor(spec.rows, spec.cols, bytes(16), dplanes.sm, nib,
+                        dplanes.esc_pre, esc, planes.n_esc)
+        if spec.name.startswith("L0.") or not args.skip_cpu_baseline:
+            host_bits[spec.name] = wh
+        tensors.append({"spec": spec, "w": w if not args.skip_twin else None,
+                        "planes": dplanes, "r4": r4,
+                        "y": torch.empty(spec.rows, dtype=torch.float32, device=dev)})
+    xs = {k: synth.vector_bf16(k, 1 + k, device=dev) for k in sorted({s.cols for s in specs})}
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f}s: {len(tensors)} tensors")
+
+    # pre-built C arguments: the timed loop calls the library directly.
+    # Decode: every tensor, 8 per launch (the library splits the list).
+    # GEMV: per layer the groups a decoder issues together -- q, k, v; o;
+    # gate, up; down -- one launch each.
+    n_t = len(tensors)
+    outs = B.rice_to_r4_batch([t["planes"] for t in tensors], status=status, stream=stream,
+                              outs=[t["r4"] for t in tensors])
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "device decode flagged corrupt planes"
+    dec_in = (B.RiceDesc * n_t)(*[t["planes"].desc() for t in tensors])
+    dec_out = (B.R4Desc * n_t)()
+    for i, t in enumerate(tensors):
+        dec_out[i].nib = t["r4"].nib.data_ptr()
+        dec_out[i].esc = t["r4"].esc.data_ptr()
+    dec_groups = [(i, min(8, n_t - i)) for i in range(0, n_t, 8)]
+    names = [t["spec"].name.split(".")[1] for t in tensors]
+    groups = []
+    i = 0
+    while i < n_t:
+        g = [i]
+        if names[i] == "q":
+            g = [i, i + 1, i + 2]
+        elif names[i] == "gate":
+            g = [i, i + 1]
+        groups.append(g)
+        i += len(g)
+    gemv_args = []
+    for g in groups:
+        ws = (B.R4Desc * len(g))(*[tensors[j]["r4"].desc() for j in g])
+        xs_ = (ctypes.c_void_p * len(g))(*[xs[tensors[j]["spec"].cols].data_ptr() for j in g])
+        ys_ = (ctypes.c_void_p * len(g))(*[tensors[j]["y"].data_ptr() for j in g])
+        gemv_args.append((ws, xs_, ys_, len(g), sum(gemv_bytes(tensors[j]["r4"]) for j in g)))
+    dec_bytes = [sum(decode_bytes(tensors[j]["planes"]) for j in range(s0, s0 + n)) for s0, n in dec_groups]
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    stat_p = ctypes.c_void_p(status.data_ptr())
+    RD = ctypes.sizeof(B.RiceDesc)
+    R4D = ctypes.sizeof(B.R4Desc)
+
+    def decode(gi):
+        s0, n = dec_groups[gi]
+        rc = L.binade_rice_to_r4_batch(ctypes.byref(dec_in, s0 * RD), ctypes.byref(dec_out, s0 * R4D),
+                                       n, stat_p, sptr)
+        if rc:
+            raise B.BinadeError("binade_rice_to_r4_batch", rc)
+
+    def gemv(gi):
+        ws, xs_, ys_, n, _ = gemv_args[gi]
+        rc = L.binade_r4_gemv_batch(ws, xs_, ys_, n, B.F32, sptr)
+        if rc:
+            raise B.BinadeError("binade_r4_gemv_batch", rc)
+
+    # ------------------------------------------------------------ parity gate
+    t0 = time.time()
+    with torch.cuda.stream(stream):
+        for gi in range(len(gemv_args)):
+            gemv(gi)
+    torch.cuda.synchronize()
+    for t in tensors:
+        if t["w"] is not None:
+            back = B.unpack(t["r4"], stream=stream)
+            yt = B.bf16_gemv(t["w"], xs[t["spec"].cols], stream=stream)
+            y1 = B.r4_gemv(t["r4"], xs[t["spec"].cols], stream=stream)
+            torch.cuda.synchronize()
+            if not torch.equal(back.view(torch.int16), t["w"].view(torch.int16)):
+                raise SystemExit(f"parity gate: unpack differs for {t['spec'].name}")
+            if not torch.equal(yt.view(torch.int32), t["y"].view(torch.int32)):
+                raise SystemExit(f"parity gate: R4 GEMV differs from bf16 twin for {t['spec'].name}")
+            if not torch.equal(y1.view(torch.int32), t["y"].view(torch.int32)):
+                raise SystemExit(f"parity gate: batched GEMV differs from single for {t['spec'].name}")
+    import oracle  # test infrastructure: parity gate and cpu baseline only
+    for t in tensors[:7]:
+        name = t["spec"].name
+        wn = host_bits[name].view(torch.int16).numpy().view(np.uint16)
+        ref = oracle.make_r4(wn, oracle.build_table(wn))
+        if not np.array_equal(t["r4"].nib.cpu().numpy(), ref["nib"].reshape(-1)):
+            raise SystemExit(f"parity gate: nibbles differ from the oracle for {name}")
+        if ref["n_esc"] and not np.array_equal(
+                t["r4"].esc[: ref["n_esc"]].cpu().numpy().view(np.uint32), ref["esc"]):
+            raise SystemExit(f"parity gate: escapes differ from the oracle for {name}")
+        rows = np.arange(0, wn.shape[0], 97)
+        xb = xs[t["spec"].cols].cpu().view(torch.int16).numpy().view(np.uint16)
+        yref = oracle.gemv_replay(wn[rows], xb)
+        if not np.array_equal(t["y"].cpu().numpy()[rows].view(np.uint32), yref.view(np.uint32)):
+            raise SystemExit(f"parity gate: GEMV rows differ from the oracle for {name}")
+    log(f"parity gate passed ({time.time() - t0:.1f}s)")
+
+    # ------------------------------------------------------------ timed
+    timer = Timer(stream)
+    for _ in range(args.warmup):
+        with torch.cuda.stream(stream):
+            for gi in range(len(dec_groups)):
+                decode(gi)
+            for gi in range(len(gemv_args)):
+                gemv(gi)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            s0 = timer.start()
+            p0 = timer.start()
+            for gi in range(len(dec_groups)):
+                e = timer.start()
+                decode(gi)
+                timer.stop("decode", e)
+            timer.stop("decode_phase", p0)
+            p1 = timer.start()
+            for gi in range(len(gemv_args)):
+                e = timer.start()
+                gemv(gi)
+                timer.stop("gemv", e)
+            timer.stop("gemv_phase", p1)
+            timer.stop("step", s0)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    assert int(status.item()) == 0
+
+    K = args.steps
+    gemv_b = sum(gemv_bytes(t["r4"]) for t in tensors)
+    dec_b = sum(decode_bytes(t["planes"]) for t in tensors)
+    syms = sum(t["spec"].rows * t["spec"].cols for t in tensors)
+    step_ms_avg = timer.total_ms("step") / K
+    gemv_phase_ms = timer.total_ms("gemv_phase") / K
+    dec_phase_ms = timer.total_ms("decode_phase") / K
+    gemv_kernel_ms = timer.total_ms("gemv") / K
+    dec_kernel_ms = timer.total_ms("decode") / K
+    n_gemv_launch = len(gemv_args)
+    n_dec_launch = len(dec_groups)
+    gemv_ach = gemv_b / (gemv_kernel_ms * 1e-3) / 1e9      # GB/s over kernel time
+    dec_ach = dec_b / (dec_kernel_ms * 1e-3) / 1e9
+    value = gemv_b / (gemv_phase_ms * 1e-3) / 1e9           # whole GEMV phase
+
+    # bf16 twin per token (same stack, untimed by the step)
+    twin = None
+    if not args.skip_twin:
+        tt = Timer(stream)
+        ys = [torch.empty(t["spec"].rows, device=dev) for t in tensors]
+        with torch.cuda.stream(stream):
+            for rep in range(2):
+                for t, y in zip(tensors, ys):
+                    e = tt.start()
+                    B.bf16_gemv(t["w"], xs[t["spec"].cols], y=y, stream=stream)
+                    tt.stop("twin" if rep else "warm", e)
+        torch.cuda.synchronize()
+        twin_ms = tt.total_ms("twin")
+        twin = {"kernel_ms_per_token": twin_ms,
+                "r4_kernel_ms_per_token": gemv_kernel_ms,
+                "speedup_per_token": twin_ms / gemv_kernel_ms,
+                "bf16_GBs": sum(twin_bytes(t["spec"].rows, t["spec"].cols) for t in tensors) / (twin_ms * 1e-3) / 1e9}
+
+    # ------------------------------------------------------------ CPU oracle
+    cpu = None
+    if not args.skip_cpu_baseline:
+        t0 = time.perf_counter()
+        done_b = 0
+        n_done = 0
+        for t in tensors:
+            wn = host_bits[t["spec"].name].view(torch.int16).numpy().view(np.uint16)
+            xb = xs[t["spec"].cols].cpu().view(torch.int16).numpy().view(np.uint16)
+            oracle.gemv_replay(wn, xb)
+            done_b += gemv_bytes(t["r4"])
+            n_done += 1
+            if time.perf_counter() - t0 > 20.0:
+                break
+        el = time.perf_counter() - t0
+        cpu = {"value": done_b / el / 1e9, "unit": "GB/s", "cores": host_cores_used(),
+               "kind": "oracle",
+               "sample": f"oracle fp32-order GEMV replay (single-threaded C) over the first "
+                         f"{n_done} of {len(tensors)} stack tensors from their bf16 bits, "
+                         f"{el:.1f} s; bytes counted as the R4 GEMV's"}
+
+    dominant = "gemv" if gemv_kernel_ms >= dec_kernel_ms else "rice_to_r4"
+    roof_g = {"kernel": "r4_gemv", "bound": "hbm", "achieved": round(gemv_ach, 1),
+              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gemv_ach / HBM_PEAK_GBS, 4),
+              "traffic": None, "launches_per_step": n_gemv_launch,
+              "avg_launch_us": round(gemv_kernel_ms * 1e3 / n_gemv_launch, 3),
+              "bytes_per_launch": gemv_b // n_gemv_launch}
+    roof_d = {"kernel": "rice_to_r4", "bound": "hbm", "achieved": round(dec_ach, 1),
+              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_ach / HBM_PEAK_GBS, 4),
+              "traffic": None, "launches_per_step": n_dec_launch,
+              "avg_launch_us": round(dec_kernel_ms * 1e3 / n_dec_launch, 3),
+              "bytes_per_launch": dec_b // n_dec_launch,
+              "gsym_per_s": round(syms / (dec_kernel_ms * 1e-3) / 1e9, 1)}
+    out = {
+        "metric": "R4 GEMV effective GB/s and % of HBM peak; Rice->R4 Gsym/s; GEMM TFLOP/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms_avg, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 weights (R4), fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": f"llama-3.2-3b linear stack, {args.layers} layers x 7 tensors: "
+                               "Rice->R4 decode + batch-1 R4 GEMV per tensor",
+                   "launches": "decode 8 tensors per launch; GEMV per layer q|k|v, o, gate|up, down",
+                   "tensors": len(tensors), "weights": syms,
+                   "r4_bytes": sum(t["r4"].nbytes() for t in tensors),
+                   "parallelism": "single GPU"},
+        "gemv_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "rice_to_r4_gsym_s": round(syms / (dec_phase_ms * 1e-3) / 1e9, 1),
+        "roofline": roof_g if dominant == "gemv" else roof_d,
+        "roofline_other": roof_d if dominant == "gemv" else roof_g,
+        "bf16_twin": twin,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,7 +25,8 @@ DEV_CORRUPT_STREAM, DEV_BAD_INDEX, DEV_CORRUPT_ESC = 0x1, 0x2, 0x4
 
 EXPORTS = ["binade_status_str", "binade_last_hip_error", "binade_build_table",
            "binade_sizes_of", "binade_pack_rice", "binade_rice_to_r4",
-           "binade_unpack", "binade_r4_gemv", "binade_bf16_gemv",
+           "binade_rice_to_r4_batch", "binade_unpack", "binade_r4_gemv",
+           "binade_r4_gemv_batch", "binade_bf16_gemv",
            "binade_r4_gemm", "binade_bf16_gemm", "binade_r4_moe_gemv",
            "binade_bf16_moe_gemv"]
 
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
                 "binade_sizes_of": [P, I64, I64, P],
                 "binade_pack_rice": [P, I64, I64, P, P],
                 "binade_rice_to_r4": [P, P, P, P],
+                "binade_rice_to_r4_batch": [P, P, I32, P, P],
+                "binade_r4_gemv_batch": [P, P, P, I32, I32, P],
                 "binade_unpack": [P, P, P],
                 "binade_r4_gemv": [P, P, P, I32, P],
                 "binade_bf16_gemv": [P, I64, I64, P, P, I32, P],
@@ -297,6 +300,44 @@ def rice_to_r4(planes: RicePlanes, status: torch.Tensor | None = None,
         return out
     return R4Tensor(planes.rows, planes.cols, lut, planes.sm, nib,
                     planes.esc_pre, esc, planes.n_esc)
+
+
+def rice_to_r4_batch(planes: list, status: torch.Tensor | None = None,
+                     stream=None, outs: list | None = None) -> list:
+    """binade_rice_to_r4_batch: decode several tensors (up to 8 per launch)."""
+    n = len(planes)
+    if outs is None:
+        outs = []
+        for p in planes:
+            dev = p.sm.device
+            outs.append(R4Tensor(p.rows, p.cols, bytes(16), p.sm,
+                                 torch.empty(p.rows * p.cols // 2, dtype=torch.uint8, device=dev),
+                                 p.esc_pre,
+                                 torch.empty(max(p.n_esc, 1), dtype=torch.int32, device=dev),
+                                 p.n_esc))
+    din = (RiceDesc * n)(*[p.desc() for p in planes])
+    dout = (R4Desc * n)()
+    for i, o in enumerate(outs):
+        dout[i].nib = o.nib.data_ptr()
+        dout[i].esc = o.esc.data_ptr()
+    _call("binade_rice_to_r4_batch", din, dout, n, _ptr(status), _stream(stream))
+    for i, o in enumerate(outs):
+        o.lut = bytes(dout[i].lut)
+    return outs
+
+
+def r4_gemv_batch(ws: list, xs: list, out_dtype=torch.float32,
+                  ys: list | None = None, stream=None) -> list:
+    """binade_r4_gemv_batch: several independent R4 GEMVs in one launch."""
+    code = _dtype_code(out_dtype)
+    n = len(ws)
+    if ys is None:
+        ys = [_y((w.rows,), code, x.device, None) for w, x in zip(ws, xs)]
+    dws = (R4Desc * n)(*[w.desc() for w in ws])
+    dxs = (ctypes.c_void_p * n)(*[_bits16(x).data_ptr() for x in xs])
+    dys = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+    _call("binade_r4_gemv_batch", dws, dxs, dys, n, code, _stream(stream))
+    return ys
 
 
 def _y(rows_shape, y_dtype, device, y):

@@ -124,12 +124,7 @@ __device__ __forceinline__ void fma_tiles(const TileLoads<R>& b, const GemvArgs&
 // active and the next chunk's loads in flight; a ragged last chunk (K not a
 // multiple of 2048) runs on its first K/32 mod 64 lanes.
 template <int R, bool kPrefetch>
-__global__ __launch_bounds__(256) void r4_gemv_kernel(GemvArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row0 =
-      uniform64((static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) +
-                 (threadIdx.x >> 6)) * R);
-  if (row0 >= a.rows) return;
+__device__ __forceinline__ void r4_gemv_rows(const GemvArgs& a, int64_t row0, int lane) {
   const int J = a.cols >> 5;
   const int Cf = J >> 6;          // full chunks
   const int tail = J & 63;        // lanes in the ragged chunk
@@ -173,6 +168,48 @@ __global__ __launch_bounds__(256) void r4_gemv_kernel(GemvArgs a) {
     const float p = slot_tree(acc0[r] + acc1[r]);
     if (lane == 0 && row0 + r < a.rows) store_y(a, row0 + r, p);
   }
+}
+
+// One wave owns rows row0 .. row0+R-1 (rows past the end are computed on a
+// clamped row index and not stored). Full row-chunks run with every lane
+// active; a ragged last chunk (K not a multiple of 2048) runs on its first
+// K/32 mod 64 lanes.
+template <int R, bool kPrefetch>
+__global__ __launch_bounds__(256) void r4_gemv_kernel(GemvArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 =
+      uniform64((static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) +
+                 (threadIdx.x >> 6)) * R);
+  if (row0 >= a.rows) return;
+  r4_gemv_rows<R, kPrefetch>(a, row0, lane);
+}
+
+// Several independent products in one launch: items 0..count-1 own the
+// consecutive block ranges [first_block[i], first_block[i+1]).
+constexpr int kMaxBatch = 16;
+struct GemvBatch {
+  GemvArgs item[kMaxBatch];
+  uint32_t first_block[kMaxBatch + 1];
+  int32_t count;
+};
+
+template <int R>
+__global__ __launch_bounds__(256) void r4_gemv_batch_kernel(GemvBatch b) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t blk = blockIdx.x;
+  int i = 0;
+#pragma unroll
+  for (int t = 1; t < kMaxBatch; ++t)
+    if (t < b.count && blk >= b.first_block[t]) i = t;
+  // the item is read through the argument segment's address (an index into
+  // a by-value argument array would be copied to scratch memory)
+  const GemvArgs* items = (const GemvArgs*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() +
+                                            offsetof(GemvBatch, item));
+  const GemvArgs a = items[uniform(i)];
+  const int64_t row0 = uniform64((static_cast<int64_t>(blk - b.first_block[i]) * (blockDim.x >> 6) +
+                                  (threadIdx.x >> 6)) * R);
+  if (row0 >= a.rows) return;
+  r4_gemv_rows<R, false>(a, row0, lane);
 }
 
 template <int R>
@@ -369,6 +406,53 @@ extern "C" int32_t binade_r4_gemv(const binade_r4* w, const uint16_t* x,
   a.y = y;
   a.y_bf16 = y_dtype == BINADE_BF16;
   return launch_gemv(a, true, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t binade_r4_gemv_batch(const binade_r4* ws,
+                                        const uint16_t* const* xs,
+                                        void* const* ys, int32_t count,
+                                        int32_t y_dtype, void* stream) {
+  if (count < 0 || (count > 0 && (ws == nullptr || xs == nullptr || ys == nullptr)))
+    return BINADE_EINVAL;
+  if (y_dtype != BINADE_F32 && y_dtype != BINADE_BF16) return BINADE_EINVAL;
+  for (int32_t i = 0; i < count; ++i) {
+    const int32_t s = check_r4(&ws[i]);
+    if (s != BINADE_OK) return s;
+    if (ws[i].rows > 0 && (xs[i] == nullptr || ys[i] == nullptr)) return BINADE_EINVAL;
+    if (ws[i].rows > 0 && !aligned16(xs[i])) return BINADE_EUNSUPPORTED;
+  }
+  const int R = gemv_shape(0).rows_per_wave == 1 ? 1 : 2;  // small shapes favour 1
+  for (int32_t base = 0; base < count; base += kMaxBatch) {
+    GemvBatch b{};
+    uint64_t blocks = 0;
+    int n = 0;
+    for (int32_t i = base; i < count && n < kMaxBatch; ++i) {
+      if (ws[i].rows == 0) continue;
+      GemvArgs a = args_from_r4(&ws[i], true);
+      a.x = xs[i];
+      a.y = ys[i];
+      a.y_bf16 = y_dtype == BINADE_BF16;
+      b.item[n] = a;
+      b.first_block[n] = static_cast<uint32_t>(blocks);
+      const int64_t waves = (a.rows + R - 1) / R;
+      blocks += static_cast<uint64_t>((waves + 3) / 4);
+      ++n;
+    }
+    if (n == 0) continue;
+    if (blocks > 0x7FFFFFFFull) return BINADE_EUNSUPPORTED;
+    b.first_block[n] = static_cast<uint32_t>(blocks);
+    b.count = n;
+    const dim3 grid(static_cast<uint32_t>(blocks));
+    if (R == 2)
+      hipLaunchKernelGGL(r4_gemv_batch_kernel<2>, grid, dim3(256), 0,
+                         static_cast<hipStream_t>(stream), b);
+    else
+      hipLaunchKernelGGL(r4_gemv_batch_kernel<1>, grid, dim3(256), 0,
+                         static_cast<hipStream_t>(stream), b);
+    const int32_t s = launch_status();
+    if (s != BINADE_OK) return s;
+  }
+  return BINADE_OK;
 }
 
 extern "C" int32_t binade_bf16_gemv(const uint16_t* w, int64_t rows,

@@ -8,15 +8,23 @@
 // staged on chip is what made the Huffman exponent decoder fast; the same
 // two ideas are used here, with the lengths found from the bits themselves.
 //
-// One wave decodes one row-chunk (<= 2048 weights). Phase 1: the lanes
-// popcount the chunk's unary words (every weight's code ends in exactly one
-// 1 bit), a wave prefix sum turns the counts into weight indices, and the
-// lane holding the terminator of weight 32m-1 records where lane tile m
-// starts. Phase 2: lane l decodes its 32 weights serially from that bit,
-// adds the k remainder bits, clamps ranks to 4 bits and writes its 16 nibble
-// bytes with one 16-byte store (so the chunk's output is one contiguous,
-// coalesced 1 KiB). Escapes (rank >= 15) wait in LDS until a second prefix
-// sum gives their place in the side list.
+// One wave decodes a run: one row-chunk (<= 2048 weights), or 2048 / cols
+// whole rows when rows are at most 1024 weights long.
+//  Phase 1: the lanes load the chunk's unary words (each weight's code ends
+//   in exactly one 1 bit) into LDS and popcount them; a wave prefix sum turns
+//   the counts into weight indices, and the lane holding the terminator of
+//   weight 32m-1 records where lane tile m starts.
+//  Phase 2: lane l decodes its 32 weights from LDS, 8 per read: a 32-bit
+//   window at the group's start bit (two LDS words, one funnel shift) holds
+//   the 8 codes, each ending at the window's lowest remaining 1 bit; rank =
+//   q << k | remainder bits (prefetched from global memory during phase 1).
+//   The loop has no branches: a lane's single escape is found from the
+//   largest (rank, index) it saw; only a lane with a code longer than its
+//   window, two escapes or a rank outside the table decodes again exactly.
+//  Each lane writes its 16 nibble bytes with one 16-byte store, so a chunk's
+//  output is one contiguous, coalesced 1 KiB. Escapes (rank >= 15) wait in
+//  LDS (8 per lane) until a prefix sum gives their place in the side list; a
+//  lane with more escapes writes them in a second, exact pass.
 #include <hip/hip_runtime.h>
 
 #include "binade.h"
@@ -28,6 +36,8 @@ namespace {
 using namespace dev;
 
 constexpr int kWavesPerBlock = 4;
+constexpr int kStageWords = 384;     // unary words staged per run (6 bits/weight)
+constexpr int kEscSlots = 8;         // escapes kept per lane in LDS
 
 struct RiceArgs {
   const uint32_t* unary;
@@ -48,19 +58,35 @@ struct RiceArgs {
   uint32_t table[64];  // exp_of_rank, 4 bytes per word
 };
 
+// The rank -> exponent table of a kernel's tensor, read in place from the
+// kernel's argument segment (only escapes look it up).
+__device__ __forceinline__ const uint8_t* kernarg_table(size_t args_offset) {
+  return (const uint8_t*)__builtin_amdgcn_kernarg_segment_ptr() + args_offset +
+         offsetof(RiceArgs, table);
+}
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t u = __shfl_up(v, d, 64);
-    if (lane >= d) v += u;
-  }
+// Inclusive prefix sum over the 64 lanes with DPP: shifts by 1, 2, 4, 8
+// inside each row of 16 lanes, then row 15 / lane 31 broadcasts carry the
+// row totals across rows.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
+  constexpr int kRowShr = 0x110, kBcast15 = 0x142, kBcast31 = 0x143;
+  v += __builtin_amdgcn_update_dpp(0u, v, kRowShr + 1, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0u, v, kRowShr + 2, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0u, v, kRowShr + 4, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0u, v, kRowShr + 8, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0u, v, kBcast15, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0u, v, kBcast31, 0xC, 0xF, false);
   return v;
+}
+
+__device__ __forceinline__ uint32_t lane63(uint32_t v) {
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Bit position of the n-th (0-based) set bit of v; v has more than n set.
@@ -88,148 +114,327 @@ __device__ __forceinline__ void flag(uint32_t* status, uint32_t bits,
   if (status != nullptr && lane == 0) atomicOr(status, bits);
 }
 
-__global__ __launch_bounds__(256) void rice_to_r4_kernel(RiceArgs a) {
-  __shared__ uint64_t tile_start[kWavesPerBlock][64];
-  __shared__ uint32_t esc_tmp[kWavesPerBlock][32][64];
-  __shared__ uint32_t expo_w[64];
+// Reads unary bits from a word source (LDS or global) through a 64-bit
+// buffer whose bit 0 is the next unread bit.
+template <bool kLds>
+struct BitReader {
+  const uint32_t* src;   // LDS words (relative) or global words (absolute)
+  uint64_t cap;          // words readable (global) / staged (LDS)
+  uint64_t buf;
+  uint32_t have;         // valid bits in buf
+  uint64_t next;         // index of the next word to append
+  uint32_t nxt;          // prefetched word `next`
+  uint64_t pos;          // bit position of buf's bit 0
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  if (threadIdx.x < 64) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int q = 0; q < 64; ++q)
-      if (static_cast<int>(threadIdx.x) == q) v = a.table[q];
-    expo_w[threadIdx.x] = v;
+  __device__ __forceinline__ uint32_t word(uint64_t i) const {
+    return i < cap ? src[i] : 0u;
   }
-  __syncthreads();
-  const uint8_t* expo = reinterpret_cast<const uint8_t*>(expo_w);
+  __device__ __forceinline__ void init(uint64_t bitpos) {
+    const uint64_t w = bitpos >> 5;
+    const uint32_t off = static_cast<uint32_t>(bitpos & 31u);
+    buf = ((static_cast<uint64_t>(word(w + 1)) << 32) | word(w)) >> off;
+    have = 64u - off;
+    next = w + 2;
+    nxt = word(next);
+    pos = bitpos;
+  }
+  // keep at least 33 valid bits
+  __device__ __forceinline__ void top_up() {
+    if (have < 33u) {
+      buf |= static_cast<uint64_t>(nxt) << have;
+      have += 32u;
+      ++next;
+      nxt = word(next);
+    }
+  }
+  // exact: zeros before the next 1 bit (the 1 is consumed); > 255 = corrupt
+  __device__ __forceinline__ uint32_t unary() {
+    uint32_t q = 0;
+    for (;;) {
+      top_up();
+      const uint32_t lo = static_cast<uint32_t>(buf);
+      if (lo != 0u) {
+        const uint32_t t = __builtin_ctz(lo);
+        buf >>= (t + 1u);
+        have -= t + 1u;
+        pos += t + 1u;
+        return q + t;
+      }
+      q += 32u;
+      buf >>= 32;
+      have -= 32u;
+      pos += 32u;
+      if (q > 255u) return q;
+    }
+  }
+};
 
-  const int64_t c = uniform64(static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave);
-  if (c >= a.n_chunks) return;
+// Exact serial decode of one lane tile (32 weights): fills out[4] with
+// nibbles, and writes escapes either to the LDS slots (emit == false; the
+// count may exceed the slots) or to the side list at esc_at (emit == true).
+// An escape's position is (run_off + i) mod chunk_mod. Returns false on a
+// corrupt code.
+template <bool kLds>
+__device__ bool decode_tile_exact(BitReader<kLds>& br, const RiceArgs& a,
+                                  const uint8_t* a_table, uint64_t rem_bit, uint32_t run_off,
+                                  uint32_t chunk_mod, uint32_t (&out)[4],
+                                  uint32_t& n_esc_lane, uint32_t* slots,
+                                  bool emit, uint32_t* esc_at) {
+  const uint32_t k = a.k;
+  out[0] = out[1] = out[2] = out[3] = 0;
+  n_esc_lane = 0;
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t q = br.unary();
+    if (q > 255u) return false;
+    uint32_t remv = 0;
+    if (k > 0) {
+      const uint64_t b = rem_bit + static_cast<uint64_t>(i) * k;
+      const uint64_t w = b >> 5;
+      const uint32_t off = static_cast<uint32_t>(b & 31u);
+      const uint64_t two = (static_cast<uint64_t>(load_word(a.rem, w + 1, a.rem_words)) << 32) |
+                           load_word(a.rem, w, a.rem_words);
+      remv = static_cast<uint32_t>(two >> off) & ((1u << k) - 1u);
+    }
+    const uint32_t r = (q << k) | remv;
+    if (r >= a.n) return false;
+    const uint32_t sh = 8u * ((i & 7) & 3) + 4u * ((i & 7) >> 2);
+    out[i >> 3] |= (r < 15u ? r : 15u) << sh;
+    if (r >= 15u) {
+      const uint32_t ent = (static_cast<uint32_t>(a_table[r & 0xFFu]) << 16) | ((run_off + i) % chunk_mod);
+      if (emit)
+        esc_at[n_esc_lane] = ent;
+      else if (n_esc_lane < kEscSlots)
+        slots[n_esc_lane * 64] = ent;
+      ++n_esc_lane;
+    }
+  }
+  return true;
+}
+
+// A wave's run of row-chunks: one row-chunk when rows are longer than a
+// chunk, else 2048 / cols whole rows.
+struct Run {
+  int64_t c0;      // first row-chunk
+  int64_t cnt;     // row-chunks in the run
+  int64_t fb;      // flat index of the first weight
+  int32_t len;     // weights in the run (multiple of 32, <= 2048)
+};
+
+__device__ __forceinline__ int64_t runs_total(const RiceArgs& a) {
   const int64_t C = (a.cols + kChunk - 1) / kChunk;
-  const int64_t row = c / C;
-  const int32_t j = static_cast<int32_t>(c - row * C);
-  const int32_t Lc = min(kChunk, a.cols - j * kChunk);
-  const int32_t T = Lc >> 5;
-  const uint64_t A = a.anchor[c];
-  const uint64_t B = a.anchor[c + 1];
-  const uint64_t fb = static_cast<uint64_t>(row) * a.cols + static_cast<uint64_t>(j) * kChunk;
+  if (C > 1) return a.n_chunks;
+  const int64_t G = kChunk / a.cols;
+  return (a.n_chunks + G - 1) / G;
+}
 
+__device__ __forceinline__ void run_of(const RiceArgs& a, int64_t r, Run& run) {
+  const int64_t C = (a.cols + kChunk - 1) / kChunk;
+  if (C == 1) {
+    const int64_t G = kChunk / a.cols;
+    run.c0 = r * G;
+    run.cnt = min(G, a.n_chunks - run.c0);
+    run.fb = run.c0 * a.cols;
+    run.len = static_cast<int32_t>(run.cnt * a.cols);
+  } else {
+    const uint32_t row = static_cast<uint32_t>(r) / static_cast<uint32_t>(C);
+    const int32_t j = static_cast<int32_t>(r - static_cast<int64_t>(row) * C);
+    run.c0 = r;
+    run.cnt = 1;
+    run.fb = static_cast<int64_t>(row) * a.cols + static_cast<int64_t>(j) * kChunk;
+    run.len = min(kChunk, a.cols - j * kChunk);
+  }
+}
+
+// What a wave loads first: the run's bounds, its first two unary words per
+// lane and the lane's remainder words.
+struct Prefetch {
+  uint64_t A, B;
+  uint32_t w0, w1;
+  uint32_t rw0, rw1;
+};
+
+__device__ __forceinline__ void prefetch_bounds(const RiceArgs& a, const Run& run,
+                                                Prefetch& pf) {
+  pf.A = a.anchor[run.c0];
+  pf.B = a.anchor[run.c0 + run.cnt];
+}
+
+__device__ __forceinline__ void prefetch_words(const RiceArgs& a, const Run& run,
+                                               int lane, Prefetch& pf) {
+  const uint64_t wA = pf.A >> 5;
+  const uint64_t wi = 2u * lane;
+  // words past the run (or past the plane) are masked or unused later
+  pf.w0 = load_word(a.unary, wA + wi, a.unary_words);
+  pf.w1 = load_word(a.unary, wA + wi + 1, a.unary_words);
+  const uint64_t rem_bit = (static_cast<uint64_t>(run.fb) + 32ull * lane) * a.k;
+  pf.rw0 = pf.rw1 = 0;
+  if (a.k == 1 || a.k == 2) {
+    pf.rw0 = load_word(a.rem, rem_bit >> 5, a.rem_words);
+    if (a.k == 2) pf.rw1 = load_word(a.rem, (rem_bit >> 5) + 1, a.rem_words);
+  }
+}
+
+// Decode one run (phases 1 and 2, escapes, nibble store).
+__device__ __forceinline__ void decode_run(const RiceArgs& a, const uint8_t* table,
+                                           const Run& run, const Prefetch& pf, int lane,
+                                           uint32_t* stage, uint32_t* tstart,
+                                           uint32_t* slots) {
+  const int64_t c = run.c0, cnt = run.cnt;
+  const int32_t Lc = run.len;
+  const int32_t T = Lc >> 5;
+  const uint64_t A = pf.A, B = pf.B;
+  const uint64_t fb = static_cast<uint64_t>(run.fb);
+  const uint32_t k = a.k;
   if (B < A + static_cast<uint64_t>(Lc) || B - A > 256ull * Lc ||
       B > a.unary_words * 32ull) {
     flag(a.status, BINADE_DEV_CORRUPT_STREAM, lane);
     return;
   }
+  const uint64_t rem_bit = (fb + 32ull * lane) * k;
 
-  // ---- phase 1: where does each lane tile start?
+  // ---- phase 1: stage the unary words, find where each lane tile starts
   const uint64_t wA = A >> 5;
   const uint64_t nw = ((B - 1) >> 5) - wA + 1;
-  if (lane == 0) tile_start[wave][0] = A;
+  const bool staged = nw <= static_cast<uint64_t>(kStageWords);
+  if (lane == 0) tstart[0] = static_cast<uint32_t>(A & 31u);
   uint32_t carry = 0;
   bool last_bit_set = false;
-  for (uint64_t base = 0; base < nw; base += 64) {
-    const uint64_t wi = base + lane;
-    uint32_t word = 0;
-    if (wi < nw) {
-      word = load_word(a.unary, wA + wi, a.unary_words);
-      if (wi == 0) word &= 0xFFFFFFFFu << (A & 31u);
-      if (wi == nw - 1) {
-        const uint32_t top = static_cast<uint32_t>((B - 1) & 31u);
-        word &= 0xFFFFFFFFu >> (31u - top);
-        last_bit_set = (word >> top) & 1u;
-      }
+  for (uint64_t base = 0; base < nw; base += 128) {
+    const uint64_t wi = base + 2u * lane;     // this lane's two words
+    uint32_t w0 = 0, w1 = 0;
+    if (base == 0) {
+      w0 = wi < nw ? pf.w0 : 0u;
+      w1 = wi + 1 < nw ? pf.w1 : 0u;
+    } else {
+      if (wi < nw) w0 = load_word(a.unary, wA + wi, a.unary_words);
+      if (wi + 1 < nw) w1 = load_word(a.unary, wA + wi + 1, a.unary_words);
     }
-    const uint32_t pc = __popc(word);
-    const uint32_t incl = wave_inclusive_sum(pc, lane);
+    if (staged) {
+      if (wi < nw) stage[wi] = w0;
+      if (wi + 1 < nw) stage[wi + 1] = w1;
+    }
+    if (wi == 0) w0 &= 0xFFFFFFFFu << (A & 31u);
+    const uint32_t top = static_cast<uint32_t>((B - 1) & 31u);
+    if (wi == nw - 1) {
+      w0 &= 0xFFFFFFFFu >> (31u - top);
+      last_bit_set = (w0 >> top) & 1u;
+    } else if (wi + 1 == nw - 1) {
+      w1 &= 0xFFFFFFFFu >> (31u - top);
+      last_bit_set = (w1 >> top) & 1u;
+    }
+    const uint32_t pc0 = __popc(w0);
+    const uint32_t pc = pc0 + __popc(w1);
+    const uint32_t incl = wave_inclusive_sum(pc);
     const uint32_t s_first = carry + incl - pc;
-    const uint32_t s = s_first | 31u;  // next weight index ending a lane tile
-    if (pc > 0 && s < s_first + pc) {
+    // weight indices 32m-1 ending in these 64 bits (at most two)
+    for (uint32_t s = s_first | 31u; s < s_first + pc; s += 32u) {
       const uint32_t m = (s + 1) >> 5;
-      if (static_cast<int32_t>(m) < T)
-        tile_start[wave][m] = (wA + wi) * 32ull + select_bit(word, s - s_first) + 1;
+      const uint32_t n = s - s_first;
+      const uint32_t bit = n < pc0 ? select_bit(w0, n) : 32u + select_bit(w1, n - pc0);
+      if (static_cast<int32_t>(m) < T) tstart[m] = static_cast<uint32_t>(wi * 32ull + bit + 1);
     }
-    carry += __shfl(incl, 63, 64);
+    carry += lane63(incl);
   }
+  if (staged && lane < 4) stage[nw + lane] = 0;  // reader look-ahead
   const bool ends_in_one = __any(last_bit_set);
   if (carry != static_cast<uint32_t>(Lc) || !ends_in_one) {
     flag(a.status, BINADE_DEV_CORRUPT_STREAM, lane);
     return;
   }
   wave_sync();
+  // Rows that start inside the run (short rows): lane m checks the row
+  // starting at its tile (rows starting inside a tile, when cols % 32 == 0
+  // but the tile holds two rows, do not occur: 32 | cols).
+  int64_t my_chunk = -1;
+  if (cnt > 1 && lane > 0 && lane < T && (32 * lane) % a.cols == 0)
+    my_chunk = c + (32 * lane) / a.cols;
+  if (cnt > 1) {
+    const bool off = my_chunk >= 0 &&
+                     static_cast<uint64_t>(tstart[lane]) + wA * 32ull != a.anchor[my_chunk];
+    if (__any(off)) {
+      flag(a.status, BINADE_DEV_CORRUPT_STREAM, lane);
+      return;
+    }
+  }
 
-  // ---- phase 2: lane l decodes weights 32l .. 32l+31 of the chunk
+  // ---- phase 2: lane l decodes weights 32l .. 32l+31 of the run
   uint32_t out[4] = {0, 0, 0, 0};
   uint32_t n_esc_lane = 0;
   bool bad = false;
+  const uint32_t run_off = 32u * lane;
+  const uint32_t chunk_mod = a.cols < kChunk ? static_cast<uint32_t>(a.cols) : kChunk;
+  const uint32_t start = lane < T ? tstart[lane] : 0u;
   if (lane < T) {
-    const uint64_t pos = tile_start[wave][lane];
-    uint64_t wnext = (pos >> 5) + 2;
-    const uint32_t off = static_cast<uint32_t>(pos & 31u);
-    uint64_t buf = (static_cast<uint64_t>(load_word(a.unary, wnext - 1, a.unary_words)) << 32 |
-                    load_word(a.unary, wnext - 2, a.unary_words)) >> off;
-    uint32_t have = 64u - off;
-
-    const uint32_t k = a.k;
-    const uint32_t kmask = (1u << k) - 1u;
-    uint64_t rbuf = 0;
-    uint32_t rhave = 0;
-    uint64_t rnext = 0;
-    if (k > 0) {
-      rnext = ((fb + 32ull * lane) * k) >> 5;  // word aligned: 32 | (fb + 32 l)
-      rbuf = static_cast<uint64_t>(load_word(a.rem, rnext + 1, a.rem_words)) << 32 |
-             load_word(a.rem, rnext, a.rem_words);
-      rnext += 2;
-      rhave = 64;
-    }
-
+    if (staged && k <= 2) {
+      // Fast path, branch-free: 8 weights per LDS read. A 32-bit window at
+      // the group's start bit holds the group's 8 codes unless one is long
+      // (then the window holds fewer than 8 one bits); code j ends at the
+      // window's j-th lowest 1 bit, found and then cleared. Every rank is
+      // exact; nibbles take min(rank, 15).
+      uint32_t p = start;
+      uint32_t fewest = 32;
+      uint32_t rmax = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      uint32_t q = 0;
-      while (buf == 0) {  // the code runs past the valid bits
-        q += have;
-        if (q > 255u) break;
-        buf = static_cast<uint64_t>(load_word(a.unary, wnext + 1, a.unary_words)) << 32 |
-              load_word(a.unary, wnext, a.unary_words);
-        wnext += 2;
-        have = 64;
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t w = p >> 5;
+        uint32_t cur = __builtin_amdgcn_alignbit(stage[w + 1], stage[w], p & 31u);
+        fewest = min(fewest, static_cast<uint32_t>(__popc(cur)));
+        const uint32_t rwd = (k == 2 && d >= 2) ? pf.rw1 : pf.rw0;
+        uint32_t prev = 0xFFFFFFFFu;
+        uint32_t o = 0;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const uint32_t t = static_cast<uint32_t>(__builtin_ctz(cur | 0x80000000u));
+          const uint32_t q = t + ~prev;                 // t - prev - 1
+          prev = t;
+          cur &= cur - 1u;
+          const uint32_t remv = __builtin_amdgcn_ubfe(rwd, ((8 * d + jj) * k) & 31u, k);
+          const uint32_t r = (q << k) | remv;
+          rmax = max(rmax, r);
+          o |= min(r, 15u) << (8u * (jj & 3) + 4u * (jj >> 2));
+        }
+        p += prev + 1u;
+        out[d] = o;
       }
-      if (q > 255u) {
-        bad = true;
-        break;
-      }
-      const uint32_t t = static_cast<uint32_t>(__builtin_ctzll(buf));
-      q += t;
-      const uint32_t sh = t + 1;
-      buf = sh >= 64 ? 0ull : (buf >> sh);
-      have -= sh;
-      if (have < 32) {
-        buf |= static_cast<uint64_t>(load_word(a.unary, wnext, a.unary_words)) << have;
-        ++wnext;
-        have += 32;
-      }
-      uint32_t remv = 0;
-      if (k > 0) {
-        remv = static_cast<uint32_t>(rbuf) & kmask;
-        rbuf >>= k;
-        rhave -= k;
-        if (rhave < 32) {
-          rbuf |= static_cast<uint64_t>(load_word(a.rem, rnext, a.rem_words)) << rhave;
-          ++rnext;
-          rhave += 32;
+      bool exact = fewest < 8u || rmax >= a.n;
+      if (!exact && rmax >= 15u) {
+        // one escape: the tile's only nibble 15, and its rank is the largest
+        int found = -1;
+        uint32_t n15 = 0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t v = out[d];
+          const uint32_t ones = v & (v >> 1) & (v >> 2) & (v >> 3) & 0x11111111u;
+          n15 += __popc(ones);
+          if (ones != 0u && found < 0) {
+            const uint32_t bp = __builtin_ctz(ones);          // 0, 4, 8, ... 28
+            found = 8 * d + static_cast<int>((bp >> 3) + 4 * ((bp >> 2) & 1u));
+          }
+        }
+        if (n15 == 1u) {
+          slots[0] = (static_cast<uint32_t>(table[rmax & 0xFFu]) << 16) | ((run_off + found) % chunk_mod);
+          n_esc_lane = 1;
+        } else {
+          exact = true;
         }
       }
-      const uint32_t r = (q << k) | remv;
-      if (r >= a.n) {
-        bad = true;
-        break;
+      if (exact) {
+        BitReader<true> lr{stage, nw + 4, 0, 0, 0, 0, 0};
+        lr.init(start);
+        bad = !decode_tile_exact(lr, a, table, rem_bit, run_off, chunk_mod, out, n_esc_lane, slots,
+                                 false, nullptr);
       }
-      const uint32_t v = r < 15u ? r : 15u;
-      out[i >> 3] |= v << (8 * ((i & 7) & 3) + 4 * ((i & 7) >> 2));
-      if (r >= 15u) {
-        esc_tmp[wave][n_esc_lane][lane] =
-            (static_cast<uint32_t>(expo[r]) << 16) | static_cast<uint32_t>(32 * lane + i);
-        ++n_esc_lane;
+    } else {
+      if (staged) {
+        BitReader<true> lr{stage, nw + 4, 0, 0, 0, 0, 0};
+        lr.init(start);
+        bad = !decode_tile_exact(lr, a, table, rem_bit, run_off, chunk_mod, out, n_esc_lane, slots,
+                                 false, nullptr);
+      } else {
+        BitReader<false> gr{a.unary, a.unary_words, 0, 0, 0, 0, 0};
+        gr.init(wA * 32ull + start);
+        bad = !decode_tile_exact(gr, a, table, rem_bit, run_off, chunk_mod, out, n_esc_lane, slots,
+                                 false, nullptr);
       }
     }
   }
@@ -239,21 +444,101 @@ __global__ __launch_bounds__(256) void rice_to_r4_kernel(RiceArgs a) {
   }
 
   // ---- escapes: place in the side list after a prefix sum over lanes
-  const uint32_t incl = wave_inclusive_sum(n_esc_lane, lane);
-  const uint32_t total = __shfl(incl, 63, 64);
   const uint32_t e0 = a.esc_pre[c];
-  const uint32_t e1 = a.esc_pre[c + 1];
-  if (e1 < e0 || e1 - e0 != total || e1 > a.n_esc) {
-    flag(a.status, BINADE_DEV_CORRUPT_ESC, lane);
+  const uint32_t e1 = a.esc_pre[c + cnt];
+  uint32_t before, total;
+  if (__ballot(n_esc_lane > 1u) == 0) {
+    const uint64_t has = __ballot(n_esc_lane != 0u);
+    before = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(has >> 32),
+                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(has), 0u));
+    total = __popcll(has);
   } else {
-    const uint32_t base = e0 + incl - n_esc_lane;
-    for (uint32_t i = 0; i < n_esc_lane; ++i) a.esc[base + i] = esc_tmp[wave][i][lane];
+    const uint32_t incl = wave_inclusive_sum(n_esc_lane);
+    before = incl - n_esc_lane;
+    total = lane63(incl);
+  }
+  const bool esc_off = my_chunk >= 0 && a.esc_pre[my_chunk] != e0 + before;
+  if (e1 < e0 || e1 - e0 != total || e1 > a.n_esc || __any(esc_off)) {
+    flag(a.status, BINADE_DEV_CORRUPT_ESC, lane);
+  } else if (n_esc_lane > 0) {
+    uint32_t* dst = a.esc + (e0 + before);
+    if (n_esc_lane <= static_cast<uint32_t>(kEscSlots)) {
+      for (uint32_t i = 0; i < n_esc_lane; ++i) dst[i] = slots[i * 64];
+    } else {
+      // more escapes than slots: decode the tile again, writing them out
+      uint32_t o2[4], cnt2 = 0;
+      if (staged) {
+        BitReader<true> lr{stage, nw + 4, 0, 0, 0, 0, 0};
+        lr.init(start);
+        decode_tile_exact(lr, a, table, rem_bit, run_off, chunk_mod, o2, cnt2, slots, true, dst);
+      } else {
+        BitReader<false> gr{a.unary, a.unary_words, 0, 0, 0, 0, 0};
+        gr.init(wA * 32ull + start);
+        decode_tile_exact(gr, a, table, rem_bit, run_off, chunk_mod, o2, cnt2, slots, true, dst);
+      }
+    }
   }
   if (lane < T) {
-    uint4* dst = reinterpret_cast<uint4*>(a.nib + static_cast<uint64_t>(row) * (a.cols >> 1) +
-                                          static_cast<uint64_t>(j) * (kChunk / 2) + 16u * lane);
+    uint4* dst = reinterpret_cast<uint4*>(a.nib + (fb >> 1) + 16u * lane);
     *dst = make_uint4(out[0], out[1], out[2], out[3]);
   }
+}
+
+__device__ __forceinline__ void decode_wave(const RiceArgs& a, const uint8_t* table,
+                                            int64_t r, int lane, uint32_t* stage,
+                                            uint32_t* tstart, uint32_t* slots) {
+  Run run;
+  Prefetch pf;
+  run_of(a, r, run);
+  prefetch_bounds(a, run, pf);
+  prefetch_words(a, run, lane, pf);
+  decode_run(a, table, run, pf, lane, stage, tstart, slots);
+}
+
+// One wave per run; the run's anchors, first unary words and remainder
+// words are requested before any other work.
+__global__ __launch_bounds__(256) void rice_to_r4_kernel(RiceArgs a) {
+  __shared__ uint32_t stage[kWavesPerBlock][kStageWords + 4];
+  __shared__ uint32_t tile_start[kWavesPerBlock][64];   // relative to the first staged word
+  __shared__ uint32_t esc_tmp[kWavesPerBlock][kEscSlots][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t r = uniform64(static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave);
+  if (r >= runs_total(a)) return;
+  decode_wave(a, kernarg_table(0), r, lane, stage[wave], tile_start[wave],
+              &esc_tmp[wave][0][lane]);
+}
+
+// Several tensors in one launch: tensor i owns blocks
+// [first_block[i], first_block[i+1]).
+constexpr int kMaxDecodeBatch = 8;
+struct RiceBatch {
+  RiceArgs item[kMaxDecodeBatch];
+  uint32_t first_block[kMaxDecodeBatch + 1];
+  int32_t count;
+};
+
+__global__ __launch_bounds__(256) void rice_to_r4_batch_kernel(RiceBatch b) {
+  __shared__ uint32_t stage[kWavesPerBlock][kStageWords + 4];
+  __shared__ uint32_t tile_start[kWavesPerBlock][64];
+  __shared__ uint32_t esc_tmp[kWavesPerBlock][kEscSlots][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t blk = blockIdx.x;
+  int i = 0;
+#pragma unroll
+  for (int t = 1; t < kMaxDecodeBatch; ++t)
+    if (t < b.count && blk >= b.first_block[t]) i = t;
+  i = uniform(i);
+  // read the item in place from the argument segment (an index into a
+  // by-value argument array would be copied to scratch memory)
+  const size_t off = offsetof(RiceBatch, item) + static_cast<size_t>(i) * sizeof(RiceArgs);
+  const RiceArgs* items = (const RiceArgs*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + off);
+  const RiceArgs a = items[0];
+  const int64_t r = uniform64(static_cast<int64_t>(blk - b.first_block[i]) * kWavesPerBlock + wave);
+  if (r >= runs_total(a)) return;
+  decode_wave(a, kernarg_table(off), r, lane, stage[wave], tile_start[wave],
+              &esc_tmp[wave][0][lane]);
 }
 
 }  // namespace
@@ -261,8 +546,12 @@ __global__ __launch_bounds__(256) void rice_to_r4_kernel(RiceArgs a) {
 
 using namespace binade;
 
-extern "C" int32_t binade_rice_to_r4(const binade_rice* in, binade_r4* out,
-                                     uint32_t* dev_status, void* stream) {
+namespace {
+
+// Checks one format 2 -> R4 request and fills its kernel arguments and the
+// host-visible R4 fields. Returns the number of runs (waves) or a status.
+int64_t prepare_decode(const binade_rice* in, binade_r4* out, uint32_t* dev_status,
+                       RiceArgs& a) {
   if (in == nullptr || out == nullptr || in->rows <= 0 || in->cols <= 0 ||
       in->n == 0 || in->n > 256 || in->k > 7)
     return BINADE_EINVAL;
@@ -279,6 +568,7 @@ extern "C" int32_t binade_rice_to_r4(const binade_rice* in, binade_r4* out,
   if (in->n_esc > 0xFFFFFFFFull) return BINADE_EUNSUPPORTED;
   const int64_t C = (in->cols + BINADE_CHUNK - 1) / BINADE_CHUNK;
   const int64_t n_chunks = in->rows * C;
+  if (n_chunks >= (1ll << 31)) return BINADE_EUNSUPPORTED;
 
   out->rows = in->rows;
   out->cols = in->cols;
@@ -288,7 +578,7 @@ extern "C" int32_t binade_rice_to_r4(const binade_rice* in, binade_r4* out,
   for (int r = 0; r < 16; ++r)
     out->lut[r] = (r < 15 && static_cast<uint32_t>(r) < in->n) ? in->exp_of_rank[r] : 0;
 
-  RiceArgs a{};
+  a = RiceArgs{};
   a.unary = in->unary;
   a.rem = in->rem;
   a.anchor = in->anchor;
@@ -308,8 +598,46 @@ extern "C" int32_t binade_rice_to_r4(const binade_rice* in, binade_r4* out,
     a.table[q] = uint32_t(in->exp_of_rank[4 * q]) | (uint32_t(in->exp_of_rank[4 * q + 1]) << 8) |
                  (uint32_t(in->exp_of_rank[4 * q + 2]) << 16) |
                  (uint32_t(in->exp_of_rank[4 * q + 3]) << 24);
-  const dim3 grid(static_cast<uint32_t>((n_chunks + kWavesPerBlock - 1) / kWavesPerBlock));
+  // runs: one row-chunk, or 2048 / cols short rows; one wave each
+  return C == 1 ? (in->rows + (BINADE_CHUNK / in->cols) - 1) / (BINADE_CHUNK / in->cols)
+                : n_chunks;
+}
+
+}  // namespace
+
+extern "C" int32_t binade_rice_to_r4(const binade_rice* in, binade_r4* out,
+                                     uint32_t* dev_status, void* stream) {
+  RiceArgs a;
+  const int64_t runs = prepare_decode(in, out, dev_status, a);
+  if (runs < 0) return static_cast<int32_t>(runs);
+  const dim3 grid(static_cast<uint32_t>((runs + kWavesPerBlock - 1) / kWavesPerBlock));
   hipLaunchKernelGGL(rice_to_r4_kernel, grid, dim3(64 * kWavesPerBlock), 0,
                      static_cast<hipStream_t>(stream), a);
   return launch_status();
+}
+
+extern "C" int32_t binade_rice_to_r4_batch(const binade_rice* in, binade_r4* out,
+                                           int32_t count, uint32_t* dev_status,
+                                           void* stream) {
+  if (count < 0 || (count > 0 && (in == nullptr || out == nullptr))) return BINADE_EINVAL;
+  for (int32_t base = 0; base < count; base += kMaxDecodeBatch) {
+    RiceBatch b{};
+    uint64_t blocks = 0;
+    int n = 0;
+    for (int32_t i = base; i < count && n < kMaxDecodeBatch; ++i) {
+      const int64_t runs = prepare_decode(&in[i], &out[i], dev_status, b.item[n]);
+      if (runs < 0) return static_cast<int32_t>(runs);
+      b.first_block[n] = static_cast<uint32_t>(blocks);
+      blocks += static_cast<uint64_t>((runs + kWavesPerBlock - 1) / kWavesPerBlock);
+      ++n;
+    }
+    if (blocks > 0x7FFFFFFFull) return BINADE_EUNSUPPORTED;
+    b.first_block[n] = static_cast<uint32_t>(blocks);
+    b.count = n;
+    hipLaunchKernelGGL(rice_to_r4_batch_kernel, dim3(static_cast<uint32_t>(blocks)),
+                       dim3(64 * kWavesPerBlock), 0, static_cast<hipStream_t>(stream), b);
+    const int32_t s = launch_status();
+    if (s != BINADE_OK) return s;
+  }
+  return BINADE_OK;
 }

@@ -29,7 +29,8 @@
  *     i * ceil(cols / BINADE_CHUNK) + c. Format 2 stores one unary-bit anchor
  *     and one escape prefix per row-chunk; R4 reuses the escape prefix.
  *
- * Format 2 (on-disk layout, readings of the pages stated in the design doc):
+ * Format 2 (on-disk layout; the pages give no byte layout, so these are this
+ * library's readings):
  *   sm      u8[rows*cols]   (sign << 7) | mantissa
  *   unary   u32 words       per weight in row-major order: q = rank >> k zero
  *                           bits, then a one; bit p is bit p%32 of word p/32
@@ -102,7 +103,7 @@ typedef struct binade_rice {
   uint8_t *sm;
   uint32_t *unary;
   uint64_t unary_bits;
-  uint64_t unary_words;   /* words the buffer holds (>= binade_rice_sizes) */
+  uint64_t unary_words;   /* words the buffer holds (>= binade_sizes_of's) */
   uint32_t *rem;
   uint64_t rem_words;
   uint64_t *anchor;       /* chunks + 1 */
@@ -176,6 +177,13 @@ int32_t binade_pack_rice(const uint16_t *w, int64_t rows, int64_t cols,
 int32_t binade_rice_to_r4(const binade_rice *in, binade_r4 *out,
                           uint32_t *dev_status, void *stream);
 
+/* Format 2 -> R4 for count tensors, up to 8 per launch (a model's load-time
+ * decode): in[i] and out[i] as for binade_rice_to_r4; the same kernel and
+ * results. The argument checks of every tensor run before its launch. */
+int32_t binade_rice_to_r4_batch(const binade_rice *in, binade_r4 *out,
+                                int32_t count, uint32_t *dev_status,
+                                void *stream);
+
 /* R4 -> bf16 bits [rows, cols] on the GPU (the rebuild path; "Binade"
  * package page, "Use": unpack restores the original BF16 bit for bit). */
 int32_t binade_unpack(const binade_r4 *w, uint16_t *out, void *stream);
@@ -190,6 +198,14 @@ int32_t binade_unpack(const binade_r4 *w, uint16_t *out, void *stream);
  * p[l] += p[l+s] for s = 32, 16, 8, 4, 2, 1; y = p[0]. */
 int32_t binade_r4_gemv(const binade_r4 *w, const uint16_t *x, void *y,
                        int32_t y_dtype, void *stream);
+
+/* count independent products y_i = W_i x_i (ws[i], xs[i], ys[i] as for
+ * binade_r4_gemv), up to 16 per launch: the products a decode step issues
+ * together, such as one layer's q, k and v projections or its gate and up
+ * projections. Every y_i is bit-identical to binade_r4_gemv's. */
+int32_t binade_r4_gemv_batch(const binade_r4 *ws, const uint16_t *const *xs,
+                             void *const *ys, int32_t count, int32_t y_dtype,
+                             void *stream);
 
 /* The same product and order with W given as plain bf16 [N, K] (device):
  * the exactness twin and the speed reference. */

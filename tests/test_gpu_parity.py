@@ -271,3 +271,27 @@ def test_gemm_random_twin_and_f64(mnk):
     assert torch.all((Y.double() - ref).abs() <= 1e-2 * scale)
     Yb = B.r4_gemm(r4, X.to(DEV), out_dtype=torch.bfloat16).cpu()
     assert np.array_equal(bits_np(Yb), oracle.f32_to_bf16(Y.numpy()))
+
+
+# ---------------------------------------------------------- batched launches
+def test_batched_decode_and_gemv_equal_single_calls():
+    shapes = [(300, 3072), (64, 8192), (37, 96), (4100, 256), (5, 4160), (1024, 1024),
+              (19, 15360), (128, 2816), (33, 704), (8, 2080)] * 2   # 20: two launches each
+    ws = [synth.normal_bf16(spec(n, k, 0.02, 200 + i, 1e-3, 20.0)) for i, (n, k) in enumerate(shapes)]
+    planes = [B.pack_rice(w).to(DEV) for w in ws]
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    outs = B.rice_to_r4_batch(planes, status=status)
+    singles = [B.rice_to_r4(p) for p in planes]
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for o, s1 in zip(outs, singles):
+        assert o.lut == s1.lut
+        assert torch.equal(o.nib, s1.nib)
+        assert torch.equal(o.esc[: o.n_esc], s1.esc[: s1.n_esc])
+    xs = [synth.vector_bf16(k, 300 + i).to(DEV) for i, (n, k) in enumerate(shapes)]
+    ys = B.r4_gemv_batch(outs, xs)
+    for i, (o, x, y) in enumerate(zip(outs, xs, ys)):
+        y1 = B.r4_gemv(o, x)
+        assert torch.equal(y.view(torch.int32), y1.view(torch.int32)), shapes[i]
+    wn = bits_np(ws[0])
+    assert same_f32(ys[0].cpu().numpy(), oracle.gemv_replay(wn, bits_np(xs[0].cpu())))
