@@ -26,7 +26,7 @@ DEV_CORRUPT_STREAM, DEV_BAD_INDEX, DEV_CORRUPT_ESC = 0x1, 0x2, 0x4
 EXPORTS = ["binade_status_str", "binade_last_hip_error", "binade_build_table",
            "binade_sizes_of", "binade_pack_rice", "binade_rice_to_r4",
            "binade_rice_to_r4_batch", "binade_unpack", "binade_r4_gemv",
-           "binade_r4_gemv_batch", "binade_bf16_gemv",
+           "binade_r4_gemv_batch", "binade_bf16_gemv", "binade_bf16_gemv_batch",
            "binade_r4_gemm", "binade_bf16_gemm", "binade_r4_moe_gemv",
            "binade_bf16_moe_gemv"]
 
@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
                 "binade_rice_to_r4": [P, P, P, P],
                 "binade_rice_to_r4_batch": [P, P, I32, P, P],
                 "binade_r4_gemv_batch": [P, P, P, I32, I32, P],
+                "binade_bf16_gemv_batch": [P, P, P, P, P, I32, I32, P],
                 "binade_unpack": [P, P, P],
                 "binade_r4_gemv": [P, P, P, I32, P],
                 "binade_bf16_gemv": [P, I64, I64, P, P, I32, P],
@@ -337,6 +338,23 @@ def r4_gemv_batch(ws: list, xs: list, out_dtype=torch.float32,
     dxs = (ctypes.c_void_p * n)(*[_bits16(x).data_ptr() for x in xs])
     dys = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
     _call("binade_r4_gemv_batch", dws, dxs, dys, n, code, _stream(stream))
+    return ys
+
+
+def bf16_gemv_batch(ws: list, xs: list, out_dtype=torch.float32,
+                    ys: list | None = None, stream=None) -> list:
+    """binade_bf16_gemv_batch: the batched twin."""
+    code = _dtype_code(out_dtype)
+    n = len(ws)
+    ws = [_bits16(w) for w in ws]
+    if ys is None:
+        ys = [_y((w.shape[0],), code, x.device, None) for w, x in zip(ws, xs)]
+    dws = (ctypes.c_void_p * n)(*[w.data_ptr() for w in ws])
+    rows = (ctypes.c_int64 * n)(*[w.shape[0] for w in ws])
+    cols = (ctypes.c_int64 * n)(*[w.shape[1] for w in ws])
+    dxs = (ctypes.c_void_p * n)(*[_bits16(x).data_ptr() for x in xs])
+    dys = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+    _call("binade_bf16_gemv_batch", dws, rows, cols, dxs, dys, n, code, _stream(stream))
     return ys
 
 

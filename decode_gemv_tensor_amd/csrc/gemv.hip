@@ -184,6 +184,9 @@ __global__ __launch_bounds__(256) void r4_gemv_kernel(GemvArgs a) {
   r4_gemv_rows<R, kPrefetch>(a, row0, lane);
 }
 
+template <int R>
+__device__ __forceinline__ void bf16_gemv_rows(const GemvArgs& a, int64_t row0, int lane);
+
 // Several independent products in one launch: items 0..count-1 own the
 // consecutive block ranges [first_block[i], first_block[i+1]).
 constexpr int kMaxBatch = 16;
@@ -193,8 +196,8 @@ struct GemvBatch {
   int32_t count;
 };
 
-template <int R>
-__global__ __launch_bounds__(256) void r4_gemv_batch_kernel(GemvBatch b) {
+template <int R, bool kR4>
+__global__ __launch_bounds__(256) void gemv_batch_kernel(GemvBatch b) {
   const int lane = threadIdx.x & 63;
   const uint32_t blk = blockIdx.x;
   int i = 0;
@@ -209,16 +212,14 @@ __global__ __launch_bounds__(256) void r4_gemv_batch_kernel(GemvBatch b) {
   const int64_t row0 = uniform64((static_cast<int64_t>(blk - b.first_block[i]) * (blockDim.x >> 6) +
                                   (threadIdx.x >> 6)) * R);
   if (row0 >= a.rows) return;
-  r4_gemv_rows<R, false>(a, row0, lane);
+  if (kR4)
+    r4_gemv_rows<R, false>(a, row0, lane);
+  else
+    bf16_gemv_rows<R>(a, row0, lane);
 }
 
 template <int R>
-__global__ __launch_bounds__(256) void bf16_gemv_kernel(GemvArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row0 =
-      uniform64((static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) +
-                 (threadIdx.x >> 6)) * R);
-  if (row0 >= a.rows) return;
+__device__ __forceinline__ void bf16_gemv_rows(const GemvArgs& a, int64_t row0, int lane) {
   const int J = a.cols >> 5;
   const int C = (J + 63) >> 6;
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.sm);
@@ -264,6 +265,16 @@ __global__ __launch_bounds__(256) void bf16_gemv_kernel(GemvArgs a) {
     const float p = slot_tree(acc0[r] + acc1[r]);
     if (lane == 0 && row < a.rows) store_y(a, row, p);
   }
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void bf16_gemv_kernel(GemvArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 =
+      uniform64((static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) +
+                 (threadIdx.x >> 6)) * R);
+  if (row0 >= a.rows) return;
+  bf16_gemv_rows<R>(a, row0, lane);
 }
 
 // One wave per row-chunk; lane l rebuilds its tile's 32 bf16 patterns.
@@ -354,8 +365,8 @@ struct GemvShape {
 };
 
 GemvShape gemv_shape(int64_t rows) {
-  GemvShape s{1, false};
-  if (rows >= 8192) s.rows_per_wave = 2;
+  (void)rows;
+  GemvShape s{1, false};   // one row per wave measured fastest at every shape
   if (const char* env = getenv("BINADE_GEMV_ROWS_PER_WAVE")) {
     const int r = atoi(env);
     if (r == 1 || r == 2 || r == 4) s.rows_per_wave = r;
@@ -408,6 +419,44 @@ extern "C" int32_t binade_r4_gemv(const binade_r4* w, const uint16_t* x,
   return launch_gemv(a, true, static_cast<hipStream_t>(stream));
 }
 
+namespace binade {
+namespace {
+
+// Launches `items` in groups of kMaxBatch (one launch per group).
+int32_t launch_gemv_batch(const GemvArgs* items, int32_t count, bool r4, hipStream_t stream) {
+  const int R = gemv_shape(0).rows_per_wave == 1 ? 1 : 2;
+  for (int32_t base = 0; base < count; base += kMaxBatch) {
+    GemvBatch b{};
+    uint64_t blocks = 0;
+    int n = 0;
+    for (int32_t i = base; i < count && n < kMaxBatch; ++i) {
+      b.item[n] = items[i];
+      b.first_block[n] = static_cast<uint32_t>(blocks);
+      const int64_t waves = (items[i].rows + R - 1) / R;
+      blocks += static_cast<uint64_t>((waves + 3) / 4);
+      ++n;
+    }
+    if (blocks == 0) continue;
+    if (blocks > 0x7FFFFFFFull) return BINADE_EUNSUPPORTED;
+    b.first_block[n] = static_cast<uint32_t>(blocks);
+    b.count = n;
+    const dim3 grid(static_cast<uint32_t>(blocks));
+    if (r4) {
+      if (R == 2) hipLaunchKernelGGL((gemv_batch_kernel<2, true>), grid, dim3(256), 0, stream, b);
+      else hipLaunchKernelGGL((gemv_batch_kernel<1, true>), grid, dim3(256), 0, stream, b);
+    } else {
+      if (R == 2) hipLaunchKernelGGL((gemv_batch_kernel<2, false>), grid, dim3(256), 0, stream, b);
+      else hipLaunchKernelGGL((gemv_batch_kernel<1, false>), grid, dim3(256), 0, stream, b);
+    }
+    const int32_t s = launch_status();
+    if (s != BINADE_OK) return s;
+  }
+  return BINADE_OK;
+}
+
+}  // namespace
+}  // namespace binade
+
 extern "C" int32_t binade_r4_gemv_batch(const binade_r4* ws,
                                         const uint16_t* const* xs,
                                         void* const* ys, int32_t count,
@@ -415,41 +464,54 @@ extern "C" int32_t binade_r4_gemv_batch(const binade_r4* ws,
   if (count < 0 || (count > 0 && (ws == nullptr || xs == nullptr || ys == nullptr)))
     return BINADE_EINVAL;
   if (y_dtype != BINADE_F32 && y_dtype != BINADE_BF16) return BINADE_EINVAL;
-  for (int32_t i = 0; i < count; ++i) {
-    const int32_t s = check_r4(&ws[i]);
-    if (s != BINADE_OK) return s;
-    if (ws[i].rows > 0 && (xs[i] == nullptr || ys[i] == nullptr)) return BINADE_EINVAL;
-    if (ws[i].rows > 0 && !aligned16(xs[i])) return BINADE_EUNSUPPORTED;
-  }
-  const int R = gemv_shape(0).rows_per_wave == 1 ? 1 : 2;  // small shapes favour 1
+  GemvArgs items[kMaxBatch];
   for (int32_t base = 0; base < count; base += kMaxBatch) {
-    GemvBatch b{};
-    uint64_t blocks = 0;
     int n = 0;
-    for (int32_t i = base; i < count && n < kMaxBatch; ++i) {
+    for (int32_t i = base; i < count && i < base + kMaxBatch; ++i) {
+      const int32_t s = check_r4(&ws[i]);
+      if (s != BINADE_OK) return s;
       if (ws[i].rows == 0) continue;
+      if (xs[i] == nullptr || ys[i] == nullptr) return BINADE_EINVAL;
+      if (!aligned16(xs[i])) return BINADE_EUNSUPPORTED;
       GemvArgs a = args_from_r4(&ws[i], true);
       a.x = xs[i];
       a.y = ys[i];
       a.y_bf16 = y_dtype == BINADE_BF16;
-      b.item[n] = a;
-      b.first_block[n] = static_cast<uint32_t>(blocks);
-      const int64_t waves = (a.rows + R - 1) / R;
-      blocks += static_cast<uint64_t>((waves + 3) / 4);
-      ++n;
+      items[n++] = a;
     }
-    if (n == 0) continue;
-    if (blocks > 0x7FFFFFFFull) return BINADE_EUNSUPPORTED;
-    b.first_block[n] = static_cast<uint32_t>(blocks);
-    b.count = n;
-    const dim3 grid(static_cast<uint32_t>(blocks));
-    if (R == 2)
-      hipLaunchKernelGGL(r4_gemv_batch_kernel<2>, grid, dim3(256), 0,
-                         static_cast<hipStream_t>(stream), b);
-    else
-      hipLaunchKernelGGL(r4_gemv_batch_kernel<1>, grid, dim3(256), 0,
-                         static_cast<hipStream_t>(stream), b);
-    const int32_t s = launch_status();
+    const int32_t s = launch_gemv_batch(items, n, true, static_cast<hipStream_t>(stream));
+    if (s != BINADE_OK) return s;
+  }
+  return BINADE_OK;
+}
+
+extern "C" int32_t binade_bf16_gemv_batch(const uint16_t* const* ws, const int64_t* rows,
+                                          const int64_t* cols, const uint16_t* const* xs,
+                                          void* const* ys, int32_t count, int32_t y_dtype,
+                                          void* stream) {
+  if (count < 0 || (count > 0 && (ws == nullptr || rows == nullptr || cols == nullptr ||
+                                  xs == nullptr || ys == nullptr)))
+    return BINADE_EINVAL;
+  if (y_dtype != BINADE_F32 && y_dtype != BINADE_BF16) return BINADE_EINVAL;
+  GemvArgs items[kMaxBatch];
+  for (int32_t base = 0; base < count; base += kMaxBatch) {
+    int n = 0;
+    for (int32_t i = base; i < count && i < base + kMaxBatch; ++i) {
+      if (rows[i] < 0 || cols[i] <= 0) return BINADE_EINVAL;
+      if (cols[i] % 32 != 0 || cols[i] > (1 << 30)) return BINADE_EUNSUPPORTED;
+      if (rows[i] == 0) continue;
+      if (ws[i] == nullptr || xs[i] == nullptr || ys[i] == nullptr) return BINADE_EINVAL;
+      if (!aligned16(ws[i]) || !aligned16(xs[i])) return BINADE_EUNSUPPORTED;
+      GemvArgs a{};
+      a.sm = reinterpret_cast<const uint8_t*>(ws[i]);
+      a.rows = rows[i];
+      a.cols = static_cast<int32_t>(cols[i]);
+      a.x = xs[i];
+      a.y = ys[i];
+      a.y_bf16 = y_dtype == BINADE_BF16;
+      items[n++] = a;
+    }
+    const int32_t s = launch_gemv_batch(items, n, false, static_cast<hipStream_t>(stream));
     if (s != BINADE_OK) return s;
   }
   return BINADE_OK;

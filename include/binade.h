@@ -207,6 +207,13 @@ int32_t binade_r4_gemv_batch(const binade_r4 *ws, const uint16_t *const *xs,
                              void *const *ys, int32_t count, int32_t y_dtype,
                              void *stream);
 
+/* The batched twin: count products y_i = W_i x_i with plain bf16 W_i
+ * [rows[i], cols[i]] (device), up to 16 per launch, in the same order. */
+int32_t binade_bf16_gemv_batch(const uint16_t *const *ws, const int64_t *rows,
+                               const int64_t *cols, const uint16_t *const *xs,
+                               void *const *ys, int32_t count, int32_t y_dtype,
+                               void *stream);
+
 /* The same product and order with W given as plain bf16 [N, K] (device):
  * the exactness twin and the speed reference. */
 int32_t binade_bf16_gemv(const uint16_t *w, int64_t rows, int64_t cols,

@@ -295,3 +295,7 @@ def test_batched_decode_and_gemv_equal_single_calls():
         assert torch.equal(y.view(torch.int32), y1.view(torch.int32)), shapes[i]
     wn = bits_np(ws[0])
     assert same_f32(ys[0].cpu().numpy(), oracle.gemv_replay(wn, bits_np(xs[0].cpu())))
+    yt = B.bf16_gemv_batch([w.to(DEV) for w in ws], xs, out_dtype=torch.bfloat16)
+    for i, (o, x, y) in enumerate(zip(outs, xs, yt)):
+        y1 = B.r4_gemv(o, x, out_dtype=torch.bfloat16)
+        assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), shapes[i]
