@@ -10,6 +10,23 @@
 //
 // One wave decodes a run: one row-chunk (<= 2048 weights), or 2048 / cols
 // whole rows when rows are at most 1024 weights long.
+//
+// Byte-table path (Rice k of 0 or 1, tables of at least 15 exponents, runs
+// whose unary bits fit 4096 bits; the tensors of LLM layers):
+//  Each lane takes a contiguous range of unary bytes. One LDS table entry per
+//  byte value gives, for the codes that end in that byte, their q << k packed
+//  as nibbles, the first code's zeros inside the byte, and the zeros left
+//  over after the last code; the zeros carried in from earlier bytes only
+//  touch the first code. A lane's first weight index comes from a wave prefix
+//  sum of its byte range's one bits, its carried zeros from a wave prefix
+//  maximum of the last one-bit positions. The nibbles go, in weight order,
+//  into a 1 KiB LDS buffer by OR; each lane then reads its 32 weights back,
+//  puts them in R4 nibble order, adds the remainder bits (an LDS table spreads
+//  8 of them to their nibbles) and writes 16 bytes. A code whose rank may
+//  reach 15 takes a rare branch that computes the rank exactly and keeps it
+//  as an escape.
+//
+// General path (every other tensor):
 //  Phase 1: the lanes load the chunk's unary words (each weight's code ends
 //   in exactly one 1 bit) into LDS and popcount them; a wave prefix sum turns
 //   the counts into weight indices, and the lane holding the terminator of
@@ -38,6 +55,66 @@ using namespace dev;
 constexpr int kWavesPerBlock = 4;
 constexpr int kStageWords = 384;     // unary words staged per run (6 bits/weight)
 constexpr int kEscSlots = 8;         // escapes kept per lane in LDS
+constexpr int kByteSlots = 4;        // escapes kept per lane (byte-table path)
+constexpr uint32_t kByteMaxBits = 4096;  // unary bits per run (byte-table path)
+// LDS words per wave: staged unary words, then 64 words (lane tile starts or
+// the run's remainder words), then the escape slots (general path) or the
+// nibble buffer and escape slots (byte-table path).
+constexpr int kNibOff = (kStageWords + 4) + 64;
+constexpr int kNibWords = 2048 / 8 + 4;
+constexpr int kWaveRegion =
+    kNibOff + (kEscSlots * 64 > kNibWords + kByteSlots * 64 ? kEscSlots * 64
+                                                            : kNibWords + kByteSlots * 64);
+static_assert(kNibOff % 4 == 0 && kWaveRegion % 4 == 0, "16-byte aligned nibble buffer");
+static_assert(kNibOff + kNibWords + kByteSlots * 64 <= kWaveRegion, "LDS carve");
+
+// Per byte value b of the unary plane and Rice k (0 or 1): the codes that end
+// in b (each ends in a one bit; bit 0 is the earliest). Entry words:
+//  [0] (q << k) of the 2nd, 3rd, ... code in nibbles 1, 2, ... (nibble 0 is
+//      left 0: the first code also has zeros carried in from earlier bytes)
+//  [1] the first code's zeros inside b, << k; kNoCode if b has no one bit
+//  [2] 4 * (codes ending in b): nibble bits the byte adds
+//  [3] zeros after b's last one bit, << k (8 << k if b == 0): the carry out
+// spread[r]: the 8 remainder bits r of weights 8g .. 8g+7 placed at the low
+// bit of each weight's nibble in R4 order (weight i -> byte i % 4, high
+// nibble for i >= 4).
+constexpr int32_t kNoCode = -(1 << 30);
+struct ByteTables {
+  uint32_t codes[2][256][4];
+  uint32_t spread[256];
+};
+
+constexpr ByteTables make_byte_tables() {
+  ByteTables t{};
+  for (int k = 0; k < 2; ++k) {
+    for (int b = 0; b < 256; ++b) {
+      uint32_t nib = 0;
+      int m = 0, prev = -1, first = 0;
+      for (int i = 0; i < 8; ++i) {
+        if (((b >> i) & 1) == 0) continue;
+        if (m == 0)
+          first = i;
+        else
+          nib |= static_cast<uint32_t>((i - prev - 1) << k) << (4 * m);
+        prev = i;
+        ++m;
+      }
+      t.codes[k][b][0] = nib;
+      t.codes[k][b][1] = m ? static_cast<uint32_t>(first << k) : static_cast<uint32_t>(kNoCode);
+      t.codes[k][b][2] = 4u * static_cast<uint32_t>(m);
+      t.codes[k][b][3] = static_cast<uint32_t>((m ? 7 - prev : 8) << k);
+    }
+  }
+  for (int r = 0; r < 256; ++r) {
+    uint32_t v = 0;
+    for (int i = 0; i < 8; ++i)
+      if ((r >> i) & 1) v |= 1u << (8 * (i & 3) + 4 * (i >> 2));
+    t.spread[r] = v;
+  }
+  return t;
+}
+
+__device__ const ByteTables kByteTables = make_byte_tables();
 
 struct RiceArgs {
   const uint32_t* unary;
@@ -83,6 +160,25 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
   v += __builtin_amdgcn_update_dpp(0u, v, kBcast15, 0xA, 0xF, false);
   v += __builtin_amdgcn_update_dpp(0u, v, kBcast31, 0xC, 0xF, false);
   return v;
+}
+
+// Inclusive prefix maximum over the 64 lanes (same DPP pattern as the sum).
+__device__ __forceinline__ int32_t wave_inclusive_max(int32_t v) {
+  constexpr int kRowShr = 0x110, kBcast15 = 0x142, kBcast31 = 0x143;
+  constexpr int kLow = -0x7FFFFFFF - 1;
+  v = max(v, __builtin_amdgcn_update_dpp(kLow, v, kRowShr + 1, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(kLow, v, kRowShr + 2, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(kLow, v, kRowShr + 4, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(kLow, v, kRowShr + 8, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(kLow, v, kBcast15, 0xA, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(kLow, v, kBcast31, 0xC, 0xF, false));
+  return v;
+}
+
+// The value of lane l - 1 (lane 0 gets first).
+__device__ __forceinline__ int32_t wave_shift_up(int32_t v, int32_t first) {
+  constexpr int kWaveShr1 = 0x138;
+  return __builtin_amdgcn_update_dpp(first, v, kWaveShr1, 0xF, 0xF, false);
 }
 
 __device__ __forceinline__ uint32_t lane63(uint32_t v) {
@@ -484,29 +580,266 @@ __device__ __forceinline__ void decode_run(const RiceArgs& a, const uint8_t* tab
   }
 }
 
+// Whether a run takes the byte-table path (wave-uniform).
+__device__ __forceinline__ bool byte_path(const RiceArgs& a, const Run& run,
+                                          const Prefetch& pf) {
+  const uint64_t span = pf.B - (pf.A & ~31ull);
+  return a.k <= 1u && a.n >= 15u && (run.cnt == 1 || a.cols >= 64) &&
+         pf.B > pf.A && span <= kByteMaxBits;
+}
+
+// Nibbles of 8 weights in weight order (weight i at bits 4i) -> R4 order
+// (weight i in byte i % 4, high nibble for i >= 4).
+__device__ __forceinline__ uint32_t to_r4_order(uint32_t n) {
+  const uint32_t lo = n & 0x0F0F0F0Fu;          // weights 0, 2, 4, 6
+  const uint32_t hi = (n >> 4) & 0x0F0F0F0Fu;   // weights 1, 3, 5, 7
+  const uint32_t p = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // 0 1 2 3
+  const uint32_t q = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // 4 5 6 7
+  return p | (q << 4);
+}
+
+// State of one lane's byte walk.
+struct ByteWalk {
+  uint32_t x0, x1;   // the lane's unary bits (<= 64), bit 0 first
+  int32_t c;         // zeros carried into the next byte, << k
+  uint32_t sb;       // 4 * index (in the run) of the next weight
+};
+
+// One lane's walk over its nsteps bytes. kEmit == false: ORs the nibbles
+// into nb, keeps up to kByteSlots escapes (index << 8 | rank) in slots and
+// counts them (and those before weight `limit`) in n_esc / n_before.
+// kEmit == true: writes the lane's escapes to dst instead. Returns false on
+// a rank outside the table.
+template <bool kEmit>
+__device__ __forceinline__ bool byte_walk(ByteWalk w, int nsteps, const uint4* lut,
+                                          const uint32_t* remw, uint32_t k, uint32_t n,
+                                          uint32_t* nb, uint32_t* slots, uint32_t& n_esc,
+                                          uint32_t limit, uint32_t& n_before,
+                                          const uint8_t* table, uint32_t chunk_mod,
+                                          uint32_t* dst) {
+  const int32_t thr = k ? 14 : 15;    // smallest (q << k) whose rank can be >= 15
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= nsteps) break;
+    const uint32_t word = j < 4 ? w.x0 : w.x1;
+    const uint32_t b = __builtin_amdgcn_ubfe(word, 8 * (j & 3), 8);
+    const uint4 e = lut[b];
+    const int32_t t = static_cast<int32_t>(e.y) + w.c;      // first code's q << k
+    if (t >= thr) {
+      // rare: the first code may be an escape
+      const uint32_t idx = w.sb >> 2;
+      const uint32_t rank =
+          static_cast<uint32_t>(t) | (k ? ((remw[idx >> 5] >> (idx & 31u)) & 1u) : 0u);
+      if (rank >= 15u) {
+        if (rank >= n) {
+          ok = false;
+        } else if (kEmit) {
+          dst[n_esc++] = (static_cast<uint32_t>(table[rank]) << 16) | (idx % chunk_mod);
+        } else {
+          if (n_esc < static_cast<uint32_t>(kByteSlots)) slots[n_esc * 64] = (idx << 8) | rank;
+          ++n_esc;
+          if (idx < limit) ++n_before;
+        }
+      }
+    }
+    if (!kEmit) {
+      const uint32_t v = e.x | static_cast<uint32_t>(min(max(t, 0), 15));
+      const uint64_t vv = static_cast<uint64_t>(v) << (w.sb & 31u);
+      uint32_t* p = nb + (w.sb >> 5);
+      __hip_atomic_fetch_or(p, static_cast<uint32_t>(vv), __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_or(p + 1, static_cast<uint32_t>(vv >> 32), __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    // carry: zeros after the last code, plus the carry if b has no code
+    const int32_t none = static_cast<int32_t>(e.y) >> 31;
+    w.c = (none & (w.c + static_cast<int32_t>(e.w))) | (~none & static_cast<int32_t>(e.w));
+    w.sb += e.z;
+  }
+  return ok;
+}
+
+// Decode one run on the byte-table path (byte_path() holds).
+__device__ __forceinline__ void decode_run_bytes(const RiceArgs& a, const uint8_t* table,
+                                                 const Run& run, const Prefetch& pf, int lane,
+                                                 uint32_t* region, const uint4* lut,
+                                                 const uint32_t* spread) {
+  uint32_t* stage = region;
+  uint32_t* remw = region + (kStageWords + 4);
+  uint32_t* nb = region + kNibOff;
+  uint32_t* slots = region + kNibOff + kNibWords + lane;
+  const int64_t c0 = run.c0, cnt = run.cnt;
+  const int32_t Lc = run.len;
+  const int32_t T = Lc >> 5;
+  const uint64_t A = pf.A, B = pf.B;
+  const uint32_t k = a.k;
+  if (B < A + static_cast<uint64_t>(Lc) || B > a.unary_words * 32ull) {
+    flag(a.status, BINADE_DEV_CORRUPT_STREAM, lane);
+    return;
+  }
+  const uint64_t wA = A >> 5;
+  const uint32_t uA = static_cast<uint32_t>(A & 31u);
+  const uint32_t Brel = static_cast<uint32_t>(B - wA * 32ull);   // <= kByteMaxBits
+  const uint32_t nw = (Brel + 31u) >> 5;                          // <= 128
+  const uint32_t spl = (((Brel + 7u) >> 3) + 63u) >> 6;           // bytes per lane, 1..8
+
+  // ---- stage the unary words and remainder words; clear the nibble buffer
+  if (2u * lane < nw) stage[2 * lane] = pf.w0;
+  if (2u * lane + 1u < nw) stage[2 * lane + 1] = pf.w1;
+  if (lane < 4) stage[nw + lane] = 0u;
+  remw[lane] = pf.rw0;
+  reinterpret_cast<uint4*>(nb)[lane] = make_uint4(0u, 0u, 0u, 0u);
+  wave_sync();
+
+  // ---- the lane's bytes [lane * spl, lane * spl + spl), bits outside the
+  // run cleared
+  const uint32_t bit0 = 8u * spl * static_cast<uint32_t>(lane);
+  const uint32_t wi = bit0 >> 5, off = bit0 & 31u;
+  const uint32_t s0 = stage[wi], s1 = stage[wi + 1], s2 = stage[wi + 2];
+  uint64_t X = (static_cast<uint64_t>(__builtin_amdgcn_alignbit(s2, s1, off)) << 32) |
+               __builtin_amdgcn_alignbit(s1, s0, off);
+  const int32_t lo = max(static_cast<int32_t>(uA) - static_cast<int32_t>(bit0), 0);
+  const int32_t hi = max(min(static_cast<int32_t>(8u * spl),
+                             static_cast<int32_t>(Brel) - static_cast<int32_t>(bit0)), 0);
+  X &= hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
+  X &= ~0ull << lo;
+  const uint32_t x0 = static_cast<uint32_t>(X), x1 = static_cast<uint32_t>(X >> 32);
+  const uint32_t pc = __popc(x0) + __popc(x1);
+  const uint32_t incl = wave_inclusive_sum(pc);
+  const uint32_t s_first = incl - pc;
+  const uint32_t last_word = stage[(Brel - 1u) >> 5];
+  if (lane63(incl) != static_cast<uint32_t>(Lc) || ((last_word >> ((Brel - 1u) & 31u)) & 1u) == 0) {
+    flag(a.status, BINADE_DEV_CORRUPT_STREAM, lane);
+    return;
+  }
+  // position of the last one bit before the lane's range
+  const int32_t top = x1 ? 63 - __clz(x1) : 31 - __clz(x0);
+  const int32_t last = pc ? static_cast<int32_t>(bit0) + top : static_cast<int32_t>(uA) - 1;
+  const int32_t prev = wave_shift_up(wave_inclusive_max(last), static_cast<int32_t>(uA) - 1);
+
+  ByteWalk w;
+  w.x0 = x0;
+  w.x1 = x1;
+  w.c = (static_cast<int32_t>(bit0) - prev - 1) * static_cast<int32_t>(1u << k);
+  w.sb = 4u * s_first;
+
+  // a row that starts inside the run (short rows): the lane holding the end
+  // of that row's previous weight checks the row's anchor and escape prefix
+  uint32_t limit = 0;
+  if (cnt > 1) {
+    const uint32_t cols = static_cast<uint32_t>(a.cols);
+    const uint32_t r = (s_first + cols) / cols;          // first row start after s_first
+    if (pc > 0 && r * cols <= s_first + pc && r * cols < static_cast<uint32_t>(Lc)) limit = r * cols;
+  }
+
+  uint32_t n_esc_lane = 0, n_before = 0;
+  const uint32_t chunk_mod = a.cols < kChunk ? static_cast<uint32_t>(a.cols) : kChunk;
+  bool ok = byte_walk<false>(w, static_cast<int>(spl), lut, remw, k, a.n, nb, slots, n_esc_lane,
+                             limit, n_before, table, chunk_mod, nullptr);
+  bool off_anchor = false;
+  if (limit != 0) {
+    const uint32_t idx = limit - 1u - s_first;          // that weight's one bit
+    const uint32_t pc0 = __popc(x0);
+    const uint32_t pos = idx < pc0 ? select_bit(x0, idx) : 32u + select_bit(x1, idx - pc0);
+    const int64_t row_chunk = c0 + limit / static_cast<uint32_t>(a.cols);
+    off_anchor = a.anchor[row_chunk] != wA * 32ull + bit0 + pos + 1u;
+  }
+  if (__any(!ok || off_anchor)) {
+    flag(a.status, BINADE_DEV_CORRUPT_STREAM, lane);
+    return;
+  }
+  wave_sync();
+
+  // ---- R4 nibbles: read back 32 weights, R4 order, remainder bits
+  if (lane < T) {
+    const uint4 nn = reinterpret_cast<const uint4*>(nb)[lane];
+    uint4 o;
+    o.x = to_r4_order(nn.x);
+    o.y = to_r4_order(nn.y);
+    o.z = to_r4_order(nn.z);
+    o.w = to_r4_order(nn.w);
+    if (k) {
+      const uint32_t rw = pf.rw0;
+      o.x |= spread[rw & 0xFFu];
+      o.y |= spread[(rw >> 8) & 0xFFu];
+      o.z |= spread[(rw >> 16) & 0xFFu];
+      o.w |= spread[rw >> 24];
+    }
+    *reinterpret_cast<uint4*>(a.nib + (static_cast<uint64_t>(run.fb) >> 1) + 16u * lane) = o;
+  }
+
+  // ---- escapes: place in the side list after a prefix sum over lanes
+  const uint32_t e0 = a.esc_pre[c0];
+  const uint32_t e1 = a.esc_pre[c0 + cnt];
+  uint32_t before, total;
+  if (__ballot(n_esc_lane > 1u) == 0) {
+    const uint64_t has = __ballot(n_esc_lane != 0u);
+    before = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(has >> 32),
+                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(has), 0u));
+    total = __popcll(has);
+  } else {
+    const uint32_t esc_incl = wave_inclusive_sum(n_esc_lane);
+    before = esc_incl - n_esc_lane;
+    total = lane63(esc_incl);
+  }
+  const bool esc_off = limit != 0 &&
+                       a.esc_pre[c0 + limit / static_cast<uint32_t>(a.cols)] != e0 + before + n_before;
+  if (e1 < e0 || e1 - e0 != total || e1 > a.n_esc || __any(esc_off)) {
+    flag(a.status, BINADE_DEV_CORRUPT_ESC, lane);
+  } else if (n_esc_lane > 0) {
+    uint32_t* dst = a.esc + (e0 + before);
+    if (n_esc_lane <= static_cast<uint32_t>(kByteSlots)) {
+      for (uint32_t i = 0; i < n_esc_lane; ++i) {
+        const uint32_t ent = slots[i * 64];
+        dst[i] = (static_cast<uint32_t>(table[ent & 0xFFu]) << 16) | ((ent >> 8) % chunk_mod);
+      }
+    } else {
+      // more escapes than slots: walk the bytes again, writing them out
+      uint32_t n2 = 0, unused = 0;
+      byte_walk<true>(w, static_cast<int>(spl), lut, remw, k, a.n, nullptr, nullptr, n2, 0u,
+                      unused, table, chunk_mod, dst);
+    }
+  }
+}
+
 __device__ __forceinline__ void decode_wave(const RiceArgs& a, const uint8_t* table,
-                                            int64_t r, int lane, uint32_t* stage,
-                                            uint32_t* tstart, uint32_t* slots) {
+                                            int64_t r, int lane, uint32_t* region,
+                                            const uint4* lut, const uint32_t* spread) {
   Run run;
   Prefetch pf;
   run_of(a, r, run);
   prefetch_bounds(a, run, pf);
   prefetch_words(a, run, lane, pf);
-  decode_run(a, table, run, pf, lane, stage, tstart, slots);
+  if (byte_path(a, run, pf))
+    decode_run_bytes(a, table, run, pf, lane, region, lut, spread);
+  else
+    decode_run(a, table, run, pf, lane, region, region + (kStageWords + 4),
+               region + kNibOff + lane);
+}
+
+// The byte tables for Rice k (k > 1 loads k = 1's; that path does not use
+// them), one entry per thread of the 256-thread block.
+__device__ __forceinline__ void load_byte_tables(uint4* lut, uint32_t* spread, uint32_t k) {
+  const int t = threadIdx.x;
+  const uint32_t* src = kByteTables.codes[k == 0 ? 0 : 1][t];
+  lut[t] = make_uint4(src[0], src[1], src[2], src[3]);
+  spread[t] = kByteTables.spread[t];
+  __syncthreads();
 }
 
 // One wave per run; the run's anchors, first unary words and remainder
 // words are requested before any other work.
 __global__ __launch_bounds__(256) void rice_to_r4_kernel(RiceArgs a) {
-  __shared__ uint32_t stage[kWavesPerBlock][kStageWords + 4];
-  __shared__ uint32_t tile_start[kWavesPerBlock][64];   // relative to the first staged word
-  __shared__ uint32_t esc_tmp[kWavesPerBlock][kEscSlots][64];
+  __shared__ __align__(16) uint32_t region[kWavesPerBlock][kWaveRegion];
+  __shared__ uint4 lut[256];
+  __shared__ uint32_t spread[256];
+  load_byte_tables(lut, spread, a.k);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t r = uniform64(static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave);
   if (r >= runs_total(a)) return;
-  decode_wave(a, kernarg_table(0), r, lane, stage[wave], tile_start[wave],
-              &esc_tmp[wave][0][lane]);
+  decode_wave(a, kernarg_table(0), r, lane, region[wave], lut, spread);
 }
 
 // Several tensors in one launch: tensor i owns blocks
@@ -519,9 +852,9 @@ struct RiceBatch {
 };
 
 __global__ __launch_bounds__(256) void rice_to_r4_batch_kernel(RiceBatch b) {
-  __shared__ uint32_t stage[kWavesPerBlock][kStageWords + 4];
-  __shared__ uint32_t tile_start[kWavesPerBlock][64];
-  __shared__ uint32_t esc_tmp[kWavesPerBlock][kEscSlots][64];
+  __shared__ __align__(16) uint32_t region[kWavesPerBlock][kWaveRegion];
+  __shared__ uint4 lut[256];
+  __shared__ uint32_t spread[256];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const uint32_t blk = blockIdx.x;
@@ -535,10 +868,10 @@ __global__ __launch_bounds__(256) void rice_to_r4_batch_kernel(RiceBatch b) {
   const size_t off = offsetof(RiceBatch, item) + static_cast<size_t>(i) * sizeof(RiceArgs);
   const RiceArgs* items = (const RiceArgs*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + off);
   const RiceArgs a = items[0];
+  load_byte_tables(lut, spread, a.k);
   const int64_t r = uniform64(static_cast<int64_t>(blk - b.first_block[i]) * kWavesPerBlock + wave);
   if (r >= runs_total(a)) return;
-  decode_wave(a, kernarg_table(off), r, lane, stage[wave], tile_start[wave],
-              &esc_tmp[wave][0][lane]);
+  decode_wave(a, kernarg_table(off), r, lane, region[wave], lut, spread);
 }
 
 }  // namespace

@@ -19,7 +19,6 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "binade_oracle.c")
-_GEMM_SRC = os.path.join(_HERE, "gemm_oracle.c")
 _OUT_DIR = os.path.join(_HERE, "_build")
 _SO = os.path.join(_OUT_DIR, "liboracle.so")
 
@@ -32,7 +31,7 @@ _lib = None
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (plain C, no fast-math, no contraction)."""
     os.makedirs(_OUT_DIR, exist_ok=True)
-    srcs = [_SRC] + ([_GEMM_SRC] if os.path.exists(_GEMM_SRC) else [])
+    srcs = [_SRC]
     if not force and os.path.exists(_SO):
         newest = max(os.path.getmtime(s) for s in srcs)
         if os.path.getmtime(_SO) >= newest:
@@ -74,8 +73,7 @@ def _load():
             lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
             lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
             lib.oracle_f32_to_bf16_array.argtypes = [P, I64, P]
-            if hasattr(lib, "oracle_gemm_replay"):
-                lib.oracle_gemm_replay.argtypes = [P, I64, I64, P, I64, P]
+            lib.oracle_gemm_f64.argtypes = [P, I64, I64, P, I64, P]
             _lib = lib
     return _lib
 
@@ -260,18 +258,16 @@ def moe_replay(experts_bits, x_bits, idx, x_per_slot: bool) -> np.ndarray:
     return y
 
 
-def gemm_replay(w_bits, x_bits) -> np.ndarray:
-    """Y = X W^T in the library's fixed GEMM order (gemm_oracle.c)."""
-    lib = _load()
-    if not hasattr(lib, "oracle_gemm_replay"):
-        raise NotImplementedError("gemm oracle not built")
+def gemm_f64(w_bits, x_bits) -> np.ndarray:
+    """Y = X W^T summed in double (the prompt GEMM's plain definition). No
+    bit replay of the GEMM exists: its parity is unpinned beyond this bound,
+    exact-arithmetic inputs and the bf16-weight twin."""
     w = _u16(w_bits)
     x = _u16(x_bits)
     N, K = w.shape
     M = x.shape[0]
-    y = np.zeros((M, N), np.float32)
-    _check("oracle_gemm_replay",
-           lib.oracle_gemm_replay(_p(w), N, K, _p(x), M, _p(y)))
+    y = np.zeros((M, N), np.float64)
+    _check("oracle_gemm_f64", _load().oracle_gemm_f64(_p(w), N, K, _p(x), M, _p(y)))
     return y
 
 

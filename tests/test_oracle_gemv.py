@@ -192,3 +192,37 @@ def test_moe_gather_picks_expert_by_index():
     assert y[:, 0].tolist() == [5.0 * K, 1.0 * K, 3.0 * K]
     with pytest.raises(oracle.OracleError):
         oracle.moe_replay(experts, x, np.array([[5, 0, 0]], np.int32), False)
+
+
+# ---------------------------------------------------------------- GEMM (fp64)
+def test_gemm_one_hot_rows_select_columns():
+    N, K = 24, 96
+    W = rand_bits(N, K, 0.02, 11)
+    cols = [0, 5, 31, 32, 95]
+    X = np.zeros((len(cols), K), np.float32)
+    for m, j in enumerate(cols):
+        X[m, j] = 1.0
+    Y = oracle.gemm_f64(W, bf16(X))
+    assert Y.shape == (len(cols), N)
+    for m, j in enumerate(cols):
+        assert np.array_equal(Y[m], f32(W[:, j]).astype(np.float64))
+
+
+def test_gemm_small_integers_equal_integer_matmul():
+    # M, N, K all different, so a transposed operand or swapped index fails
+    rng = np.random.default_rng(3)
+    M, N, K = 5, 7, 64
+    Xi = rng.integers(-8, 9, size=(M, K))
+    Wi = rng.integers(-8, 9, size=(N, K))
+    Y = oracle.gemm_f64(bf16(Wi), bf16(Xi))
+    assert np.array_equal(Y.astype(np.int64), Xi @ Wi.T)
+
+
+def test_gemm_rows_equal_the_matvec_definition():
+    W = rand_bits(33, 160, 0.02, 12)
+    X = synth.bits(synth.vector_bf16(160, 13, count=4)).numpy().view(np.uint16)
+    Y = oracle.gemm_f64(W, X)
+    for m in range(4):
+        assert np.array_equal(Y[m], oracle.gemv_f64(W, X[m]))
+    with pytest.raises(oracle.OracleError):
+        oracle.gemm_f64(W[:, :0], X[:, :0])
