@@ -83,11 +83,12 @@ def lib() -> ctypes.CDLL:
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(LIB_PATH):
+            path = os.environ.get("BINADE_LIB") or LIB_PATH   # another build of the library
+            if not os.path.exists(path):
                 raise RuntimeError(
-                    f"{LIB_PATH} is not built; run "
+                    f"{path} is not built; run "
                     "`python -m decode_gemv_tensor_amd.build` (hipcc, gfx950)")
-            L = ctypes.CDLL(LIB_PATH)
+            L = ctypes.CDLL(path)
             P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
             L.binade_status_str.argtypes = [I32]
             L.binade_status_str.restype = ctypes.c_char_p

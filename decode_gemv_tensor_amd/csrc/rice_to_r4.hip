@@ -47,6 +47,7 @@
 #include "binade.h"
 #include "device_common.h"
 
+
 namespace binade {
 namespace {
 
@@ -55,18 +56,20 @@ using namespace dev;
 constexpr int kWavesPerBlock = 4;
 constexpr int kStageWords = 384;     // unary words staged per run (6 bits/weight)
 constexpr int kEscSlots = 8;         // escapes kept per lane in LDS
-constexpr int kByteSlots = 4;        // escapes kept per lane (byte-table path)
-constexpr uint32_t kByteMaxBits = 4096;  // unary bits per run (byte-table path)
-// LDS words per wave: staged unary words, then 64 words (lane tile starts or
-// the run's remainder words), then the escape slots (general path) or the
-// nibble buffer and escape slots (byte-table path).
-constexpr int kNibOff = (kStageWords + 4) + 64;
-constexpr int kNibWords = 2048 / 8 + 4;
-constexpr int kWaveRegion =
-    kNibOff + (kEscSlots * 64 > kNibWords + kByteSlots * 64 ? kEscSlots * 64
-                                                            : kNibWords + kByteSlots * 64);
-static_assert(kNibOff % 4 == 0 && kWaveRegion % 4 == 0, "16-byte aligned nibble buffer");
-static_assert(kNibOff + kNibWords + kByteSlots * 64 <= kWaveRegion, "LDS carve");
+constexpr int kByteSlots = 3;        // escapes kept per lane (byte-table path)
+constexpr uint32_t kByteMaxBits = 4096 - 64;  // unary bits per run (byte-table path)
+// LDS per wave: a general region (staged unary words, then 64 words of lane
+// tile starts) and a 2 KiB-aligned buffer region, which holds the general
+// path's escape slots, or the byte-table path's nibble buffer and escape
+// slots. The byte-table path keeps the run's remainder words in the stage
+// area above the unary words it uses (at most 132).
+constexpr int kGeneralWords = (kStageWords + 4) + 64;
+constexpr int kBufWords = 512;
+constexpr int kNibWords = 2048 / 8 + 2;
+constexpr int kRemOff = 256;
+static_assert(kEscSlots * 64 <= kBufWords, "general path escape slots");
+static_assert(kNibWords + kByteSlots * 64 <= kBufWords, "byte path buffer");
+static_assert(kRemOff >= 132 && kRemOff + 64 <= kStageWords, "byte path remainder words");
 
 // Per byte value b of the unary plane and Rice k (0 or 1): the codes that end
 // in b (each ends in a one bit; bit 0 is the earliest). Entry words:
@@ -74,7 +77,8 @@ static_assert(kNibOff + kNibWords + kByteSlots * 64 <= kWaveRegion, "LDS carve")
 //      left 0: the first code also has zeros carried in from earlier bytes)
 //  [1] the first code's zeros inside b, << k; kNoCode if b has no one bit
 //  [2] 4 * (codes ending in b): nibble bits the byte adds
-//  [3] zeros after b's last one bit, << k (8 << k if b == 0): the carry out
+//  [3] zeros after b's last one bit, << k: the carry out (INT32_MAX if b == 0,
+//      so that min(carry in + (8 << k), [3]) is the carry out either way)
 // spread[r]: the 8 remainder bits r of weights 8g .. 8g+7 placed at the low
 // bit of each weight's nibble in R4 order (weight i -> byte i % 4, high
 // nibble for i >= 4).
@@ -102,7 +106,7 @@ constexpr ByteTables make_byte_tables() {
       t.codes[k][b][0] = nib;
       t.codes[k][b][1] = m ? static_cast<uint32_t>(first << k) : static_cast<uint32_t>(kNoCode);
       t.codes[k][b][2] = 4u * static_cast<uint32_t>(m);
-      t.codes[k][b][3] = static_cast<uint32_t>((m ? 7 - prev : 8) << k);
+      t.codes[k][b][3] = m ? static_cast<uint32_t>((7 - prev) << k) : 0x7FFFFFFFu;
     }
   }
   for (int r = 0; r < 256; ++r) {
@@ -132,7 +136,12 @@ struct RiceArgs {
   int32_t cols;
   uint32_t k;
   uint32_t n;
-  uint32_t table[64];  // exp_of_rank, 4 bytes per word
+  uint32_t cols_recip;  // ceil(2^32 / cols) when cols < 2048: i / cols = mulhi(i, recip)
+  uint32_t chunks_per_row;  // C = ceil(cols / 2048)
+  uint32_t c_recip;         // ceil(2^32 / C): r / C = mulhi(r, c_recip), or one less
+  uint32_t rows_per_run;    // G = 2048 / cols when C == 1, else 1
+  int64_t runs;             // waves' worth of work: row-chunks (C > 1) or ceil(rows / G)
+  uint32_t table[64];       // exp_of_rank, 4 bytes per word
 };
 
 // The rank -> exponent table of a kernel's tensor, read in place from the
@@ -316,24 +325,22 @@ struct Run {
   int32_t len;     // weights in the run (multiple of 32, <= 2048)
 };
 
-__device__ __forceinline__ int64_t runs_total(const RiceArgs& a) {
-  const int64_t C = (a.cols + kChunk - 1) / kChunk;
-  if (C > 1) return a.n_chunks;
-  const int64_t G = kChunk / a.cols;
-  return (a.n_chunks + G - 1) / G;
-}
+__device__ __forceinline__ int64_t runs_total(const RiceArgs& a) { return a.runs; }
 
+// The run r (wave-uniform) of a tensor; all arithmetic on scalars.
 __device__ __forceinline__ void run_of(const RiceArgs& a, int64_t r, Run& run) {
-  const int64_t C = (a.cols + kChunk - 1) / kChunk;
-  if (C == 1) {
-    const int64_t G = kChunk / a.cols;
+  if (a.chunks_per_row == 1u) {
+    const int64_t G = a.rows_per_run;
     run.c0 = r * G;
     run.cnt = min(G, a.n_chunks - run.c0);
     run.fb = run.c0 * a.cols;
-    run.len = static_cast<int32_t>(run.cnt * a.cols);
+    run.len = static_cast<int32_t>(run.cnt) * a.cols;
   } else {
-    const uint32_t row = static_cast<uint32_t>(r) / static_cast<uint32_t>(C);
-    const int32_t j = static_cast<int32_t>(r - static_cast<int64_t>(row) * C);
+    const uint32_t C = a.chunks_per_row;
+    const uint32_t r32 = static_cast<uint32_t>(r);   // < 2^31
+    uint32_t row = __umulhi(r32, a.c_recip);
+    if (row * C > r32) --row;
+    const int32_t j = static_cast<int32_t>(r32 - row * C);
     run.c0 = r;
     run.cnt = 1;
     run.fb = static_cast<int64_t>(row) * a.cols + static_cast<int64_t>(j) * kChunk;
@@ -357,16 +364,25 @@ __device__ __forceinline__ void prefetch_bounds(const RiceArgs& a, const Run& ru
 
 __device__ __forceinline__ void prefetch_words(const RiceArgs& a, const Run& run,
                                                int lane, Prefetch& pf) {
+  // uniform bases and a 32-bit lane offset; words past the plane read as 0
   const uint64_t wA = pf.A >> 5;
-  const uint64_t wi = 2u * lane;
-  // words past the run (or past the plane) are masked or unused later
-  pf.w0 = load_word(a.unary, wA + wi, a.unary_words);
-  pf.w1 = load_word(a.unary, wA + wi + 1, a.unary_words);
-  const uint64_t rem_bit = (static_cast<uint64_t>(run.fb) + 32ull * lane) * a.k;
+  const uint64_t left = a.unary_words > wA ? a.unary_words - wA : 0ull;
+  const uint32_t avail = left > 0x7FFFFFFFull ? 0x7FFFFFFFu : static_cast<uint32_t>(left);
+  const uint32_t* ub = a.unary + wA;
+  const uint32_t wi = 2u * static_cast<uint32_t>(lane);
+  pf.w0 = wi < avail ? ub[wi] : 0u;
+  pf.w1 = wi + 1u < avail ? ub[wi + 1u] : 0u;
   pf.rw0 = pf.rw1 = 0;
   if (a.k == 1 || a.k == 2) {
-    pf.rw0 = load_word(a.rem, rem_bit >> 5, a.rem_words);
-    if (a.k == 2) pf.rw1 = load_word(a.rem, (rem_bit >> 5) + 1, a.rem_words);
+    // remainder bits of lane tile l start at bit (fb + 32 l) * k, a word
+    // boundary since fb is a multiple of 32
+    const uint64_t r0 = (static_cast<uint64_t>(run.fb) * a.k) >> 5;
+    const uint64_t rleft = a.rem_words > r0 ? a.rem_words - r0 : 0ull;
+    const uint32_t ravail = rleft > 0x7FFFFFFFull ? 0x7FFFFFFFu : static_cast<uint32_t>(rleft);
+    const uint32_t* rb = a.rem + r0;
+    const uint32_t ri = static_cast<uint32_t>(lane) * a.k;
+    pf.rw0 = ri < ravail ? rb[ri] : 0u;
+    if (a.k == 2) pf.rw1 = ri + 1u < ravail ? rb[ri + 1u] : 0u;
   }
 }
 
@@ -580,57 +596,61 @@ __device__ __forceinline__ void decode_run(const RiceArgs& a, const uint8_t* tab
   }
 }
 
+// LDS words by byte address (the 32-bit offset in the workgroup's LDS).
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+__device__ __forceinline__ uint32_t lds_address(const uint32_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u32*)p));
+}
+__device__ __forceinline__ void lds_or(uint32_t addr, uint32_t v) {
+  __hip_atomic_fetch_or((lds_u32*)addr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // Whether a run takes the byte-table path (wave-uniform).
 __device__ __forceinline__ bool byte_path(const RiceArgs& a, const Run& run,
                                           const Prefetch& pf) {
-  const uint64_t span = pf.B - (pf.A & ~31ull);
-  return a.k <= 1u && a.n >= 15u && (run.cnt == 1 || a.cols >= 64) &&
-         pf.B > pf.A && span <= kByteMaxBits;
+  return a.k == 1u && a.n >= 15u && (run.cnt == 1 || a.cols >= 64) && pf.B > pf.A &&
+         pf.B - pf.A <= kByteMaxBits;
 }
 
 // Nibbles of 8 weights in weight order (weight i at bits 4i) -> R4 order
 // (weight i in byte i % 4, high nibble for i >= 4).
 __device__ __forceinline__ uint32_t to_r4_order(uint32_t n) {
-  const uint32_t lo = n & 0x0F0F0F0Fu;          // weights 0, 2, 4, 6
-  const uint32_t hi = (n >> 4) & 0x0F0F0F0Fu;   // weights 1, 3, 5, 7
-  const uint32_t p = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // 0 1 2 3
-  const uint32_t q = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // 4 5 6 7
-  return p | (q << 4);
+  // low nibbles: weights 0..3 from bytes of n and n >> 4; high nibbles:
+  // weights 4..7 from bytes of n << 4 and n
+  const uint32_t lo = __builtin_amdgcn_perm(n >> 4, n, 0x05010400u);
+  const uint32_t hi = __builtin_amdgcn_perm(n << 4, n, 0x03070206u);
+  return (lo & 0x0F0F0F0Fu) | (hi & 0xF0F0F0F0u);
 }
 
-// State of one lane's byte walk.
-struct ByteWalk {
-  uint32_t x0, x1;   // the lane's unary bits (<= 64), bit 0 first
-  int32_t c;         // zeros carried into the next byte, << k
-  uint32_t sb;       // 4 * index (in the run) of the next weight
-};
-
-// One lane's walk over its nsteps bytes. kEmit == false: ORs the nibbles
-// into nb, keeps up to kByteSlots escapes (index << 8 | rank) in slots and
-// counts them (and those before weight `limit`) in n_esc / n_before.
-// kEmit == true: writes the lane's escapes to dst instead. Returns false on
-// a rank outside the table.
-template <bool kEmit>
-__device__ __forceinline__ bool byte_walk(ByteWalk w, int nsteps, const uint4* lut,
-                                          const uint32_t* remw, uint32_t k, uint32_t n,
-                                          uint32_t* nb, uint32_t* slots, uint32_t& n_esc,
+// One lane's walk over kSteps bytes of unary bits (x0 then x1, bit 0 first;
+// bits past the lane's range are zero). c: zeros carried in, << K. sb: 4 *
+// index of the lane's first weight in the run. kEmit == false: ORs the
+// nibbles (q << K, 15 at most; remainders come later) into the 2 KiB-aligned
+// nibble buffer at LDS byte address nb, keeps up to kByteSlots escapes
+// (index << 8 | rank) in slots and counts them (and those before weight
+// limit) in n_esc / n_before. kEmit == true: writes the escapes to dst.
+// Returns false on a rank outside the table.
+template <uint32_t K, int kSteps, bool kEmit>
+__device__ __forceinline__ bool byte_walk(uint32_t x0, uint32_t x1, int32_t c, uint32_t sb,
+                                          const uint4* lut, const uint32_t* remw, uint32_t n,
+                                          uint32_t nb, uint32_t* slots, uint32_t& n_esc,
                                           uint32_t limit, uint32_t& n_before,
                                           const uint8_t* table, uint32_t chunk_mod,
                                           uint32_t* dst) {
-  const int32_t thr = k ? 14 : 15;    // smallest (q << k) whose rank can be >= 15
+  constexpr int32_t kThr = K ? 14 : 15;   // smallest q << K whose rank can be >= 15
+  uint4 e[kSteps];
+#pragma unroll
+  for (int j = 0; j < kSteps; ++j)
+    e[j] = lut[__builtin_amdgcn_ubfe(j < 4 ? x0 : x1, 8 * (j & 3), 8)];
   bool ok = true;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= nsteps) break;
-    const uint32_t word = j < 4 ? w.x0 : w.x1;
-    const uint32_t b = __builtin_amdgcn_ubfe(word, 8 * (j & 3), 8);
-    const uint4 e = lut[b];
-    const int32_t t = static_cast<int32_t>(e.y) + w.c;      // first code's q << k
-    if (t >= thr) {
+  for (int j = 0; j < kSteps; ++j) {
+    const int32_t t = static_cast<int32_t>(e[j].y) + c;     // first code's q << K
+    if (t >= kThr) {
       // rare: the first code may be an escape
-      const uint32_t idx = w.sb >> 2;
+      const uint32_t idx = sb >> 2;
       const uint32_t rank =
-          static_cast<uint32_t>(t) | (k ? ((remw[idx >> 5] >> (idx & 31u)) & 1u) : 0u);
+          static_cast<uint32_t>(t) | (K ? ((remw[idx >> 5] >> (idx & 31u)) & 1u) : 0u);
       if (rank >= 15u) {
         if (rank >= n) {
           ok = false;
@@ -644,105 +664,119 @@ __device__ __forceinline__ bool byte_walk(ByteWalk w, int nsteps, const uint4* l
       }
     }
     if (!kEmit) {
-      const uint32_t v = e.x | static_cast<uint32_t>(min(max(t, 0), 15));
-      const uint64_t vv = static_cast<uint64_t>(v) << (w.sb & 31u);
-      uint32_t* p = nb + (w.sb >> 5);
-      __hip_atomic_fetch_or(p, static_cast<uint32_t>(vv), __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_fetch_or(p + 1, static_cast<uint32_t>(vv >> 32), __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_WORKGROUP);
+      const uint32_t v = e[j].x | static_cast<uint32_t>(min(max(t, 0), 15));
+      // v << (sb % 32) as two words; v_bfe_u32 takes offset and width mod
+      // 32, so the high word is v >> (32 - sb % 32), and 0 when sb % 32 == 0
+      const uint32_t lo = v << (sb & 31u);
+      const uint32_t hi = __builtin_amdgcn_ubfe(v, (0u - sb) & 31u, sb & 31u);
+      const uint32_t addr = ((sb >> 3) & 0x7FCu) | nb;   // nb is 2 KiB aligned
+      lds_or(addr, lo);
+      lds_or(addr + 4u, hi);
     }
-    // carry: zeros after the last code, plus the carry if b has no code
-    const int32_t none = static_cast<int32_t>(e.y) >> 31;
-    w.c = (none & (w.c + static_cast<int32_t>(e.w))) | (~none & static_cast<int32_t>(e.w));
-    w.sb += e.z;
+    // zeros carried to the next byte: those after its last code, or all 8
+    c = min(c + static_cast<int32_t>(8u << K), static_cast<int32_t>(e[j].w));
+    sb += e[j].z;
   }
   return ok;
 }
-
-// Decode one run on the byte-table path (byte_path() holds).
+// Decode one run on the byte-table path (byte_path() holds), Rice k = K.
+// Lane l takes the run's unary bits [spl*8*l, spl*8*(l+1)) (spl bytes, 1..8,
+// counted from the run's first bit).
+template <uint32_t K>
 __device__ __forceinline__ void decode_run_bytes(const RiceArgs& a, const uint8_t* table,
                                                  const Run& run, const Prefetch& pf, int lane,
-                                                 uint32_t* region, const uint4* lut,
+                                                 uint32_t* stage, uint32_t* buf, const uint4* lut,
                                                  const uint32_t* spread) {
-  uint32_t* stage = region;
-  uint32_t* remw = region + (kStageWords + 4);
-  uint32_t* nb = region + kNibOff;
-  uint32_t* slots = region + kNibOff + kNibWords + lane;
+  uint32_t* remw = stage + kRemOff;
+  uint32_t* slots = buf + kNibWords + lane;
   const int64_t c0 = run.c0, cnt = run.cnt;
   const int32_t Lc = run.len;
   const int32_t T = Lc >> 5;
   const uint64_t A = pf.A, B = pf.B;
-  const uint32_t k = a.k;
   if (B < A + static_cast<uint64_t>(Lc) || B > a.unary_words * 32ull) {
     flag(a.status, BINADE_DEV_CORRUPT_STREAM, lane);
     return;
   }
   const uint64_t wA = A >> 5;
   const uint32_t uA = static_cast<uint32_t>(A & 31u);
-  const uint32_t Brel = static_cast<uint32_t>(B - wA * 32ull);   // <= kByteMaxBits
-  const uint32_t nw = (Brel + 31u) >> 5;                          // <= 128
-  const uint32_t spl = (((Brel + 7u) >> 3) + 63u) >> 6;           // bytes per lane, 1..8
+  const uint32_t nbits = static_cast<uint32_t>(B - A);            // <= kByteMaxBits
+  const uint32_t Brel = uA + nbits;                                // end, from word wA
+  const uint32_t nw = (Brel + 31u) >> 5;                           // <= 128
+  const uint32_t spl = (((nbits + 7u) >> 3) + 63u) >> 6;           // 1..8
 
-  // ---- stage the unary words and remainder words; clear the nibble buffer
-  if (2u * lane < nw) stage[2 * lane] = pf.w0;
-  if (2u * lane + 1u < nw) stage[2 * lane + 1] = pf.w1;
-  if (lane < 4) stage[nw + lane] = 0u;
-  remw[lane] = pf.rw0;
-  reinterpret_cast<uint4*>(nb)[lane] = make_uint4(0u, 0u, 0u, 0u);
+  // ---- stage the run's unary words (bits outside the run cleared, zeros up
+  // to word 131) and remainder words; clear the nibble buffer
+  {
+    const uint32_t i0 = 2u * lane, i1 = i0 + 1u;
+    const uint32_t last = nw - 1u;
+    const uint32_t keep_last = 0xFFFFFFFFu >> (31u - ((Brel - 1u) & 31u));
+    uint32_t v0 = i0 < nw ? pf.w0 : 0u, v1 = i1 < nw ? pf.w1 : 0u;
+    if (i0 == 0u) v0 &= 0xFFFFFFFFu << uA;
+    if (i0 == last) v0 &= keep_last;
+    if (i1 == last) v1 &= keep_last;
+    stage[i0] = v0;
+    stage[i1] = v1;
+    if (lane < 4) stage[128 + lane] = 0u;
+    remw[lane] = pf.rw0;
+    reinterpret_cast<uint4*>(buf)[lane] = make_uint4(0u, 0u, 0u, 0u);
+  }
   wave_sync();
 
-  // ---- the lane's bytes [lane * spl, lane * spl + spl), bits outside the
-  // run cleared
-  const uint32_t bit0 = 8u * spl * static_cast<uint32_t>(lane);
+  // ---- the lane's bits
+  const uint32_t bit0 = uA + 8u * spl * static_cast<uint32_t>(lane);
   const uint32_t wi = bit0 >> 5, off = bit0 & 31u;
   const uint32_t s0 = stage[wi], s1 = stage[wi + 1], s2 = stage[wi + 2];
-  uint64_t X = (static_cast<uint64_t>(__builtin_amdgcn_alignbit(s2, s1, off)) << 32) |
-               __builtin_amdgcn_alignbit(s1, s0, off);
-  const int32_t lo = max(static_cast<int32_t>(uA) - static_cast<int32_t>(bit0), 0);
-  const int32_t hi = max(min(static_cast<int32_t>(8u * spl),
-                             static_cast<int32_t>(Brel) - static_cast<int32_t>(bit0)), 0);
-  X &= hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
-  X &= ~0ull << lo;
-  const uint32_t x0 = static_cast<uint32_t>(X), x1 = static_cast<uint32_t>(X >> 32);
+  uint32_t x0 = __builtin_amdgcn_alignbit(s1, s0, off);
+  uint32_t x1 = __builtin_amdgcn_alignbit(s2, s1, off);
+  if (spl < 8u) {   // uniform: the next lane's bits
+    const uint64_t keep = (1ull << (8u * spl)) - 1ull;
+    x0 &= static_cast<uint32_t>(keep);
+    x1 &= static_cast<uint32_t>(keep >> 32);
+  }
   const uint32_t pc = __popc(x0) + __popc(x1);
   const uint32_t incl = wave_inclusive_sum(pc);
   const uint32_t s_first = incl - pc;
   const uint32_t last_word = stage[(Brel - 1u) >> 5];
-  if (lane63(incl) != static_cast<uint32_t>(Lc) || ((last_word >> ((Brel - 1u) & 31u)) & 1u) == 0) {
+  if (lane63(incl) != static_cast<uint32_t>(Lc) ||
+      ((last_word >> ((Brel - 1u) & 31u)) & 1u) == 0u) {
     flag(a.status, BINADE_DEV_CORRUPT_STREAM, lane);
     return;
   }
-  // position of the last one bit before the lane's range
+  // zeros carried into the lane: from its first bit back to the last one bit
+  // of an earlier lane (every lane's bits start after the run's first bit)
   const int32_t top = x1 ? 63 - __clz(x1) : 31 - __clz(x0);
   const int32_t last = pc ? static_cast<int32_t>(bit0) + top : static_cast<int32_t>(uA) - 1;
   const int32_t prev = wave_shift_up(wave_inclusive_max(last), static_cast<int32_t>(uA) - 1);
+  const int32_t c_in = (static_cast<int32_t>(bit0) - prev - 1) << K;
+  const uint32_t sb0 = 4u * s_first;
 
-  ByteWalk w;
-  w.x0 = x0;
-  w.x1 = x1;
-  w.c = (static_cast<int32_t>(bit0) - prev - 1) * static_cast<int32_t>(1u << k);
-  w.sb = 4u * s_first;
-
-  // a row that starts inside the run (short rows): the lane holding the end
-  // of that row's previous weight checks the row's anchor and escape prefix
+  // a row that starts inside the run (short rows): the lane holding the one
+  // bit that ends the row's previous weight checks the row's anchor and
+  // escape prefix
   uint32_t limit = 0;
   if (cnt > 1) {
     const uint32_t cols = static_cast<uint32_t>(a.cols);
-    const uint32_t r = (s_first + cols) / cols;          // first row start after s_first
-    if (pc > 0 && r * cols <= s_first + pc && r * cols < static_cast<uint32_t>(Lc)) limit = r * cols;
+    const uint32_t r = __umulhi(s_first, a.cols_recip) + 1u;   // first row start > s_first
+    const uint32_t start = r * cols;
+    if (pc > 0u && start <= s_first + pc && start < static_cast<uint32_t>(Lc)) limit = start;
   }
 
   uint32_t n_esc_lane = 0, n_before = 0;
   const uint32_t chunk_mod = a.cols < kChunk ? static_cast<uint32_t>(a.cols) : kChunk;
-  bool ok = byte_walk<false>(w, static_cast<int>(spl), lut, remw, k, a.n, nb, slots, n_esc_lane,
-                             limit, n_before, table, chunk_mod, nullptr);
+  const uint32_t nb = lds_address(buf);
+  bool ok;
+  if (spl <= 4u)
+    ok = byte_walk<K, 4, false>(x0, x1, c_in, sb0, lut, remw, a.n, nb, slots, n_esc_lane, limit,
+                                n_before, table, chunk_mod, nullptr);
+  else
+    ok = byte_walk<K, 8, false>(x0, x1, c_in, sb0, lut, remw, a.n, nb, slots, n_esc_lane, limit,
+                                n_before, table, chunk_mod, nullptr);
   bool off_anchor = false;
-  if (limit != 0) {
+  if (limit != 0u) {
     const uint32_t idx = limit - 1u - s_first;          // that weight's one bit
     const uint32_t pc0 = __popc(x0);
     const uint32_t pos = idx < pc0 ? select_bit(x0, idx) : 32u + select_bit(x1, idx - pc0);
-    const int64_t row_chunk = c0 + limit / static_cast<uint32_t>(a.cols);
+    const int64_t row_chunk = c0 + __umulhi(limit, a.cols_recip);
     off_anchor = a.anchor[row_chunk] != wA * 32ull + bit0 + pos + 1u;
   }
   if (__any(!ok || off_anchor)) {
@@ -753,13 +787,13 @@ __device__ __forceinline__ void decode_run_bytes(const RiceArgs& a, const uint8_
 
   // ---- R4 nibbles: read back 32 weights, R4 order, remainder bits
   if (lane < T) {
-    const uint4 nn = reinterpret_cast<const uint4*>(nb)[lane];
+    const uint4 nn = reinterpret_cast<const uint4*>(buf)[lane];
     uint4 o;
     o.x = to_r4_order(nn.x);
     o.y = to_r4_order(nn.y);
     o.z = to_r4_order(nn.z);
     o.w = to_r4_order(nn.w);
-    if (k) {
+    if (K) {
       const uint32_t rw = pf.rw0;
       o.x |= spread[rw & 0xFFu];
       o.y |= spread[(rw >> 8) & 0xFFu];
@@ -783,8 +817,8 @@ __device__ __forceinline__ void decode_run_bytes(const RiceArgs& a, const uint8_
     before = esc_incl - n_esc_lane;
     total = lane63(esc_incl);
   }
-  const bool esc_off = limit != 0 &&
-                       a.esc_pre[c0 + limit / static_cast<uint32_t>(a.cols)] != e0 + before + n_before;
+  const bool esc_off = limit != 0u &&
+                       a.esc_pre[c0 + __umulhi(limit, a.cols_recip)] != e0 + before + n_before;
   if (e1 < e0 || e1 - e0 != total || e1 > a.n_esc || __any(esc_off)) {
     flag(a.status, BINADE_DEV_CORRUPT_ESC, lane);
   } else if (n_esc_lane > 0) {
@@ -797,14 +831,18 @@ __device__ __forceinline__ void decode_run_bytes(const RiceArgs& a, const uint8_
     } else {
       // more escapes than slots: walk the bytes again, writing them out
       uint32_t n2 = 0, unused = 0;
-      byte_walk<true>(w, static_cast<int>(spl), lut, remw, k, a.n, nullptr, nullptr, n2, 0u,
-                      unused, table, chunk_mod, dst);
+      byte_walk<K, 8, true>(x0, x1, c_in, sb0, lut, remw, a.n, 0u, nullptr, n2, 0u, unused, table,
+                            chunk_mod, dst);
     }
   }
 }
 
+// One run per wave: its anchors, then its unary and remainder words are
+// requested first. (Several runs per wave, with all their loads issued up
+// front, measured slower: the decode is bound by instruction issue, not by
+// the memory round trip.)
 __device__ __forceinline__ void decode_wave(const RiceArgs& a, const uint8_t* table,
-                                            int64_t r, int lane, uint32_t* region,
+                                            int64_t r, int lane, uint32_t* region, uint32_t* buf,
                                             const uint4* lut, const uint32_t* spread) {
   Run run;
   Prefetch pf;
@@ -812,17 +850,16 @@ __device__ __forceinline__ void decode_wave(const RiceArgs& a, const uint8_t* ta
   prefetch_bounds(a, run, pf);
   prefetch_words(a, run, lane, pf);
   if (byte_path(a, run, pf))
-    decode_run_bytes(a, table, run, pf, lane, region, lut, spread);
+    decode_run_bytes<1>(a, table, run, pf, lane, region, buf, lut, spread);
   else
-    decode_run(a, table, run, pf, lane, region, region + (kStageWords + 4),
-               region + kNibOff + lane);
+    decode_run(a, table, run, pf, lane, region, region + (kStageWords + 4), buf + lane);
 }
 
-// The byte tables for Rice k (k > 1 loads k = 1's; that path does not use
-// them), one entry per thread of the 256-thread block.
-__device__ __forceinline__ void load_byte_tables(uint4* lut, uint32_t* spread, uint32_t k) {
+// The byte tables for Rice k = 1 (the byte-table path's k), one entry per
+// thread of the 256-thread block.
+__device__ __forceinline__ void load_byte_tables(uint4* lut, uint32_t* spread) {
   const int t = threadIdx.x;
-  const uint32_t* src = kByteTables.codes[k == 0 ? 0 : 1][t];
+  const uint32_t* src = kByteTables.codes[1][t];
   lut[t] = make_uint4(src[0], src[1], src[2], src[3]);
   spread[t] = kByteTables.spread[t];
   __syncthreads();
@@ -831,15 +868,16 @@ __device__ __forceinline__ void load_byte_tables(uint4* lut, uint32_t* spread, u
 // One wave per run; the run's anchors, first unary words and remainder
 // words are requested before any other work.
 __global__ __launch_bounds__(256) void rice_to_r4_kernel(RiceArgs a) {
-  __shared__ __align__(16) uint32_t region[kWavesPerBlock][kWaveRegion];
+  __shared__ __align__(16) uint32_t region[kWavesPerBlock][kGeneralWords];
+  __shared__ __align__(2048) uint32_t buf[kWavesPerBlock][kBufWords];
   __shared__ uint4 lut[256];
   __shared__ uint32_t spread[256];
-  load_byte_tables(lut, spread, a.k);
+  load_byte_tables(lut, spread);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t r = uniform64(static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave);
   if (r >= runs_total(a)) return;
-  decode_wave(a, kernarg_table(0), r, lane, region[wave], lut, spread);
+  decode_wave(a, kernarg_table(0), r, lane, region[wave], buf[wave], lut, spread);
 }
 
 // Several tensors in one launch: tensor i owns blocks
@@ -852,7 +890,8 @@ struct RiceBatch {
 };
 
 __global__ __launch_bounds__(256) void rice_to_r4_batch_kernel(RiceBatch b) {
-  __shared__ __align__(16) uint32_t region[kWavesPerBlock][kWaveRegion];
+  __shared__ __align__(16) uint32_t region[kWavesPerBlock][kGeneralWords];
+  __shared__ __align__(2048) uint32_t buf[kWavesPerBlock][kBufWords];
   __shared__ uint4 lut[256];
   __shared__ uint32_t spread[256];
   const int lane = threadIdx.x & 63;
@@ -868,10 +907,10 @@ __global__ __launch_bounds__(256) void rice_to_r4_batch_kernel(RiceBatch b) {
   const size_t off = offsetof(RiceBatch, item) + static_cast<size_t>(i) * sizeof(RiceArgs);
   const RiceArgs* items = (const RiceArgs*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + off);
   const RiceArgs a = items[0];
-  load_byte_tables(lut, spread, a.k);
+  load_byte_tables(lut, spread);
   const int64_t r = uniform64(static_cast<int64_t>(blk - b.first_block[i]) * kWavesPerBlock + wave);
   if (r >= runs_total(a)) return;
-  decode_wave(a, kernarg_table(off), r, lane, region[wave], lut, spread);
+  decode_wave(a, kernarg_table(off), r, lane, region[wave], buf[wave], lut, spread);
 }
 
 }  // namespace
@@ -927,13 +966,22 @@ int64_t prepare_decode(const binade_rice* in, binade_r4* out, uint32_t* dev_stat
   a.cols = static_cast<int32_t>(in->cols);
   a.k = in->k;
   a.n = in->n;
+  a.chunks_per_row = static_cast<uint32_t>(C);
+  a.c_recip = C > 1 ? static_cast<uint32_t>(((1ull << 32) + static_cast<uint64_t>(C) - 1) /
+                                            static_cast<uint64_t>(C))
+                    : 0u;
+  a.rows_per_run = C == 1 ? static_cast<uint32_t>(BINADE_CHUNK / in->cols) : 1u;
+  a.runs = C == 1 ? (in->rows + a.rows_per_run - 1) / a.rows_per_run : n_chunks;
+  a.cols_recip = in->cols < BINADE_CHUNK
+                     ? static_cast<uint32_t>(((1ull << 32) + static_cast<uint64_t>(in->cols) - 1) /
+                                             static_cast<uint64_t>(in->cols))
+                     : 0u;
   for (int q = 0; q < 64; ++q)
     a.table[q] = uint32_t(in->exp_of_rank[4 * q]) | (uint32_t(in->exp_of_rank[4 * q + 1]) << 8) |
                  (uint32_t(in->exp_of_rank[4 * q + 2]) << 16) |
                  (uint32_t(in->exp_of_rank[4 * q + 3]) << 24);
   // runs: one row-chunk, or 2048 / cols short rows; one wave each
-  return C == 1 ? (in->rows + (BINADE_CHUNK / in->cols) - 1) / (BINADE_CHUNK / in->cols)
-                : n_chunks;
+  return a.runs;
 }
 
 }  // namespace
