@@ -2,10 +2,11 @@
 // R4 -> bf16 unpack.
 //
 // "Binade" package page (pypi.org/project/binade), "Results": the batch-1
-// matvec on R4 runs at BF16's bandwidth efficiency, so it is faster per
-// token by the byte ratio; "How it works": R4 keeps every rank in 4 bits
-// with rare escapes, and the matvec adds its products in one fixed order so
-// its outputs equal the BF16 computation's bit for bit.
+// matvec on R4 moves its bytes as efficiently as the BF16 one does, so a
+// token is faster by the ratio of bytes; "How it works": R4 holds each rank as a 4-bit
+// code, the few large ranks going to a side list, and the matvec adds its
+// products in one fixed order so its outputs equal the BF16 computation's
+// bit for bit.
 //
 // Order (shared with the twin, independent of the launch shape): K is cut
 // into lane tiles of 32 columns; tile j belongs to slot j mod 64; slot l's

@@ -1,10 +1,11 @@
 // Host half of libbinade: exponent table, plane sizes and the format 2
 // (Rice) packer.
 //
-// "Binade" package page (pypi.org/project/binade), intro: the sign and the
-// mantissa stay one raw byte, the exponent becomes its frequency rank in a
-// per-tensor table, and the ranks are stored in Rice codes. Section "How it
-// works": one table per tensor; format 2 is the Rice format.
+// "Binade" package page (pypi.org/project/binade), intro: sign and mantissa
+// bits are kept unchanged in a byte, the exponent is stored as its rank
+// among the tensor's exponents ordered by frequency, and the ranks are
+// stored in Rice codes. Section "How it works": one table per tensor;
+// format 2 is the Rice format.
 //
 // Packing is offline work (the pages run it as a command-line step), so it
 // lives on the host; the device kernels start from its planes.

@@ -2,7 +2,8 @@
 //
 // "Binade" package page (pypi.org/project/binade), intro and "How it works":
 // the file stores ranks in Rice codes (~10.75 bits per weight); at load a
-// GPU kernel turns them into R4, every rank in 4 bits with rare escapes.
+// GPU kernel rewrites them as R4: a 4-bit code per rank, with the few
+// large ranks sent to a side list.
 // "Lossless BF16 weight compression" page, "Best measured configuration":
 // a decoder with per-block lengths found by a warp prefix sum and its output
 // staged on chip is what made the Huffman exponent decoder fast; the same

@@ -2,15 +2,16 @@
  * binade.h -- C ABI of libbinade, the Binade hot path on MI355X (gfx950).
  *
  * What it computes (the pages):
- *   "Binade" package page (pypi.org/project/binade), intro: a BF16 weight
- *   keeps its sign and mantissa as one raw byte; its 8-bit exponent is
- *   replaced by its frequency rank in a per-tensor table, stored on disk in
- *   Rice codes; at load the ranks become a 4-bit runtime layout that the
- *   kernels read during inference, and outputs are bit-identical.
- *   Same page, "How it works": one table per tensor (no exponent locality);
- *   format 2 = Rice codes; runtime layout R4 = every rank in 4 bits with rare
- *   escapes, converted by a GPU kernel at load; matvec, MoE expert gather and
- *   GEMM add their products in one fixed order.
+ *   "Binade" package page (pypi.org/project/binade), intro: each BF16
+ *   weight is stored as a byte of its sign and mantissa bits, unchanged,
+ *   plus its exponent's rank among the tensor's exponents ordered by
+ *   frequency; the ranks are Rice-coded on disk and rewritten at load into
+ *   a 4-bit form that the kernels read directly, with bit-identical outputs.
+ *   Same page, "How it works": a single table per tensor, because nearby
+ *   weights do not share exponents; format 2 = Rice codes; runtime layout
+ *   R4 = 4-bit rank codes with the few large ranks in a side list, produced
+ *   by a GPU kernel at load; the matvec, the MoE expert gather and the GEMM
+ *   each add their products in one fixed order.
  *
  * Conventions
  *   - Every function returns a binade_status (0 = OK). Nothing aborts or

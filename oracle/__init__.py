@@ -184,8 +184,8 @@ def rice_decode(pk: dict) -> np.ndarray:
 
 # ---------------------------------------------------------------- R4
 def make_r4(w_bits, table: dict) -> dict:
-    """R4 runtime layout ("Binade" package page, "How it works": every rank
-    in 4 bits with rare escapes)."""
+    """R4 runtime layout ("Binade" package page, "How it works": a 4-bit code
+    per rank, the few large ranks escaping to a side list)."""
     w = _u16(w_bits)
     rows, cols = w.shape
     cpr = (cols + CHUNK - 1) // CHUNK

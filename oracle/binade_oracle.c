@@ -8,11 +8,12 @@
  *
  * Sources (the pages):
  *   [P1] "Binade" package page, pypi.org/project/binade: intro paragraph
- *        (sign and mantissa kept as one raw byte; exponent replaced by its
- *        frequency rank in a per-tensor table; Rice codes on disk; a 4-bit
- *        runtime layout at load) and section "How it works" (one table per
- *        tensor; format 2 = Rice codes; runtime layout R4 = every rank in
- *        4 bits with rare escapes; exactness by a fixed summation order).
+ *        (sign and mantissa bits kept unchanged in a byte; the exponent
+ *        stored as its rank by frequency within the tensor; Rice codes on
+ *        disk; a 4-bit code per rank at run time) and section "How it
+ *        works" (one table per tensor; format 2 = Rice codes; runtime layout
+ *        R4 = 4-bit rank codes plus a side list for the few large ranks;
+ *        exactness by a fixed summation order).
  *   [P5] "Lossless BF16 weight compression" page, intro (only the exponent
  *        field is entropy coded; sign and mantissa stay raw).
  *
@@ -263,8 +264,8 @@ int oracle_rice_decode(int64_t rows, int64_t cols, int k,
 }
 
 /* ------------------------------------------------------------------ */
-/* R4 runtime layout ([P1] "How it works": every rank in 4 bits with rare
- * escapes). Readings:
+/* R4 runtime layout ([P1] "How it works": a 4-bit code per rank, the few
+ * large ranks escaping to a side list). Readings:
  *  - nibble = rank for ranks 0..14; nibble 15 marks an escape;
  *  - lut[r] = exponent of rank r for r < 15 (0 where the table has no such
  *    rank), lut[15] = 0;
