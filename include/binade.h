@@ -225,8 +225,12 @@ int32_t binade_bf16_gemv(const uint16_t *w, int64_t rows, int64_t cols,
  * and multiplied on bf16 MFMA with fp32 accumulation ("Binade" package page,
  * "Results" and "Limitations": prompt processing with fused GEMM). X: device
  * bf16 with row stride ldx (elements); Y: fp32 or bf16 with row stride ldy.
- * Order: per output, one fp32 accumulator, K taken in blocks of 32 in
- * increasing order, each block one bf16 MFMA step. */
+ * Order (depends on K only, never on M or the launch shape): K is cut into
+ * S = min(8, ceil(K / 1024)) slices of whole 32-column blocks (slice s =
+ * blocks [s*nb/S, (s+1)*nb/S) of the nb = K/32); per output and slice one
+ * fp32 accumulator from +0.0 takes the slice's blocks in increasing order,
+ * one v_mfma_f32_16x16x32_bf16 step each; the output adds the slices'
+ * accumulators in slice order. */
 int32_t binade_r4_gemm(const binade_r4 *w, const uint16_t *x, int64_t m,
                        int64_t ldx, void *y, int64_t ldy, int32_t y_dtype,
                        void *stream);

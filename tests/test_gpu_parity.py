@@ -301,3 +301,26 @@ def test_batched_decode_and_gemv_equal_single_calls():
     for i, (o, x, y) in enumerate(zip(outs, xs, yt)):
         y1 = B.r4_gemv(o, x, out_dtype=torch.bfloat16)
         assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), shapes[i]
+
+
+@pytest.mark.parametrize("nk", [(200, 15360), (136, 8192), (72, 3840)])
+def test_gemm_rows_do_not_depend_on_m(nk):
+    """The GEMM order depends on K only: the same X row gives the same bits
+    whether the call has 16, 32, 128 (small-M kernel) or 300 rows (tiled
+    kernel), with split-K slices (K = 8192, 15360) and escapes."""
+    N, K = nk
+    W = synth.normal_bf16(spec(N, K, 0.015, N + 7, 2e-3, 1e3))
+    X = synth.vector_bf16(K, N + 8, count=300)
+    _, r4 = to_r4(W)
+    Xd, Wd = X.to(DEV), W.to(DEV)
+    full = B.r4_gemm(r4, Xd).cpu()
+    assert torch.equal(full.view(torch.int32), B.bf16_gemm(Wd, Xd).cpu().view(torch.int32))
+    for m in (16, 32, 128, 129):
+        part = B.r4_gemm(r4, Xd[:m].contiguous()).cpu()
+        assert torch.equal(part.view(torch.int32), full[:m].view(torch.int32)), m
+        twin = B.bf16_gemm(Wd, Xd[:m].contiguous()).cpu()
+        assert torch.equal(twin.view(torch.int32), part.view(torch.int32)), m
+    wb, xb = bits_np(W), bits_np(X[:40])
+    ref = oracle.gemm_f64(wb, xb)
+    scale = oracle.gemm_f64(wb & 0x7FFF, xb & 0x7FFF)
+    assert np.all(np.abs(full[:40].numpy().astype(np.float64) - ref) <= 1e-2 * scale)
