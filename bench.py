@@ -97,6 +97,108 @@ def host_cores_used() -> int:
     return 1
 
 
+MFMA_BF16_PEAK_TFS = 2500.0   # MI355X dense bf16 matrix peak
+
+
+def graph_time_ms(stream, body, reps: int = 3) -> float:
+    """Best of `reps` replays of `body` captured once in a HIP graph, in ms
+    (events recorded on the stream the graph replays on)."""
+    with torch.cuda.stream(stream):
+        body()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        body()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    return best
+
+
+def r4_bytes(r4: B.R4Tensor) -> int:
+    return r4.rows * r4.cols * 3 // 2 + 4 * r4.n_esc + 4 * r4.esc_pre.numel()
+
+
+def measure_gemm(dev, stream) -> dict:
+    """Prompt GEMM on the 12B-class FFN shapes (R4 and its bf16 twin), each
+    shape and M timed as 10 launches in one HIP graph; outputs checked equal."""
+    out = {}
+    for spec in synth.gemma_12b_ffn()[1:]:   # up 15360x3840, down 3840x15360
+        w = synth.normal_bf16(spec, device=dev)
+        r4 = B.rice_to_r4(B.pack_rice(w.cpu()).to(dev))
+        N, K = spec.rows, spec.cols
+        for M in synth.GEMM_ROWS:
+            x = synth.vector_bf16(K, 500 + M, device=dev, count=M)
+            y = torch.empty(M, N, dtype=torch.float32, device=dev)
+            y2 = torch.empty_like(y)
+            reps = 10 if M < 2048 else 3
+            tr = graph_time_ms(stream, lambda: [B.r4_gemm(r4, x, y=y, stream=stream)
+                                                for _ in range(reps)]) / reps
+            tt = graph_time_ms(stream, lambda: [B.bf16_gemm(w, x, y=y2, stream=stream)
+                                                for _ in range(reps)]) / reps
+            torch.cuda.synchronize()
+            if not torch.equal(y.view(torch.int32), y2.view(torch.int32)):
+                raise SystemExit(f"parity gate: R4 GEMM differs from its twin ({N}x{K}, M={M})")
+            fl = 2.0 * M * N * K
+            nbytes = r4_bytes(r4) + 2 * M * K + 4 * M * N
+            out[f"{N}x{K}_M{M}"] = {
+                "r4_us": round(tr * 1e3, 2), "r4_TFLOPs": round(fl / tr / 1e9, 1),
+                "mfma_frac": round(fl / tr / 1e9 / MFMA_BF16_PEAK_TFS, 4),
+                "r4_GBs": round(nbytes / tr / 1e6, 1),
+                "bf16_twin_us": round(tt * 1e3, 2), "speedup_vs_twin": round(tt / tr, 3)}
+        del w, r4
+    return out
+
+
+def measure_moe(dev, stream) -> dict:
+    """One gathered MoE step: 8 tokens x top-8 of 128 experts through gate,
+    up (shared token input) and down (per-slot input) in R4 and bf16."""
+    specs = synth.moe_layer()
+    ws = [synth.normal_bf16(sp, device=dev) for sp in specs]
+    r4s = [B.rice_to_r4(B.pack_rice(w.cpu()).to(dev)) for w in ws]
+    E, T, k = synth.MOE_EXPERTS, synth.MOE_TOKENS, synth.MOE_TOP_K
+    idx = synth.topk_indices(T, k, E, 3100, device=dev)
+    xh = synth.vector_bf16(synth.MOE_HIDDEN, 3101, device=dev, count=T)
+    xf = synth.vector_bf16(synth.MOE_FFN, 3102, device=dev, count=T * k)
+    ins = [(xh, False), (xh, False), (xf, True)]
+    ys = [torch.empty(T * k, sp.rows // E, dtype=torch.float32, device=dev) for sp in specs]
+    ys2 = [torch.empty_like(y) for y in ys]
+
+    def r4_step():
+        for r4, (x, per), y in zip(r4s, ins, ys):
+            B.r4_moe_gemv(r4, E, x, idx, x_per_slot=per, y=y, stream=stream)
+
+    def twin_step():
+        for w, (x, per), y in zip(ws, ins, ys2):
+            B.bf16_moe_gemv(w, E, x, idx, x_per_slot=per, y=y, stream=stream)
+
+    tr = graph_time_ms(stream, r4_step)
+    tt = graph_time_ms(stream, twin_step)
+    torch.cuda.synchronize()
+    for y, y2 in zip(ys, ys2):
+        if not torch.equal(y.view(torch.int32), y2.view(torch.int32)):
+            raise SystemExit("parity gate: R4 MoE differs from its twin")
+    used = int(torch.unique(idx).numel())
+    nbytes = sum(r4_bytes(r4) * used // E for r4 in r4s)
+    nbytes += 2 * (xh.numel() * 2 + xf.numel()) + 4 * sum(y.numel() for y in ys)
+    return {"workload": "128 experts, gate/up 704x2816 and down 2816x704; 8 tokens x top-8",
+            "unique_experts": used, "r4_us_per_step": round(tr * 1e3, 2),
+            "r4_GBs": round(nbytes / tr / 1e6, 1), "bf16_twin_us_per_step": round(tt * 1e3, 2),
+            "speedup_vs_twin": round(tt / tr, 3),
+            "bytes": "unique experts' R4 bytes once + inputs + fp32 outputs"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,6 +207,8 @@ def main():
     ap.add_argument("--layers", type=int, default=synth.LLAMA_3B_LAYERS)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-twin", action="store_true")
+    ap.add_argument("--skip-gemm", action="store_true")
+    ap.add_argument("--skip-moe", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -294,27 +398,7 @@ def main():
     # in a HIP graph and replayed. The per-layer schedule, and one launch per
     # tensor on both sides of the bf16-twin comparison.
     def graph_ms(body):
-        with torch.cuda.stream(stream):
-            body()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            body()
-        with torch.cuda.stream(stream):
-            g.replay()
-        torch.cuda.synchronize()
-        best = None
-        for _ in range(3):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            with torch.cuda.stream(stream):   # replay runs on the current stream
-                e0.record(stream)
-                g.replay()
-                e1.record(stream)
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1)
-            best = ms if best is None else min(best, ms)
-        return best
+        return graph_time_ms(stream, body)
 
     def layer_schedule():
         for gi in range(len(layer_args)):
@@ -371,26 +455,34 @@ def main():
                 "note": "both sides HIP-graph replays of the same schedule; bytes per side "
                         "are that side's own weight bytes"}
 
+    # ------------------------------------------------------------ GEMM, MoE
+    # (the other rows of the path, reported beside the step; not in `value`)
+    gemm = None if args.skip_gemm else measure_gemm(dev, stream)
+    moe = None if args.skip_moe else measure_moe(dev, stream)
+
     # ------------------------------------------------------------ CPU oracle
     cpu = None
     if not args.skip_cpu_baseline:
+        # whole passes over the stack until at least 10 s of CPU work
         t0 = time.perf_counter()
         done_b = 0
         n_done = 0
-        for t in tensors:
-            wn = host_bits[t["spec"].name].view(torch.int16).numpy().view(np.uint16)
-            xb = xs[t["spec"].cols].cpu().view(torch.int16).numpy().view(np.uint16)
-            oracle.gemv_replay(wn, xb)
-            done_b += gemv_bytes(t["r4"])
-            n_done += 1
-            if time.perf_counter() - t0 > 20.0:
-                break
+        while time.perf_counter() - t0 < 10.0 and n_done < 20 * len(tensors):
+            for t in tensors:
+                wn = host_bits[t["spec"].name].view(torch.int16).numpy().view(np.uint16)
+                xb = xs[t["spec"].cols].cpu().view(torch.int16).numpy().view(np.uint16)
+                oracle.gemv_replay(wn, xb)
+                done_b += gemv_bytes(t["r4"])
+                n_done += 1
+                if time.perf_counter() - t0 > 30.0:
+                    break
         el = time.perf_counter() - t0
         cpu = {"value": done_b / el / 1e9, "unit": "GB/s", "cores": host_cores_used(),
                "kind": "oracle",
-               "sample": f"oracle fp32-order GEMV replay (single-threaded C) over the first "
-                         f"{n_done} of {len(tensors)} stack tensors from their bf16 bits, "
-                         f"{el:.1f} s; bytes counted as the R4 GEMV's"}
+               "sample": f"oracle fp32-order GEMV replay (single-threaded C), {n_done} tensor "
+                         f"products over the {len(tensors)} stack tensors' bf16 bits "
+                         f"({n_done / len(tensors):.2f} passes), {el:.1f} s; bytes counted as "
+                         f"the R4 GEMV's"}
 
     dominant = "gemv" if gemv_kernel_ms >= dec_kernel_ms else "rice_to_r4"
     roof_g = {"kernel": "r4_gemv", "bound": "hbm", "achieved": round(gemv_ach, 1),
@@ -429,6 +521,8 @@ def main():
         "roofline_other": roof_d if dominant == "gemv" else roof_g,
         "bf16_twin": twin,
         "gemv_per_layer_schedule": sched,
+        "prompt_gemm": gemm,
+        "moe_gather": moe,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
