@@ -84,6 +84,17 @@ __device__ __forceinline__ uint32_t weight_pair_bf16(uint32_t H, uint32_t Lo) {
   return vperm(H, Lo, sel);
 }
 
+// fma 4 weights of one split group into the two running sums of a lane
+// tile, columns 4d .. 4d+3 (4d is even: even columns go to a0, odd to a1).
+__device__ __forceinline__ void fma_group(uint32_t H, uint32_t Lo,
+                                          const float* xg, float& a0,
+                                          float& a1) {
+  a0 = __builtin_fmaf(weight_f32<0>(H, Lo), xg[0], a0);
+  a1 = __builtin_fmaf(weight_f32<1>(H, Lo), xg[1], a1);
+  a0 = __builtin_fmaf(weight_f32<2>(H, Lo), xg[2], a0);
+  a1 = __builtin_fmaf(weight_f32<3>(H, Lo), xg[3], a1);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t d) {
   return __uint_as_float(d << 16);
 }

@@ -48,17 +48,6 @@ struct GemvArgs {
   uint32_t lut0, lut1, lut2, lut3;
 };
 
-// fma 4 weights of one split group into the two running sums, columns
-// 4d .. 4d+3 of the tile (4d is even).
-__device__ __forceinline__ void fma_group(uint32_t H, uint32_t Lo,
-                                          const float* xg, float& a0,
-                                          float& a1) {
-  a0 = __builtin_fmaf(weight_f32<0>(H, Lo), xg[0], a0);
-  a1 = __builtin_fmaf(weight_f32<1>(H, Lo), xg[1], a1);
-  a0 = __builtin_fmaf(weight_f32<2>(H, Lo), xg[2], a0);
-  a1 = __builtin_fmaf(weight_f32<3>(H, Lo), xg[3], a1);
-}
-
 __device__ __forceinline__ void store_y(const GemvArgs& a, int64_t row,
                                         float v) {
   if (a.y_bf16)

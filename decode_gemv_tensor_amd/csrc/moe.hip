@@ -6,12 +6,21 @@
 // expert idx[p]; its output row is that expert's matvec of the pair's input,
 // with exactly the binade_r4_gemv order.
 //
-// Mapping: block (g, e) covers rows 4g..4g+3 of expert e, one wave per row.
-// A wave first finds, with one ballot per 64 pairs, every pair that chose
-// expert e (an expert nobody chose costs one idx read and exits), then walks
-// the row's chunks once per group of up to 4 such pairs: the 32 weights of
-// its lane tile are rebuilt in registers once and multiplied against each
-// pair's x tile. So an expert chosen by several pairs is read from HBM once.
+// Mapping: block (g, e) covers a group of rows of expert e. A row of J lane
+// tiles (32 columns each) with J > 32 takes a whole wave (lane l: tiles l,
+// l + 64, ...); shorter rows are packed 64 / 2^ceil(log2 J) to a wave, one
+// lane group per row, lane i of a group holding tile i. Block row y takes
+// the y-th expert that some pair chose (the block finds the chosen set from
+// idx in LDS), so experts nobody chose cost no blocks. A wave then finds,
+// with one ballot per 64 pairs, the pairs that chose its expert and walks
+// its rows once per pair: lane tiles rebuilt with v_perm_b32 table lookups,
+// escapes patched from registers (the wave's escape prefixes and side-list
+// entries are loaded once, a lane each). A second pair of the same expert
+// re-reads the rows the wave has just read, from cache.
+//
+// A packed row's slots 32, 16, ... down to its group width hold no tile, so
+// the matvec's tree adds +0.0 to each of the group's slots at those levels;
+// one "+ 0.0f" does the same, and the rest of the tree runs inside the group.
 #include <hip/hip_runtime.h>
 
 #include "binade.h"
@@ -22,7 +31,7 @@ namespace {
 
 using namespace dev;
 
-constexpr int kPairsPerPass = 4;
+constexpr int kPairsPerPass = 1;   // more per pass measured slower (registers)
 
 struct MoeArgs {
   const uint8_t* w;        // R4 sm plane, or bf16 experts (twin)
@@ -41,51 +50,9 @@ struct MoeArgs {
   int32_t x_per_slot;
   int32_t y_bf16;
   uint32_t n_esc;
-  uint32_t lut0, lut1, lut2, lut3;
+  uint32_t lut0, lut1, lut2, lut3;   // rotated exponents of ranks 0..15
+  int32_t width_log2;      // lanes per row: 6 (a whole wave) or less (packed)
 };
-
-template <bool kR4>
-__device__ __forceinline__ void tile_weights(const MoeArgs& a, int64_t grow,
-                                             int64_t chunk, int t, bool active,
-                                             int lane, float (&w)[32]) {
-  if (kR4) {
-    uint4 s0 = make_uint4(0, 0, 0, 0), s1 = s0, nb = s0;
-    if (active) {
-      const uint4* ps = reinterpret_cast<const uint4*>(a.w + grow * a.cols + 32 * t);
-      s0 = ps[0];
-      s1 = ps[1];
-      nb = *reinterpret_cast<const uint4*>(a.nib + grow * (a.cols >> 1) + 16 * t);
-    }
-    const Lut L{a.lut0, a.lut1, a.lut2, a.lut3};
-    uint32_t E[8];
-    tile_exponents(nb, L, a.esc_pre, a.esc, a.n_esc, chunk, lane, E);
-    const uint32_t S[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      uint32_t H, Lo;
-      split4(S[d], E[d], H, Lo);
-      w[4 * d] = weight_f32<0>(H, Lo);
-      w[4 * d + 1] = weight_f32<1>(H, Lo);
-      w[4 * d + 2] = weight_f32<2>(H, Lo);
-      w[4 * d + 3] = weight_f32<3>(H, Lo);
-    }
-  } else {
-    if (active) {
-      const uint4* p = reinterpret_cast<const uint4*>(
-          reinterpret_cast<const uint16_t*>(a.w) + grow * a.cols + 32 * t);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint4 d = p[v];
-        const uint32_t q[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[8 * v + 2 * e] = bf16_lo(q[e]);
-          w[8 * v + 2 * e + 1] = bf16_hi(q[e]);
-        }
-      }
-    }
-  }
-}
 
 __device__ __forceinline__ void store_out(const MoeArgs& a, int64_t i, float v) {
   if (a.y_bf16)
@@ -94,26 +61,222 @@ __device__ __forceinline__ void store_out(const MoeArgs& a, int64_t i, float v) 
     static_cast<float*>(a.y)[i] = v;
 }
 
+// Exponent dwords of one lane tile of a packed wave: table lookups, then
+// every packed row's escapes (uniform loop per row; the lane holding the
+// entry's tile patches it).
+__device__ __forceinline__ void moe_tile_exponents(const MoeArgs& a, uint4 nb, const Lut& L,
+                                                   int64_t grow0, int64_t n_valid, int G,
+                                                   int wl, int C, int j, int lane,
+                                                   uint32_t (&E)[8]) {
+  const uint32_t P[4] = {nb.x, nb.y, nb.z, nb.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    E[2 * q] = lookup4(P[q], L);
+    E[2 * q + 1] = lookup4(P[q] >> 4, L);
+  }
+  const int gi = lane >> wl;
+  for (int r = 0; r < G; ++r) {
+    if (r >= n_valid) break;
+    const int64_t chunk = (grow0 + r) * C + j;
+    uint32_t e_end = uniform(a.esc_pre[chunk + 1]);
+    uint32_t e_beg = uniform(a.esc_pre[chunk]);
+    e_end = e_end < a.n_esc ? e_end : a.n_esc;
+    e_beg = e_beg < e_end ? e_beg : e_end;
+    for (uint32_t e = e_beg; e < e_end; ++e) {
+      const uint32_t ent = uniform(a.esc[e]);
+      const uint32_t off = ent & 0xFFFFu;
+      // off is the column within the 2048-column chunk: tile off >> 5 of it
+      const uint32_t tile = off >> 5;
+      const uint32_t my_tile = G > 1 ? static_cast<uint32_t>(lane & ((1 << wl) - 1))
+                                     : static_cast<uint32_t>(lane);
+      if (gi == r && my_tile == tile)
+        patch_exponent(E, off & 31u, rot_exponent((ent >> 16) & 0xFFu));
+    }
+  }
+}
+
+constexpr int kMaxExpertWords = 2048;   // experts <= 65536
+constexpr int kMaxPairsLds = 2048;      // idx values kept in LDS
+
+// The rank-th expert (increasing index) that some pair chose, or -1; every
+// thread of the block takes part. Out-of-range indices are not experts.
+__device__ __forceinline__ int32_t chosen_expert(const MoeArgs& a, uint32_t* present,
+                                                 int32_t* idx_s, int32_t* picked, int32_t rank) {
+  const int nw = (a.n_experts + 31) >> 5;
+  for (int i = threadIdx.x; i < nw; i += blockDim.x) present[i] = 0u;
+  if (threadIdx.x == 0) *picked = -1;
+  __syncthreads();
+  for (int32_t p = threadIdx.x; p < a.n_pairs; p += blockDim.x) {
+    const int32_t v = a.idx[p];
+    if (p < kMaxPairsLds) idx_s[p] = v;
+    if (v >= 0 && v < a.n_experts) atomicOr(&present[v >> 5], 1u << (v & 31));
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    // wave 0: prefix count of set bits over the words, 64 words at a time
+    int32_t before = 0;
+    for (int base = 0; base < nw; base += 64) {
+      const int i = base + static_cast<int>(threadIdx.x);
+      const uint32_t word = i < nw ? present[i] : 0u;
+      const int32_t c = __popc(word);
+      int32_t incl = c;
+      for (int sh = 1; sh < 64; sh <<= 1) {
+        const int32_t o = __shfl_up(incl, sh, 64);
+        if (static_cast<int>(threadIdx.x) >= sh) incl += o;
+      }
+      const int32_t excl = before + incl - c;
+      if (rank >= excl && rank < excl + c) {
+        uint32_t w = word;
+        for (int32_t k = rank - excl; k > 0; --k) w &= w - 1u;
+        *picked = (i << 5) + __builtin_ctz(w);
+      }
+      before += __shfl(incl, 63, 64);
+    }
+  }
+  __syncthreads();
+  return *picked;
+}
+
+// The same patches from registers: lane c holds the escape prefix of the
+// wave's c-th chunk (chunks of its rows in order, pre_lane), lane i holds
+// side-list entry e0 + i (ent_lane). Chunk c = (row r, chunk j) of the rows'
+// flat chunk range; only chunks j of this pass are walked.
+__device__ __forceinline__ void moe_patch_regs(uint32_t pre_lane, uint32_t ent_lane, uint32_t e0,
+                                               int n_valid, int C, int j, int wl, int G,
+                                               int lane, uint32_t (&E)[8]) {
+  const int gi = lane >> wl;
+  const uint32_t my_tile = G > 1 ? static_cast<uint32_t>(lane & ((1 << wl) - 1))
+                                 : static_cast<uint32_t>(lane);
+  for (int r = 0; r < n_valid; ++r) {
+    const int c = r * C + j;
+    const uint32_t lo = __builtin_amdgcn_readlane(pre_lane, c);
+    const uint32_t hi = __builtin_amdgcn_readlane(pre_lane, c + 1);
+    for (uint32_t q = lo; q < hi; ++q) {
+      const uint32_t ent = __builtin_amdgcn_readlane(ent_lane, static_cast<int>(q - e0));
+      const uint32_t off = ent & 0xFFFFu;
+      if (gi == r && my_tile == (off >> 5))
+        patch_exponent(E, off & 31u, rot_exponent((ent >> 16) & 0xFFu));
+    }
+  }
+}
+
+// Raw loads of one lane tile: R4 sm + nibbles, or the twin's bf16 words.
 template <bool kR4>
-__global__ __launch_bounds__(256) void moe_gemv_kernel(MoeArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int32_t e = static_cast<int32_t>(blockIdx.y);
-  const int64_t row = uniform64(static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6));
-  if (row >= a.n_rows) return;
-  const int J = a.cols >> 5;
-  const int C = (J + 63) >> 6;
-  const int64_t grow = static_cast<int64_t>(e) * a.n_rows + row;
+struct MoeRaw {
+  uint4 s0, s1, nb;   // R4
+  uint4 q[4];         // twin
+};
+
+template <bool kR4>
+__device__ __forceinline__ void moe_load(const MoeArgs& a, int64_t grow, int t, bool active,
+                                         MoeRaw<kR4>& r) {
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  if (kR4) {
+    r.s0 = r.s1 = r.nb = z;
+    if (active) {
+      const uint4* ps = reinterpret_cast<const uint4*>(a.w + grow * a.cols + 32 * t);
+      r.s0 = ps[0];
+      r.s1 = ps[1];
+      r.nb = *reinterpret_cast<const uint4*>(a.nib + grow * (a.cols >> 1) + 16 * t);
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) r.q[v] = z;
+    if (active) {
+      const uint4* pw = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.w) +
+                                                       grow * a.cols + 32 * t);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) r.q[v] = pw[v];
+    }
+  }
+}
+
+// One lane tile's 32 weights as fp32 (escapes patched for R4).
+template <bool kR4>
+__device__ __forceinline__ void moe_weights(const MoeArgs& a, const MoeRaw<kR4>& r, const Lut& L,
+                                            bool regs, uint32_t pre_lane, uint32_t ent_lane,
+                                            uint32_t e0, int64_t grow0, int64_t n_valid, int G,
+                                            int wl, int C, int j, int lane, float (&w)[32]) {
+  if (kR4) {
+    uint32_t E[8];
+    if (regs) {
+      const uint32_t P[4] = {r.nb.x, r.nb.y, r.nb.z, r.nb.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        E[2 * q] = lookup4(P[q], L);
+        E[2 * q + 1] = lookup4(P[q] >> 4, L);
+      }
+      moe_patch_regs(pre_lane, ent_lane, e0, static_cast<int>(n_valid), C, j, wl, G, lane, E);
+    } else {
+      moe_tile_exponents(a, r.nb, L, grow0, n_valid, G, wl, C, j, lane, E);
+    }
+    const uint32_t S[8] = {r.s0.x, r.s0.y, r.s0.z, r.s0.w, r.s1.x, r.s1.y, r.s1.z, r.s1.w};
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      uint32_t H, Lo;
+      split4_rot(S[d], E[d], H, Lo);
+      w[4 * d] = weight_f32<0>(H, Lo);
+      w[4 * d + 1] = weight_f32<1>(H, Lo);
+      w[4 * d + 2] = weight_f32<2>(H, Lo);
+      w[4 * d + 3] = weight_f32<3>(H, Lo);
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t q[4] = {r.q[v].x, r.q[v].y, r.q[v].z, r.q[v].w};
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        w[8 * v + 2 * k2] = bf16_lo(q[k2]);
+        w[8 * v + 2 * k2 + 1] = bf16_hi(q[k2]);
+      }
+    }
+  }
+}
+
+// The rows row0 .. row0+G-1 of expert e (G = 1: a whole-wave row). Tiles
+// are loaded per chunk inside each pass over a pair group, which keeps the
+// register count (and so the waves per SIMD) where this latency-bound
+// kernel wants it.
+template <bool kR4>
+__device__ __forceinline__ void moe_row_set(const MoeArgs& a, const Lut& L, int32_t e, int64_t row0,
+                                            int G, int gi, int ti, int wl, int J, int C,
+                                            int lane, const int32_t* idx_s) {
+  const int64_t n_valid = a.n_rows - row0 < G ? a.n_rows - row0 : G;
+  const bool row_ok = gi < n_valid;
+  const int64_t row = row0 + (row_ok ? gi : 0);
+  const int64_t grow0 = static_cast<int64_t>(e < 0 ? 0 : e) * a.n_rows + row0;
+  const int64_t grow = grow0 + (row - row0);
+
+  // the wave's escape prefixes and side-list entries, in registers when
+  // they fit a lane each (the usual case)
+  const int F = static_cast<int>(n_valid) * C;   // chunks of the wave's rows
+  uint32_t pre_lane = 0, ent_lane = 0, e0 = 0;
+  bool regs = false;
+  if (kR4 && e >= 0 && F + 1 <= 64) {
+    const uint32_t pv = lane <= F ? a.esc_pre[grow0 * C + lane] : 0u;
+    pre_lane = pv < a.n_esc ? pv : a.n_esc;
+    e0 = __builtin_amdgcn_readlane(pre_lane, 0);
+    const uint32_t e1 = __builtin_amdgcn_readlane(pre_lane, F);
+    if (e1 >= e0 && e1 - e0 <= 64u) {
+      regs = true;
+      ent_lane = static_cast<uint32_t>(lane) < e1 - e0 ? a.esc[e0 + lane] : 0u;
+      // prefixes must not decrease, or the register walk would misread
+      const uint32_t prev = __shfl_up(pre_lane, 1, 64);
+      if (__any(lane >= 1 && lane <= F && pre_lane < prev)) regs = false;
+    }
+  }
 
   for (int32_t base = 0; base < a.n_pairs; base += 64) {
     const int32_t p = base + lane;
-    const int32_t v = p < a.n_pairs ? a.idx[p] : 0;
-    uint64_t mine = __ballot(p < a.n_pairs && v == e);
+    const int32_t v = p < a.n_pairs ? (p < kMaxPairsLds ? idx_s[p] : a.idx[p]) : 0;
+    uint64_t mine = e < 0 ? 0ull : __ballot(p < a.n_pairs && v == e);
     const uint64_t badm = __ballot(p < a.n_pairs && (v < 0 || v >= a.n_experts));
-    if (badm != 0 && e == 0) {
-      // out-of-range indices: flag once per row and zero those output rows
-      if (lane == 0 && row == 0 && a.status != nullptr)
+    if (badm != 0 && blockIdx.y == 0) {
+      // out-of-range indices: flag once and zero those pairs' rows
+      if (lane == 0 && row0 == 0 && a.status != nullptr)
         atomicOr(a.status, static_cast<uint32_t>(BINADE_DEV_BAD_INDEX));
-      if (((badm >> lane) & 1u) != 0) store_out(a, static_cast<int64_t>(p) * a.n_rows + row, 0.0f);
+      if (((badm >> lane) & 1u) != 0)
+        for (int r = 0; r < n_valid; ++r) store_out(a, static_cast<int64_t>(p) * a.n_rows + row0 + r, 0.0f);
     }
     while (mine != 0) {
       // next group of up to 4 pairs, in increasing pair order
@@ -133,10 +296,13 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(MoeArgs a) {
 #pragma unroll
       for (int g = 0; g < kPairsPerPass; ++g) a0[g] = a1[g] = 0.0f;
       for (int j = 0; j < C; ++j) {
-        const int t = j * 64 + lane;
+        const int t = G > 1 ? ti : j * 64 + lane;
         const bool active = t < J;
+        MoeRaw<kR4> rj;
+        moe_load<kR4>(a, grow, t, active, rj);
         float w[32];
-        tile_weights<kR4>(a, grow, grow * C + j, t, active, lane, w);
+        moe_weights<kR4>(a, rj, L, regs, pre_lane, ent_lane, e0, grow0, n_valid, G, wl, C, j,
+                         lane, w);
         if (!active) continue;
 #pragma unroll
         for (int g = 0; g < kPairsPerPass; ++g) {
@@ -154,16 +320,50 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(MoeArgs a) {
 #pragma unroll
       for (int g = 0; g < kPairsPerPass; ++g) {
         if (g >= np) break;
-        const float r = slot_tree(a0[g] + a1[g]);
-        if (lane == 0) store_out(a, static_cast<int64_t>(pp[g]) * a.n_rows + row, r);
+        float r = a0[g] + a1[g];
+        if (G == 1) {
+          r = slot_tree(r);
+        } else {
+          r = r + 0.0f;   // the tree levels whose partner slots hold no tile
+          for (int sh = (1 << wl) >> 1; sh >= 1; sh >>= 1) r = r + __shfl_xor(r, sh, 64);
+        }
+        if (ti == 0 && row_ok) store_out(a, static_cast<int64_t>(pp[g]) * a.n_rows + row, r);
       }
     }
   }
 }
 
-int32_t launch(const MoeArgs& a, bool r4, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>((a.n_rows + 3) / 4),
-                  static_cast<uint32_t>(a.n_experts));
+template <bool kR4>
+__global__ __launch_bounds__(256) void moe_gemv_kernel(MoeArgs a) {
+  __shared__ uint32_t present[kMaxExpertWords];
+  __shared__ int32_t idx_s[kMaxPairsLds];
+  __shared__ int32_t picked;
+  const int lane = threadIdx.x & 63;
+  const int32_t e =
+      uniform(chosen_expert(a, present, idx_s, &picked, static_cast<int32_t>(blockIdx.y)));
+  if (e < 0 && blockIdx.y != 0) return;
+  const int wl = a.width_log2;
+  const int G = 64 >> wl;                       // rows per row set
+  const int gi = lane >> wl;                    // this lane's row in the set
+  const int ti = lane & ((1 << wl) - 1);        // this lane's tile (packed)
+  const int J = a.cols >> 5;
+  const int C = (J + 63) >> 6;
+  const Lut L{a.lut0, a.lut1, a.lut2, a.lut3};
+  const int64_t row0 = uniform64((static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * G);
+  if (row0 >= a.n_rows) return;
+  moe_row_set<kR4>(a, L, e, row0, G, gi, ti, wl, J, C, lane, idx_s);
+}
+
+int32_t launch(MoeArgs a, bool r4, hipStream_t stream) {
+  const int J = a.cols >> 5;
+  int wl = 0;
+  while ((1 << wl) < J && wl < 6) ++wl;
+  a.width_log2 = J > 32 ? 6 : wl;
+  const int64_t rows_per_block = 4ll * (64 >> a.width_log2);
+  // grid y: one block row per chosen expert (at most min(experts, pairs))
+  const int64_t slots = a.n_experts < a.n_pairs ? a.n_experts : a.n_pairs;
+  const dim3 grid(static_cast<uint32_t>((a.n_rows + rows_per_block - 1) / rows_per_block),
+                  static_cast<uint32_t>(slots));
   if (r4)
     hipLaunchKernelGGL(moe_gemv_kernel<true>, grid, dim3(256), 0, stream, a);
   else
@@ -216,10 +416,10 @@ extern "C" int32_t binade_r4_moe_gemv(const binade_r4* w, int32_t n_experts,
   a.esc_pre = w->esc_pre;
   a.esc = w->esc;
   a.n_esc = static_cast<uint32_t>(w->n_esc);
-  a.lut0 = pack4(w->lut);
-  a.lut1 = pack4(w->lut + 4);
-  a.lut2 = pack4(w->lut + 8);
-  a.lut3 = pack4(w->lut + 12);
+  a.lut0 = rot_exponents4(pack4(w->lut));
+  a.lut1 = rot_exponents4(pack4(w->lut + 4));
+  a.lut2 = rot_exponents4(pack4(w->lut + 8));
+  a.lut3 = rot_exponents4(pack4(w->lut + 12));
   a.x = x;
   a.idx = idx;
   a.y = y;

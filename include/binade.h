@@ -246,8 +246,9 @@ int32_t binade_bf16_gemm(const uint16_t *w, int64_t rows, int64_t cols,
  * stored as one [n_experts*N, K] tensor with one table. idx: device
  * int32[n_tokens*top_k]. x: device bf16 [n_tokens, K] (x_per_slot = 0) or
  * [n_tokens*top_k, K] (x_per_slot = 1). y: [n_tokens*top_k, N], row p =
- * expert idx[p] times its input, in the binade_r4_gemv order. Experts chosen
- * by several pairs are read from HBM once per launch. An index outside
+ * expert idx[p] times its input, in the binade_r4_gemv order. Experts no
+ * pair chose are not read; a wave that serves several pairs of one expert
+ * re-reads its rows from cache. An index outside
  * [0, n_experts) sets BINADE_DEV_BAD_INDEX in dev_status (if not NULL) and
  * leaves that output row as zeros. */
 int32_t binade_r4_moe_gemv(const binade_r4 *experts, int32_t n_experts,
