@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import subprocess
@@ -98,6 +99,47 @@ def host_cores_used() -> int:
 
 
 MFMA_BF16_PEAK_TFS = 2500.0   # MI355X dense bf16 matrix peak
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "decode_gemv_tensor_amd", "csrc")
+# sources whose text decides each kernel's memory traffic
+KERNEL_SOURCES = {"rice_to_r4": ["rice_to_r4.hip", "device_common.h"],
+                  "r4_gemv": ["gemv.hip", "device_common.h"]}
+
+
+def source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE runs
+    (profiles/traffic.json), if they were taken on this kernel's current
+    source; else None."""
+    path = os.path.join(HERE, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def copy_probe(dev) -> None:
+    """A plain elementwise copy of 1 GiB (fp32 x 1), five times: the counter
+    runs read FETCH_SIZE and WRITE_SIZE on it to scale the kernels' readings."""
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy probe: 5 x {n * 4} bytes read and written")
 
 
 def graph_time_ms(stream, body, reps: int = 3) -> float:
@@ -209,6 +251,8 @@ def main():
     ap.add_argument("--skip-twin", action="store_true")
     ap.add_argument("--skip-gemm", action="store_true")
     ap.add_argument("--skip-moe", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run the 1 GiB copy used to scale memory counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -220,6 +264,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        copy_probe(dev)
+        return
     stream = torch.cuda.Stream()
     L = B.lib()
 
@@ -487,12 +534,12 @@ def main():
     dominant = "gemv" if gemv_kernel_ms >= dec_kernel_ms else "rice_to_r4"
     roof_g = {"kernel": "r4_gemv", "bound": "hbm", "achieved": round(gemv_ach, 1),
               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gemv_ach / HBM_PEAK_GBS, 4),
-              "traffic": None, "launches_per_step": n_gemv_launch,
+              "traffic": measured_traffic("r4_gemv"), "launches_per_step": n_gemv_launch,
               "avg_launch_us": round(gemv_kernel_ms * 1e3 / n_gemv_launch, 3),
               "bytes_per_launch": gemv_b // n_gemv_launch}
     roof_d = {"kernel": "rice_to_r4", "bound": "hbm", "achieved": round(dec_ach, 1),
               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_ach / HBM_PEAK_GBS, 4),
-              "traffic": None, "launches_per_step": n_dec_launch,
+              "traffic": measured_traffic("rice_to_r4"), "launches_per_step": n_dec_launch,
               "avg_launch_us": round(dec_kernel_ms * 1e3 / n_dec_launch, 3),
               "bytes_per_launch": dec_b // n_dec_launch,
               "gsym_per_s": round(syms / (dec_kernel_ms * 1e-3) / 1e9, 1)}
