@@ -366,9 +366,12 @@ __device__ __forceinline__ void prefetch_bounds(const RiceArgs& a, const Run& ru
 __device__ __forceinline__ void prefetch_words(const RiceArgs& a, const Run& run,
                                                int lane, Prefetch& pf) {
   // uniform bases and a 32-bit lane offset; words past the plane read as 0
+  // (only the run's own words: up to the word holding its last bit)
   const uint64_t wA = pf.A >> 5;
   const uint64_t left = a.unary_words > wA ? a.unary_words - wA : 0ull;
-  const uint32_t avail = left > 0x7FFFFFFFull ? 0x7FFFFFFFu : static_cast<uint32_t>(left);
+  const uint64_t need = pf.B > pf.A ? ((pf.B - 1) >> 5) - wA + 1 : 0ull;
+  const uint64_t lim = need < left ? need : left;
+  const uint32_t avail = lim > 0x7FFFFFFFull ? 0x7FFFFFFFu : static_cast<uint32_t>(lim);
   const uint32_t* ub = a.unary + wA;
   const uint32_t wi = 2u * static_cast<uint32_t>(lane);
   pf.w0 = wi < avail ? ub[wi] : 0u;
@@ -379,7 +382,9 @@ __device__ __forceinline__ void prefetch_words(const RiceArgs& a, const Run& run
     // boundary since fb is a multiple of 32
     const uint64_t r0 = (static_cast<uint64_t>(run.fb) * a.k) >> 5;
     const uint64_t rleft = a.rem_words > r0 ? a.rem_words - r0 : 0ull;
-    const uint32_t ravail = rleft > 0x7FFFFFFFull ? 0x7FFFFFFFu : static_cast<uint32_t>(rleft);
+    const uint64_t rneed = static_cast<uint64_t>(run.len >> 5) * a.k;   // the run's tiles
+    const uint64_t rlim = rneed < rleft ? rneed : rleft;
+    const uint32_t ravail = rlim > 0x7FFFFFFFull ? 0x7FFFFFFFu : static_cast<uint32_t>(rlim);
     const uint32_t* rb = a.rem + r0;
     const uint32_t ri = static_cast<uint32_t>(lane) * a.k;
     pf.rw0 = ri < ravail ? rb[ri] : 0u;
