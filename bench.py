@@ -174,7 +174,8 @@ def r4_bytes(r4: B.R4Tensor) -> int:
 
 def measure_gemm(dev, stream) -> dict:
     """Prompt GEMM on the 12B-class FFN shapes (R4 and its bf16 twin), each
-    shape and M timed as 10 launches in one HIP graph; outputs checked equal."""
+    shape and M timed as 10 launches in one HIP graph (with the workspace the
+    shape asks for, allocated once); outputs checked equal."""
     out = {}
     for spec in synth.gemma_12b_ffn()[1:]:   # up 15360x3840, down 3840x15360
         w = synth.normal_bf16(spec, device=dev)
@@ -184,10 +185,12 @@ def measure_gemm(dev, stream) -> dict:
             x = synth.vector_bf16(K, 500 + M, device=dev, count=M)
             y = torch.empty(M, N, dtype=torch.float32, device=dev)
             y2 = torch.empty_like(y)
+            ws = torch.empty(B.gemm_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
             reps = 10 if M < 2048 else 3
-            tr = graph_time_ms(stream, lambda: [B.r4_gemm(r4, x, y=y, stream=stream)
+            tr = graph_time_ms(stream, lambda: [B.r4_gemm(r4, x, y=y, stream=stream, workspace=ws)
                                                 for _ in range(reps)]) / reps
-            tt = graph_time_ms(stream, lambda: [B.bf16_gemm(w, x, y=y2, stream=stream)
+            tt = graph_time_ms(stream, lambda: [B.bf16_gemm(w, x, y=y2, stream=stream,
+                                                            workspace=ws)
                                                 for _ in range(reps)]) / reps
             torch.cuda.synchronize()
             if not torch.equal(y.view(torch.int32), y2.view(torch.int32)):

@@ -27,8 +27,8 @@ EXPORTS = ["binade_status_str", "binade_last_hip_error", "binade_build_table",
            "binade_sizes_of", "binade_pack_rice", "binade_rice_to_r4",
            "binade_rice_to_r4_batch", "binade_unpack", "binade_r4_gemv",
            "binade_r4_gemv_batch", "binade_bf16_gemv", "binade_bf16_gemv_batch",
-           "binade_r4_gemm", "binade_bf16_gemm", "binade_r4_moe_gemv",
-           "binade_bf16_moe_gemv"]
+           "binade_r4_gemm", "binade_bf16_gemm", "binade_gemm_workspace_bytes",
+           "binade_r4_moe_gemv", "binade_bf16_moe_gemv"]
 
 
 class Table(ctypes.Structure):
@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
             L.binade_status_str.argtypes = [I32]
             L.binade_status_str.restype = ctypes.c_char_p
             L.binade_last_hip_error.restype = I32
+            L.binade_gemm_workspace_bytes.argtypes = [I64, I64, I64]
+            L.binade_gemm_workspace_bytes.restype = I64
             sig = {
                 "binade_build_table": [P, I64, P],
                 "binade_sizes_of": [P, I64, I64, P],
@@ -104,8 +106,9 @@ def lib() -> ctypes.CDLL:
                 "binade_unpack": [P, P, P],
                 "binade_r4_gemv": [P, P, P, I32, P],
                 "binade_bf16_gemv": [P, I64, I64, P, P, I32, P],
-                "binade_r4_gemm": [P, P, I64, I64, P, I64, I32, P],
-                "binade_bf16_gemm": [P, I64, I64, P, I64, I64, P, I64, I32, P],
+                "binade_r4_gemm": [P, P, I64, I64, P, I64, I32, P, I64, P],
+                "binade_bf16_gemm": [P, I64, I64, P, I64, I64, P, I64, I32, P, I64,
+                                     P],
                 "binade_r4_moe_gemv": [P, I32, P, I32, P, I64, I32, P, I32, P, P],
                 "binade_bf16_moe_gemv": [P, I32, I64, I64, P, I32, P, I64, I32,
                                          P, I32, P, P],
@@ -404,28 +407,49 @@ def unpack(w: R4Tensor, out: torch.Tensor | None = None, stream=None) -> torch.T
     return out
 
 
+def gemm_workspace_bytes(m: int, n: int, k: int) -> int:
+    """Bytes of workspace with which an M x N x K GEMM splits its slices
+    over blocks (0: it never does)."""
+    return int(lib().binade_gemm_workspace_bytes(m, n, k))
+
+
+def _workspace(m, n, k, device, workspace):
+    if workspace is None:
+        nb = gemm_workspace_bytes(m, n, k)
+        if nb == 0:
+            return None, 0
+        workspace = torch.empty(nb, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def r4_gemm(w: R4Tensor, x: torch.Tensor, out_dtype=torch.float32,
-            y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+            y: torch.Tensor | None = None, stream=None,
+            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X W^T. workspace: optional device buffer (a fresh one of
+    gemm_workspace_bytes is taken from torch's allocator when None)."""
     code = _dtype_code(out_dtype)
     x = _bits16(x)
     m = x.shape[0]
     y = _y((m, w.rows), code, x.device, y)
+    ws, nb = _workspace(m, w.rows, w.cols, x.device, workspace)
     d = w.desc()
     _call("binade_r4_gemm", ctypes.byref(d), _ptr(x), m, x.stride(0), _ptr(y),
-          y.stride(0), code, _stream(stream))
+          y.stride(0), code, _ptr(ws), nb, _stream(stream))
     return y
 
 
 def bf16_gemm(w: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32,
-              y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+              y: torch.Tensor | None = None, stream=None,
+              workspace: torch.Tensor | None = None) -> torch.Tensor:
     code = _dtype_code(out_dtype)
     w = _bits16(w)
     x = _bits16(x)
     rows, cols = w.shape
     m = x.shape[0]
     y = _y((m, rows), code, x.device, y)
+    ws, nb = _workspace(m, rows, cols, x.device, workspace)
     _call("binade_bf16_gemm", _ptr(w), rows, cols, _ptr(x), m, x.stride(0),
-          _ptr(y), y.stride(0), code, _stream(stream))
+          _ptr(y), y.stride(0), code, _ptr(ws), nb, _stream(stream))
     return y
 
 

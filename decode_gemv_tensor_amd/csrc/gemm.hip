@@ -7,25 +7,34 @@
 // "NVIDIA GPUs": a GEMM's order is a chain of matrix-core steps along K, with
 // split-K partitions that follow a fixed rule.
 //
-// Order (every kernel here, independent of M, tiling and launch shape): K is
-// cut into S = min(8, ceil(K / 1024)) slices of whole 32-column blocks (slice
-// s holds blocks [s*nb/S, (s+1)*nb/S) of the nb = K/32 blocks). In a slice,
-// an output's fp32 accumulator starts at +0.0 and takes the slice's blocks in
-// increasing order, one v_mfma_f32_16x16x32_bf16 step per block (lane group
-// g of the step carries columns 8g..8g+7 of the block). The output is
-// (((p0 + p1) + p2) + ...) + p(S-1) over the slices' accumulators. The R4 kernels
-// rebuild exactly the bf16 weights the twins read, so both issue identical
-// MFMA sequences and their outputs agree bit for bit.
+// Order (every kernel here, independent of M, tiling and launch shape):
+// K is cut into nsb = K / 128 super-blocks of 128 columns, then (K % 128)/32
+// tail blocks of 32. Super-block u is four v_mfma_f32_16x16x32_bf16 steps;
+// in step j, lane group g (lanes 16g .. 16g+15) carries columns
+// 128u + 32g + 8j .. +7, so a lane's operands for the four steps are 32
+// contiguous columns of its row. A tail block is one step whose lane group
+// g carries columns 8g .. 8g+7 of the block. The super-blocks are split into
+// S = min(8, ceil(K / 1024)) slices (slice s: [s*nsb/S, (s+1)*nsb/S); the
+// last slice also takes the tail blocks). Per output and slice one fp32
+// accumulator starts at +0.0 and takes the slice's steps in order; the
+// output is (((p0 + p1) + p2) + ...) in slice order. The R4 kernels rebuild
+// exactly the bf16 weights the twins read, so both issue identical MFMA
+// sequences and their outputs agree bit for bit.
 //
-// Small M (<= 128): one wave per 16 weight rows, 1-8 tiles of 16 X rows; the
-// weights are rebuilt straight into MFMA operands in registers, the next
-// blocks are loaded while the current ones multiply, and the S slices of a
-// tile are S waves of one block, added in slice order through LDS. Blocks
-// that share weight rows are placed on the same XCD (blocks are dealt to the
-// 8 XCDs round robin), so their weight reads meet in that XCD's L2.
-// Large M: 128x128 tiles, 4 waves of 64x64 (4x4 MFMA tiles); per block the
-// X and rebuilt W tiles go through double-buffered LDS; slices run in order
-// with a running total.
+// Small M (<= 16): one wave per 16 weight rows and 16 X rows; each lane
+// loads its 32 columns of a super-block with 16-byte loads, the weights are
+// rebuilt straight into MFMA operands in registers, the next super-block is
+// loaded while the current one multiplies, and the S slices of a tile are S
+// waves of one block, added in slice order through LDS. Blocks that share
+// weight rows are placed on the same XCD (blocks are dealt to the 8 XCDs
+// round robin), so their weight reads meet in that XCD's L2.
+// Larger M: tiles of 128 or 256 X rows by 128 weight rows, 8 waves; per
+// super-block the X rows and the rebuilt weights go through LDS (rows
+// padded to 272 bytes) while the next super-block is loaded into
+// registers. A block runs all slices of its tile with a running total, or,
+// when the tiles alone cannot fill the chip and the caller gave a
+// workspace, one slice, whose fp32 partials a second kernel adds in slice
+// order.
 #include <hip/hip_runtime.h>
 
 #include "binade.h"
@@ -54,16 +63,20 @@ struct GemmArgs {
   int32_t slices;                    // S
   int32_t mtiles;                    // small kernel: tiles of 16*MT X rows
   int64_t tiles;                     // small kernel: weight-row tiles * mtiles
+  float* part;                       // split large kernel: [S][M][N] partials
 };
 
 constexpr int kXcds = 8;
 
-// Block range [lo, hi) of slice s.
-__device__ __forceinline__ void slice_blocks(int32_t k, int32_t S, int32_t s, int32_t& lo,
-                                             int32_t& hi) {
-  const int32_t nb = k >> 5;
-  lo = (s * nb) / S;
-  hi = ((s + 1) * nb) / S;
+constexpr int kSB = 128;   // columns per super-block
+
+// Super-block range [lo, hi) of slice s; the last slice also owns the tail
+// blocks (K % 128) / 32.
+__device__ __forceinline__ void slice_superblocks(int32_t k, int32_t S, int32_t s, int32_t& lo,
+                                                  int32_t& hi) {
+  const int32_t nsb = k / kSB;
+  lo = (s * nsb) / S;
+  hi = ((s + 1) * nsb) / S;
 }
 
 __device__ __forceinline__ bool has_escape(uint32_t P) {
@@ -131,38 +144,65 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int64_t m, int64_t 
 }
 
 // ---------------------------------------------------------------- small M
-// Raw loads of one 32-column block for one lane: the weight row's 8 columns
-// (R4: sm + nibbles; twin: bf16) and MT X rows' 8 columns.
+// One lane's loads for one super-block: 32 columns of its weight row (R4:
+// 32 sm bytes + 16 nibble bytes; twin: 32 bf16) and of MT X rows.
 template <bool kR4, int MT>
 struct SmallRaw {
-  uint2 sm;
-  uint32_t nib;
-  uint4 w;
-  uint4 x[MT];
+  uint4 s0, s1, nb;   // R4
+  uint4 w[4];         // twin
+  uint4 x[MT][4];
 };
 
 // Rows past N (or M) are read from the last row instead: an MFMA output
 // depends only on its own A row and B column, and those outputs are never
-// stored, so every load is unconditional.
+// stored, so every load is unconditional. c = first of the lane's columns.
 template <bool kR4, int MT>
-__device__ __forceinline__ void small_load(const GemmArgs& a, const uint8_t* wrow,
-                                           const uint8_t* nrow, const uint16_t* const (&xrow)[MT],
-                                           int32_t c, SmallRaw<kR4, MT>& r) {
+__device__ __forceinline__ void small_load(const uint8_t* wrow, const uint8_t* nrow,
+                                           const uint16_t* const (&xrow)[MT], int32_t c,
+                                           SmallRaw<kR4, MT>& r) {
   if (kR4) {
-    r.sm = *reinterpret_cast<const uint2*>(wrow + c);
-    r.nib = *reinterpret_cast<const uint32_t*>(nrow + (c >> 1));
+    const uint4* ps = reinterpret_cast<const uint4*>(wrow + c);
+    r.s0 = ps[0];
+    r.s1 = ps[1];
+    r.nb = *reinterpret_cast<const uint4*>(nrow + (c >> 1));
   } else {
-    r.w = *reinterpret_cast<const uint4*>(wrow + 2 * c);
+    const uint4* pw = reinterpret_cast<const uint4*>(wrow + 2 * c);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) r.w[v] = pw[v];
   }
 #pragma unroll
-  for (int t = 0; t < MT; ++t) r.x[t] = *reinterpret_cast<const uint4*>(xrow[t] + c);
+  for (int t = 0; t < MT; ++t) {
+    const uint4* px = reinterpret_cast<const uint4*>(xrow[t] + c);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) r.x[t][v] = px[v];
+  }
+}
+
+// The four MFMA steps of one super-block (columns c .. c+31 of this lane).
+template <bool kR4, int MT>
+__device__ __forceinline__ void small_steps(const GemmArgs& a, const Lut& L, int64_t n,
+                                            int32_t c, const SmallRaw<kR4, MT>& q,
+                                            floatx4 (&acc)[MT]) {
+  const uint32_t S[8] = {q.s0.x, q.s0.y, q.s0.z, q.s0.w, q.s1.x, q.s1.y, q.s1.z, q.s1.w};
+  const uint32_t P[4] = {q.nb.x, q.nb.y, q.nb.z, q.nb.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf16x8 B;
+    if (kR4)
+      B = as_bf16x8(rebuild8(a, L, make_uint2(S[2 * j], S[2 * j + 1]), P[j], n, c + 8 * j));
+    else
+      B = as_bf16x8(q.w[j]);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(q.x[t][j]), B, acc[t], 0, 0, 0);
+  }
 }
 
 // Block (x = tile of 16 weight rows and 16*MT X rows, as dealt to XCDs),
-// one wave per slice. kDepth blocks are in flight per wave.
+// one wave per slice; the next super-block's loads are in flight while the
+// current one multiplies.
 template <bool kR4, int MT>
 __global__ __launch_bounds__(512) void gemm_small_kernel(GemmArgs a) {
-  constexpr int kDepth = MT == 1 ? 8 : (MT == 2 ? 4 : 2);
   constexpr int kMaxSlices = 8;
   __shared__ floatx4 part[kMaxSlices][64];
   const int lane = threadIdx.x & 63;
@@ -182,50 +222,40 @@ __global__ __launch_bounds__(512) void gemm_small_kernel(GemmArgs a) {
 #pragma unroll
   for (int t = 0; t < MT; ++t) xrow[t] = a.x + min((mt * MT + t) * 16 + r, a.m - 1) * a.ldx;
   const Lut L{a.lut0, a.lut1, a.lut2, a.lut3};
-  int32_t b0, b1;
-  slice_blocks(a.k, a.slices, s, b0, b1);
+  int32_t u0, u1;
+  slice_superblocks(a.k, a.slices, s, u0, u1);
 
   floatx4 acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  SmallRaw<kR4, MT> q[kDepth];
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d)
-    if (b0 + d < b1) small_load<kR4, MT>(a, wrow, nrow, xrow, (b0 + d) * 32 + 8 * g, q[d]);
-  int32_t b = b0;
-  // steady state: every refill is in range, no branches inside
-  for (; b + 2 * kDepth <= b1; b += kDepth) {
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      const int32_t c = (b + d) * 32 + 8 * g;
+  SmallRaw<kR4, MT> q0, q1;
+  if (u0 < u1) small_load<kR4, MT>(wrow, nrow, xrow, u0 * kSB + 32 * g, q0);
+  int32_t u = u0;
+  for (; u + 2 <= u1; u += 2) {
+    small_load<kR4, MT>(wrow, nrow, xrow, (u + 1) * kSB + 32 * g, q1);
+    small_steps<kR4, MT>(a, L, n, u * kSB + 32 * g, q0, acc);
+    if (u + 2 < u1) small_load<kR4, MT>(wrow, nrow, xrow, (u + 2) * kSB + 32 * g, q0);
+    small_steps<kR4, MT>(a, L, n, (u + 1) * kSB + 32 * g, q1, acc);
+  }
+  if (u < u1) small_steps<kR4, MT>(a, L, n, u * kSB + 32 * g, q0, acc);
+
+  if (s == a.slices - 1) {
+    // tail blocks: one plain 32-column step each
+    const int32_t tail0 = (a.k / kSB) * kSB;
+    for (int32_t c0 = tail0; c0 < a.k; c0 += 32) {
+      const int32_t c = c0 + 8 * g;
       bf16x8 B;
       if (kR4)
-        B = as_bf16x8(rebuild8(a, L, q[d].sm, q[d].nib, n, c));
+        B = as_bf16x8(rebuild8(a, L, *reinterpret_cast<const uint2*>(wrow + c),
+                               *reinterpret_cast<const uint32_t*>(nrow + (c >> 1)), n, c));
       else
-        B = as_bf16x8(q[d].w);
+        B = as_bf16x8(*reinterpret_cast<const uint4*>(wrow + 2 * c));
 #pragma unroll
       for (int t = 0; t < MT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(q[d].x[t]), B, acc[t], 0, 0, 0);
-      small_load<kR4, MT>(a, wrow, nrow, xrow, c + 32 * kDepth, q[d]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(*reinterpret_cast<const uint4*>(xrow[t] + c)), B, acc[t], 0, 0, 0);
     }
-  }
-  // the last < 2 * kDepth blocks
-#pragma unroll
-  for (int d = 0; d < 2 * kDepth; ++d) {
-    if (b + d >= b1) break;
-    const int dd = d % kDepth;
-    const int32_t c = (b + d) * 32 + 8 * g;
-    bf16x8 B;
-    if (kR4)
-      B = as_bf16x8(rebuild8(a, L, q[dd].sm, q[dd].nib, n, c));
-    else
-      B = as_bf16x8(q[dd].w);
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(q[dd].x[t]), B, acc[t], 0, 0, 0);
-    if (d < kDepth && b + d + kDepth < b1)
-      small_load<kR4, MT>(a, wrow, nrow, xrow, c + 32 * kDepth, q[dd]);
   }
 
   // slices in order: ((p0 + p1) + p2) + ..., one X tile at a time
@@ -249,147 +279,275 @@ __global__ __launch_bounds__(512) void gemm_small_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------- large M
-constexpr int kBM = 128, kBN = 128;
-constexpr int kLdsStride = 32 + 8;   // bf16 elements per LDS row (80 bytes)
+// Tiles of BM = 64*WM X rows by 128 weight rows, 8 waves of 64 x (16*WM):
+// each rebuilt weight feeds BM X rows. Unsplit, a block runs every slice of
+// its tile in order with a running total. Split, a block runs one slice and
+// writes its accumulators to the workspace; gemm_combine_kernel then adds
+// the slices in order (the same fp32 adds as the running total).
+constexpr int kBN = 128, kLargeThreads = 512;
+// bf16 elements per LDS row: 128 + 8, so that rows start 4 banks apart and
+// both the 16-byte stores of staging and the 16-byte MFMA operand reads of
+// 8 consecutive rows fall in distinct banks
+constexpr int kLdsStride = kSB + 8;
 
-// One thread's share of a 32-column block: 16 columns of one X row and of
-// one weight row (raw).
-template <bool kR4>
-struct LargeRaw {
-  uint4 x0, x1;
-  uint4 sm;          // R4: 16 sm bytes
-  uint2 nib;         // R4: 16 nibbles
-  uint4 w0, w1;      // twin: 16 bf16
+// One thread's loads for one super-block. X: BM/32 rows (v*32 + tid/16) x 16
+// bytes (segment tid%16); twin weights: 4 such rows; R4: 2 rows
+// (v*64 + tid/8) x 16 sm bytes (segment tid%8) and their 8 nibble bytes.
+template <bool kR4, int WM>
+struct LargeRaw;
+template <int WM>
+struct LargeRaw<true, WM> {
+  uint4 x[2 * WM];
+  uint4 sm[2];
+  uint2 nb[2];
+};
+template <int WM>
+struct LargeRaw<false, WM> {
+  uint4 x[2 * WM];
+  uint4 w[4];
 };
 
-template <bool kR4>
-__device__ __forceinline__ void large_load(const GemmArgs& a, int32_t blk, int sc, int64_t xm,
-                                           bool xm_ok, int64_t wnr, bool wn_ok,
-                                           LargeRaw<kR4>& q) {
-  const int32_t c = blk * 32 + sc;
-  if (xm_ok) {
-    const uint4* px = reinterpret_cast<const uint4*>(a.x + xm * a.ldx + c);
-    q.x0 = px[0];
-    q.x1 = px[1];
-  } else {
-    q.x0 = q.x1 = make_uint4(0, 0, 0, 0);
+// Rows past M or N load zeros (their outputs are never stored; the zero is
+// assigned first and the load made conditional, since a conditional
+// expression over two uint4 lvalues would select an address). Each load
+// address is a block-uniform base plus a 32-bit per-lane byte offset, so the
+// loop keeps one offset register per operand instead of a pointer per row.
+template <bool kR4, int WM>
+__device__ __forceinline__ void large_load(const GemmArgs& a, int32_t c0, int tid, int64_t m0,
+                                           int64_t n0, uint32_t xo, uint32_t wo, uint32_t no,
+                                           LargeRaw<kR4, WM>& q) {
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int v = 0; v < 2 * WM; ++v) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x + (m0 + v * 32) * a.ldx + c0);
+    q.x[v] = z4;
+    if (m0 + v * 32 + (tid >> 4) < a.m) q.x[v] = *reinterpret_cast<const uint4*>(base + xo);
   }
-  if (kR4) {
-    q.sm = wn_ok ? *reinterpret_cast<const uint4*>(a.w + wnr * a.k + c) : make_uint4(0, 0, 0, 0);
-    q.nib = wn_ok ? *reinterpret_cast<const uint2*>(a.nib + wnr * (a.k >> 1) + (c >> 1))
-                  : make_uint2(0, 0);
-  } else if (wn_ok) {
-    const uint4* pw =
-        reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.w) + wnr * a.k + c);
-    q.w0 = pw[0];
-    q.w1 = pw[1];
+  if constexpr (kR4) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const bool ok = n0 + v * 64 + (tid >> 3) < a.n;
+      const uint8_t* bs = a.w + (n0 + v * 64) * a.k + c0;
+      const uint8_t* bn = a.nib + (n0 + v * 64) * (a.k >> 1) + (c0 >> 1);
+      q.sm[v] = z4;
+      q.nb[v] = make_uint2(0, 0);
+      if (ok) {
+        q.sm[v] = *reinterpret_cast<const uint4*>(bs + wo);
+        q.nb[v] = *reinterpret_cast<const uint2*>(bn + no);
+      }
+    }
   } else {
-    q.w0 = q.w1 = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint8_t* base = a.w + ((n0 + v * 32) * a.k + c0) * 2;
+      q.w[v] = z4;
+      if (n0 + v * 32 + (tid >> 4) < a.n) q.w[v] = *reinterpret_cast<const uint4*>(base + wo);
+    }
   }
 }
 
-template <bool kR4>
-__device__ __forceinline__ void large_stage(const GemmArgs& a, const Lut& L,
-                                            uint16_t (*xs)[kLdsStride],
-                                            uint16_t (*ws)[kLdsStride], int sr, int sc,
-                                            int32_t blk, int64_t wnr, const LargeRaw<kR4>& q) {
-  *reinterpret_cast<uint4*>(&xs[sr][sc]) = q.x0;
-  *reinterpret_cast<uint4*>(&xs[sr][sc + 8]) = q.x1;
-  uint4 w0, w1;
-  if (kR4) {
-    const int32_t c = blk * 32 + sc;
-    w0 = rebuild8(a, L, make_uint2(q.sm.x, q.sm.y), q.nib.x, wnr, c);
-    w1 = rebuild8(a, L, make_uint2(q.sm.z, q.sm.w), q.nib.y, wnr, c + 8);
+template <bool kR4, int WM>
+__device__ __forceinline__ void large_stage(const GemmArgs& a, const Lut& L, int32_t c0, int tid,
+                                            int64_t n0, uint16_t (*xs)[kLdsStride],
+                                            uint16_t (*ws)[kLdsStride],
+                                            const LargeRaw<kR4, WM>& q) {
+#pragma unroll
+  for (int v = 0; v < 2 * WM; ++v)
+    *reinterpret_cast<uint4*>(&xs[v * 32 + (tid >> 4)][8 * (tid & 15)]) = q.x[v];
+  if constexpr (kR4) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int row = v * 64 + (tid >> 3);
+      const int cc = 16 * (tid & 7);
+      // rows past N hold zeros, which have no escapes
+      const uint4 lo = rebuild8(a, L, make_uint2(q.sm[v].x, q.sm[v].y), q.nb[v].x, n0 + row,
+                                c0 + cc);
+      const uint4 hi = rebuild8(a, L, make_uint2(q.sm[v].z, q.sm[v].w), q.nb[v].y, n0 + row,
+                                c0 + cc + 8);
+      *reinterpret_cast<uint4*>(&ws[row][cc]) = lo;
+      *reinterpret_cast<uint4*>(&ws[row][cc + 8]) = hi;
+    }
   } else {
-    w0 = q.w0;
-    w1 = q.w1;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      *reinterpret_cast<uint4*>(&ws[v * 32 + (tid >> 4)][8 * (tid & 15)]) = q.w[v];
   }
-  *reinterpret_cast<uint4*>(&ws[sr][sc]) = w0;
-  *reinterpret_cast<uint4*>(&ws[sr][sc + 8]) = w1;
 }
 
-template <bool kR4>
-__global__ __launch_bounds__(256, 2) void gemm_large_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kBM][kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t ws[2][kBN][kLdsStride];
+// Staging of one 32-column tail block (plain lane-group mapping).
+template <bool kR4, int BM>
+__device__ __forceinline__ void large_stage_tail(const GemmArgs& a, const Lut& L, int32_t c0,
+                                                 int tid, int64_t m0, int64_t n0,
+                                                 uint16_t (*xs)[kLdsStride],
+                                                 uint16_t (*ws)[kLdsStride]) {
+  if (tid < 2 * BM) {
+    const int row = tid >> 1, cc = 16 * (tid & 1);
+    const int64_t xm = min(m0 + row, a.m - 1);   // rows past M: never stored
+    const uint4* px = reinterpret_cast<const uint4*>(a.x + xm * a.ldx + c0 + cc);
+    *reinterpret_cast<uint4*>(&xs[row][cc]) = px[0];
+    *reinterpret_cast<uint4*>(&xs[row][cc + 8]) = px[1];
+  }
+  if (tid < 2 * kBN) {
+    const int row = tid >> 1, cc = 16 * (tid & 1);
+    const int64_t wn = min(n0 + row, a.n - 1);   // rows past N: never stored
+    uint4 lo, hi;
+    if constexpr (kR4) {
+      const uint4 sm = *reinterpret_cast<const uint4*>(a.w + wn * a.k + c0 + cc);
+      const uint2 nb = *reinterpret_cast<const uint2*>(a.nib + wn * (a.k >> 1) + ((c0 + cc) >> 1));
+      lo = rebuild8(a, L, make_uint2(sm.x, sm.y), nb.x, wn, c0 + cc);
+      hi = rebuild8(a, L, make_uint2(sm.z, sm.w), nb.y, wn, c0 + cc + 8);
+    } else {
+      const uint4* pw = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.w) +
+                                                       wn * a.k + c0 + cc);
+      lo = pw[0];
+      hi = pw[1];
+    }
+    *reinterpret_cast<uint4*>(&ws[row][cc]) = lo;
+    *reinterpret_cast<uint4*>(&ws[row][cc + 8]) = hi;
+  }
+}
+
+// One MFMA step over the staged operands: A rows from xs, B rows from ws,
+// 8 columns starting at column `col` of the staged block.
+template <int NJ>
+__device__ __forceinline__ void large_step(const uint16_t (*xs)[kLdsStride],
+                                           const uint16_t (*ws)[kLdsStride], int wm, int wn,
+                                           int r, int col, floatx4 (&acc)[4][NJ]) {
+  bf16x8 A[4], Bv[NJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    A[i] = *reinterpret_cast<const bf16x8*>(&xs[wm + 16 * i + r][col]);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    Bv[j] = *reinterpret_cast<const bf16x8*>(&ws[wn + 16 * j + r][col]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i], Bv[j], acc[i][j], 0, 0, 0);
+}
+
+template <int NJ>
+__device__ __forceinline__ void fold(int32_t s, floatx4 (&acc)[4][NJ], floatx4 (&tot)[4][NJ]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      tot[i][j] = s == 0 ? acc[i][j] : tot[i][j] + acc[i][j];
+      acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+}
+
+// kSplit: blockIdx -> (tile, slice), one slice per block, fp32 partials to
+// a.part[slice][m][n]; otherwise blockIdx -> tile, all slices in order.
+template <bool kR4, int WM, bool kSplit>
+__global__ __launch_bounds__(kLargeThreads, WM == 2 && kSplit ? 4 : 2) void gemm_large_kernel(GemmArgs a) {
+  constexpr int BM = 64 * WM;
+  constexpr int NW = 8 / WM;    // waves along N
+  constexpr int NJ = WM;        // 16-row MFMA tiles per wave along N
+  __shared__ __attribute__((aligned(16))) uint16_t xs[BM][kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[kBN][kLdsStride];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  // XCD-aware tile order: consecutive tiles (same weight columns) per XCD
-  const int64_t tiles_n = (a.n + kBN - 1) / kBN, tiles_m = (a.m + kBM - 1) / kBM;
-  const int64_t tiles = tiles_n * tiles_m;
-  const int64_t per = (tiles + kXcds - 1) / kXcds;
-  const int64_t tile = static_cast<int64_t>(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-  if (tile >= tiles) return;
+  // XCD-aware order: consecutive items (same weight rows) per XCD
+  const int64_t tiles_n = (a.n + kBN - 1) / kBN, tiles_m = (a.m + BM - 1) / BM;
+  const int32_t S = a.slices;
+  const int64_t items = tiles_n * tiles_m * (kSplit ? S : 1);
+  const int64_t per = (items + kXcds - 1) / kXcds;
+  const int64_t item = static_cast<int64_t>(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (item >= items) return;
+  const int64_t tile = kSplit ? item / S : item;
+  const int32_t s_only = kSplit ? static_cast<int32_t>(item - tile * S) : 0;
   const int64_t n0 = (tile / tiles_m) * kBN;
-  const int64_t m0 = (tile % tiles_m) * kBM;
-  const int wm = (wave >> 1) * 64;
-  const int wn = (wave & 1) * 64;
-  const int sr = tid >> 1;           // staging row 0..127
-  const int sc = (tid & 1) * 16;     // staging column 0 or 16
-  const int64_t xm = m0 + sr, wnr = n0 + sr;
-  const bool xm_ok = xm < a.m, wn_ok = wnr < a.n;
+  const int64_t m0 = (tile % tiles_m) * BM;
+  const int wm = (wave / NW) * 64;
+  const int wn = (wave % NW) * (16 * NJ);
   const Lut L{a.lut0, a.lut1, a.lut2, a.lut3};
   const int r = lane & 15, g = lane >> 4;
 
-  floatx4 acc[4][4], tot[4][4];
+  floatx4 acc[4][NJ], tot[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tot[i][j] = acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < NJ; ++j) tot[i][j] = acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int32_t nb = a.k >> 5;
-  LargeRaw<kR4> q;
-  large_load<kR4>(a, 0, sc, xm, xm_ok, wnr, wn_ok, q);
-  large_stage<kR4>(a, L, xs[0], ws[0], sr, sc, 0, wnr, q);
-  __syncthreads();
-  int32_t s = 0, s_hi;
-  {
-    int32_t lo;
-    slice_blocks(a.k, a.slices, 0, lo, s_hi);
-  }
-  for (int32_t blk = 0; blk < nb; ++blk) {
-    const int buf = blk & 1;
-    if (blk + 1 < nb) large_load<kR4>(a, blk + 1, sc, xm, xm_ok, wnr, wn_ok, q);
-    bf16x8 A[4], Bv[4];
+  const int32_t nsb = a.k / kSB;
+  int32_t s = s_only, u_lo, s_hi;
+  slice_superblocks(a.k, S, s, u_lo, s_hi);
+  const int32_t u_end = kSplit ? s_hi : nsb;
+  const bool with_tail = !kSplit || s_only == S - 1;
+  // per-lane byte offsets (the launch bounds K and ldx so these fit)
+  const uint32_t xo = static_cast<uint32_t>(((tid >> 4) * a.ldx + 8 * (tid & 15)) * 2);
+  const uint32_t wo = kR4 ? static_cast<uint32_t>((tid >> 3) * a.k + 16 * (tid & 7))
+                          : static_cast<uint32_t>(((tid >> 4) * a.k + 8 * (tid & 15)) * 2);
+  const uint32_t no = static_cast<uint32_t>((tid >> 3) * (a.k >> 1) + 8 * (tid & 7));
+  if (u_lo < u_end) {
+    LargeRaw<kR4, WM> q;
+    large_load<kR4, WM>(a, u_lo * kSB, tid, m0, n0, xo, wo, no, q);
+    for (int32_t u = u_lo; u < u_end; ++u) {
+      __syncthreads();   // every wave is done reading the previous super-block
+      large_stage<kR4, WM>(a, L, u * kSB, tid, n0, xs, ws, q);
+      __syncthreads();
+      // the next super-block (the last one again on the last pass: always in
+      // bounds, and the load stays unconditional)
+      large_load<kR4, WM>(a, min(u + 1, u_end - 1) * kSB, tid, m0, n0, xo, wo, no, q);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      A[i] = *reinterpret_cast<const bf16x8*>(&xs[buf][wm + 16 * i + r][8 * g]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      Bv[j] = *reinterpret_cast<const bf16x8*>(&ws[buf][wn + 16 * j + r][8 * g]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i], Bv[j], acc[i][j], 0, 0, 0);
-    if (blk + 1 == s_hi) {
-      // end of slice s: add its accumulators to the total in slice order
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          tot[i][j] = s == 0 ? acc[i][j] : tot[i][j] + acc[i][j];
-          acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-      ++s;
-      if (s < a.slices) {
-        int32_t lo;
-        slice_blocks(a.k, a.slices, s, lo, s_hi);
+      for (int j = 0; j < 4; ++j) large_step<NJ>(xs, ws, wm, wn, r, 32 * g + 8 * j, acc);
+      if (!kSplit && u + 1 == s_hi && s + 1 < S) {
+        fold<NJ>(s, acc, tot);   // end of slice s (the last slice ends after the tail)
+        ++s;
+        slice_superblocks(a.k, S, s, u_lo, s_hi);
       }
     }
-    if (blk + 1 < nb) large_stage<kR4>(a, L, xs[buf ^ 1], ws[buf ^ 1], sr, sc, blk + 1, wnr, q);
-    __syncthreads();
+  }
+  if (with_tail) {
+    for (int32_t c0 = nsb * kSB; c0 < a.k; c0 += 32) {
+      __syncthreads();
+      large_stage_tail<kR4, BM>(a, L, c0, tid, m0, n0, xs, ws);
+      __syncthreads();
+      large_step<NJ>(xs, ws, wm, wn, r, 8 * g, acc);
+    }
   }
 
+  if (kSplit && S > 1) {
+    float* part = a.part + static_cast<int64_t>(s_only) * a.m * a.n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t on = n0 + wn + 16 * j + r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t om = m0 + wm + 16 * i + 4 * g + e;
+          if (om < a.m && on < a.n) part[om * a.n + on] = acc[i][j][e];
+        }
+      }
+    return;
+  }
+  if (!kSplit) fold<NJ>(s, acc, tot);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int64_t on = n0 + wn + 16 * j + r;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) store_out(a, m0 + wm + 16 * i + 4 * g + e, on, tot[i][j][e]);
+      for (int e = 0; e < 4; ++e)
+        store_out(a, m0 + wm + 16 * i + 4 * g + e, on, kSplit ? acc[i][j][e] : tot[i][j][e]);
     }
+}
+
+// y[m][n] = ((p0 + p1) + p2) + ... over the S slice partials, in slice order.
+__global__ __launch_bounds__(256) void gemm_combine_kernel(GemmArgs a) {
+  const int64_t mn = a.m * a.n;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < mn;
+       e += stride) {
+    float v = a.part[e];
+    for (int32_t s = 1; s < a.slices; ++s) v = v + a.part[s * mn + e];
+    const int64_t m = e / a.n;
+    store_out(a, m, e - m * a.n, v);
+  }
 }
 
 int32_t check_xy(const uint16_t* x, int64_t m, int64_t ldx, void* y,
@@ -407,49 +565,104 @@ int32_t check_xy(const uint16_t* x, int64_t m, int64_t ldx, void* y,
 
 int32_t slices_for(int64_t k) {
   const int64_t s = (k + 1023) / 1024;
-  const int64_t nb = k / 32;
+  const int64_t nsb = k / kSB;
   int64_t S = s < 8 ? s : 8;
-  if (S > nb) S = nb;
+  if (S > nsb) S = nsb;
   return static_cast<int32_t>(S < 1 ? 1 : S);
 }
 
-constexpr int64_t kSmallMaxM = 128;
+// M up to this runs the small kernel (16*MT X rows per wave, no LDS).
+#ifndef BINADE_GEMM_SMALL_MAX_M
+#define BINADE_GEMM_SMALL_MAX_M 16
+#endif
+// The tiled kernel splits the slices over blocks when it has fewer tiles
+// than this and M is at most kSplitMaxM (the partials cost 8*S*M*N bytes of
+// traffic).
+#ifndef BINADE_GEMM_SPLIT_BELOW
+#define BINADE_GEMM_SPLIT_BELOW 512
+#endif
+constexpr int64_t kSmallMaxM = BINADE_GEMM_SMALL_MAX_M;
+constexpr int64_t kSplitBelow = BINADE_GEMM_SPLIT_BELOW;
+constexpr int64_t kSplitMaxM = 512;
 
-template <bool kR4, int MT>
-int32_t launch_small(GemmArgs a, hipStream_t stream) {
-  a.mtiles = static_cast<int32_t>((a.m + 16 * MT - 1) / (16 * MT));
-  a.tiles = ((a.n + 15) / 16) * a.mtiles;
-  const int64_t per = (a.tiles + kXcds - 1) / kXcds;
-  const int64_t blocks = per * kXcds;
-  if (blocks > 0x7FFFFFFFll) return BINADE_EUNSUPPORTED;
-  hipLaunchKernelGGL((gemm_small_kernel<kR4, MT>), dim3(static_cast<uint32_t>(blocks)),
-                     dim3(64 * a.slices), 0, stream, a);
-  return launch_status();
+struct Plan {
+  int mt = 0;        // small kernel: X tiles of 16 per wave (0: tiled kernel)
+  int wm = 0;        // tiled kernel: BM = 64*wm
+  bool split = false;
+  int64_t blocks = 0;
+  int64_t part_bytes = 0;   // workspace the split needs
+};
+
+Plan plan_for(int64_t m, int64_t n, int64_t k) {
+  Plan p;
+  const int32_t S = slices_for(k);
+  if (m <= kSmallMaxM) {
+    p.mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
+    const int64_t mtiles = (m + 16 * p.mt - 1) / (16 * p.mt);
+    const int64_t tiles = ((n + 15) / 16) * mtiles;
+    p.blocks = ((tiles + kXcds - 1) / kXcds) * kXcds;
+    return p;
+  }
+  p.wm = m <= 128 ? 2 : 4;
+  const int64_t tiles = ((n + kBN - 1) / kBN) * ((m + 64 * p.wm - 1) / (64 * p.wm));
+  p.split = S > 1 && tiles < kSplitBelow && m <= kSplitMaxM;
+  const int64_t items = tiles * (p.split ? S : 1);
+  p.blocks = ((items + kXcds - 1) / kXcds) * kXcds;
+  p.part_bytes = p.split ? static_cast<int64_t>(S) * m * n * 4 : 0;
+  return p;
 }
 
-int32_t launch(GemmArgs a, bool r4, hipStream_t stream) {
-  a.slices = slices_for(a.k);
-  if (a.m <= kSmallMaxM) {
-    if (r4) {
-      if (a.m <= 16) return launch_small<true, 1>(a, stream);
-      if (a.m <= 32) return launch_small<true, 2>(a, stream);
-      if (a.m <= 64) return launch_small<true, 4>(a, stream);
-      return launch_small<true, 8>(a, stream);
-    }
-    if (a.m <= 16) return launch_small<false, 1>(a, stream);
-    if (a.m <= 32) return launch_small<false, 2>(a, stream);
-    if (a.m <= 64) return launch_small<false, 4>(a, stream);
-    return launch_small<false, 8>(a, stream);
-  }
-  const int64_t tiles = ((a.n + kBN - 1) / kBN) * ((a.m + kBM - 1) / kBM);
-  const int64_t blocks = ((tiles + kXcds - 1) / kXcds) * kXcds;
-  if (blocks > 0x7FFFFFFFll) return BINADE_EUNSUPPORTED;
-  if (r4)
-    hipLaunchKernelGGL(gemm_large_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                       stream, a);
+template <bool kR4, int MT>
+void launch_small(GemmArgs a, int64_t blocks, hipStream_t stream) {
+  a.mtiles = static_cast<int32_t>((a.m + 16 * MT - 1) / (16 * MT));
+  a.tiles = ((a.n + 15) / 16) * a.mtiles;
+  hipLaunchKernelGGL((gemm_small_kernel<kR4, MT>), dim3(static_cast<uint32_t>(blocks)),
+                     dim3(64 * a.slices), 0, stream, a);
+}
+
+template <bool kR4, int WM>
+void launch_large(const GemmArgs& a, bool split, int64_t blocks, hipStream_t stream) {
+  if (split)
+    hipLaunchKernelGGL((gemm_large_kernel<kR4, WM, true>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kLargeThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(gemm_large_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_large_kernel<kR4, WM, false>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kLargeThreads), 0, stream, a);
+}
+
+int32_t launch(GemmArgs a, bool r4, void* workspace, int64_t workspace_bytes,
+               hipStream_t stream) {
+  a.slices = slices_for(a.k);
+  Plan p = plan_for(a.m, a.n, a.k);
+  if (p.blocks > 0x7FFFFFFFll) return BINADE_EUNSUPPORTED;
+  if (p.mt == 1) r4 ? launch_small<true, 1>(a, p.blocks, stream)
+                    : launch_small<false, 1>(a, p.blocks, stream);
+  else if (p.mt == 2) r4 ? launch_small<true, 2>(a, p.blocks, stream)
+                         : launch_small<false, 2>(a, p.blocks, stream);
+  else if (p.mt == 4) r4 ? launch_small<true, 4>(a, p.blocks, stream)
+                         : launch_small<false, 4>(a, p.blocks, stream);
+  if (p.mt != 0) return launch_status();
+  // per-lane offsets in the tiled kernel are 32-bit: 64 rows of K bytes or
+  // 32 rows of 2*ldx bytes must stay below 2^32
+  if (a.k > (1 << 25) || a.ldx > (1 << 25)) return BINADE_EUNSUPPORTED;
+  if (p.split && (workspace == nullptr || workspace_bytes < p.part_bytes ||
+                  !aligned16(workspace))) {
+    // no room for the partials: run every slice in one block (same bits)
+    p.split = false;
+    const int64_t tiles = ((a.n + kBN - 1) / kBN) * ((a.m + 64 * p.wm - 1) / (64 * p.wm));
+    p.blocks = ((tiles + kXcds - 1) / kXcds) * kXcds;
+  }
+  a.part = p.split ? static_cast<float*>(workspace) : nullptr;
+  if (p.wm == 2) r4 ? launch_large<true, 2>(a, p.split, p.blocks, stream)
+                    : launch_large<false, 2>(a, p.split, p.blocks, stream);
+  else r4 ? launch_large<true, 4>(a, p.split, p.blocks, stream)
+          : launch_large<false, 4>(a, p.split, p.blocks, stream);
+  if (p.split) {
+    const int64_t mn = a.m * a.n;
+    const int64_t cb = min((mn + 255) / 256, static_cast<int64_t>(4096));
+    hipLaunchKernelGGL(gemm_combine_kernel, dim3(static_cast<uint32_t>(cb)), dim3(256), 0,
                        stream, a);
+  }
   return launch_status();
 }
 
@@ -463,9 +676,15 @@ uint32_t pack4(const uint8_t* l) {
 
 using namespace binade;
 
+extern "C" int64_t binade_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || k % 32 != 0 || k > (1 << 30)) return 0;
+  return plan_for(m, n, k).part_bytes;
+}
+
 extern "C" int32_t binade_r4_gemm(const binade_r4* w, const uint16_t* x,
                                   int64_t m, int64_t ldx, void* y, int64_t ldy,
-                                  int32_t y_dtype, void* stream) {
+                                  int32_t y_dtype, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
   if (w == nullptr || w->rows < 0 || w->cols <= 0) return BINADE_EINVAL;
   int32_t s = check_xy(x, m, ldx, y, ldy, w->rows, w->cols, y_dtype);
   if (s != BINADE_OK || m == 0 || w->rows == 0) return s;
@@ -492,13 +711,14 @@ extern "C" int32_t binade_r4_gemm(const binade_r4* w, const uint16_t* x,
   a.ldx = ldx;
   a.ldy = ldy;
   a.y_bf16 = y_dtype == BINADE_BF16;
-  return launch(a, true, static_cast<hipStream_t>(stream));
+  return launch(a, true, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int32_t binade_bf16_gemm(const uint16_t* w, int64_t rows,
                                     int64_t cols, const uint16_t* x, int64_t m,
                                     int64_t ldx, void* y, int64_t ldy,
-                                    int32_t y_dtype, void* stream) {
+                                    int32_t y_dtype, void* workspace,
+                                    int64_t workspace_bytes, void* stream) {
   if (rows < 0 || cols <= 0) return BINADE_EINVAL;
   int32_t s = check_xy(x, m, ldx, y, ldy, rows, cols, y_dtype);
   if (s != BINADE_OK || m == 0 || rows == 0) return s;
@@ -514,5 +734,5 @@ extern "C" int32_t binade_bf16_gemm(const uint16_t* w, int64_t rows,
   a.ldx = ldx;
   a.ldy = ldy;
   a.y_bf16 = y_dtype == BINADE_BF16;
-  return launch(a, false, static_cast<hipStream_t>(stream));
+  return launch(a, false, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }

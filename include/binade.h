@@ -224,21 +224,36 @@ int32_t binade_bf16_gemv(const uint16_t *w, int64_t rows, int64_t cols,
 /* Prompt GEMM Y[M,N] = X[M,K] W[N,K]^T with W in R4, tiles decoded into LDS
  * and multiplied on bf16 MFMA with fp32 accumulation ("Binade" package page,
  * "Results" and "Limitations": prompt processing with fused GEMM). X: device
- * bf16 with row stride ldx (elements); Y: fp32 or bf16 with row stride ldy.
- * Order (depends on K only, never on M or the launch shape): K is cut into
- * S = min(8, ceil(K / 1024)) slices of whole 32-column blocks (slice s =
- * blocks [s*nb/S, (s+1)*nb/S) of the nb = K/32); per output and slice one
- * fp32 accumulator from +0.0 takes the slice's blocks in increasing order,
- * one v_mfma_f32_16x16x32_bf16 step each; the output adds the slices'
- * accumulators in slice order. */
+ * bf16 with row stride ldx (elements, a multiple of 8); Y: fp32 or bf16 with
+ * row stride ldy. K must be a multiple of 32.
+ * Order (depends on K only, never on M, the workspace or the launch shape):
+ * K is cut into nsb = K/128 super-blocks of 128 columns, then (K%128)/32
+ * tail blocks of 32. Super-block u is four v_mfma_f32_16x16x32_bf16 steps;
+ * in step j, lanes 16g..16g+15 carry columns 128u + 32g + 8j .. +7. A tail
+ * block is one step with columns 8g .. 8g+7 of the block. The super-blocks
+ * form S = min(8, ceil(K/1024)) slices, slice s = [s*nsb/S, (s+1)*nsb/S),
+ * the last one also taking the tail blocks. Per output and slice one fp32
+ * accumulator from +0.0 takes the slice's steps in order; the output adds
+ * the slices' accumulators in slice order.
+ * workspace: optional device memory (16-byte aligned, caller-owned, not
+ * read before written) of workspace_bytes; with at least
+ * binade_gemm_workspace_bytes(M, N, K) bytes the slices of a shape with few
+ * tiles run in separate blocks, otherwise in one. NULL/0 is always valid.
+ * Calls that share a workspace must not overlap. */
 int32_t binade_r4_gemm(const binade_r4 *w, const uint16_t *x, int64_t m,
                        int64_t ldx, void *y, int64_t ldy, int32_t y_dtype,
-                       void *stream);
+                       void *workspace, int64_t workspace_bytes, void *stream);
 
 /* The same GEMM with plain bf16 W [N, K] (device). */
 int32_t binade_bf16_gemm(const uint16_t *w, int64_t rows, int64_t cols,
                          const uint16_t *x, int64_t m, int64_t ldx, void *y,
-                         int64_t ldy, int32_t y_dtype, void *stream);
+                         int64_t ldy, int32_t y_dtype, void *workspace,
+                         int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes with which binade_r4_gemm / binade_bf16_gemm split the
+ * slices of an M x N x K product over blocks (0: that shape never splits;
+ * also 0 for invalid sizes). Pure host function. */
+int64_t binade_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 /* MoE expert-gather GEMV ("Binade" package page, "How it works": the MoE
  * expert gather in the matvec's order; "Limitations": fused kernels cover

@@ -243,7 +243,8 @@ def test_moe_shared_experts_and_bad_index():
 
 
 # ---------------------------------------------------------- GEMM
-@pytest.mark.parametrize("mnk", [(16, 64, 64), (33, 200, 96), (128, 384, 3840), (5, 70, 4160)])
+@pytest.mark.parametrize("mnk", [(16, 64, 64), (33, 200, 96), (128, 384, 3840), (5, 70, 4160),
+                                 (300, 136, 4160), (260, 40, 96)])
 def test_gemm_small_integers_exact_and_twin(mnk):
     M, N, K = mnk
     g = torch.Generator().manual_seed(M * N)
@@ -303,11 +304,12 @@ def test_batched_decode_and_gemv_equal_single_calls():
         assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), shapes[i]
 
 
-@pytest.mark.parametrize("nk", [(200, 15360), (136, 8192), (72, 3840)])
+@pytest.mark.parametrize("nk", [(200, 15360), (136, 8192), (72, 3840), (72, 4160), (40, 96)])
 def test_gemm_rows_do_not_depend_on_m(nk):
     """The GEMM order depends on K only: the same X row gives the same bits
-    whether the call has 16, 32, 128 (small-M kernel) or 300 rows (tiled
-    kernel), with split-K slices (K = 8192, 15360) and escapes."""
+    whether the call has 16 or 32 rows (small-M kernel) or 33 .. 300 rows
+    (tiled kernel, slices in separate blocks or in one), with split-K slices
+    (K = 8192, 15360), 32-column tail blocks (K = 4160, 96) and escapes."""
     N, K = nk
     W = synth.normal_bf16(spec(N, K, 0.015, N + 7, 2e-3, 1e3))
     X = synth.vector_bf16(K, N + 8, count=300)
@@ -315,11 +317,17 @@ def test_gemm_rows_do_not_depend_on_m(nk):
     Xd, Wd = X.to(DEV), W.to(DEV)
     full = B.r4_gemm(r4, Xd).cpu()
     assert torch.equal(full.view(torch.int32), B.bf16_gemm(Wd, Xd).cpu().view(torch.int32))
-    for m in (16, 32, 128, 129):
-        part = B.r4_gemm(r4, Xd[:m].contiguous()).cpu()
+    no_ws = torch.empty(0, dtype=torch.uint8, device=DEV)   # slices in one block
+    for m in (16, 32, 33, 64, 65, 128, 129):
+        xm = Xd[:m].contiguous()
+        part = B.r4_gemm(r4, xm).cpu()
         assert torch.equal(part.view(torch.int32), full[:m].view(torch.int32)), m
-        twin = B.bf16_gemm(Wd, Xd[:m].contiguous()).cpu()
+        twin = B.bf16_gemm(Wd, xm).cpu()
         assert torch.equal(twin.view(torch.int32), part.view(torch.int32)), m
+        one = B.r4_gemm(r4, xm, workspace=no_ws).cpu()
+        assert torch.equal(one.view(torch.int32), part.view(torch.int32)), m
+    assert torch.equal(B.r4_gemm(r4, Xd, workspace=no_ws).cpu().view(torch.int32),
+                       full.view(torch.int32))
     wb, xb = bits_np(W), bits_np(X[:40])
     ref = oracle.gemm_f64(wb, xb)
     scale = oracle.gemm_f64(wb & 0x7FFF, xb & 0x7FFF)

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _header_functions():
     text = open(os.path.join(ROOT, "include", "binade.h")).read()
-    pat = r"^(?:int32_t|const char \*)\s*(binade_\w+)\("
+    pat = r"^(?:int32_t|int64_t|const char \*)\s*(binade_\w+)\("
     return sorted(set(re.findall(pat, text, flags=re.M)))
 
 
@@ -30,6 +30,23 @@ def test_library_exports_every_declared_function():
     for name in declared:
         assert hasattr(L, name), name
     assert sorted(B.EXPORTS) == declared
+
+
+def test_gemm_workspace_bytes_policy():
+    """Host-only sizing: partials are S*M*N fp32 for shapes the tiled kernel
+    splits (S = min(8, ceil(K/1024)) slices), 0 where it never splits."""
+    # small M runs the no-LDS kernel: never a workspace
+    assert B.gemm_workspace_bytes(16, 3840, 15360) == 0
+    # few tiles, K = 15360 -> 8 slices
+    assert B.gemm_workspace_bytes(128, 3840, 15360) == 8 * 128 * 3840 * 4
+    # K = 3840 -> 4 slices
+    assert B.gemm_workspace_bytes(128, 15360, 3840) == 4 * 128 * 15360 * 4
+    # one slice: nothing to split
+    assert B.gemm_workspace_bytes(200, 512, 1024) == 0
+    # large M: enough tiles, and partials would cost more than they save
+    assert B.gemm_workspace_bytes(2048, 15360, 3840) == 0
+    for bad in ((0, 64, 64), (64, 0, 64), (64, 64, 0), (64, 64, 48), (-1, 64, 64)):
+        assert B.gemm_workspace_bytes(*bad) == 0
 
 
 def test_struct_layouts_match_header_sizes():
