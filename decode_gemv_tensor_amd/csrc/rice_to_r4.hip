@@ -9,25 +9,29 @@
 // staged on chip is what made the Huffman exponent decoder fast; the same
 // two ideas are used here, with the lengths found from the bits themselves.
 //
-// One wave decodes a run: one row-chunk (<= 2048 weights), or 2048 / cols
-// whole rows when rows are at most 1024 weights long.
+// One wave decodes a job of at most 4096 weights: two row-chunks of one row
+// when rows are longer than a chunk, else 2 * (2048 / cols) whole rows. A
+// job is made of one or two runs (one row-chunk, or 2048 / cols rows).
 //
-// Byte-table path (Rice k of 0 or 1, tables of at least 15 exponents, runs
-// whose unary bits fit 4096 bits; the tensors of LLM layers):
-//  Each lane takes a contiguous range of unary bytes. One LDS table entry per
-//  byte value gives, for the codes that end in that byte, their q << k packed
-//  as nibbles, the first code's zeros inside the byte, and the zeros left
-//  over after the last code; the zeros carried in from earlier bytes only
-//  touch the first code. A lane's first weight index comes from a wave prefix
-//  sum of its byte range's one bits, its carried zeros from a wave prefix
-//  maximum of the last one-bit positions. The nibbles go, in weight order,
-//  into a 1 KiB LDS buffer by OR; each lane then reads its 32 weights back,
-//  puts them in R4 nibble order, adds the remainder bits (an LDS table spreads
-//  8 of them to their nibbles) and writes 16 bytes. A code whose rank may
-//  reach 15 takes a rare branch that computes the rank exactly and keeps it
-//  as an escape.
+// Byte-table path (Rice k = 1, tables of at least 15 exponents, jobs whose
+// unary bits fit 8128 bits and whose chunk starts are at least 128 weights
+// apart; the tensors of LLM layers), one job at a time:
+//  Each lane takes a contiguous range of unary bytes (up to 16). One LDS
+//  table entry per byte value gives, for the codes that end in that byte,
+//  their q << k packed as nibbles, the first code's zeros inside the byte,
+//  and the zeros left over after the last code; the zeros carried in from
+//  earlier bytes only touch the first code. A lane's first weight index
+//  comes from a wave prefix sum of its byte range's one bits, its carried
+//  zeros from a wave prefix maximum of the last one-bit positions. The
+//  nibbles go, in weight order, into a 2 KiB LDS buffer by OR; each lane
+//  then reads two 32-weight tiles back, puts them in R4 nibble order, adds
+//  the remainder bits (an LDS table spreads 8 of them to their nibbles) and
+//  writes 16 bytes per tile. A code whose rank may reach 15 takes a rare
+//  branch that computes the rank exactly and records the escape in LDS.
+//  The job's bounds, escape prefixes and inner chunk starts are loaded
+//  first, then its words.
 //
-// General path (every other tensor):
+// General path (every other job), run by run:
 //  Phase 1: the lanes load the chunk's unary words (each weight's code ends
 //   in exactly one 1 bit) into LDS and popcount them; a wave prefix sum turns
 //   the counts into weight indices, and the lane holding the terminator of
@@ -55,22 +59,39 @@ namespace {
 using namespace dev;
 
 constexpr int kWavesPerBlock = 4;
+// waves per SIMD the register budget must allow (launch bound)
+#ifndef BINADE_DECODE_MIN_WAVES
+#define BINADE_DECODE_MIN_WAVES 1
+#endif
+#ifndef BINADE_DECODE_GROUP
+#define BINADE_DECODE_GROUP 4
+#endif
+constexpr int kWalkGroup = BINADE_DECODE_GROUP;   // byte-table entries a lane loads ahead
 constexpr int kStageWords = 384;     // unary words staged per run (6 bits/weight)
-constexpr int kEscSlots = 8;         // escapes kept per lane in LDS
-constexpr int kByteSlots = 3;        // escapes kept per lane (byte-table path)
-constexpr uint32_t kByteMaxBits = 4096 - 64;  // unary bits per run (byte-table path)
-// LDS per wave: a general region (staged unary words, then 64 words of lane
-// tile starts) and a 2 KiB-aligned buffer region, which holds the general
-// path's escape slots, or the byte-table path's nibble buffer and escape
-// slots. The byte-table path keeps the run's remainder words in the stage
-// area above the unary words it uses (at most 132).
+constexpr int kEscSlots = 7;         // escapes kept per lane in LDS
+constexpr int kByteSlots = 2;        // escapes kept per lane (byte-table path)
+constexpr int kJobWeights = 2 * kChunk;            // weights per job, at most
+constexpr uint32_t kByteMaxBits = 8192 - 64;       // unary bits per job (byte-table path)
+// LDS per wave (words). General path: staged unary words, 64 words of lane
+// tile starts, then the escape slots. Byte-table path: the job's unary
+// words (plus look-ahead), its remainder words, the nibble buffer and the
+// escape slots.
 constexpr int kGeneralWords = (kStageWords + 4) + 64;
-constexpr int kBufWords = 512;
-constexpr int kNibWords = 2048 / 8 + 2;
-constexpr int kRemOff = 256;
-static_assert(kEscSlots * 64 <= kBufWords, "general path escape slots");
-static_assert(kNibWords + kByteSlots * 64 <= kBufWords, "byte path buffer");
-static_assert(kRemOff >= 132 && kRemOff + 64 <= kStageWords, "byte path remainder words");
+// Byte-table path: the stage area holds the job's unary words until every
+// lane has its bits; then its first 128 words hold the escape counters and
+// the next 128 the escape slots.
+constexpr int kByteStage = 256 + 4;
+constexpr int kByteCtrOff = 0;                      // 2 x 64 escape counters
+constexpr int kByteSlotOff = 128;                   // kByteSlots x 64 escape slots
+constexpr int kByteRem = kByteStage;                // 128 remainder words
+constexpr int kByteNib = kByteRem + 128;            // 4096 nibbles + 4 words
+constexpr int kWaveWords = kByteNib + kJobWeights / 8 + 4;
+// 8 blocks of 4 waves per CU: LDS (160 KiB) holds them
+static_assert(8 * (kWavesPerBlock * kWaveWords * 4 + 256 * 20) <= 160 * 1024, "LDS per block");
+static_assert(256 + 4 <= kByteStage && kByteSlotOff + kByteSlots * 64 <= kByteStage,
+              "byte path stage area");
+static_assert(kGeneralWords + kEscSlots * 64 <= kWaveWords, "general path LDS");
+static_assert(kByteNib % 4 == 0 && kWaveWords % 4 == 0, "16-byte aligned LDS regions");
 
 // Per byte value b of the unary plane and Rice k (0 or 1): the codes that end
 // in b (each ends in a one bit; bit 0 is the earliest). Entry words:
@@ -137,11 +158,18 @@ struct RiceArgs {
   int32_t cols;
   uint32_t k;
   uint32_t n;
-  uint32_t cols_recip;  // ceil(2^32 / cols) when cols < 2048: i / cols = mulhi(i, recip)
-  uint32_t chunks_per_row;  // C = ceil(cols / 2048)
-  uint32_t c_recip;         // ceil(2^32 / C): r / C = mulhi(r, c_recip), or one less
-  uint32_t rows_per_run;    // G = 2048 / cols when C == 1, else 1
-  int64_t runs;             // waves' worth of work: row-chunks (C > 1) or ceil(rows / G)
+  // jobs (one per wave): two row-chunks of one row when C = ceil(cols /
+  // 2048) > 1, else 2G whole rows (G = 2048 / cols); a job is the runs
+  // (one row-chunk, or G rows) sub_rows row-chunks apiece
+  uint32_t chunks_per_row;  // C
+  uint32_t pairs_per_row;   // P = ceil(C / 2) when C > 1
+  uint32_t p_recip;         // ceil(2^32 / P) when P > 1: j / P = mulhi(j, p_recip), or one less
+  uint32_t job_rows;        // 2G when C == 1
+  uint32_t sub_rows;        // row-chunks per run: 1 (C > 1) or G
+  int32_t sub_len;          // weights per full run: 2048 or G * cols
+  uint32_t unit;            // distance between row-chunk starts in a job: 2048 or cols
+  uint32_t unit_recip;      // ceil(2^32 / unit): i / unit = mulhi(i, unit_recip) for i <= 4096
+  int64_t jobs;
   uint32_t table[64];       // exp_of_rank, 4 bytes per word
 };
 
@@ -317,8 +345,17 @@ __device__ bool decode_tile_exact(BitReader<kLds>& br, const RiceArgs& a,
   return true;
 }
 
-// A wave's run of row-chunks: one row-chunk when rows are longer than a
-// chunk, else 2048 / cols whole rows.
+// A wave's job: consecutive row-chunks [c0, c0 + cnt), weights
+// [fb, fb + len) (len <= 4096), made of up to two runs.
+struct Job {
+  int64_t c0;
+  int64_t cnt;
+  int64_t fb;
+  int32_t len;
+};
+
+// A run of row-chunks: one row-chunk when rows are longer than a chunk,
+// else G = 2048 / cols whole rows.
 struct Run {
   int64_t c0;      // first row-chunk
   int64_t cnt;     // row-chunks in the run
@@ -326,27 +363,38 @@ struct Run {
   int32_t len;     // weights in the run (multiple of 32, <= 2048)
 };
 
-__device__ __forceinline__ int64_t runs_total(const RiceArgs& a) { return a.runs; }
-
-// The run r (wave-uniform) of a tensor; all arithmetic on scalars.
-__device__ __forceinline__ void run_of(const RiceArgs& a, int64_t r, Run& run) {
+// The job j (wave-uniform) of a tensor; all arithmetic on scalars.
+__device__ __forceinline__ void job_of(const RiceArgs& a, int64_t j, Job& job) {
   if (a.chunks_per_row == 1u) {
-    const int64_t G = a.rows_per_run;
-    run.c0 = r * G;
-    run.cnt = min(G, a.n_chunks - run.c0);
-    run.fb = run.c0 * a.cols;
-    run.len = static_cast<int32_t>(run.cnt) * a.cols;
+    const int64_t G2 = a.job_rows;
+    job.c0 = j * G2;
+    job.cnt = min(G2, a.n_chunks - job.c0);
+    job.fb = job.c0 * a.cols;
+    job.len = static_cast<int32_t>(job.cnt) * a.cols;
   } else {
-    const uint32_t C = a.chunks_per_row;
-    const uint32_t r32 = static_cast<uint32_t>(r);   // < 2^31
-    uint32_t row = __umulhi(r32, a.c_recip);
-    if (row * C > r32) --row;
-    const int32_t j = static_cast<int32_t>(r32 - row * C);
-    run.c0 = r;
-    run.cnt = 1;
-    run.fb = static_cast<int64_t>(row) * a.cols + static_cast<int64_t>(j) * kChunk;
-    run.len = min(kChunk, a.cols - j * kChunk);
+    const uint32_t C = a.chunks_per_row, P = a.pairs_per_row;
+    const uint32_t j32 = static_cast<uint32_t>(j);   // < 2^31
+    uint32_t row = j32;
+    if (P > 1u) {
+      row = __umulhi(j32, a.p_recip);
+      if (row * P > j32) --row;
+    }
+    const uint32_t jp = j32 - row * P;
+    job.c0 = static_cast<int64_t>(row) * C + 2u * jp;
+    job.cnt = min(2u, C - 2u * jp);
+    job.fb = static_cast<int64_t>(row) * a.cols + static_cast<int64_t>(jp) * kJobWeights;
+    job.len = min(kJobWeights, a.cols - static_cast<int32_t>(jp) * kJobWeights);
   }
+}
+
+// Run i (0 or 1) of a job; false if the job has no such run.
+__device__ __forceinline__ bool run_of(const RiceArgs& a, const Job& job, int i, Run& run) {
+  const int64_t g = a.sub_rows;
+  run.c0 = job.c0 + i * g;
+  run.cnt = min(g, job.cnt - i * g);
+  run.fb = job.fb + static_cast<int64_t>(i) * a.sub_len;
+  run.len = min(a.sub_len, job.len - i * a.sub_len);
+  return run.cnt > 0;
 }
 
 // What a wave loads first: the run's bounds, its first two unary words per
@@ -611,13 +659,6 @@ __device__ __forceinline__ void lds_or(uint32_t addr, uint32_t v) {
   __hip_atomic_fetch_or((lds_u32*)addr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Whether a run takes the byte-table path (wave-uniform).
-__device__ __forceinline__ bool byte_path(const RiceArgs& a, const Run& run,
-                                          const Prefetch& pf) {
-  return a.k == 1u && a.n >= 15u && (run.cnt == 1 || a.cols >= 64) && pf.B > pf.A &&
-         pf.B - pf.A <= kByteMaxBits;
-}
-
 // Nibbles of 8 weights in weight order (weight i at bits 4i) -> R4 order
 // (weight i in byte i % 4, high nibble for i >= 4).
 __device__ __forceinline__ uint32_t to_r4_order(uint32_t n) {
@@ -628,77 +669,165 @@ __device__ __forceinline__ uint32_t to_r4_order(uint32_t n) {
   return (lo & 0x0F0F0F0Fu) | (hi & 0xF0F0F0F0u);
 }
 
-// One lane's walk over kSteps bytes of unary bits (x0 then x1, bit 0 first;
-// bits past the lane's range are zero). c: zeros carried in, << K. sb: 4 *
-// index of the lane's first weight in the run. kEmit == false: ORs the
-// nibbles (q << K, 15 at most; remainders come later) into the 2 KiB-aligned
-// nibble buffer at LDS byte address nb, keeps up to kByteSlots escapes
-// (index << 8 | rank) in slots and counts them (and those before weight
-// limit) in n_esc / n_before. kEmit == true: writes the escapes to dst.
-// Returns false on a rank outside the table.
+// LDS atomics on a lane's own words (no other lane touches them).
+__device__ __forceinline__ uint32_t lds_add_rtn(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add((lds_u32*)lds_address(p), v, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Escape bookkeeping of a lane in LDS, so that the rare branch of the walk
+// changes no register the common path carries: ctr[0] counts the lane's
+// escapes (bit 31: a rank outside the table), ctr[64] those before the
+// weight limit; slots[64 i] holds escape i (index << 8 | rank), i < 3.
+constexpr uint32_t kBadRank = 0x80000000u;
+
+// One lane's walk over kSteps bytes of unary bits (byte j is byte j % 4 of
+// x[j / 4], bit 0 first; bits past the lane's range are zero). c: zeros
+// carried in, << K. sb: 4 * index of the lane's first weight in the job.
+// kEmit == false: ORs the nibbles (q << K, 15 at most; remainders come
+// later) into the nibble buffer at LDS byte address nb and records escapes
+// in ctr / slots. kEmit == true: writes the escapes to dst (n_esc counts
+// them).
 template <uint32_t K, int kSteps, bool kEmit>
-__device__ __forceinline__ bool byte_walk(uint32_t x0, uint32_t x1, int32_t c, uint32_t sb,
+__device__ __forceinline__ void byte_walk(const uint32_t (&x)[4], int32_t c, uint32_t sb,
                                           const uint4* lut, const uint32_t* remw, uint32_t n,
-                                          uint32_t nb, uint32_t* slots, uint32_t& n_esc,
-                                          uint32_t limit, uint32_t& n_before,
-                                          const uint8_t* table, uint32_t chunk_mod,
-                                          uint32_t* dst) {
+                                          uint32_t nb, uint32_t* ctr, uint32_t* slots,
+                                          uint32_t limit, const uint8_t* table,
+                                          uint32_t chunk_mod, uint32_t* dst, uint32_t& n_esc) {
   constexpr int32_t kThr = K ? 14 : 15;   // smallest q << K whose rank can be >= 15
-  uint4 e[kSteps];
+  constexpr int kGroup = kSteps < kWalkGroup ? kSteps : kWalkGroup;   // table entries loaded ahead
 #pragma unroll
-  for (int j = 0; j < kSteps; ++j)
-    e[j] = lut[__builtin_amdgcn_ubfe(j < 4 ? x0 : x1, 8 * (j & 3), 8)];
-  bool ok = true;
+  for (int j0 = 0; j0 < kSteps; j0 += kGroup) {
+    uint4 e[kGroup];
 #pragma unroll
-  for (int j = 0; j < kSteps; ++j) {
-    const int32_t t = static_cast<int32_t>(e[j].y) + c;     // first code's q << K
-    if (t >= kThr) {
-      // rare: the first code may be an escape
-      const uint32_t idx = sb >> 2;
-      const uint32_t rank =
-          static_cast<uint32_t>(t) | (K ? ((remw[idx >> 5] >> (idx & 31u)) & 1u) : 0u);
-      if (rank >= 15u) {
-        if (rank >= n) {
-          ok = false;
-        } else if (kEmit) {
-          dst[n_esc++] = (static_cast<uint32_t>(table[rank]) << 16) | (idx % chunk_mod);
-        } else {
-          if (n_esc < static_cast<uint32_t>(kByteSlots)) slots[n_esc * 64] = (idx << 8) | rank;
-          ++n_esc;
-          if (idx < limit) ++n_before;
+    for (int jj = 0; jj < kGroup; ++jj) {
+      const int j = j0 + jj;
+      e[jj] = lut[__builtin_amdgcn_ubfe(x[j >> 2], 8 * (j & 3), 8)];
+    }
+#pragma unroll
+    for (int jj = 0; jj < kGroup; ++jj) {
+      const int32_t t = static_cast<int32_t>(e[jj].y) + c;     // first code's q << K
+      if (t >= kThr) {
+        // rare: the first code may be an escape
+        const uint32_t idx = sb >> 2;
+        const uint32_t rank =
+            static_cast<uint32_t>(t) | (K ? ((remw[idx >> 5] >> (idx & 31u)) & 1u) : 0u);
+        if (rank >= 15u) {
+          if (kEmit) {
+            if (rank < n)
+              dst[n_esc++] = (static_cast<uint32_t>(table[rank]) << 16) | (idx % chunk_mod);
+          } else {
+            const uint32_t pos = lds_add_rtn(ctr, rank < n ? 1u : kBadRank) & ~kBadRank;
+            if (pos < static_cast<uint32_t>(kByteSlots)) slots[pos * 64] = (idx << 8) | rank;
+            if (idx < limit) lds_add_rtn(ctr + 64, 1u);
+          }
         }
       }
+      if (!kEmit) {
+        const uint32_t v = e[jj].x | static_cast<uint32_t>(min(max(t, 0), 15));
+        // v << (sb % 32) over the word holding nibble sb / 4 and the next
+        const uint64_t w = static_cast<uint64_t>(v) << (sb & 31u);
+        const uint32_t addr = nb + (__builtin_amdgcn_ubfe(sb, 5, 27) << 2);
+        lds_or(addr, static_cast<uint32_t>(w));
+        lds_or(addr + 4u, static_cast<uint32_t>(w >> 32));
+      }
+      // zeros carried to the next byte: those after its last code, or all 8
+      c = min(c + static_cast<int32_t>(8u << K), static_cast<int32_t>(e[jj].w));
+      sb += e[jj].z;
     }
-    if (!kEmit) {
-      const uint32_t v = e[j].x | static_cast<uint32_t>(min(max(t, 0), 15));
-      // v << (sb % 32) as two words; v_bfe_u32 takes offset and width mod
-      // 32, so the high word is v >> (32 - sb % 32), and 0 when sb % 32 == 0
-      const uint32_t lo = v << (sb & 31u);
-      const uint32_t hi = __builtin_amdgcn_ubfe(v, (0u - sb) & 31u, sb & 31u);
-      const uint32_t addr = ((sb >> 3) & 0x7FCu) | nb;   // nb is 2 KiB aligned
-      lds_or(addr, lo);
-      lds_or(addr + 4u, hi);
-    }
-    // zeros carried to the next byte: those after its last code, or all 8
-    c = min(c + static_cast<int32_t>(8u << K), static_cast<int32_t>(e[j].w));
-    sb += e[j].z;
   }
-  return ok;
 }
-// Decode one run on the byte-table path (byte_path() holds), Rice k = K.
-// Lane l takes the run's unary bits [spl*8*l, spl*8*(l+1)) (spl bytes, 1..8,
-// counted from the run's first bit).
+
+// Bit position (0..127) of the n-th (0-based) set bit of x[0..3]; x has more
+// than n set bits.
+__device__ __forceinline__ uint32_t select_bit4(const uint32_t (&x)[4], uint32_t n) {
+  uint32_t base = 0;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const uint32_t pcq = __popc(x[q]);
+    if (n < pcq) return base + select_bit(x[q], n);
+    n -= pcq;
+    base += 32u;
+  }
+  return base + select_bit(x[3], n);
+}
+
+// One job's loads: its bit bounds (uniform) and escape prefixes, four unary
+// words and two remainder words per lane.
+struct JobLoads {
+  uint64_t A, B;      // anchors of the first and one-past-last row-chunk
+  uint32_t e0, e1;    // escape prefixes of the same
+  uint64_t ia;        // anchor of row-chunk c0 + 1 + lane (lane < cnt - 1)
+  uint32_t ie;        // escape prefix of the same
+  uint4 w;            // unary words A/32 + 4*lane .. +3 (0 past the job)
+  uint32_t rw0, rw1;  // remainder words of tiles lane and lane + 64 (k = 1)
+};
+
+// The job's bounds, and for a job of several row-chunks the anchors and
+// escape prefixes of its inner chunk starts (lane i: chunk c0 + 1 + i), all
+// requested before any other work.
+__device__ __forceinline__ void job_bounds(const RiceArgs& a, const Job& job, int lane,
+                                           JobLoads& L) {
+  L.A = a.anchor[job.c0];
+  L.B = a.anchor[job.c0 + job.cnt];
+  L.e0 = a.esc_pre[job.c0];
+  L.e1 = a.esc_pre[job.c0 + job.cnt];
+  L.ia = 0;
+  L.ie = 0;
+  if (job.cnt > 1) {
+    const int64_t inner = job.c0 + 1 + min(static_cast<int64_t>(lane), job.cnt - 2);
+    L.ia = a.anchor[inner];
+    L.ie = a.esc_pre[inner];
+  }
+  L.A = uniform64(static_cast<int64_t>(L.A));
+  L.B = uniform64(static_cast<int64_t>(L.B));
+}
+
+// The job's words (B > A): uniform bases and 32-bit lane offsets; only the
+// job's own words are read.
+__device__ __forceinline__ void job_words(const RiceArgs& a, const Job& job, int lane,
+                                          JobLoads& L) {
+  const uint64_t wA = L.A >> 5;
+  const uint64_t left = a.unary_words > wA ? a.unary_words - wA : 0ull;
+  const uint64_t need = ((L.B - 1) >> 5) - wA + 1;
+  const uint32_t avail = static_cast<uint32_t>(need < left ? need : left);   // <= 255
+  const uint32_t* ub = a.unary + wA;
+  const uint32_t wi = 4u * static_cast<uint32_t>(lane);
+  if (wi + 3u < avail) {
+    L.w = make_uint4(ub[wi], ub[wi + 1u], ub[wi + 2u], ub[wi + 3u]);
+  } else {
+    L.w.x = wi < avail ? ub[wi] : 0u;
+    L.w.y = wi + 1u < avail ? ub[wi + 1u] : 0u;
+    L.w.z = wi + 2u < avail ? ub[wi + 2u] : 0u;
+    L.w.w = 0u;
+  }
+  // remainder bits (k = 1) of the job's tile t: word fb / 32 + t
+  const uint64_t r0 = static_cast<uint64_t>(job.fb) >> 5;
+  const uint64_t rleft = a.rem_words > r0 ? a.rem_words - r0 : 0ull;
+  const uint64_t rneed = static_cast<uint64_t>(job.len >> 5);
+  const uint32_t ravail = static_cast<uint32_t>(rneed < rleft ? rneed : rleft);   // <= 128
+  const uint32_t* rb = a.rem + r0;
+  L.rw0 = static_cast<uint32_t>(lane) < ravail ? rb[lane] : 0u;
+  L.rw1 = static_cast<uint32_t>(lane) + 64u < ravail ? rb[lane + 64] : 0u;
+}
+
+// Decode one job on the byte-table path, Rice k = K. Lane l takes the job's
+// unary bits [spl*8*l, spl*8*(l+1)) (spl bytes, 1..16, counted from the
+// job's first bit).
 template <uint32_t K>
-__device__ __forceinline__ void decode_run_bytes(const RiceArgs& a, const uint8_t* table,
-                                                 const Run& run, const Prefetch& pf, int lane,
-                                                 uint32_t* stage, uint32_t* buf, const uint4* lut,
+__device__ __forceinline__ void decode_job_bytes(const RiceArgs& a, const uint8_t* table,
+                                                 const Job& job, const JobLoads& f, int lane,
+                                                 uint32_t* lds, const uint4* lut,
                                                  const uint32_t* spread) {
-  uint32_t* remw = stage + kRemOff;
-  uint32_t* slots = buf + kNibWords + lane;
-  const int64_t c0 = run.c0, cnt = run.cnt;
-  const int32_t Lc = run.len;
+  uint32_t* stage = lds;
+  uint32_t* remw = lds + kByteRem;
+  uint32_t* nibw = lds + kByteNib;
+  uint32_t* slots = lds + kByteSlotOff + lane;
+  uint32_t* ctr = lds + kByteCtrOff + lane;
+  const int64_t c0 = job.c0, cnt = job.cnt;
+  const int32_t Lc = job.len;
   const int32_t T = Lc >> 5;
-  const uint64_t A = pf.A, B = pf.B;
+  const uint64_t A = f.A, B = f.B;
   if (B < A + static_cast<uint64_t>(Lc) || B > a.unary_words * 32ull) {
     flag(a.status, BINADE_DEV_CORRUPT_STREAM, lane);
     return;
@@ -707,83 +836,112 @@ __device__ __forceinline__ void decode_run_bytes(const RiceArgs& a, const uint8_
   const uint32_t uA = static_cast<uint32_t>(A & 31u);
   const uint32_t nbits = static_cast<uint32_t>(B - A);            // <= kByteMaxBits
   const uint32_t Brel = uA + nbits;                                // end, from word wA
-  const uint32_t nw = (Brel + 31u) >> 5;                           // <= 128
-  const uint32_t spl = (((nbits + 7u) >> 3) + 63u) >> 6;           // 1..8
+  const uint32_t nw = (Brel + 31u) >> 5;                           // <= 255
+  const uint32_t spl = (((nbits + 7u) >> 3) + 63u) >> 6;           // 1..16
 
-  // ---- stage the run's unary words (bits outside the run cleared, zeros up
-  // to word 131) and remainder words; clear the nibble buffer
+  // ---- stage the job's unary words (bits outside the job cleared, zeros
+  // up to word 259) and remainder words; clear the nibble buffer
   {
-    const uint32_t i0 = 2u * lane, i1 = i0 + 1u;
+    const uint32_t i0 = 4u * lane;
     const uint32_t last = nw - 1u;
     const uint32_t keep_last = 0xFFFFFFFFu >> (31u - ((Brel - 1u) & 31u));
-    uint32_t v0 = i0 < nw ? pf.w0 : 0u, v1 = i1 < nw ? pf.w1 : 0u;
-    if (i0 == 0u) v0 &= 0xFFFFFFFFu << uA;
-    if (i0 == last) v0 &= keep_last;
-    if (i1 == last) v1 &= keep_last;
-    stage[i0] = v0;
-    stage[i1] = v1;
-    if (lane < 4) stage[128 + lane] = 0u;
-    remw[lane] = pf.rw0;
-    reinterpret_cast<uint4*>(buf)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t v[4] = {f.w.x, f.w.y, f.w.z, f.w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t i = i0 + q;
+      if (i >= nw) v[q] = 0u;
+      if (i == 0u) v[q] &= 0xFFFFFFFFu << uA;
+      if (i == last) v[q] &= keep_last;
+    }
+    reinterpret_cast<uint4*>(stage)[lane] = make_uint4(v[0], v[1], v[2], v[3]);
+    if (lane < 4) stage[256 + lane] = 0u;
+    remw[lane] = f.rw0;
+    remw[64 + lane] = f.rw1;
+    reinterpret_cast<uint4*>(nibw)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    reinterpret_cast<uint4*>(nibw)[64 + lane] = make_uint4(0u, 0u, 0u, 0u);
+    if (lane == 0) reinterpret_cast<uint4*>(nibw)[128] = make_uint4(0u, 0u, 0u, 0u);
   }
   wave_sync();
 
   // ---- the lane's bits
   const uint32_t bit0 = uA + 8u * spl * static_cast<uint32_t>(lane);
   const uint32_t wi = bit0 >> 5, off = bit0 & 31u;
-  const uint32_t s0 = stage[wi], s1 = stage[wi + 1], s2 = stage[wi + 2];
-  uint32_t x0 = __builtin_amdgcn_alignbit(s1, s0, off);
-  uint32_t x1 = __builtin_amdgcn_alignbit(s2, s1, off);
-  if (spl < 8u) {   // uniform: the next lane's bits
-    const uint64_t keep = (1ull << (8u * spl)) - 1ull;
-    x0 &= static_cast<uint32_t>(keep);
-    x1 &= static_cast<uint32_t>(keep >> 32);
+  uint32_t x[4];
+  {
+    uint32_t sw[5];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) sw[q] = stage[wi + q];
+    const uint32_t bits = 8u * spl;   // 8 .. 128
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t xq = __builtin_amdgcn_alignbit(sw[q + 1], sw[q], off);
+      const uint32_t lo = 32u * q;
+      const uint32_t keep =
+          bits <= lo ? 0u : (bits - lo >= 32u ? 0xFFFFFFFFu : (1u << (bits - lo)) - 1u);
+      x[q] = xq & keep;
+    }
   }
-  const uint32_t pc = __popc(x0) + __popc(x1);
+  const uint32_t last_word = stage[(Brel - 1u) >> 5];
+  // the unary words are read: the escape counters take over their area (a
+  // wave's LDS operations complete in order)
+  ctr[0] = 0u;
+  ctr[64] = 0u;
+  const uint32_t pc = __popc(x[0]) + __popc(x[1]) + __popc(x[2]) + __popc(x[3]);
   const uint32_t incl = wave_inclusive_sum(pc);
   const uint32_t s_first = incl - pc;
-  const uint32_t last_word = stage[(Brel - 1u) >> 5];
   if (lane63(incl) != static_cast<uint32_t>(Lc) ||
       ((last_word >> ((Brel - 1u) & 31u)) & 1u) == 0u) {
     flag(a.status, BINADE_DEV_CORRUPT_STREAM, lane);
     return;
   }
   // zeros carried into the lane: from its first bit back to the last one bit
-  // of an earlier lane (every lane's bits start after the run's first bit)
-  const int32_t top = x1 ? 63 - __clz(x1) : 31 - __clz(x0);
+  // of an earlier lane (every lane's bits start after the job's first bit)
+  const int32_t top = x[3]   ? 127 - __clz(x[3])
+                      : x[2] ? 95 - __clz(x[2])
+                      : x[1] ? 63 - __clz(x[1])
+                             : 31 - __clz(x[0]);
   const int32_t last = pc ? static_cast<int32_t>(bit0) + top : static_cast<int32_t>(uA) - 1;
   const int32_t prev = wave_shift_up(wave_inclusive_max(last), static_cast<int32_t>(uA) - 1);
   const int32_t c_in = (static_cast<int32_t>(bit0) - prev - 1) << K;
   const uint32_t sb0 = 4u * s_first;
 
-  // a row that starts inside the run (short rows): the lane holding the one
-  // bit that ends the row's previous weight checks the row's anchor and
-  // escape prefix
+  // a row-chunk that starts inside the job: the lane holding the one bit
+  // that ends the chunk's previous weight checks the chunk's anchor and
+  // escape prefix (a lane holds at most 128 codes and chunk starts are at
+  // least 128 weights apart, so at most one per lane)
   uint32_t limit = 0;
   if (cnt > 1) {
-    const uint32_t cols = static_cast<uint32_t>(a.cols);
-    const uint32_t r = __umulhi(s_first, a.cols_recip) + 1u;   // first row start > s_first
-    const uint32_t start = r * cols;
+    const uint32_t r = __umulhi(s_first, a.unit_recip) + 1u;   // first start > s_first
+    const uint32_t start = r * a.unit;
     if (pc > 0u && start <= s_first + pc && start < static_cast<uint32_t>(Lc)) limit = start;
   }
 
-  uint32_t n_esc_lane = 0, n_before = 0;
   const uint32_t chunk_mod = a.cols < kChunk ? static_cast<uint32_t>(a.cols) : kChunk;
-  const uint32_t nb = lds_address(buf);
-  bool ok;
+  const uint32_t nb = lds_address(nibw);
+  uint32_t unused = 0;
   if (spl <= 4u)
-    ok = byte_walk<K, 4, false>(x0, x1, c_in, sb0, lut, remw, a.n, nb, slots, n_esc_lane, limit,
-                                n_before, table, chunk_mod, nullptr);
+    byte_walk<K, 4, false>(x, c_in, sb0, lut, remw, a.n, nb, ctr, slots, limit, table, chunk_mod,
+                           nullptr, unused);
+  else if (spl <= 8u)
+    byte_walk<K, 8, false>(x, c_in, sb0, lut, remw, a.n, nb, ctr, slots, limit, table, chunk_mod,
+                           nullptr, unused);
   else
-    ok = byte_walk<K, 8, false>(x0, x1, c_in, sb0, lut, remw, a.n, nb, slots, n_esc_lane, limit,
-                                n_before, table, chunk_mod, nullptr);
+    byte_walk<K, 16, false>(x, c_in, sb0, lut, remw, a.n, nb, ctr, slots, limit, table,
+                            chunk_mod, nullptr, unused);
+  const uint32_t cw = ctr[0];
+  const bool ok = (cw & kBadRank) == 0u;
+  const uint32_t n_esc_lane = cw & ~kBadRank;
+  const uint32_t n_before = ctr[64];
+  // the inner chunk start's anchor and escape prefix, from the lane that
+  // loaded them (chunk c0 + r: lane r - 1)
+  const int inner = limit != 0u ? static_cast<int>(__umulhi(limit, a.unit_recip)) - 1 : 0;
+  const uint32_t ia_lo = __shfl(static_cast<uint32_t>(f.ia), inner);
+  const uint32_t ia_hi = __shfl(static_cast<uint32_t>(f.ia >> 32), inner);
+  const uint32_t ie = __shfl(f.ie, inner);
   bool off_anchor = false;
   if (limit != 0u) {
-    const uint32_t idx = limit - 1u - s_first;          // that weight's one bit
-    const uint32_t pc0 = __popc(x0);
-    const uint32_t pos = idx < pc0 ? select_bit(x0, idx) : 32u + select_bit(x1, idx - pc0);
-    const int64_t row_chunk = c0 + __umulhi(limit, a.cols_recip);
-    off_anchor = a.anchor[row_chunk] != wA * 32ull + bit0 + pos + 1u;
+    const uint32_t pos = select_bit4(x, limit - 1u - s_first);   // that weight's one bit
+    off_anchor = (static_cast<uint64_t>(ia_hi) << 32 | ia_lo) != wA * 32ull + bit0 + pos + 1u;
   }
   if (__any(!ok || off_anchor)) {
     flag(a.status, BINADE_DEV_CORRUPT_STREAM, lane);
@@ -791,27 +949,31 @@ __device__ __forceinline__ void decode_run_bytes(const RiceArgs& a, const uint8_
   }
   wave_sync();
 
-  // ---- R4 nibbles: read back 32 weights, R4 order, remainder bits
-  if (lane < T) {
-    const uint4 nn = reinterpret_cast<const uint4*>(buf)[lane];
-    uint4 o;
-    o.x = to_r4_order(nn.x);
-    o.y = to_r4_order(nn.y);
-    o.z = to_r4_order(nn.z);
-    o.w = to_r4_order(nn.w);
-    if (K) {
-      const uint32_t rw = pf.rw0;
-      o.x |= spread[rw & 0xFFu];
-      o.y |= spread[(rw >> 8) & 0xFFu];
-      o.z |= spread[(rw >> 16) & 0xFFu];
-      o.w |= spread[rw >> 24];
+  // ---- R4 nibbles: read back 32 weights per tile, R4 order, remainder bits
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = lane + 64 * h;
+    if (t < T) {
+      const uint4 nn = reinterpret_cast<const uint4*>(nibw)[t];
+      uint4 o;
+      o.x = to_r4_order(nn.x);
+      o.y = to_r4_order(nn.y);
+      o.z = to_r4_order(nn.z);
+      o.w = to_r4_order(nn.w);
+      if (K) {
+        const uint32_t rw = h ? f.rw1 : f.rw0;
+        o.x |= spread[rw & 0xFFu];
+        o.y |= spread[(rw >> 8) & 0xFFu];
+        o.z |= spread[(rw >> 16) & 0xFFu];
+        o.w |= spread[rw >> 24];
+      }
+      *reinterpret_cast<uint4*>(a.nib + (static_cast<uint64_t>(job.fb) >> 1) + 16u * t) = o;
     }
-    *reinterpret_cast<uint4*>(a.nib + (static_cast<uint64_t>(run.fb) >> 1) + 16u * lane) = o;
   }
 
   // ---- escapes: place in the side list after a prefix sum over lanes
-  const uint32_t e0 = a.esc_pre[c0];
-  const uint32_t e1 = a.esc_pre[c0 + cnt];
+  const uint32_t e0 = f.e0;
+  const uint32_t e1 = f.e1;
   uint32_t before, total;
   if (__ballot(n_esc_lane > 1u) == 0) {
     const uint64_t has = __ballot(n_esc_lane != 0u);
@@ -823,8 +985,7 @@ __device__ __forceinline__ void decode_run_bytes(const RiceArgs& a, const uint8_
     before = esc_incl - n_esc_lane;
     total = lane63(esc_incl);
   }
-  const bool esc_off = limit != 0u &&
-                       a.esc_pre[c0 + __umulhi(limit, a.cols_recip)] != e0 + before + n_before;
+  const bool esc_off = limit != 0u && ie != e0 + before + n_before;
   if (e1 < e0 || e1 - e0 != total || e1 > a.n_esc || __any(esc_off)) {
     flag(a.status, BINADE_DEV_CORRUPT_ESC, lane);
   } else if (n_esc_lane > 0) {
@@ -836,29 +997,11 @@ __device__ __forceinline__ void decode_run_bytes(const RiceArgs& a, const uint8_
       }
     } else {
       // more escapes than slots: walk the bytes again, writing them out
-      uint32_t n2 = 0, unused = 0;
-      byte_walk<K, 8, true>(x0, x1, c_in, sb0, lut, remw, a.n, 0u, nullptr, n2, 0u, unused, table,
-                            chunk_mod, dst);
+      uint32_t n2 = 0;
+      byte_walk<K, 16, true>(x, c_in, sb0, lut, remw, a.n, 0u, nullptr, nullptr, 0u, table,
+                             chunk_mod, dst, n2);
     }
   }
-}
-
-// One run per wave: its anchors, then its unary and remainder words are
-// requested first. (Several runs per wave, with all their loads issued up
-// front, measured slower: the decode is bound by instruction issue, not by
-// the memory round trip.)
-__device__ __forceinline__ void decode_wave(const RiceArgs& a, const uint8_t* table,
-                                            int64_t r, int lane, uint32_t* region, uint32_t* buf,
-                                            const uint4* lut, const uint32_t* spread) {
-  Run run;
-  Prefetch pf;
-  run_of(a, r, run);
-  prefetch_bounds(a, run, pf);
-  prefetch_words(a, run, lane, pf);
-  if (byte_path(a, run, pf))
-    decode_run_bytes<1>(a, table, run, pf, lane, region, buf, lut, spread);
-  else
-    decode_run(a, table, run, pf, lane, region, region + (kStageWords + 4), buf + lane);
 }
 
 // The byte tables for Rice k = 1 (the byte-table path's k), one entry per
@@ -871,52 +1014,61 @@ __device__ __forceinline__ void load_byte_tables(uint4* lut, uint32_t* spread) {
   __syncthreads();
 }
 
-// One wave per run; the run's anchors, first unary words and remainder
-// words are requested before any other work.
-__global__ __launch_bounds__(256) void rice_to_r4_kernel(RiceArgs a) {
-  __shared__ __align__(16) uint32_t region[kWavesPerBlock][kGeneralWords];
-  __shared__ __align__(2048) uint32_t buf[kWavesPerBlock][kBufWords];
-  __shared__ uint4 lut[256];
-  __shared__ uint32_t spread[256];
-  load_byte_tables(lut, spread);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t r = uniform64(static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave);
-  if (r >= runs_total(a)) return;
-  decode_wave(a, kernarg_table(0), r, lane, region[wave], buf[wave], lut, spread);
-}
-
-// Several tensors in one launch: tensor i owns blocks
-// [first_block[i], first_block[i+1]).
+// Up to 8 tensors per launch: tensor i owns the launch's jobs
+// [first_job[i], first_job[i+1]).
 constexpr int kMaxDecodeBatch = 8;
 struct RiceBatch {
   RiceArgs item[kMaxDecodeBatch];
-  uint32_t first_block[kMaxDecodeBatch + 1];
+  uint32_t first_job[kMaxDecodeBatch + 1];
   int32_t count;
 };
 
-__global__ __launch_bounds__(256) void rice_to_r4_batch_kernel(RiceBatch b) {
-  __shared__ __align__(16) uint32_t region[kWavesPerBlock][kGeneralWords];
-  __shared__ __align__(2048) uint32_t buf[kWavesPerBlock][kBufWords];
+// One wave per job (job g of the launch is wave g). The tensor's arguments
+// are read in place from the argument segment (an index into a by-value
+// argument array would be copied to scratch memory). The job's bounds, then
+// its words, are requested before any other work.
+__global__ __launch_bounds__(256, BINADE_DECODE_MIN_WAVES) void rice_to_r4_batch_kernel(RiceBatch b) {
+  __shared__ __align__(16) uint32_t lds[kWavesPerBlock][kWaveWords];
   __shared__ uint4 lut[256];
   __shared__ uint32_t spread[256];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const uint32_t blk = blockIdx.x;
+  const uint32_t g = uniform(blockIdx.x * kWavesPerBlock + static_cast<uint32_t>(wave));
+  const bool live = g < b.first_job[b.count];
   int i = 0;
 #pragma unroll
   for (int t = 1; t < kMaxDecodeBatch; ++t)
-    if (t < b.count && blk >= b.first_block[t]) i = t;
+    if (t < b.count && g >= b.first_job[t]) i = t;
   i = uniform(i);
-  // read the item in place from the argument segment (an index into a
-  // by-value argument array would be copied to scratch memory)
   const size_t off = offsetof(RiceBatch, item) + static_cast<size_t>(i) * sizeof(RiceArgs);
-  const RiceArgs* items = (const RiceArgs*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + off);
-  const RiceArgs a = items[0];
+  const RiceArgs& a = *(const RiceArgs*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + off);
+  Job job;
+  JobLoads L;
+  bool bytes = false;
+  if (live) {
+    job_of(a, static_cast<int64_t>(g - b.first_job[i]), job);
+    job_bounds(a, job, lane, L);
+    bytes = a.k == 1u && a.n >= 15u && (job.cnt == 1 || a.unit >= 128u) && L.B > L.A &&
+            L.B - L.A <= kByteMaxBits;
+    if (bytes) job_words(a, job, lane, L);
+  }
   load_byte_tables(lut, spread);
-  const int64_t r = uniform64(static_cast<int64_t>(blk - b.first_block[i]) * kWavesPerBlock + wave);
-  if (r >= runs_total(a)) return;
-  decode_wave(a, kernarg_table(off), r, lane, region[wave], buf[wave], lut, spread);
+  if (!live) return;
+  if (bytes) {
+    decode_job_bytes<1>(a, kernarg_table(off), job, L, lane, lds[wave], lut, spread);
+    return;
+  }
+  // general path: each run of the job
+  for (int r = 0; r < 2; ++r) {
+    Run run;
+    if (!run_of(a, job, r, run)) break;
+    Prefetch pf;
+    prefetch_bounds(a, run, pf);
+    prefetch_words(a, run, lane, pf);
+    decode_run(a, kernarg_table(off), run, pf, lane, lds[wave], lds[wave] + (kStageWords + 4),
+               lds[wave] + kGeneralWords + lane);
+    wave_sync();   // the next run reuses the same LDS
+  }
 }
 
 }  // namespace
@@ -927,7 +1079,7 @@ using namespace binade;
 namespace {
 
 // Checks one format 2 -> R4 request and fills its kernel arguments and the
-// host-visible R4 fields. Returns the number of runs (waves) or a status.
+// host-visible R4 fields. Returns the number of jobs (waves) or a status.
 int64_t prepare_decode(const binade_rice* in, binade_r4* out, uint32_t* dev_status,
                        RiceArgs& a) {
   if (in == nullptr || out == nullptr || in->rows <= 0 || in->cols <= 0 ||
@@ -973,58 +1125,88 @@ int64_t prepare_decode(const binade_rice* in, binade_r4* out, uint32_t* dev_stat
   a.k = in->k;
   a.n = in->n;
   a.chunks_per_row = static_cast<uint32_t>(C);
-  a.c_recip = C > 1 ? static_cast<uint32_t>(((1ull << 32) + static_cast<uint64_t>(C) - 1) /
-                                            static_cast<uint64_t>(C))
-                    : 0u;
-  a.rows_per_run = C == 1 ? static_cast<uint32_t>(BINADE_CHUNK / in->cols) : 1u;
-  a.runs = C == 1 ? (in->rows + a.rows_per_run - 1) / a.rows_per_run : n_chunks;
-  a.cols_recip = in->cols < BINADE_CHUNK
-                     ? static_cast<uint32_t>(((1ull << 32) + static_cast<uint64_t>(in->cols) - 1) /
-                                             static_cast<uint64_t>(in->cols))
-                     : 0u;
+  auto recip = [](uint64_t d) {   // ceil(2^32 / d), d >= 2
+    return static_cast<uint32_t>(((1ull << 32) + d - 1) / d);
+  };
+  if (C > 1) {
+    // jobs: two row-chunks of one row (the last one alone when C is odd)
+    const int64_t P = (C + 1) / 2;
+    a.pairs_per_row = static_cast<uint32_t>(P);
+    a.p_recip = P > 1 ? recip(static_cast<uint64_t>(P)) : 0u;
+    a.sub_rows = 1;
+    a.sub_len = BINADE_CHUNK;
+    a.unit = BINADE_CHUNK;
+    a.unit_recip = 1u << 21;   // 2^32 / 2048, exact
+    a.jobs = in->rows * P;
+  } else {
+    // jobs: 2G whole rows, runs of G = 2048 / cols rows
+    const int64_t G = BINADE_CHUNK / in->cols;
+    a.job_rows = static_cast<uint32_t>(2 * G);
+    a.sub_rows = static_cast<uint32_t>(G);
+    a.sub_len = static_cast<int32_t>(G * in->cols);
+    a.unit = static_cast<uint32_t>(in->cols);
+    a.unit_recip = in->cols > 1 ? recip(static_cast<uint64_t>(in->cols)) : 0u;
+    a.jobs = (in->rows + 2 * G - 1) / (2 * G);
+  }
   for (int q = 0; q < 64; ++q)
     a.table[q] = uint32_t(in->exp_of_rank[4 * q]) | (uint32_t(in->exp_of_rank[4 * q + 1]) << 8) |
                  (uint32_t(in->exp_of_rank[4 * q + 2]) << 16) |
                  (uint32_t(in->exp_of_rank[4 * q + 3]) << 24);
-  // runs: one row-chunk, or 2048 / cols short rows; one wave each
-  return a.runs;
+  return a.jobs;
+}
+
+}  // namespace
+
+namespace {
+
+int32_t launch_batch(const RiceBatch& b, hipStream_t stream) {
+  const uint32_t total = b.first_job[b.count];
+  if (total == 0) return BINADE_OK;
+  const int64_t blocks = (static_cast<int64_t>(total) + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL(rice_to_r4_batch_kernel, dim3(static_cast<uint32_t>(blocks)),
+                     dim3(64 * kWavesPerBlock), 0, stream, b);
+  return launch_status();
 }
 
 }  // namespace
 
 extern "C" int32_t binade_rice_to_r4(const binade_rice* in, binade_r4* out,
                                      uint32_t* dev_status, void* stream) {
-  RiceArgs a;
-  const int64_t runs = prepare_decode(in, out, dev_status, a);
-  if (runs < 0) return static_cast<int32_t>(runs);
-  const dim3 grid(static_cast<uint32_t>((runs + kWavesPerBlock - 1) / kWavesPerBlock));
-  hipLaunchKernelGGL(rice_to_r4_kernel, grid, dim3(64 * kWavesPerBlock), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return launch_status();
+  return binade_rice_to_r4_batch(in, out, 1, dev_status, stream);
 }
 
 extern "C" int32_t binade_rice_to_r4_batch(const binade_rice* in, binade_r4* out,
                                            int32_t count, uint32_t* dev_status,
                                            void* stream) {
   if (count < 0 || (count > 0 && (in == nullptr || out == nullptr))) return BINADE_EINVAL;
-  for (int32_t base = 0; base < count; base += kMaxDecodeBatch) {
-    RiceBatch b{};
-    uint64_t blocks = 0;
-    int n = 0;
-    for (int32_t i = base; i < count && n < kMaxDecodeBatch; ++i) {
-      const int64_t runs = prepare_decode(&in[i], &out[i], dev_status, b.item[n]);
-      if (runs < 0) return static_cast<int32_t>(runs);
-      b.first_block[n] = static_cast<uint32_t>(blocks);
-      blocks += static_cast<uint64_t>((runs + kWavesPerBlock - 1) / kWavesPerBlock);
-      ++n;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  RiceBatch b{};
+  int n = 0;
+  uint64_t jobs = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    RiceArgs a;
+    const int64_t nj = prepare_decode(&in[i], &out[i], dev_status, a);
+    if (nj < 0) return static_cast<int32_t>(nj);
+    // a launch holds up to 8 tensors and fewer than 2^31 jobs
+    if (n == kMaxDecodeBatch || jobs + static_cast<uint64_t>(nj) >= (1ull << 31)) {
+      b.first_job[n] = static_cast<uint32_t>(jobs);
+      b.count = n;
+      const int32_t s = launch_batch(b, st);
+      if (s != BINADE_OK) return s;
+      b = RiceBatch{};
+      n = 0;
+      jobs = 0;
     }
-    if (blocks > 0x7FFFFFFFull) return BINADE_EUNSUPPORTED;
-    b.first_block[n] = static_cast<uint32_t>(blocks);
+    if (static_cast<uint64_t>(nj) >= (1ull << 31)) return BINADE_EUNSUPPORTED;
+    b.item[n] = a;
+    b.first_job[n] = static_cast<uint32_t>(jobs);
+    jobs += static_cast<uint64_t>(nj);
+    ++n;
+  }
+  if (n > 0) {
+    b.first_job[n] = static_cast<uint32_t>(jobs);
     b.count = n;
-    hipLaunchKernelGGL(rice_to_r4_batch_kernel, dim3(static_cast<uint32_t>(blocks)),
-                       dim3(64 * kWavesPerBlock), 0, static_cast<hipStream_t>(stream), b);
-    const int32_t s = launch_status();
-    if (s != BINADE_OK) return s;
+    return launch_batch(b, st);
   }
   return BINADE_OK;
 }
