@@ -538,16 +538,32 @@ __global__ __launch_bounds__(kLargeThreads, WM == 2 && kSplit ? 4 : 2) void gemm
 }
 
 // y[m][n] = ((p0 + p1) + p2) + ... over the S slice partials, in slice order.
+// Block (x, y): row y, columns 1024x .. 1024x+1023, four per thread (one
+// 16-byte load per slice when N is a multiple of 4).
 __global__ __launch_bounds__(256) void gemm_combine_kernel(GemmArgs a) {
+  const int64_t m = blockIdx.y;
+  const int64_t n0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (n0 >= a.n) return;
   const int64_t mn = a.m * a.n;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < mn;
-       e += stride) {
-    float v = a.part[e];
-    for (int32_t s = 1; s < a.slices; ++s) v = v + a.part[s * mn + e];
-    const int64_t m = e / a.n;
-    store_out(a, m, e - m * a.n, v);
+  const float* p = a.part + m * a.n + n0;
+  float v[4];
+  if ((a.n & 3) == 0) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    for (int32_t s = 1; s < a.slices; ++s) {
+      const float4 r = *reinterpret_cast<const float4*>(p + s * mn);
+      v[0] = v[0] + r.x; v[1] = v[1] + r.y; v[2] = v[2] + r.z; v[3] = v[3] + r.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = n0 + i < a.n ? p[i] : 0.0f;
+    for (int32_t s = 1; s < a.slices; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n0 + i < a.n) v[i] = v[i] + p[s * mn + i];
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) store_out(a, m, n0 + i, v[i]);
 }
 
 int32_t check_xy(const uint16_t* x, int64_t m, int64_t ldx, void* y,
@@ -658,10 +674,8 @@ int32_t launch(GemmArgs a, bool r4, void* workspace, int64_t workspace_bytes,
   else r4 ? launch_large<true, 4>(a, p.split, p.blocks, stream)
           : launch_large<false, 4>(a, p.split, p.blocks, stream);
   if (p.split) {
-    const int64_t mn = a.m * a.n;
-    const int64_t cb = min((mn + 255) / 256, static_cast<int64_t>(4096));
-    hipLaunchKernelGGL(gemm_combine_kernel, dim3(static_cast<uint32_t>(cb)), dim3(256), 0,
-                       stream, a);
+    const dim3 cg(static_cast<uint32_t>((a.n + 1023) / 1024), static_cast<uint32_t>(a.m));
+    hipLaunchKernelGGL(gemm_combine_kernel, cg, dim3(256), 0, stream, a);
   }
   return launch_status();
 }

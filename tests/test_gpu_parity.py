@@ -244,7 +244,7 @@ def test_moe_shared_experts_and_bad_index():
 
 # ---------------------------------------------------------- GEMM
 @pytest.mark.parametrize("mnk", [(16, 64, 64), (33, 200, 96), (128, 384, 3840), (5, 70, 4160),
-                                 (300, 136, 4160), (260, 40, 96)])
+                                 (300, 136, 4160), (260, 40, 96), (130, 70, 4160)])
 def test_gemm_small_integers_exact_and_twin(mnk):
     M, N, K = mnk
     g = torch.Generator().manual_seed(M * N)
