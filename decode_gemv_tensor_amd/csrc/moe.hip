@@ -11,9 +11,10 @@
 // l + 64, ...); shorter rows are packed 64 / 2^ceil(log2 J) to a wave, one
 // lane group per row, lane i of a group holding tile i. Block row y takes
 // the y-th expert that some pair chose (the block finds the chosen set from
-// idx in LDS), so experts nobody chose cost no blocks. A wave then finds,
-// with one ballot per 64 pairs, the pairs that chose its expert and walks
-// its rows once per pair: lane tiles rebuilt with v_perm_b32 table lookups,
+// idx in LDS), so experts nobody chose cost no blocks. A wave takes 2 row
+// sets (whole-wave rows) or 4 (packed rows), finds with one ballot per 64
+// pairs the pairs that chose its expert, loads its rows' escape metadata
+// once, and walks each row set once per pair: lane tiles rebuilt with v_perm_b32 table lookups,
 // escapes patched from registers (the wave's escape prefixes and side-list
 // entries are loaded once, a lane each). A second pair of the same expert
 // re-reads the rows the wave has just read, from cache.
@@ -31,7 +32,10 @@ namespace {
 
 using namespace dev;
 
-constexpr int kPairsPerPass = 1;   // more per pass measured slower (registers)
+// Row sets per wave (MoeArgs::sets): the expert choice and the escape
+// metadata are found once for all of them. Measured best: 2 for whole-wave
+// rows, 4 for packed rows.
+constexpr int kSetsWholeRows = 2, kSetsPackedRows = 4;
 
 struct MoeArgs {
   const uint8_t* w;        // R4 sm plane, or bf16 experts (twin)
@@ -52,6 +56,7 @@ struct MoeArgs {
   uint32_t n_esc;
   uint32_t lut0, lut1, lut2, lut3;   // rotated exponents of ranks 0..15
   int32_t width_log2;      // lanes per row: 6 (a whole wave) or less (packed)
+  int32_t sets;            // row sets per wave
 };
 
 __device__ __forceinline__ void store_out(const MoeArgs& a, int64_t i, float v) {
@@ -142,13 +147,13 @@ __device__ __forceinline__ int32_t chosen_expert(const MoeArgs& a, uint32_t* pre
 // side-list entry e0 + i (ent_lane). Chunk c = (row r, chunk j) of the rows'
 // flat chunk range; only chunks j of this pass are walked.
 __device__ __forceinline__ void moe_patch_regs(uint32_t pre_lane, uint32_t ent_lane, uint32_t e0,
-                                               int n_valid, int C, int j, int wl, int G,
-                                               int lane, uint32_t (&E)[8]) {
+                                               int cbase, int n_valid, int C, int j, int wl,
+                                               int G, int lane, uint32_t (&E)[8]) {
   const int gi = lane >> wl;
   const uint32_t my_tile = G > 1 ? static_cast<uint32_t>(lane & ((1 << wl) - 1))
                                  : static_cast<uint32_t>(lane);
   for (int r = 0; r < n_valid; ++r) {
-    const int c = r * C + j;
+    const int c = cbase + r * C + j;
     const uint32_t lo = __builtin_amdgcn_readlane(pre_lane, c);
     const uint32_t hi = __builtin_amdgcn_readlane(pre_lane, c + 1);
     for (uint32_t q = lo; q < hi; ++q) {
@@ -195,8 +200,9 @@ __device__ __forceinline__ void moe_load(const MoeArgs& a, int64_t grow, int t, 
 template <bool kR4>
 __device__ __forceinline__ void moe_weights(const MoeArgs& a, const MoeRaw<kR4>& r, const Lut& L,
                                             bool regs, uint32_t pre_lane, uint32_t ent_lane,
-                                            uint32_t e0, int64_t grow0, int64_t n_valid, int G,
-                                            int wl, int C, int j, int lane, float (&w)[32]) {
+                                            uint32_t e0, int cbase, int64_t grow0,
+                                            int64_t n_valid, int G, int wl, int C, int j,
+                                            int lane, float (&w)[32]) {
   if (kR4) {
     uint32_t E[8];
     if (regs) {
@@ -206,7 +212,8 @@ __device__ __forceinline__ void moe_weights(const MoeArgs& a, const MoeRaw<kR4>&
         E[2 * q] = lookup4(P[q], L);
         E[2 * q + 1] = lookup4(P[q] >> 4, L);
       }
-      moe_patch_regs(pre_lane, ent_lane, e0, static_cast<int>(n_valid), C, j, wl, G, lane, E);
+      moe_patch_regs(pre_lane, ent_lane, e0, cbase, static_cast<int>(n_valid), C, j, wl, G, lane,
+                     E);
     } else {
       moe_tile_exponents(a, r.nb, L, grow0, n_valid, G, wl, C, j, lane, E);
     }
@@ -233,27 +240,27 @@ __device__ __forceinline__ void moe_weights(const MoeArgs& a, const MoeRaw<kR4>&
   }
 }
 
-// The rows row0 .. row0+G-1 of expert e (G = 1: a whole-wave row). Tiles
-// are loaded per chunk inside each pass over a pair group, which keeps the
+// A wave's rows: a.sets row sets of expert e, set s = rows
+// row0 + s*G .. +G-1 (G = 1: a whole-wave row). The expert, the pairs that
+// chose it and the rows' escape metadata are found once for all the sets;
+// tiles are loaded per chunk inside each pass over a pair, which keeps the
 // register count (and so the waves per SIMD) where this latency-bound
 // kernel wants it.
 template <bool kR4>
-__device__ __forceinline__ void moe_row_set(const MoeArgs& a, const Lut& L, int32_t e, int64_t row0,
-                                            int G, int gi, int ti, int wl, int J, int C,
-                                            int lane, const int32_t* idx_s) {
-  const int64_t n_valid = a.n_rows - row0 < G ? a.n_rows - row0 : G;
-  const bool row_ok = gi < n_valid;
-  const int64_t row = row0 + (row_ok ? gi : 0);
-  const int64_t grow0 = static_cast<int64_t>(e < 0 ? 0 : e) * a.n_rows + row0;
-  const int64_t grow = grow0 + (row - row0);
+__device__ __forceinline__ void moe_rows(const MoeArgs& a, const Lut& L, int32_t e, int64_t row0,
+                                         int G, int gi, int ti, int wl, int J, int C, int lane,
+                                         const int32_t* idx_s) {
+  const int64_t left = a.n_rows - row0;
+  const int64_t n_rows_w = left < G * a.sets ? left : G * a.sets;   // >= 1
+  const int64_t grow_w = static_cast<int64_t>(e < 0 ? 0 : e) * a.n_rows + row0;
 
   // the wave's escape prefixes and side-list entries, in registers when
   // they fit a lane each (the usual case)
-  const int F = static_cast<int>(n_valid) * C;   // chunks of the wave's rows
+  const int F = static_cast<int>(n_rows_w) * C;   // chunks of the wave's rows
   uint32_t pre_lane = 0, ent_lane = 0, e0 = 0;
   bool regs = false;
   if (kR4 && e >= 0 && F + 1 <= 64) {
-    const uint32_t pv = lane <= F ? a.esc_pre[grow0 * C + lane] : 0u;
+    const uint32_t pv = lane <= F ? a.esc_pre[grow_w * C + lane] : 0u;
     pre_lane = pv < a.n_esc ? pv : a.n_esc;
     e0 = __builtin_amdgcn_readlane(pre_lane, 0);
     const uint32_t e1 = __builtin_amdgcn_readlane(pre_lane, F);
@@ -269,65 +276,57 @@ __device__ __forceinline__ void moe_row_set(const MoeArgs& a, const Lut& L, int3
   for (int32_t base = 0; base < a.n_pairs; base += 64) {
     const int32_t p = base + lane;
     const int32_t v = p < a.n_pairs ? (p < kMaxPairsLds ? idx_s[p] : a.idx[p]) : 0;
-    uint64_t mine = e < 0 ? 0ull : __ballot(p < a.n_pairs && v == e);
+    const uint64_t mine_all = e < 0 ? 0ull : __ballot(p < a.n_pairs && v == e);
     const uint64_t badm = __ballot(p < a.n_pairs && (v < 0 || v >= a.n_experts));
     if (badm != 0 && blockIdx.y == 0) {
       // out-of-range indices: flag once and zero those pairs' rows
       if (lane == 0 && row0 == 0 && a.status != nullptr)
         atomicOr(a.status, static_cast<uint32_t>(BINADE_DEV_BAD_INDEX));
       if (((badm >> lane) & 1u) != 0)
-        for (int r = 0; r < n_valid; ++r) store_out(a, static_cast<int64_t>(p) * a.n_rows + row0 + r, 0.0f);
+        for (int64_t r = 0; r < n_rows_w; ++r) store_out(a, static_cast<int64_t>(p) * a.n_rows + row0 + r, 0.0f);
     }
-    while (mine != 0) {
-      // next group of up to 4 pairs, in increasing pair order
-      int32_t pp[kPairsPerPass];
-      int np = 0;
-#pragma unroll
-      for (int g = 0; g < kPairsPerPass; ++g) {
-        pp[g] = -1;
-        if (mine != 0) {
-          const int b = __builtin_ctzll(mine);
-          mine &= mine - 1;
-          pp[g] = base + b;
-          ++np;
-        }
-      }
-      float a0[kPairsPerPass], a1[kPairsPerPass];
-#pragma unroll
-      for (int g = 0; g < kPairsPerPass; ++g) a0[g] = a1[g] = 0.0f;
-      for (int j = 0; j < C; ++j) {
-        const int t = G > 1 ? ti : j * 64 + lane;
-        const bool active = t < J;
-        MoeRaw<kR4> rj;
-        moe_load<kR4>(a, grow, t, active, rj);
-        float w[32];
-        moe_weights<kR4>(a, rj, L, regs, pre_lane, ent_lane, e0, grow0, n_valid, G, wl, C, j,
-                         lane, w);
-        if (!active) continue;
-#pragma unroll
-        for (int g = 0; g < kPairsPerPass; ++g) {
-          if (g >= np) break;
-          const int64_t xrow = a.x_per_slot ? pp[g] : pp[g] / a.top_k;
+    if (mine_all == 0) continue;
+    for (int set = 0; set < a.sets; ++set) {
+      const int64_t set0 = row0 + static_cast<int64_t>(set) * G;
+      if (set0 >= a.n_rows) break;
+      const int64_t n_valid = a.n_rows - set0 < G ? a.n_rows - set0 : G;
+      const bool row_ok = gi < n_valid;
+      const int64_t row = set0 + (row_ok ? gi : 0);
+      const int64_t grow0 = grow_w + (set0 - row0);
+      const int64_t grow = grow0 + (row - set0);
+      const int cbase = set * G * C;   // this set's first chunk in the wave's metadata
+      uint64_t mine = mine_all;
+      while (mine != 0) {
+        const int b = __builtin_ctzll(mine);
+        mine &= mine - 1;
+        const int32_t pp = base + b;
+        float a0 = 0.0f, a1 = 0.0f;
+        for (int j = 0; j < C; ++j) {
+          const int t = G > 1 ? ti : j * 64 + lane;
+          const bool active = t < J;
+          MoeRaw<kR4> rj;
+          moe_load<kR4>(a, grow, t, active, rj);
+          float w[32];
+          moe_weights<kR4>(a, rj, L, regs, pre_lane, ent_lane, e0, cbase, grow0, n_valid, G, wl,
+                           C, j, lane, w);
+          if (!active) continue;
+          const int64_t xrow = a.x_per_slot ? pp : pp / a.top_k;
           float xf[32];
           load_x_tile(a.x + xrow * a.cols, t, xf);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            a0[g] = __builtin_fmaf(w[2 * i], xf[2 * i], a0[g]);
-            a1[g] = __builtin_fmaf(w[2 * i + 1], xf[2 * i + 1], a1[g]);
+            a0 = __builtin_fmaf(w[2 * i], xf[2 * i], a0);
+            a1 = __builtin_fmaf(w[2 * i + 1], xf[2 * i + 1], a1);
           }
         }
-      }
-#pragma unroll
-      for (int g = 0; g < kPairsPerPass; ++g) {
-        if (g >= np) break;
-        float r = a0[g] + a1[g];
+        float r = a0 + a1;
         if (G == 1) {
           r = slot_tree(r);
         } else {
           r = r + 0.0f;   // the tree levels whose partner slots hold no tile
           for (int sh = (1 << wl) >> 1; sh >= 1; sh >>= 1) r = r + __shfl_xor(r, sh, 64);
         }
-        if (ti == 0 && row_ok) store_out(a, static_cast<int64_t>(pp[g]) * a.n_rows + row, r);
+        if (ti == 0 && row_ok) store_out(a, static_cast<int64_t>(pp) * a.n_rows + row, r);
       }
     }
   }
@@ -349,9 +348,10 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(MoeArgs a) {
   const int J = a.cols >> 5;
   const int C = (J + 63) >> 6;
   const Lut L{a.lut0, a.lut1, a.lut2, a.lut3};
-  const int64_t row0 = uniform64((static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * G);
+  const int64_t row0 = uniform64((static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * G *
+                                 a.sets);
   if (row0 >= a.n_rows) return;
-  moe_row_set<kR4>(a, L, e, row0, G, gi, ti, wl, J, C, lane, idx_s);
+  moe_rows<kR4>(a, L, e, row0, G, gi, ti, wl, J, C, lane, idx_s);
 }
 
 int32_t launch(MoeArgs a, bool r4, hipStream_t stream) {
@@ -359,7 +359,8 @@ int32_t launch(MoeArgs a, bool r4, hipStream_t stream) {
   int wl = 0;
   while ((1 << wl) < J && wl < 6) ++wl;
   a.width_log2 = J > 32 ? 6 : wl;
-  const int64_t rows_per_block = 4ll * (64 >> a.width_log2);
+  a.sets = a.width_log2 == 6 ? kSetsWholeRows : kSetsPackedRows;
+  const int64_t rows_per_block = 4ll * (64 >> a.width_log2) * a.sets;
   // grid y: one block row per chosen expert (at most min(experts, pairs))
   const int64_t slots = a.n_experts < a.n_pairs ? a.n_experts : a.n_pairs;
   const dim3 grid(static_cast<uint32_t>((a.n_rows + rows_per_block - 1) / rows_per_block),
