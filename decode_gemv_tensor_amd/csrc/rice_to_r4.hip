@@ -105,42 +105,30 @@ static_assert(kByteNib % 4 == 0 && kWaveWords % 4 == 0, "16-byte aligned LDS reg
 // bit of each weight's nibble in R4 order (weight i -> byte i % 4, high
 // nibble for i >= 4).
 constexpr int32_t kNoCode = -(1 << 30);
-struct ByteTables {
-  uint32_t codes[2][256][4];
-  uint32_t spread[256];
-};
-
-constexpr ByteTables make_byte_tables() {
-  ByteTables t{};
-  for (int k = 0; k < 2; ++k) {
-    for (int b = 0; b < 256; ++b) {
-      uint32_t nib = 0;
-      int m = 0, prev = -1, first = 0;
-      for (int i = 0; i < 8; ++i) {
-        if (((b >> i) & 1) == 0) continue;
-        if (m == 0)
-          first = i;
-        else
-          nib |= static_cast<uint32_t>((i - prev - 1) << k) << (4 * m);
-        prev = i;
-        ++m;
-      }
-      t.codes[k][b][0] = nib;
-      t.codes[k][b][1] = m ? static_cast<uint32_t>(first << k) : static_cast<uint32_t>(kNoCode);
-      t.codes[k][b][2] = 4u * static_cast<uint32_t>(m);
-      t.codes[k][b][3] = m ? static_cast<uint32_t>((7 - prev) << k) : 0x7FFFFFFFu;
-    }
+// The table entry of byte value b for Rice parameter k (words as above),
+// computed by each thread of a block for its own b (no table in memory).
+__device__ __forceinline__ uint4 byte_entry(uint32_t k, uint32_t b) {
+  uint32_t nib = 0, m = 0, first = 0, prev = 0;
+#pragma unroll
+  for (uint32_t i = 0; i < 8; ++i) {
+    if (((b >> i) & 1u) == 0u) continue;
+    if (m == 0)
+      first = i;
+    else
+      nib |= ((i - prev - 1u) << k) << (4u * m);
+    prev = i;
+    ++m;
   }
-  for (int r = 0; r < 256; ++r) {
-    uint32_t v = 0;
-    for (int i = 0; i < 8; ++i)
-      if ((r >> i) & 1) v |= 1u << (8 * (i & 3) + 4 * (i >> 2));
-    t.spread[r] = v;
-  }
-  return t;
+  return make_uint4(nib, m ? first << k : static_cast<uint32_t>(kNoCode), 4u * m,
+                    m ? (7u - prev) << k : 0x7FFFFFFFu);
 }
 
-__device__ const ByteTables kByteTables = make_byte_tables();
+__device__ __forceinline__ uint32_t spread_entry(uint32_t r) {
+  uint32_t v = 0;
+#pragma unroll
+  for (uint32_t i = 0; i < 8; ++i) v |= ((r >> i) & 1u) << (8u * (i & 3u) + 4u * (i >> 2));
+  return v;
+}
 
 struct RiceArgs {
   const uint32_t* unary;
@@ -702,10 +690,11 @@ __device__ __forceinline__ void byte_walk(const uint32_t (&x)[4], int32_t c, uin
 #pragma unroll
     for (int jj = 0; jj < kGroup; ++jj) {
       const int j = j0 + jj;
-      e[jj] = lut[__builtin_amdgcn_ubfe(x[j >> 2], 8 * (j & 3), 8)];
+      if (j < kSteps) e[jj] = lut[__builtin_amdgcn_ubfe(x[j >> 2], 8 * (j & 3), 8)];
     }
 #pragma unroll
     for (int jj = 0; jj < kGroup; ++jj) {
+      if (j0 + jj >= kSteps) break;
       const int32_t t = static_cast<int32_t>(e[jj].y) + c;     // first code's q << K
       if (t >= kThr) {
         // rare: the first code may be an escape
@@ -824,7 +813,7 @@ __device__ __forceinline__ void decode_job_bytes(const RiceArgs& a, const uint8_
   uint32_t* nibw = lds + kByteNib;
   uint32_t* slots = lds + kByteSlotOff + lane;
   uint32_t* ctr = lds + kByteCtrOff + lane;
-  const int64_t c0 = job.c0, cnt = job.cnt;
+  const int64_t cnt = job.cnt;
   const int32_t Lc = job.len;
   const int32_t T = Lc >> 5;
   const uint64_t A = f.A, B = f.B;
@@ -925,6 +914,12 @@ __device__ __forceinline__ void decode_job_bytes(const RiceArgs& a, const uint8_
   else if (spl <= 8u)
     byte_walk<K, 8, false>(x, c_in, sb0, lut, remw, a.n, nb, ctr, slots, limit, table, chunk_mod,
                            nullptr, unused);
+  else if (spl <= 12u)
+    byte_walk<K, 12, false>(x, c_in, sb0, lut, remw, a.n, nb, ctr, slots, limit, table,
+                            chunk_mod, nullptr, unused);
+  else if (spl <= 14u)
+    byte_walk<K, 14, false>(x, c_in, sb0, lut, remw, a.n, nb, ctr, slots, limit, table,
+                            chunk_mod, nullptr, unused);
   else
     byte_walk<K, 16, false>(x, c_in, sb0, lut, remw, a.n, nb, ctr, slots, limit, table,
                             chunk_mod, nullptr, unused);
@@ -1004,13 +999,12 @@ __device__ __forceinline__ void decode_job_bytes(const RiceArgs& a, const uint8_
   }
 }
 
-// The byte tables for Rice k = 1 (the byte-table path's k), one entry per
+// The byte tables for Rice k = 1 (the byte-table path's k), computed, one entry per
 // thread of the 256-thread block.
 __device__ __forceinline__ void load_byte_tables(uint4* lut, uint32_t* spread) {
-  const int t = threadIdx.x;
-  const uint32_t* src = kByteTables.codes[1][t];
-  lut[t] = make_uint4(src[0], src[1], src[2], src[3]);
-  spread[t] = kByteTables.spread[t];
+  const uint32_t t = threadIdx.x;
+  lut[t] = byte_entry(1u, t);
+  spread[t] = spread_entry(t);
   __syncthreads();
 }
 
