@@ -61,7 +61,19 @@ GEMV_SHAPES = [(1024, 1024, 0.02, 0, 0.0, 1.0, 16, 50.0),   # single 1024 tensor
                (4100, 256, 0.015, 6, 0.0, 1.0, 0, 1.0)]       # short rows, many
 
 
-@pytest.mark.parametrize("shape", GEMV_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+# Decode jobs: two row-chunks of a row, or 2 * (2048 / cols) short rows.
+# Edge cases of that mapping: rows of exactly one chunk, a 32-column second
+# chunk, an odd chunk count, 32 short rows per job (31 inner chunk starts),
+# one row per run, and rows too short for the byte-table path.
+DECODE_SHAPES = [(9, 2048, 0.02, 7, 1e-3, 20.0, 0, 1.0),
+                 (7, 2080, 0.02, 8, 2e-3, 1e3, 0, 1.0),
+                 (11, 6144, 0.02, 9, 1e-3, 20.0, 0, 1.0),
+                 (130, 128, 0.02, 10, 5e-3, 1e3, 0, 1.0),
+                 (33, 1344, 0.015, 11, 1e-3, 20.0, 0, 1.0),
+                 (50, 64, 0.02, 12, 1e-2, 1e3, 0, 1.0)]
+
+
+@pytest.mark.parametrize("shape", GEMV_SHAPES + DECODE_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
 def test_rice_to_r4_is_byte_exact_and_unpacks(shape):
     rows, cols, sigma, seed, frac, scale, count, cscale = shape
     sp = spec(rows, cols, sigma, seed, frac, scale if count == 0 else cscale, count)
