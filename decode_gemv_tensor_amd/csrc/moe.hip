@@ -6,18 +6,19 @@
 // expert idx[p]; its output row is that expert's matvec of the pair's input,
 // with exactly the binade_r4_gemv order.
 //
-// Mapping: block (g, e) covers a group of rows of expert e. A row of J lane
-// tiles (32 columns each) with J > 32 takes a whole wave (lane l: tiles l,
-// l + 64, ...); shorter rows are packed 64 / 2^ceil(log2 J) to a wave, one
-// lane group per row, lane i of a group holding tile i. Block row y takes
-// the y-th expert that some pair chose (the block finds the chosen set from
-// idx in LDS), so experts nobody chose cost no blocks. A wave takes 2 row
-// sets (whole-wave rows) or 4 (packed rows), finds with one ballot per 64
-// pairs the pairs that chose its expert, loads its rows' escape metadata
-// once, and walks each row set once per pair: lane tiles rebuilt with v_perm_b32 table lookups,
-// escapes patched from registers (the wave's escape prefixes and side-list
-// entries are loaded once, a lane each). A second pair of the same expert
-// re-reads the rows the wave has just read, from cache.
+// Mapping: a row of J lane tiles (32 columns each) with J > 32 takes a
+// whole wave (lane l: tiles l, l + 64, ...); shorter rows are packed
+// 64 / 2^ceil(log2 J) to a wave, one lane group per row, lane i of a group
+// holding tile i. The blocks are persistent: each finds the set of chosen
+// experts once (a bit per expert from idx, in LDS, with per-word counts),
+// so experts nobody chose cost nothing; waves then take jobs (u-th chosen
+// expert, row group of 2 row sets for whole-wave rows or 4 for packed rows)
+// in turn. A job finds with one ballot per 64 pairs the pairs that chose its
+// expert, loads its rows' escape metadata once (escape prefixes and
+// side-list entries, a lane each), and walks each row set once per pair:
+// lane tiles rebuilt with v_perm_b32 table lookups, escapes patched from
+// registers. A second pair of the same expert re-reads the rows the wave
+// has just read, from cache.
 //
 // A packed row's slots 32, 16, ... down to its group width hold no tile, so
 // the matvec's tree adds +0.0 to each of the group's slots at those levels;
@@ -35,7 +36,13 @@ using namespace dev;
 // Row sets per wave (MoeArgs::sets): the expert choice and the escape
 // metadata are found once for all of them. Measured best: 2 for whole-wave
 // rows, 4 for packed rows.
-constexpr int kSetsWholeRows = 2, kSetsPackedRows = 4;
+#ifndef BINADE_MOE_SETS_WHOLE
+#define BINADE_MOE_SETS_WHOLE 2
+#endif
+#ifndef BINADE_MOE_SETS_PACKED
+#define BINADE_MOE_SETS_PACKED 4
+#endif
+constexpr int kSetsWholeRows = BINADE_MOE_SETS_WHOLE, kSetsPackedRows = BINADE_MOE_SETS_PACKED;
 
 struct MoeArgs {
   const uint8_t* w;        // R4 sm plane, or bf16 experts (twin)
@@ -57,6 +64,7 @@ struct MoeArgs {
   uint32_t lut0, lut1, lut2, lut3;   // rotated exponents of ranks 0..15
   int32_t width_log2;      // lanes per row: 6 (a whole wave) or less (packed)
   int32_t sets;            // row sets per wave
+  int64_t groups;          // row groups (of sets row sets) per expert
 };
 
 __device__ __forceinline__ void store_out(const MoeArgs& a, int64_t i, float v) {
@@ -103,43 +111,61 @@ __device__ __forceinline__ void moe_tile_exponents(const MoeArgs& a, uint4 nb, c
 constexpr int kMaxExpertWords = 2048;   // experts <= 65536
 constexpr int kMaxPairsLds = 2048;      // idx values kept in LDS
 
-// The rank-th expert (increasing index) that some pair chose, or -1; every
-// thread of the block takes part. Out-of-range indices are not experts.
-__device__ __forceinline__ int32_t chosen_expert(const MoeArgs& a, uint32_t* present,
-                                                 int32_t* idx_s, int32_t* picked, int32_t rank) {
+// Block setup, once per block: the set of experts some pair chose (a bit per
+// expert) and, per 32-expert word, the count of chosen experts before it;
+// *n_chosen = their number, *any_bad = whether an index is out of range.
+// Every thread of the block takes part.
+__device__ __forceinline__ void chosen_set(const MoeArgs& a, uint32_t* present, uint32_t* before,
+                                           int32_t* idx_s, uint32_t* n_chosen,
+                                           uint32_t* any_bad) {
   const int nw = (a.n_experts + 31) >> 5;
   for (int i = threadIdx.x; i < nw; i += blockDim.x) present[i] = 0u;
-  if (threadIdx.x == 0) *picked = -1;
+  if (threadIdx.x == 0) *any_bad = 0u;
   __syncthreads();
   for (int32_t p = threadIdx.x; p < a.n_pairs; p += blockDim.x) {
     const int32_t v = a.idx[p];
     if (p < kMaxPairsLds) idx_s[p] = v;
-    if (v >= 0 && v < a.n_experts) atomicOr(&present[v >> 5], 1u << (v & 31));
+    if (v >= 0 && v < a.n_experts)
+      atomicOr(&present[v >> 5], 1u << (v & 31));
+    else
+      *any_bad = 1u;
   }
   __syncthreads();
   if (threadIdx.x < 64) {
-    // wave 0: prefix count of set bits over the words, 64 words at a time
-    int32_t before = 0;
+    // wave 0: exclusive prefix count of set bits over the words
+    uint32_t acc = 0;
     for (int base = 0; base < nw; base += 64) {
       const int i = base + static_cast<int>(threadIdx.x);
-      const uint32_t word = i < nw ? present[i] : 0u;
-      const int32_t c = __popc(word);
-      int32_t incl = c;
+      const uint32_t c = i < nw ? __popc(present[i]) : 0u;
+      uint32_t incl = c;
       for (int sh = 1; sh < 64; sh <<= 1) {
-        const int32_t o = __shfl_up(incl, sh, 64);
+        const uint32_t o = __shfl_up(incl, sh, 64);
         if (static_cast<int>(threadIdx.x) >= sh) incl += o;
       }
-      const int32_t excl = before + incl - c;
-      if (rank >= excl && rank < excl + c) {
-        uint32_t w = word;
-        for (int32_t k = rank - excl; k > 0; --k) w &= w - 1u;
-        *picked = (i << 5) + __builtin_ctz(w);
-      }
-      before += __shfl(incl, 63, 64);
+      if (i < nw) before[i] = acc + incl - c;
+      acc += __shfl(incl, 63, 64);
     }
+    if (threadIdx.x == 0) *n_chosen = acc;
   }
   __syncthreads();
-  return *picked;
+}
+
+// The u-th chosen expert (increasing index), u < n_chosen: the last word
+// whose count before it is <= u, then the matching set bit in it.
+__device__ __forceinline__ int32_t chosen_expert(const MoeArgs& a, const uint32_t* present,
+                                                 const uint32_t* before, uint32_t u) {
+  const int nw = (a.n_experts + 31) >> 5;
+  int lo = 0, hi = nw - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (before[mid] <= u)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  uint32_t w = present[lo];
+  for (uint32_t k = u - before[lo]; k > 0; --k) w &= w - 1u;
+  return (lo << 5) + __builtin_ctz(w);
 }
 
 // The same patches from registers: lane c holds the escape prefix of the
@@ -276,15 +302,7 @@ __device__ __forceinline__ void moe_rows(const MoeArgs& a, const Lut& L, int32_t
   for (int32_t base = 0; base < a.n_pairs; base += 64) {
     const int32_t p = base + lane;
     const int32_t v = p < a.n_pairs ? (p < kMaxPairsLds ? idx_s[p] : a.idx[p]) : 0;
-    const uint64_t mine_all = e < 0 ? 0ull : __ballot(p < a.n_pairs && v == e);
-    const uint64_t badm = __ballot(p < a.n_pairs && (v < 0 || v >= a.n_experts));
-    if (badm != 0 && blockIdx.y == 0) {
-      // out-of-range indices: flag once and zero those pairs' rows
-      if (lane == 0 && row0 == 0 && a.status != nullptr)
-        atomicOr(a.status, static_cast<uint32_t>(BINADE_DEV_BAD_INDEX));
-      if (((badm >> lane) & 1u) != 0)
-        for (int64_t r = 0; r < n_rows_w; ++r) store_out(a, static_cast<int64_t>(p) * a.n_rows + row0 + r, 0.0f);
-    }
+    const uint64_t mine_all = __ballot(p < a.n_pairs && v == e);
     if (mine_all == 0) continue;
     for (int set = 0; set < a.sets; ++set) {
       const int64_t set0 = row0 + static_cast<int64_t>(set) * G;
@@ -332,15 +350,17 @@ __device__ __forceinline__ void moe_rows(const MoeArgs& a, const Lut& L, int32_t
   }
 }
 
+// Persistent blocks: the chosen set is found once per block; wave w then
+// takes the jobs w, w + W, ... (W waves in the grid), job = (u-th chosen
+// expert, row group) with a.groups row groups per expert.
 template <bool kR4>
 __global__ __launch_bounds__(256) void moe_gemv_kernel(MoeArgs a) {
   __shared__ uint32_t present[kMaxExpertWords];
+  __shared__ uint32_t before[kMaxExpertWords];
   __shared__ int32_t idx_s[kMaxPairsLds];
-  __shared__ int32_t picked;
+  __shared__ uint32_t n_chosen, any_bad;
+  chosen_set(a, present, before, idx_s, &n_chosen, &any_bad);
   const int lane = threadIdx.x & 63;
-  const int32_t e =
-      uniform(chosen_expert(a, present, idx_s, &picked, static_cast<int32_t>(blockIdx.y)));
-  if (e < 0 && blockIdx.y != 0) return;
   const int wl = a.width_log2;
   const int G = 64 >> wl;                       // rows per row set
   const int gi = lane >> wl;                    // this lane's row in the set
@@ -348,10 +368,56 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(MoeArgs a) {
   const int J = a.cols >> 5;
   const int C = (J + 63) >> 6;
   const Lut L{a.lut0, a.lut1, a.lut2, a.lut3};
-  const int64_t row0 = uniform64((static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * G *
-                                 a.sets);
-  if (row0 >= a.n_rows) return;
-  moe_rows<kR4>(a, L, e, row0, G, gi, ti, wl, J, C, lane, idx_s);
+  const uint32_t U = uniform(n_chosen);
+  const uint64_t jobs = static_cast<uint64_t>(U) * a.groups;
+  const uint64_t W = static_cast<uint64_t>(gridDim.x) * (blockDim.x >> 6);
+  for (uint64_t job = uniform64(static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) +
+                                (threadIdx.x >> 6));
+       job < jobs; job += W) {
+    const uint32_t u = static_cast<uint32_t>(job / a.groups);
+    const int32_t e = uniform(chosen_expert(a, present, before, u));
+    const int64_t row0 = static_cast<int64_t>(job - static_cast<uint64_t>(u) * a.groups) * G *
+                         a.sets;
+    moe_rows<kR4>(a, L, e, row0, G, gi, ti, wl, J, C, lane, idx_s);
+  }
+  if (uniform(any_bad) != 0u) {
+    // out-of-range indices: flag once, and zero those pairs' rows (rows
+    // dealt to the blocks in equal ranges)
+    if (blockIdx.x == 0 && threadIdx.x == 0 && a.status != nullptr)
+      atomicOr(a.status, static_cast<uint32_t>(BINADE_DEV_BAD_INDEX));
+    const int64_t per = (a.n_rows + gridDim.x - 1) / gridDim.x;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * per;
+    const int64_t r1 = r0 + per < a.n_rows ? r0 + per : a.n_rows;
+    for (int32_t p = 0; p < a.n_pairs; ++p) {
+      const int32_t v = p < kMaxPairsLds ? idx_s[p] : a.idx[p];
+      if (v >= 0 && v < a.n_experts) continue;
+      for (int64_t r = r0 + threadIdx.x; r < r1; r += blockDim.x)
+        store_out(a, static_cast<int64_t>(p) * a.n_rows + r, 0.0f);
+    }
+  }
+}
+
+// Blocks of the persistent MoE kernel that fit on the current device at once
+// (queried once per device and kind).
+int32_t resident_blocks(bool r4, int64_t& blocks) {
+  static int64_t cached[2][64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return launch_status();
+  if (dev < 64 && cached[r4][dev] > 0) {
+    blocks = cached[r4][dev];
+    return BINADE_OK;
+  }
+  int per_cu = 0, cus = 0;
+  const hipError_t q = r4 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                                &per_cu, moe_gemv_kernel<true>, 256, 0)
+                          : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                                &per_cu, moe_gemv_kernel<false>, 256, 0);
+  if (q != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return launch_status();
+  blocks = static_cast<int64_t>(per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+  if (dev < 64) cached[r4][dev] = blocks;
+  return BINADE_OK;
 }
 
 int32_t launch(MoeArgs a, bool r4, hipStream_t stream) {
@@ -360,15 +426,22 @@ int32_t launch(MoeArgs a, bool r4, hipStream_t stream) {
   while ((1 << wl) < J && wl < 6) ++wl;
   a.width_log2 = J > 32 ? 6 : wl;
   a.sets = a.width_log2 == 6 ? kSetsWholeRows : kSetsPackedRows;
-  const int64_t rows_per_block = 4ll * (64 >> a.width_log2) * a.sets;
-  // grid y: one block row per chosen expert (at most min(experts, pairs))
-  const int64_t slots = a.n_experts < a.n_pairs ? a.n_experts : a.n_pairs;
-  const dim3 grid(static_cast<uint32_t>((a.n_rows + rows_per_block - 1) / rows_per_block),
-                  static_cast<uint32_t>(slots));
+  const int64_t rows_per_group = static_cast<int64_t>(64 >> a.width_log2) * a.sets;
+  a.groups = (a.n_rows + rows_per_group - 1) / rows_per_group;
+  // at most min(experts, pairs) experts are chosen
+  const int64_t chosen_max = a.n_experts < a.n_pairs ? a.n_experts : a.n_pairs;
+  const int64_t waves = chosen_max * a.groups;
+  int64_t resident = 0;
+  const int32_t st = resident_blocks(r4, resident);
+  if (st != BINADE_OK) return st;
+  const int64_t need = (waves + 3) / 4;
+  const int64_t blocks = need < resident ? (need > 0 ? need : 1) : resident;
   if (r4)
-    hipLaunchKernelGGL(moe_gemv_kernel<true>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(moe_gemv_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL(moe_gemv_kernel<false>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(moe_gemv_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       stream, a);
   return launch_status();
 }
 
