@@ -93,6 +93,19 @@ class Timer:
     def count(self, key):
         return len(self.pairs.get(key, []))
 
+    def spread_us(self, key):
+        """p10 / median / p90 of the single intervals, in us."""
+        v = [a.elapsed_time(b) * 1e3 for a, b in self.pairs.get(key, [])]
+        return {k: round(x, 3) for k, x in spread(v).items()}
+
+
+def spread(v) -> dict:
+    v = sorted(v)
+    if not v:
+        return {}
+    at = lambda q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+    return {"p10": at(0.1), "median": at(0.5), "p90": at(0.9)}
+
 
 def host_cores_used() -> int:
     return 1
@@ -142,9 +155,10 @@ def copy_probe(dev) -> None:
     log(f"copy probe: 5 x {n * 4} bytes read and written")
 
 
-def graph_time_ms(stream, body, reps: int = 3) -> float:
-    """Best of `reps` replays of `body` captured once in a HIP graph, in ms
-    (events recorded on the stream the graph replays on)."""
+def graph_replays_ms(stream, body, reps: int = 15) -> list:
+    """`body` captured once in a HIP graph and replayed `reps` times; the
+    duration of each replay in ms (events recorded on the stream the graph
+    replays on)."""
     with torch.cuda.stream(stream):
         body()
     torch.cuda.synchronize()
@@ -154,7 +168,7 @@ def graph_time_ms(stream, body, reps: int = 3) -> float:
     with torch.cuda.stream(stream):
         g.replay()
     torch.cuda.synchronize()
-    best = None
+    out = []
     for _ in range(reps):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -163,46 +177,104 @@ def graph_time_ms(stream, body, reps: int = 3) -> float:
             g.replay()
             e1.record(stream)
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        best = ms if best is None else min(best, ms)
-    return best
+        out.append(e0.elapsed_time(e1))
+    del g
+    return out
+
+
+def graph_time_ms(stream, body, reps: int = 15) -> float:
+    """Median replay of `body` captured in a HIP graph, in ms."""
+    return spread(graph_replays_ms(stream, body, reps))["median"]
 
 
 def r4_bytes(r4: B.R4Tensor) -> int:
     return r4.rows * r4.cols * 3 // 2 + 4 * r4.n_esc + 4 * r4.esc_pre.numel()
 
 
+ROTATE_BYTES = 1 << 30   # working set per timed GEMM replay: well past the 256 MiB last-level cache
+
+
+def r4_replica(r4: B.R4Tensor) -> B.R4Tensor:
+    return B.R4Tensor(r4.rows, r4.cols, r4.lut, r4.sm.clone(), r4.nib.clone(),
+                      r4.esc_pre.clone(), r4.esc.clone(), r4.n_esc)
+
+
 def measure_gemm(dev, stream) -> dict:
-    """Prompt GEMM on the 12B-class FFN shapes (R4 and its bf16 twin), each
-    shape and M timed as 10 launches in one HIP graph (with the workspace the
-    shape asks for, allocated once); outputs checked equal."""
+    """Prompt GEMM on the 12B-class FFN shapes (R4 and its bf16 twin).
+
+    Each HIP-graph replay runs one launch on each of several weight copies, so
+    that the replay reads at least 1 GiB of weights and no launch finds its
+    weights in the last-level cache; the median replay is reported with p10 /
+    p90, and cache-hot figures (one copy launched ten times) beside it.
+    torch.nn.functional.linear on the same bf16 weights (bf16 output, the
+    vendor BLAS) is timed the same way as an outside reference; it is not
+    bit-identical to the path. Outputs of R4 and twin are checked equal."""
     out = {}
     for spec in synth.gemma_12b_ffn()[1:]:   # up 15360x3840, down 3840x15360
         w = synth.normal_bf16(spec, device=dev)
         r4 = B.rice_to_r4(B.pack_rice(w.cpu()).to(dev))
         N, K = spec.rows, spec.cols
+        n_r4 = -(-ROTATE_BYTES // r4.nbytes())
+        n_bf = -(-ROTATE_BYTES // (2 * N * K))
+        r4s = [r4] + [r4_replica(r4) for _ in range(n_r4 - 1)]
+        wts = [w] + [w.clone() for _ in range(n_bf - 1)]
         for M in synth.GEMM_ROWS:
             x = synth.vector_bf16(K, 500 + M, device=dev, count=M)
             y = torch.empty(M, N, dtype=torch.float32, device=dev)
             y2 = torch.empty_like(y)
             ws = torch.empty(B.gemm_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
-            reps = 10 if M < 2048 else 3
-            tr = graph_time_ms(stream, lambda: [B.r4_gemm(r4, x, y=y, stream=stream, workspace=ws)
-                                                for _ in range(reps)]) / reps
-            tt = graph_time_ms(stream, lambda: [B.bf16_gemm(w, x, y=y2, stream=stream,
-                                                            workspace=ws)
-                                                for _ in range(reps)]) / reps
+            reps = 5 if M >= 2048 else 15
+
+            def r4_rot():
+                for t in r4s:
+                    B.r4_gemm(t, x, y=y, stream=stream, workspace=ws)
+
+            def bf_rot():
+                for t in wts:
+                    B.bf16_gemm(t, x, y=y2, stream=stream, workspace=ws)
+
+            def lin_rot():
+                for t in wts:
+                    torch.nn.functional.linear(x, t)
+
+            def r4_hot():
+                for _ in range(10):
+                    B.r4_gemm(r4, x, y=y, stream=stream, workspace=ws)
+
+            def bf_hot():
+                for _ in range(10):
+                    B.bf16_gemm(w, x, y=y2, stream=stream, workspace=ws)
+
+            def per_launch(body, n):
+                v = graph_replays_ms(stream, body, reps)
+                return {k: x_ / n for k, x_ in spread(v).items()}
+
+            tr = per_launch(r4_rot, len(r4s))
+            tt = per_launch(bf_rot, len(wts))
+            tl = per_launch(lin_rot, len(wts))
+            hr = per_launch(r4_hot, 10)
+            ht = per_launch(bf_hot, 10)
             torch.cuda.synchronize()
             if not torch.equal(y.view(torch.int32), y2.view(torch.int32)):
                 raise SystemExit(f"parity gate: R4 GEMM differs from its twin ({N}x{K}, M={M})")
             fl = 2.0 * M * N * K
             nbytes = r4_bytes(r4) + 2 * M * K + 4 * M * N
+            m = tr["median"]
+            us = lambda d: {k: round(v * 1e3, 2) for k, v in d.items()}
             out[f"{N}x{K}_M{M}"] = {
-                "r4_us": round(tr * 1e3, 2), "r4_TFLOPs": round(fl / tr / 1e9, 1),
-                "mfma_frac": round(fl / tr / 1e9 / MFMA_BF16_PEAK_TFS, 4),
-                "r4_GBs": round(nbytes / tr / 1e6, 1),
-                "bf16_twin_us": round(tt * 1e3, 2), "speedup_vs_twin": round(tt / tr, 3)}
-        del w, r4
+                "r4_us": round(m * 1e3, 2), "r4_us_spread": us(tr),
+                "r4_TFLOPs": round(fl / m / 1e9, 1),
+                "mfma_frac": round(fl / m / 1e9 / MFMA_BF16_PEAK_TFS, 4),
+                "r4_GBs": round(nbytes / m / 1e6, 1),
+                "bf16_twin_us": round(tt["median"] * 1e3, 2), "bf16_twin_us_spread": us(tt),
+                "speedup_vs_twin": round(tt["median"] / m, 3),
+                "torch_linear_bf16_us": round(tl["median"] * 1e3, 2),
+                "speedup_vs_torch_linear": round(tl["median"] / m, 3),
+                "cache_hot": {"r4_us": round(hr["median"] * 1e3, 2),
+                              "bf16_twin_us": round(ht["median"] * 1e3, 2)},
+                "weight_copies": {"r4": len(r4s), "bf16": len(wts)}}
+        del w, r4, r4s, wts
+        torch.cuda.empty_cache()
     return out
 
 
@@ -488,7 +560,12 @@ def main():
                 if rc:
                     raise B.BinadeError("binade_bf16_gemv_batch", rc)
 
+        def torch_linear():
+            for t in tensors:
+                torch.nn.functional.linear(xs[t["spec"].cols].view(1, -1), t["w"])
+
         twin_b = sum(twin_bytes(t["spec"].rows, t["spec"].cols) for t in tensors)
+        lin_ms = graph_ms(torch_linear)
         r4s_ms = graph_ms(r4_single)
         twin_ms = graph_ms(bf16_single)
         r4b_ms = graph_ms(r4_batched)
@@ -502,7 +579,13 @@ def main():
                     "speedup": round(twinb_ms / r4b_ms, 4),
                     "bf16_GBs": round(twin_b / (twinb_ms * 1e-3) / 1e9, 1),
                     "r4_GBs": round(gemv_b_total(tensors) / (r4b_ms * 1e-3) / 1e9, 1)},
-                "note": "both sides HIP-graph replays of the same schedule; bytes per side "
+                "torch_linear_bf16": {
+                    "ms_per_token": round(lin_ms, 4),
+                    "GBs": round(twin_b / (lin_ms * 1e-3) / 1e9, 1),
+                    "r4_sixteen_per_launch_speedup": round(lin_ms / r4b_ms, 4),
+                    "note": "nn.functional.linear, bf16 output, one call per tensor; an outside "
+                            "reference, not bit-identical"},
+                "note": "HIP-graph replays of the same schedule, median of 15; bytes per side "
                         "are that side's own weight bytes"}
 
     # ------------------------------------------------------------ GEMM, MoE
@@ -539,11 +622,13 @@ def main():
               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gemv_ach / HBM_PEAK_GBS, 4),
               "traffic": measured_traffic("r4_gemv"), "launches_per_step": n_gemv_launch,
               "avg_launch_us": round(gemv_kernel_ms * 1e3 / n_gemv_launch, 3),
+              "launch_us_spread": timer.spread_us("gemv"),
               "bytes_per_launch": gemv_b // n_gemv_launch}
     roof_d = {"kernel": "rice_to_r4", "bound": "hbm", "achieved": round(dec_ach, 1),
               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_ach / HBM_PEAK_GBS, 4),
               "traffic": measured_traffic("rice_to_r4"), "launches_per_step": n_dec_launch,
               "avg_launch_us": round(dec_kernel_ms * 1e3 / n_dec_launch, 3),
+              "launch_us_spread": timer.spread_us("decode"),
               "bytes_per_launch": dec_b // n_dec_launch,
               "gsym_per_s": round(syms / (dec_kernel_ms * 1e-3) / 1e9, 1)}
     out = {
@@ -554,6 +639,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(step_ms_avg, 4),
+        "step_us_spread": timer.spread_us("step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
