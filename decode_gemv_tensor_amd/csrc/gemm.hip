@@ -37,6 +37,8 @@
 // order.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "binade.h"
 #include "device_common.h"
 
@@ -123,6 +125,84 @@ __device__ __forceinline__ uint4 rebuild8(const GemmArgs& a, const Lut& L, uint2
   uint32_t E0 = lookup4(P, L);
   uint32_t E1 = lookup4(P >> 4, L);
   if (has_escape(P)) patch8(a, n, c0, E0, E1);
+  uint32_t H0, L0, H1, L1;
+  split4_rot(sm.x, E0, H0, L0);
+  split4_rot(sm.y, E1, H1, L1);
+  return make_uint4(weight_pair_bf16<0>(H0, L0), weight_pair_bf16<2>(H0, L0),
+                    weight_pair_bf16<0>(H1, L1), weight_pair_bf16<2>(H1, L1));
+}
+
+// The side-list entries of one weight row over a column range [col0, col1)
+// that touches at most two row-chunks, at most four per chunk, read once
+// before the range is walked, so that an escape is patched from registers.
+// Entry: (rotated exponent << 16) | column - col0; 0xFFFF: none. `over`: the range
+// touches a third chunk or a chunk has more than four entries (then the
+// search of patch8 is used).
+struct EscTab {
+  uint32_t ent[8];
+  uint32_t over;
+};
+
+__device__ __forceinline__ void esc_tab_build(const GemmArgs& a, int64_t n, int32_t col0,
+                                              int32_t col1, EscTab& t) {
+  const int64_t C = (a.k + kChunk - 1) / kChunk;
+  const int32_t j0 = col0 / kChunk, jl = (col1 - 1) / kChunk;
+  uint32_t over = jl > j0 + 1 ? 1u : 0u;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int32_t j = j0 + h;
+    uint32_t eb = 0, ee = 0;
+    if (j <= jl) {
+      ee = a.esc_pre[n * C + j + 1];
+      eb = a.esc_pre[n * C + j];
+      ee = ee < a.n_esc ? ee : a.n_esc;
+      eb = eb < ee ? eb : ee;
+    }
+    if (ee - eb > 4u) over = 1u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t v = 0xFFFFu;
+      if (eb + i < ee) {
+        const uint32_t ent = a.esc[eb + i];
+        const int32_t col = j * kChunk + static_cast<int32_t>(ent & 0xFFFFu);
+        if (col >= col0 && col < col1)
+          v = (rot_exponent((ent >> 16) & 0xFFu) << 16) | static_cast<uint32_t>(col - col0);
+      }
+      t.ent[4 * h + i] = v;
+    }
+  }
+  t.over = over;
+}
+
+// Patch the exponents of columns c .. c+7 (c = col0 + c_rel) from the table.
+__device__ __forceinline__ void esc_tab_patch(const EscTab& t, int32_t c_rel, uint32_t& E0,
+                                              uint32_t& E1) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t d = (t.ent[i] & 0xFFFFu) - static_cast<uint32_t>(c_rel);
+    if (d < 8u) {
+      const uint32_t sh = (d & 3u) * 8u;
+      const uint32_t ex = (t.ent[i] >> 16) << sh;
+      if (d < 4u)
+        E0 = (E0 & ~(0xFFu << sh)) | ex;
+      else
+        E1 = (E1 & ~(0xFFu << sh)) | ex;
+    }
+  }
+}
+
+// rebuild8 with the escapes of the row taken from its table.
+__device__ __forceinline__ uint4 rebuild8_tab(const GemmArgs& a, const Lut& L, uint2 sm,
+                                              uint32_t P, int64_t n, int32_t c0,
+                                              const EscTab& t, int32_t c_rel) {
+  uint32_t E0 = lookup4(P, L);
+  uint32_t E1 = lookup4(P >> 4, L);
+  if (has_escape(P)) {
+    if (t.over)
+      patch8(a, n, c0, E0, E1);
+    else
+      esc_tab_patch(t, c_rel, E0, E1);
+  }
   uint32_t H0, L0, H1, L1;
   split4_rot(sm.x, E0, H0, L0);
   split4_rot(sm.y, E1, H1, L1);
@@ -278,33 +358,284 @@ __global__ __launch_bounds__(512) void gemm_small_kernel(GemmArgs a) {
     for (int i = 0; i < 4; ++i) store_out(a, (mt * MT + t) * 16 + 4 * g + i, on, acc[t][i]);
 }
 
+// ---------------------------------------------------------------- small M, streamed
+// One block per (slice, group of 8 weight-row tiles): the block copies its
+// slice's X columns (16*MT rows) into LDS once, then each wave streams one
+// or more 16-row tiles over the slice's super-blocks, kRing super-blocks of
+// weight loads in flight (the ring runs on across tiles), X operands read
+// from LDS. A tile's slice partial goes to the workspace (or to Y when there
+// is one slice); gemm_combine_kernel adds the slices in order.
+constexpr int kStreamWaves = 8;
+#ifndef BINADE_GEMM_STREAM_RING
+#define BINADE_GEMM_STREAM_RING 2
+#endif
+constexpr int kRing = BINADE_GEMM_STREAM_RING;
+
+template <bool kR4>
+struct StreamRaw;
+template <>
+struct StreamRaw<true> {
+  uint4 s0, s1, nb;
+};
+template <>
+struct StreamRaw<false> {
+  uint4 w[4];
+};
+
+// Weight loads of one super-block for lane (r, g): 32 columns from column
+// offset c of the row (R4: sm and nibble rows; twin: bf16 row in `srow`).
+template <bool kR4>
+__device__ __forceinline__ void stream_load(const uint8_t* srow, const uint8_t* nrow, int32_t c,
+                                            StreamRaw<kR4>& q) {
+  if constexpr (kR4) {
+    const uint4* ps = reinterpret_cast<const uint4*>(srow + c);
+    q.s0 = ps[0];
+    q.s1 = ps[1];
+    q.nb = *reinterpret_cast<const uint4*>(nrow + (c >> 1));
+  } else {
+    const uint4* pw = reinterpret_cast<const uint4*>(srow + 2 * c);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) q.w[v] = pw[v];
+  }
+}
+
+// Nonzero when any of the 32 nibbles of q is 15 (an escape): a nibble of
+// ~P is zero exactly where P's is 15, and (v - 0x11..) & ~v & 0x88.. flags a
+// word holding a zero nibble.
+__device__ __forceinline__ uint32_t any_escape32(uint4 nb) {
+  const uint32_t P[4] = {nb.x, nb.y, nb.z, nb.w};
+  uint32_t f = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f |= (0xEEEEEEEEu - P[j]) & P[j] & 0x88888888u;
+  return f;
+}
+
+// Escapes among the 8 ranks of nibble word P (columns c .. c+7 of row n):
+// patch their exponents in E0 (c .. c+3) and E1 (c+4 .. c+7).
+__device__ __forceinline__ void esc_patch_word(const GemmArgs& a, const EscTab& t, int64_t n,
+                                               int32_t c, int32_t c_rel, uint32_t P,
+                                               uint32_t& E0, uint32_t& E1) {
+  if (has_escape(P)) {
+    if (t.over)
+      patch8(a, n, c, E0, E1);
+    else
+      esc_tab_patch(t, c_rel, E0, E1);
+  }
+}
+
+// The four weights of sm word S with exponents E as two bf16 pairs.
+__device__ __forceinline__ uint2 bf16_pairs4(uint32_t S, uint32_t E) {
+  uint32_t H, Lo;
+  split4_rot(S, E, H, Lo);
+  return make_uint2(weight_pair_bf16<0>(H, Lo), weight_pair_bf16<2>(H, Lo));
+}
+
+// The 32 weights of one super-block for lane (r, g) (columns c .. c+31 of
+// row n; c_rel: c relative to the table's first column), as the four MFMA
+// operands of steps 0..3. Values, not references: the words stay in VGPRs.
+__device__ __forceinline__ void rebuild32(const GemmArgs& a, const Lut& L, uint4 s0, uint4 s1,
+                                          uint4 nb, int64_t n, int32_t c, const EscTab& t,
+                                          int32_t c_rel, bf16x8 (&B)[4]) {
+  uint32_t E0 = lookup4(nb.x, L), E1 = lookup4(nb.x >> 4, L);
+  uint32_t E2 = lookup4(nb.y, L), E3 = lookup4(nb.y >> 4, L);
+  uint32_t E4 = lookup4(nb.z, L), E5 = lookup4(nb.z >> 4, L);
+  uint32_t E6 = lookup4(nb.w, L), E7 = lookup4(nb.w >> 4, L);
+  if (any_escape32(nb)) {
+    esc_patch_word(a, t, n, c, c_rel, nb.x, E0, E1);
+    esc_patch_word(a, t, n, c + 8, c_rel + 8, nb.y, E2, E3);
+    esc_patch_word(a, t, n, c + 16, c_rel + 16, nb.z, E4, E5);
+    esc_patch_word(a, t, n, c + 24, c_rel + 24, nb.w, E6, E7);
+  }
+  uint2 p0 = bf16_pairs4(s0.x, E0), p1 = bf16_pairs4(s0.y, E1);
+  B[0] = as_bf16x8(make_uint4(p0.x, p0.y, p1.x, p1.y));
+  p0 = bf16_pairs4(s0.z, E2), p1 = bf16_pairs4(s0.w, E3);
+  B[1] = as_bf16x8(make_uint4(p0.x, p0.y, p1.x, p1.y));
+  p0 = bf16_pairs4(s1.x, E4), p1 = bf16_pairs4(s1.y, E5);
+  B[2] = as_bf16x8(make_uint4(p0.x, p0.y, p1.x, p1.y));
+  p0 = bf16_pairs4(s1.z, E6), p1 = bf16_pairs4(s1.w, E7);
+  B[3] = as_bf16x8(make_uint4(p0.x, p0.y, p1.x, p1.y));
+}
+
+// X operand of m-tile t for lane (r, g), LDS column col (bf16 elements).
+template <int MT>
+__device__ __forceinline__ bf16x8 stream_x(const uint16_t* xs, int32_t xstride, int t, int r,
+                                           int32_t col) {
+  return *reinterpret_cast<const bf16x8*>(xs + (t * 16 + r) * xstride + col);
+}
+
+template <bool kR4, int MT>
+__global__ __launch_bounds__(64 * kStreamWaves) void gemm_stream_kernel(GemmArgs a,
+                                                                        int32_t xstride,
+                                                                        int32_t groups) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(static_cast<int>(tid >> 6));
+  const int32_t S = a.slices;
+  const int32_t s = static_cast<int32_t>(blockIdx.x % S);
+  const int32_t gi = static_cast<int32_t>(blockIdx.x / S);
+  int32_t lo, hi;
+  slice_superblocks(a.k, S, s, lo, hi);
+  const int32_t nsb = a.k / kSB;
+  const int32_t c_lo = lo * kSB;
+  const int32_t tails = s == S - 1 ? (a.k - nsb * kSB) / 32 : 0;
+  const int32_t cols = (hi - lo) * kSB + 32 * tails;
+
+  const int64_t ntiles = (a.n + 15) / 16;
+  const int64_t t0 = (ntiles * gi) / groups, t1 = (ntiles * (gi + 1)) / groups;
+  const int32_t len = hi - lo;
+  // this wave's tiles: t0 + wave, t0 + wave + 8, ...
+  const int64_t my = t1 > t0 + wave ? (t1 - t0 - wave + kStreamWaves - 1) / kStreamWaves : 0;
+  const int64_t items = my * len;
+  const int r = lane & 15, g = lane >> 4;
+  int64_t cs_tile = t0 + wave;
+  const Lut L{a.lut0, a.lut1, a.lut2, a.lut3};
+
+  floatx4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // load side and consume side walk the same (tile, u) sequence; a row
+  // past N reads row N-1 (its outputs are never stored)
+  const int64_t rstep = static_cast<int64_t>(kStreamWaves) * 16;
+  const int64_t sm_row = kR4 ? a.k : 2 * static_cast<int64_t>(a.k);
+  int64_t ld_row = t0 * 16 + wave * 16 + r, cs_n = min(ld_row, a.n - 1);
+  const uint8_t* ld_s = a.w + min(ld_row, a.n - 1) * sm_row;
+  const uint8_t* ld_nb = a.nib + min(ld_row, a.n - 1) * (a.k >> 1);
+  int32_t ld_u = lo, cs_u = lo;
+  StreamRaw<kR4> ring[kRing];
+#pragma unroll
+  for (int k = 0; k < kRing; ++k) {
+    if (k < items) {
+      stream_load<kR4>(ld_s, ld_nb, ld_u * kSB + 32 * g, ring[k]);
+      if (++ld_u == hi) {
+        ld_u = lo;
+        ld_row += rstep;
+        ld_s = a.w + min(ld_row, a.n - 1) * sm_row;
+        ld_nb = a.nib + min(ld_row, a.n - 1) * (a.k >> 1);
+      }
+    }
+  }
+  // the escapes of this lane's row over the slice's columns
+  EscTab tab;
+  if (kR4 && items > 0) esc_tab_build(a, cs_n, c_lo, c_lo + cols, tab);
+  // (the first weight loads are in flight while the block copies X)
+  // the slice's X columns, rows past M repeated from row M-1 (never stored)
+  {
+    const int32_t segs = cols / 8;
+    for (int32_t i = tid; i < 16 * MT * segs; i += 64 * kStreamWaves) {
+      const int32_t row = i / segs, seg = i - row * segs;
+      const int64_t xm = min(static_cast<int64_t>(row), a.m - 1);
+      *reinterpret_cast<uint4*>(xs + row * xstride + 8 * seg) =
+          *reinterpret_cast<const uint4*>(a.x + xm * a.ldx + c_lo + 8 * seg);
+    }
+  }
+  __syncthreads();
+
+  for (int64_t i = 0; i < items; i += kRing) {
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) {
+      if (i + k < items) {
+        const int64_t n = cs_n;
+        const int32_t c = cs_u * kSB + 32 * g;
+        const int32_t xc = (cs_u - lo) * kSB + 32 * g;
+        const StreamRaw<kR4> q = ring[k];
+        if (i + k + kRing < items) {
+          stream_load<kR4>(ld_s, ld_nb, ld_u * kSB + 32 * g, ring[k]);
+          if (++ld_u == hi) {
+            ld_u = lo;
+            ld_row += rstep;
+            ld_s = a.w + min(ld_row, a.n - 1) * sm_row;
+            ld_nb = a.nib + min(ld_row, a.n - 1) * (a.k >> 1);
+          }
+        }
+        bf16x8 B[4];
+        if constexpr (kR4) {
+          rebuild32(a, L, q.s0, q.s1, q.nb, n, c, tab, xc, B);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) B[j] = as_bf16x8(q.w[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                stream_x<MT>(xs, xstride, t, r, xc + 8 * j), B[j], acc[t], 0, 0, 0);
+        if (++cs_u == hi) {
+          // tail blocks (last slice only), then the tile's partial
+          for (int32_t b = 0; b < tails; ++b) {
+            const int32_t c0 = nsb * kSB + 32 * b + 8 * g;
+            bf16x8 B;
+            if constexpr (kR4)
+              B = as_bf16x8(rebuild8_tab(
+                  a, L, *reinterpret_cast<const uint2*>(a.w + n * a.k + c0),
+                  *reinterpret_cast<const uint32_t*>(a.nib + n * (a.k >> 1) + (c0 >> 1)), n, c0,
+                  tab, c0 - c_lo));
+            else
+              B = as_bf16x8(*reinterpret_cast<const uint4*>(a.w + 2 * (n * a.k + c0)));
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  stream_x<MT>(xs, xstride, t, r, len * kSB + 32 * b + 8 * g), B, acc[t], 0, 0,
+                  0);
+          }
+          const int64_t on = cs_tile * 16 + r;   // (tile of the consume side)
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int64_t om = t * 16 + 4 * g + e;
+              if (S == 1)
+                store_out(a, om, on, acc[t][e]);
+              else if (om < a.m && on < a.n)
+                a.part[(static_cast<int64_t>(s) * a.m + om) * a.n + on] = acc[t][e];
+            }
+            acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+          }
+          cs_u = lo;
+          cs_tile += kStreamWaves;
+          cs_n = min(cs_tile * 16 + r, a.n - 1);
+          if (kR4 && i + k + 1 < items) esc_tab_build(a, cs_n, c_lo, c_lo + cols, tab);
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- large M
-// Tiles of BM = 64*WM X rows by 128 weight rows, 8 waves of 64 x (16*WM):
-// each rebuilt weight feeds BM X rows. Unsplit, a block runs every slice of
-// its tile in order with a running total. Split, a block runs one slice and
-// writes its accumulators to the workspace; gemm_combine_kernel then adds
-// the slices in order (the same fp32 adds as the running total).
-constexpr int kBN = 128, kLargeThreads = 512;
+// Tiles of BM X rows by 128 weight rows; waves of 64 X rows x 16*NJ weight
+// rows: (BM/64) x (128/(16*NJ)) waves. Each rebuilt weight feeds BM X rows.
+// Unsplit, a block runs every slice of its tile in order with a running
+// total. Split, a block runs one slice and writes its accumulators to the
+// workspace; gemm_combine_kernel then adds the slices in order (the same
+// fp32 adds as the running total).
+constexpr int kBN = 128;
 // bf16 elements per LDS row: 128 + 8, so that rows start 4 banks apart and
 // both the 16-byte stores of staging and the 16-byte MFMA operand reads of
 // 8 consecutive rows fall in distinct banks
 constexpr int kLdsStride = kSB + 8;
 
-// One thread's loads for one super-block. X: BM/32 rows (v*32 + tid/16) x 16
-// bytes (segment tid%16); twin weights: 4 such rows; R4: 2 rows
-// (v*64 + tid/8) x 16 sm bytes (segment tid%8) and their 8 nibble bytes.
-template <bool kR4, int WM>
+template <int BM, int NJ>
+constexpr int large_threads() {
+  return (BM / 64) * (kBN / (16 * NJ)) * 64;
+}
+
+// One thread's loads for one super-block, T threads. X: BM*16/T rows
+// (v*T/16 + tid/16) x 16 bytes (segment tid%16); twin weights: 128*16/T
+// such rows; R4: 128*8/T rows (v*T/8 + tid/8) x 16 sm bytes (segment tid%8)
+// and their 8 nibble bytes.
+template <bool kR4, int BM, int T>
 struct LargeRaw;
-template <int WM>
-struct LargeRaw<true, WM> {
-  uint4 x[2 * WM];
-  uint4 sm[2];
-  uint2 nb[2];
+template <int BM, int T>
+struct LargeRaw<true, BM, T> {
+  uint4 x[BM * 16 / T];
+  uint4 sm[kBN * 8 / T];
+  uint2 nb[kBN * 8 / T];
 };
-template <int WM>
-struct LargeRaw<false, WM> {
-  uint4 x[2 * WM];
-  uint4 w[4];
+template <int BM, int T>
+struct LargeRaw<false, BM, T> {
+  uint4 x[BM * 16 / T];
+  uint4 w[kBN * 16 / T];
 };
 
 // Rows past M or N load zeros (their outputs are never stored; the zero is
@@ -312,23 +643,25 @@ struct LargeRaw<false, WM> {
 // expression over two uint4 lvalues would select an address). Each load
 // address is a block-uniform base plus a 32-bit per-lane byte offset, so the
 // loop keeps one offset register per operand instead of a pointer per row.
-template <bool kR4, int WM>
+template <bool kR4, int BM, int T>
 __device__ __forceinline__ void large_load(const GemmArgs& a, int32_t c0, int tid, int64_t m0,
                                            int64_t n0, uint32_t xo, uint32_t wo, uint32_t no,
-                                           LargeRaw<kR4, WM>& q) {
+                                           LargeRaw<kR4, BM, T>& q) {
   const uint4 z4 = make_uint4(0, 0, 0, 0);
+  constexpr int XR = T / 16;
 #pragma unroll
-  for (int v = 0; v < 2 * WM; ++v) {
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x + (m0 + v * 32) * a.ldx + c0);
+  for (int v = 0; v < BM / XR; ++v) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x + (m0 + v * XR) * a.ldx + c0);
     q.x[v] = z4;
-    if (m0 + v * 32 + (tid >> 4) < a.m) q.x[v] = *reinterpret_cast<const uint4*>(base + xo);
+    if (m0 + v * XR + (tid >> 4) < a.m) q.x[v] = *reinterpret_cast<const uint4*>(base + xo);
   }
   if constexpr (kR4) {
+    constexpr int RR = T / 8;
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const bool ok = n0 + v * 64 + (tid >> 3) < a.n;
-      const uint8_t* bs = a.w + (n0 + v * 64) * a.k + c0;
-      const uint8_t* bn = a.nib + (n0 + v * 64) * (a.k >> 1) + (c0 >> 1);
+    for (int v = 0; v < kBN / RR; ++v) {
+      const bool ok = n0 + v * RR + (tid >> 3) < a.n;
+      const uint8_t* bs = a.w + (n0 + v * RR) * a.k + c0;
+      const uint8_t* bn = a.nib + (n0 + v * RR) * (a.k >> 1) + (c0 >> 1);
       q.sm[v] = z4;
       q.nb[v] = make_uint2(0, 0);
       if (ok) {
@@ -337,27 +670,30 @@ __device__ __forceinline__ void large_load(const GemmArgs& a, int32_t c0, int ti
       }
     }
   } else {
+    constexpr int WR = T / 16;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const uint8_t* base = a.w + ((n0 + v * 32) * a.k + c0) * 2;
+    for (int v = 0; v < kBN / WR; ++v) {
+      const uint8_t* base = a.w + ((n0 + v * WR) * a.k + c0) * 2;
       q.w[v] = z4;
-      if (n0 + v * 32 + (tid >> 4) < a.n) q.w[v] = *reinterpret_cast<const uint4*>(base + wo);
+      if (n0 + v * WR + (tid >> 4) < a.n) q.w[v] = *reinterpret_cast<const uint4*>(base + wo);
     }
   }
 }
 
-template <bool kR4, int WM>
+template <bool kR4, int BM, int T>
 __device__ __forceinline__ void large_stage(const GemmArgs& a, const Lut& L, int32_t c0, int tid,
                                             int64_t n0, uint16_t (*xs)[kLdsStride],
                                             uint16_t (*ws)[kLdsStride],
-                                            const LargeRaw<kR4, WM>& q) {
+                                            const LargeRaw<kR4, BM, T>& q) {
+  constexpr int XR = T / 16;
 #pragma unroll
-  for (int v = 0; v < 2 * WM; ++v)
-    *reinterpret_cast<uint4*>(&xs[v * 32 + (tid >> 4)][8 * (tid & 15)]) = q.x[v];
+  for (int v = 0; v < BM / XR; ++v)
+    *reinterpret_cast<uint4*>(&xs[v * XR + (tid >> 4)][8 * (tid & 15)]) = q.x[v];
   if constexpr (kR4) {
+    constexpr int RR = T / 8;
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const int row = v * 64 + (tid >> 3);
+    for (int v = 0; v < kBN / RR; ++v) {
+      const int row = v * RR + (tid >> 3);
       const int cc = 16 * (tid & 7);
       // rows past N hold zeros, which have no escapes
       const uint4 lo = rebuild8(a, L, make_uint2(q.sm[v].x, q.sm[v].y), q.nb[v].x, n0 + row,
@@ -368,13 +704,15 @@ __device__ __forceinline__ void large_stage(const GemmArgs& a, const Lut& L, int
       *reinterpret_cast<uint4*>(&ws[row][cc + 8]) = hi;
     }
   } else {
+    constexpr int WR = T / 16;
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      *reinterpret_cast<uint4*>(&ws[v * 32 + (tid >> 4)][8 * (tid & 15)]) = q.w[v];
+    for (int v = 0; v < kBN / WR; ++v)
+      *reinterpret_cast<uint4*>(&ws[v * WR + (tid >> 4)][8 * (tid & 15)]) = q.w[v];
   }
 }
 
-// Staging of one 32-column tail block (plain lane-group mapping).
+// Staging of one 32-column tail block (plain lane-group mapping); needs at
+// least 2*BM and 2*128 threads.
 template <bool kR4, int BM>
 __device__ __forceinline__ void large_stage_tail(const GemmArgs& a, const Lut& L, int32_t c0,
                                                  int tid, int64_t m0, int64_t n0,
@@ -438,13 +776,20 @@ __device__ __forceinline__ void fold(int32_t s, floatx4 (&acc)[4][NJ], floatx4 (
     }
 }
 
+// Waves per SIMD the launch bounds ask the register allocator for.
+template <int BM, int NJ, bool kSplit>
+constexpr int large_min_waves() {
+  return large_threads<BM, NJ>() == 512 && NJ == 2 && kSplit ? 4 : 2;
+}
+
 // kSplit: blockIdx -> (tile, slice), one slice per block, fp32 partials to
 // a.part[slice][m][n]; otherwise blockIdx -> tile, all slices in order.
-template <bool kR4, int WM, bool kSplit>
-__global__ __launch_bounds__(kLargeThreads, WM == 2 && kSplit ? 4 : 2) void gemm_large_kernel(GemmArgs a) {
-  constexpr int BM = 64 * WM;
-  constexpr int NW = 8 / WM;    // waves along N
-  constexpr int NJ = WM;        // 16-row MFMA tiles per wave along N
+template <bool kR4, int BM, int NJ, bool kSplit>
+__global__ __launch_bounds__((large_threads<BM, NJ>()), (large_min_waves<BM, NJ, kSplit>()))
+void gemm_large_kernel(GemmArgs a) {
+  constexpr int T = large_threads<BM, NJ>();
+  constexpr int NW = kBN / (16 * NJ);   // waves along N
+  static_assert(T >= 2 * BM && T >= 2 * kBN, "tail staging needs 2 threads per row");
   __shared__ __attribute__((aligned(16))) uint16_t xs[BM][kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t ws[kBN][kLdsStride];
   const int tid = threadIdx.x;
@@ -483,15 +828,15 @@ __global__ __launch_bounds__(kLargeThreads, WM == 2 && kSplit ? 4 : 2) void gemm
                           : static_cast<uint32_t>(((tid >> 4) * a.k + 8 * (tid & 15)) * 2);
   const uint32_t no = static_cast<uint32_t>((tid >> 3) * (a.k >> 1) + 8 * (tid & 7));
   if (u_lo < u_end) {
-    LargeRaw<kR4, WM> q;
-    large_load<kR4, WM>(a, u_lo * kSB, tid, m0, n0, xo, wo, no, q);
+    LargeRaw<kR4, BM, T> q;
+    large_load<kR4, BM, T>(a, u_lo * kSB, tid, m0, n0, xo, wo, no, q);
     for (int32_t u = u_lo; u < u_end; ++u) {
       __syncthreads();   // every wave is done reading the previous super-block
-      large_stage<kR4, WM>(a, L, u * kSB, tid, n0, xs, ws, q);
+      large_stage<kR4, BM, T>(a, L, u * kSB, tid, n0, xs, ws, q);
       __syncthreads();
       // the next super-block (the last one again on the last pass: always in
       // bounds, and the load stays unconditional)
-      large_load<kR4, WM>(a, min(u + 1, u_end - 1) * kSB, tid, m0, n0, xo, wo, no, q);
+      large_load<kR4, BM, T>(a, min(u + 1, u_end - 1) * kSB, tid, m0, n0, xo, wo, no, q);
 #pragma unroll
       for (int j = 0; j < 4; ++j) large_step<NJ>(xs, ws, wm, wn, r, 32 * g + 8 * j, acc);
       if (!kSplit && u + 1 == s_hi && s + 1 < S) {
@@ -537,10 +882,11 @@ __global__ __launch_bounds__(kLargeThreads, WM == 2 && kSplit ? 4 : 2) void gemm
     }
 }
 
-// y[m][n] = ((p0 + p1) + p2) + ... over the S slice partials, in slice order.
-// Block (x, y): row y, columns 1024x .. 1024x+1023, four per thread (one
-// 16-byte load per slice when N is a multiple of 4).
+// y[m][n] = ((p0 + p1) + p2) + ... over the S (<= 8) slice partials, in
+// slice order. Block (x, y): row y, columns 1024x .. 1024x+1023, four per
+// thread; every slice's load is issued before the adds.
 __global__ __launch_bounds__(256) void gemm_combine_kernel(GemmArgs a) {
+  constexpr int kMaxSlices = 8;
   const int64_t m = blockIdx.y;
   const int64_t n0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
   if (n0 >= a.n) return;
@@ -548,12 +894,16 @@ __global__ __launch_bounds__(256) void gemm_combine_kernel(GemmArgs a) {
   const float* p = a.part + m * a.n + n0;
   float v[4];
   if ((a.n & 3) == 0) {
-    const float4 q = *reinterpret_cast<const float4*>(p);
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-    for (int32_t s = 1; s < a.slices; ++s) {
-      const float4 r = *reinterpret_cast<const float4*>(p + s * mn);
-      v[0] = v[0] + r.x; v[1] = v[1] + r.y; v[2] = v[2] + r.z; v[3] = v[3] + r.w;
-    }
+    float4 q[kMaxSlices];
+#pragma unroll
+    for (int s = 0; s < kMaxSlices; ++s)
+      if (s < a.slices) q[s] = *reinterpret_cast<const float4*>(p + s * mn);
+    v[0] = q[0].x; v[1] = q[0].y; v[2] = q[0].z; v[3] = q[0].w;
+#pragma unroll
+    for (int s = 1; s < kMaxSlices; ++s)
+      if (s < a.slices) {
+        v[0] = v[0] + q[s].x; v[1] = v[1] + q[s].y; v[2] = v[2] + q[s].z; v[3] = v[3] + q[s].w;
+      }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = n0 + i < a.n ? p[i] : 0.0f;
@@ -601,17 +951,71 @@ constexpr int64_t kSmallMaxM = BINADE_GEMM_SMALL_MAX_M;
 constexpr int64_t kSplitBelow = BINADE_GEMM_SPLIT_BELOW;
 constexpr int64_t kSplitMaxM = 512;
 
+// Tiles for M above 128: 256 X rows (8 waves, one block per CU) or 128
+// (4 waves, two blocks per CU).
+#ifndef BINADE_GEMM_LARGE_BM
+#define BINADE_GEMM_LARGE_BM 128
+#endif
+
+// M up to this runs the streamed kernel when the slices' partials have a
+// workspace (or K has one slice) and the X slice fits in LDS.
+#ifndef BINADE_GEMM_STREAM_MAX_M
+#define BINADE_GEMM_STREAM_MAX_M 32
+#endif
+// weight-row tiles per wave in the streamed kernel
+#ifndef BINADE_GEMM_STREAM_TPW
+#define BINADE_GEMM_STREAM_TPW 1
+#endif
+constexpr int64_t kStreamMaxM = BINADE_GEMM_STREAM_MAX_M;
+constexpr int64_t kStreamLdsMax = 160 * 1024;
+
+// LDS row stride (bf16 elements) of the streamed kernel's X slice: the
+// widest slice plus 8, so that rows start 4 banks apart.
+int32_t stream_xstride(int64_t k, int32_t S) {
+  const int64_t nsb = k / kSB;
+  int64_t w = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    int64_t c = (((s + 1) * nsb) / S - (s * nsb) / S) * kSB;
+    if (s == S - 1) c += k - nsb * kSB;
+    w = c > w ? c : w;
+  }
+  return static_cast<int32_t>(w + 8);
+}
+
 struct Plan {
+  int smt = 0;       // streamed kernel: X tiles of 16 (0: not streamed)
+  int32_t groups = 0;
+  int64_t lds = 0;
   int mt = 0;        // small kernel: X tiles of 16 per wave (0: tiled kernel)
-  int wm = 0;        // tiled kernel: BM = 64*wm
+  int bm = 0;        // tiled kernel: X rows per tile
+  int nj = 0;        // tiled kernel: 16-row MFMA tiles per wave along N
   bool split = false;
   int64_t blocks = 0;
   int64_t part_bytes = 0;   // workspace the split needs
 };
 
+int64_t large_blocks(int64_t m, int64_t n, int bm, int64_t per_tile) {
+  const int64_t items = ((n + kBN - 1) / kBN) * ((m + bm - 1) / bm) * per_tile;
+  return ((items + kXcds - 1) / kXcds) * kXcds;
+}
+
 Plan plan_for(int64_t m, int64_t n, int64_t k) {
   Plan p;
   const int32_t S = slices_for(k);
+  if (m <= kStreamMaxM && k >= kSB) {
+    const int smt = m <= 16 ? 1 : 2;
+    const int64_t lds = static_cast<int64_t>(16 * smt) * stream_xstride(k, S) * 2;
+    if (lds <= kStreamLdsMax) {
+      const int64_t ntiles = (n + 15) / 16;
+      const int64_t per = static_cast<int64_t>(kStreamWaves) * BINADE_GEMM_STREAM_TPW;
+      p.smt = smt;
+      p.lds = lds;
+      p.groups = static_cast<int32_t>((ntiles + per - 1) / per);
+      p.blocks = static_cast<int64_t>(p.groups) * S;
+      p.part_bytes = S > 1 ? static_cast<int64_t>(S) * m * n * 4 : 0;
+      return p;
+    }
+  }
   if (m <= kSmallMaxM) {
     p.mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
     const int64_t mtiles = (m + 16 * p.mt - 1) / (16 * p.mt);
@@ -619,11 +1023,16 @@ Plan plan_for(int64_t m, int64_t n, int64_t k) {
     p.blocks = ((tiles + kXcds - 1) / kXcds) * kXcds;
     return p;
   }
-  p.wm = m <= 128 ? 2 : 4;
-  const int64_t tiles = ((n + kBN - 1) / kBN) * ((m + 64 * p.wm - 1) / (64 * p.wm));
+  if (m <= 128) {
+    p.bm = 128;
+    p.nj = 2;
+  } else {
+    p.bm = BINADE_GEMM_LARGE_BM;
+    p.nj = 4;
+  }
+  const int64_t tiles = ((n + kBN - 1) / kBN) * ((m + p.bm - 1) / p.bm);
   p.split = S > 1 && tiles < kSplitBelow && m <= kSplitMaxM;
-  const int64_t items = tiles * (p.split ? S : 1);
-  p.blocks = ((items + kXcds - 1) / kXcds) * kXcds;
+  p.blocks = large_blocks(m, n, p.bm, p.split ? S : 1);
   p.part_bytes = p.split ? static_cast<int64_t>(S) * m * n * 4 : 0;
   return p;
 }
@@ -636,14 +1045,34 @@ void launch_small(GemmArgs a, int64_t blocks, hipStream_t stream) {
                      dim3(64 * a.slices), 0, stream, a);
 }
 
-template <bool kR4, int WM>
+template <bool kR4, int MT>
+void launch_stream(const GemmArgs& a, const Plan& p, hipStream_t stream) {
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_stream_kernel<kR4, MT>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(kStreamLdsMax));
+  });
+  hipLaunchKernelGGL((gemm_stream_kernel<kR4, MT>), dim3(static_cast<uint32_t>(p.blocks)),
+                     dim3(64 * kStreamWaves), static_cast<uint32_t>(p.lds), stream, a,
+                     static_cast<int32_t>(p.lds / (32 * MT)), p.groups);
+}
+
+template <bool kR4, int BM, int NJ>
 void launch_large(const GemmArgs& a, bool split, int64_t blocks, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>(blocks)), block(large_threads<BM, NJ>());
   if (split)
-    hipLaunchKernelGGL((gemm_large_kernel<kR4, WM, true>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kLargeThreads), 0, stream, a);
+    hipLaunchKernelGGL((gemm_large_kernel<kR4, BM, NJ, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((gemm_large_kernel<kR4, WM, false>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kLargeThreads), 0, stream, a);
+    hipLaunchKernelGGL((gemm_large_kernel<kR4, BM, NJ, false>), grid, block, 0, stream, a);
+}
+
+template <bool kR4>
+void launch_large_cfg(const GemmArgs& a, const Plan& p, hipStream_t stream) {
+  if (p.nj == 2)
+    launch_large<kR4, 128, 2>(a, p.split, p.blocks, stream);
+  else
+    launch_large<kR4, BINADE_GEMM_LARGE_BM, 4>(a, p.split, p.blocks, stream);
 }
 
 int32_t launch(GemmArgs a, bool r4, void* workspace, int64_t workspace_bytes,
@@ -651,6 +1080,31 @@ int32_t launch(GemmArgs a, bool r4, void* workspace, int64_t workspace_bytes,
   a.slices = slices_for(a.k);
   Plan p = plan_for(a.m, a.n, a.k);
   if (p.blocks > 0x7FFFFFFFll) return BINADE_EUNSUPPORTED;
+  if (p.smt != 0) {
+    if (p.part_bytes == 0 ||
+        (workspace != nullptr && workspace_bytes >= p.part_bytes && aligned16(workspace))) {
+      a.part = p.part_bytes ? static_cast<float*>(workspace) : nullptr;
+      if (p.smt == 1) r4 ? launch_stream<true, 1>(a, p, stream) : launch_stream<false, 1>(a, p, stream);
+      else r4 ? launch_stream<true, 2>(a, p, stream) : launch_stream<false, 2>(a, p, stream);
+      if (p.part_bytes) {
+        const dim3 cg(static_cast<uint32_t>((a.n + 1023) / 1024), static_cast<uint32_t>(a.m));
+        hipLaunchKernelGGL(gemm_combine_kernel, cg, dim3(256), 0, stream, a);
+      }
+      return launch_status();
+    }
+    // no room for the partials: the kernels below give the same bits
+    p = Plan{};
+    p.mt = a.m <= 16 ? 1 : 0;
+    if (p.mt) {
+      const int64_t tiles = (a.n + 15) / 16;
+      p.blocks = ((tiles + kXcds - 1) / kXcds) * kXcds;
+    } else {
+      p.bm = 128;
+      p.nj = 2;
+      p.split = false;
+      p.blocks = large_blocks(a.m, a.n, p.bm, 1);
+    }
+  }
   if (p.mt == 1) r4 ? launch_small<true, 1>(a, p.blocks, stream)
                     : launch_small<false, 1>(a, p.blocks, stream);
   else if (p.mt == 2) r4 ? launch_small<true, 2>(a, p.blocks, stream)
@@ -665,14 +1119,10 @@ int32_t launch(GemmArgs a, bool r4, void* workspace, int64_t workspace_bytes,
                   !aligned16(workspace))) {
     // no room for the partials: run every slice in one block (same bits)
     p.split = false;
-    const int64_t tiles = ((a.n + kBN - 1) / kBN) * ((a.m + 64 * p.wm - 1) / (64 * p.wm));
-    p.blocks = ((tiles + kXcds - 1) / kXcds) * kXcds;
+    p.blocks = large_blocks(a.m, a.n, p.bm, 1);
   }
   a.part = p.split ? static_cast<float*>(workspace) : nullptr;
-  if (p.wm == 2) r4 ? launch_large<true, 2>(a, p.split, p.blocks, stream)
-                    : launch_large<false, 2>(a, p.split, p.blocks, stream);
-  else r4 ? launch_large<true, 4>(a, p.split, p.blocks, stream)
-          : launch_large<false, 4>(a, p.split, p.blocks, stream);
+  r4 ? launch_large_cfg<true>(a, p, stream) : launch_large_cfg<false>(a, p, stream);
   if (p.split) {
     const dim3 cg(static_cast<uint32_t>((a.n + 1023) / 1024), static_cast<uint32_t>(a.m));
     hipLaunchKernelGGL(gemm_combine_kernel, cg, dim3(256), 0, stream, a);

@@ -33,10 +33,17 @@ def test_library_exports_every_declared_function():
 
 
 def test_gemm_workspace_bytes_policy():
-    """Host-only sizing: partials are S*M*N fp32 for shapes the tiled kernel
-    splits (S = min(8, ceil(K/1024)) slices), 0 where it never splits."""
-    # small M runs the no-LDS kernel: never a workspace
-    assert B.gemm_workspace_bytes(16, 3840, 15360) == 0
+    """Host-only sizing: partials are S*M*N fp32 for shapes whose slices run
+    in separate blocks (S = min(8, ceil(K/1024)) slices), 0 otherwise."""
+    # M <= 32 streams each slice separately when its X columns fit in LDS
+    assert B.gemm_workspace_bytes(16, 3840, 15360) == 8 * 16 * 3840 * 4
+    assert B.gemm_workspace_bytes(32, 64, 15360) == 8 * 32 * 64 * 4
+    assert B.gemm_workspace_bytes(16, 15360, 3840) == 4 * 16 * 15360 * 4
+    # ... but not with one slice, without a full super-block, or when a
+    # slice's X columns would not fit in LDS
+    assert B.gemm_workspace_bytes(16, 512, 1024) == 0
+    assert B.gemm_workspace_bytes(16, 512, 96) == 0
+    assert B.gemm_workspace_bytes(16, 64, 131072) == 0
     # few tiles, K = 15360 -> 8 slices
     assert B.gemm_workspace_bytes(128, 3840, 15360) == 8 * 128 * 3840 * 4
     # K = 3840 -> 4 slices
