@@ -399,6 +399,37 @@ __device__ __forceinline__ void stream_load(const uint8_t* srow, const uint8_t* 
   }
 }
 
+// Escape tables of a tile's weight rows in LDS (the tiled kernel): per row
+// the 8 entries and the `over` word of an EscTab built over a column range
+// of at most two row-chunks (kEscRange columns from a chunk pair's start).
+constexpr int kEscWords = 9;
+constexpr int kEscRange = 2 * kChunk;
+
+__device__ __forceinline__ void esc_tab_store(const EscTab& t, uint32_t* row) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) row[i] = t.ent[i];
+  row[8] = t.over;
+}
+
+// Escapes among the 8 ranks of nibble word P (columns c0 .. c0+7 of row n):
+// patch E0 (c0 .. c0+3) and E1 (c0+4 .. c0+7) from the row's LDS table
+// (c_rel: c0 relative to the table's first column).
+__device__ __forceinline__ void esc_patch_lds(const GemmArgs& a, int64_t n, int32_t c0,
+                                              uint32_t P, const uint32_t* trow, int32_t c_rel,
+                                              uint32_t& E0, uint32_t& E1) {
+  if (has_escape(P)) {
+    if (trow[8]) {
+      patch8(a, n, c0, E0, E1);
+    } else {
+      EscTab t;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t.ent[i] = trow[i];
+      t.over = 0;
+      esc_tab_patch(t, c_rel, E0, E1);
+    }
+  }
+}
+
 // Nonzero when any of the 32 nibbles of q is 15 (an escape): a nibble of
 // ~P is zero exactly where P's is 15, and (v - 0x11..) & ~v & 0x88.. flags a
 // word holding a zero nibble.
@@ -684,24 +715,46 @@ template <bool kR4, int BM, int T>
 __device__ __forceinline__ void large_stage(const GemmArgs& a, const Lut& L, int32_t c0, int tid,
                                             int64_t n0, uint16_t (*xs)[kLdsStride],
                                             uint16_t (*ws)[kLdsStride],
-                                            const LargeRaw<kR4, BM, T>& q) {
+                                            const LargeRaw<kR4, BM, T>& q,
+                                            const uint32_t (*etab)[kEscWords], int32_t tcol0) {
   constexpr int XR = T / 16;
 #pragma unroll
   for (int v = 0; v < BM / XR; ++v)
     *reinterpret_cast<uint4*>(&xs[v * XR + (tid >> 4)][8 * (tid & 15)]) = q.x[v];
   if constexpr (kR4) {
-    constexpr int RR = T / 8;
+    constexpr int RR = T / 8, RP = kBN / RR;
+    const int cc = 16 * (tid & 7);
+    // exponents of every row first, one test for an escape among all of
+    // this thread's nibbles, then the (rare) patches from the row tables
+    uint32_t E[RP][4];
+    uint32_t esc = 0;
 #pragma unroll
-    for (int v = 0; v < kBN / RR; ++v) {
+    for (int v = 0; v < RP; ++v) {
+      E[v][0] = lookup4(q.nb[v].x, L);
+      E[v][1] = lookup4(q.nb[v].x >> 4, L);
+      E[v][2] = lookup4(q.nb[v].y, L);
+      E[v][3] = lookup4(q.nb[v].y >> 4, L);
+      esc |= (0xEEEEEEEEu - q.nb[v].x) & q.nb[v].x & 0x88888888u;
+      esc |= (0xEEEEEEEEu - q.nb[v].y) & q.nb[v].y & 0x88888888u;
+    }
+    if (esc) {
+#pragma unroll
+      for (int v = 0; v < RP; ++v) {
+        const int row = v * RR + (tid >> 3);
+        // rows past N hold zeros, which have no escapes
+        esc_patch_lds(a, n0 + row, c0 + cc, q.nb[v].x, etab[row], c0 + cc - tcol0, E[v][0],
+                      E[v][1]);
+        esc_patch_lds(a, n0 + row, c0 + cc + 8, q.nb[v].y, etab[row], c0 + cc + 8 - tcol0,
+                      E[v][2], E[v][3]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < RP; ++v) {
       const int row = v * RR + (tid >> 3);
-      const int cc = 16 * (tid & 7);
-      // rows past N hold zeros, which have no escapes
-      const uint4 lo = rebuild8(a, L, make_uint2(q.sm[v].x, q.sm[v].y), q.nb[v].x, n0 + row,
-                                c0 + cc);
-      const uint4 hi = rebuild8(a, L, make_uint2(q.sm[v].z, q.sm[v].w), q.nb[v].y, n0 + row,
-                                c0 + cc + 8);
-      *reinterpret_cast<uint4*>(&ws[row][cc]) = lo;
-      *reinterpret_cast<uint4*>(&ws[row][cc + 8]) = hi;
+      const uint2 p0 = bf16_pairs4(q.sm[v].x, E[v][0]), p1 = bf16_pairs4(q.sm[v].y, E[v][1]);
+      const uint2 p2 = bf16_pairs4(q.sm[v].z, E[v][2]), p3 = bf16_pairs4(q.sm[v].w, E[v][3]);
+      *reinterpret_cast<uint4*>(&ws[row][cc]) = make_uint4(p0.x, p0.y, p1.x, p1.y);
+      *reinterpret_cast<uint4*>(&ws[row][cc + 8]) = make_uint4(p2.x, p2.y, p3.x, p3.y);
     }
   } else {
     constexpr int WR = T / 16;
@@ -792,6 +845,7 @@ void gemm_large_kernel(GemmArgs a) {
   static_assert(T >= 2 * BM && T >= 2 * kBN, "tail staging needs 2 threads per row");
   __shared__ __attribute__((aligned(16))) uint16_t xs[BM][kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t ws[kBN][kLdsStride];
+  __shared__ uint32_t etab[kR4 ? kBN : 1][kEscWords];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -830,9 +884,28 @@ void gemm_large_kernel(GemmArgs a) {
   if (u_lo < u_end) {
     LargeRaw<kR4, BM, T> q;
     large_load<kR4, BM, T>(a, u_lo * kSB, tid, m0, n0, xo, wo, no, q);
+    int32_t tcol0 = 0;   // first column of the escape tables
+    const int32_t u_first = u_lo;
     for (int32_t u = u_lo; u < u_end; ++u) {
       __syncthreads();   // every wave is done reading the previous super-block
-      large_stage<kR4, BM, T>(a, L, u * kSB, tid, n0, xs, ws, q);
+      if (kR4 && (u == u_first || (u * kSB) % kEscRange == 0)) {
+        // tables of the tile's rows from here to the end of this chunk pair
+        tcol0 = u * kSB;
+        const int32_t tcol1 = min(a.k, (tcol0 / kEscRange + 1) * kEscRange);
+        if (tid < kBN) {
+          EscTab t;
+          if (n0 + tid < a.n) {
+            esc_tab_build(a, n0 + tid, tcol0, tcol1, t);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) t.ent[i] = 0xFFFFu;
+            t.over = 0;
+          }
+          esc_tab_store(t, etab[tid]);
+        }
+        __syncthreads();
+      }
+      large_stage<kR4, BM, T>(a, L, u * kSB, tid, n0, xs, ws, q, etab, tcol0);
       __syncthreads();
       // the next super-block (the last one again on the last pass: always in
       // bounds, and the load stays unconditional)
@@ -954,7 +1027,7 @@ constexpr int64_t kSplitMaxM = 512;
 // Tiles for M above 128: 256 X rows (8 waves, one block per CU) or 128
 // (4 waves, two blocks per CU).
 #ifndef BINADE_GEMM_LARGE_BM
-#define BINADE_GEMM_LARGE_BM 128
+#define BINADE_GEMM_LARGE_BM 256
 #endif
 
 // M up to this runs the streamed kernel when the slices' partials have a
