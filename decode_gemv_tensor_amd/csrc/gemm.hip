@@ -21,20 +21,27 @@
 // exactly the bf16 weights the twins read, so both issue identical MFMA
 // sequences and their outputs agree bit for bit.
 //
-// Small M (<= 16): one wave per 16 weight rows and 16 X rows; each lane
-// loads its 32 columns of a super-block with 16-byte loads, the weights are
-// rebuilt straight into MFMA operands in registers, the next super-block is
+// Small M without a workspace (<= 16): one wave per 16 weight rows and 16 X
+// rows; each lane loads its 32 columns of a super-block with 16-byte loads,
+// the weights are rebuilt straight into MFMA operands in registers, the
+// next super-block is
 // loaded while the current one multiplies, and the S slices of a tile are S
 // waves of one block, added in slice order through LDS. Blocks that share
 // weight rows are placed on the same XCD (blocks are dealt to the 8 XCDs
 // round robin), so their weight reads meet in that XCD's L2.
-// Larger M: tiles of 128 or 256 X rows by 128 weight rows, 8 waves; per
+// M up to 32 (streamed): one block per (slice, group of 8 weight-row
+// tiles) holds its slice's X columns in LDS; waves stream their tiles'
+// weights two super-blocks ahead; slice partials go to the workspace and a
+// second kernel adds them in slice order.
+// M up to 128: tiles of 128 X rows by 128 weight rows, 8 waves; per
 // super-block the X rows and the rebuilt weights go through LDS (rows
 // padded to 272 bytes) while the next super-block is loaded into
-// registers. A block runs all slices of its tile with a running total, or,
-// when the tiles alone cannot fill the chip and the caller gave a
-// workspace, one slice, whose fp32 partials a second kernel adds in slice
-// order.
+// registers. Larger M: tiles of 256 X rows, X copied by DMA straight into
+// two alternating LDS buffers one super-block ahead, weights through
+// registers into one buffer; both tiles swizzled instead of padded. A
+// block runs all slices of its tile with a running total, or, when the
+// tiles alone cannot fill the chip and the caller gave a workspace, one
+// slice, whose fp32 partials a second kernel adds in slice order.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -955,6 +962,360 @@ void gemm_large_kernel(GemmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- large M, X by DMA
+// Tiles of 256 X rows by 128 weight rows, 8 waves of 64 x 64 (4 along M, 2
+// along N). Per super-block the X tile goes from global memory straight
+// into LDS (16 bytes per lane, no registers) one super-block ahead, into two
+// alternating buffers; the weights go through registers (rebuilt for R4,
+// escapes patched from per-row tables held in registers) into one buffer.
+// Both LDS tiles are unpadded rows of 16 pieces of 8 columns, piece p of
+// row R stored at slot p ^ (R & 7): the DMA writes whole rows in order, and
+// the 8 rows an MFMA operand read touches hit 8 different bank groups.
+constexpr int kDmaBM = 256;
+constexpr int kDmaThreads = 512;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from src to LDS dst + 16 * lane (dst wave-uniform).
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+// The compiler does not see the DMA's LDS writes: wait for every vector
+// memory load of this wave, with fences so LDS accesses stay on their side.
+__device__ __forceinline__ void dma_wait() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Block barrier for LDS hand-offs only: this wave's LDS operations are
+// complete, then s_barrier. (__syncthreads also waits for every outstanding
+// global load, which would drain the loads issued ahead for the next
+// super-block.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Element offset of piece p of row R in a swizzled tile.
+__device__ __forceinline__ int swz(int R, int p) {
+  return R * kSB + 8 * (p ^ (R & 7));
+}
+
+// One MFMA step over swizzled tiles: lane (r, g) reads piece pc (= 4g + j
+// for step j of a super-block, g for a tail block) of its rows.
+__device__ __forceinline__ void dma_step(const uint16_t* xt, const uint16_t* wt, int wm, int wn,
+                                         int r, int pc, floatx4 (&acc)[4][4]) {
+  bf16x8 A[4], Bv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    A[i] = *reinterpret_cast<const bf16x8*>(xt + swz(wm + 16 * i + r, pc));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    Bv[j] = *reinterpret_cast<const bf16x8*>(wt + swz(wn + 16 * j + r, pc));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i], Bv[j], acc[i][j], 0, 0, 0);
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+
+// dma_step with the operand reads issued from inline asm: the compiler
+// would otherwise wait for every outstanding DMA before any LDS read (it
+// cannot tell the buffers apart), stalling on the next super-block's X.
+// The reads complete inside the asm (lgkmcnt(0)). xa / wa: LDS byte
+// addresses of this lane's piece in rows wm + r and wn + r; the other rows
+// are 16 rows (4096 bytes) apart, at the same slot.
+__device__ __forceinline__ void dma_step_asm(uint32_t xa, uint32_t wa, floatx4 (&acc)[4][4]) {
+  bf16x8 A0, A1, A2, A3, B0, B1, B2, B3;
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:4096\n\t"
+      "ds_read_b128 %2, %8 offset:8192\n\t"
+      "ds_read_b128 %3, %8 offset:12288\n\t"
+      "ds_read_b128 %4, %9\n\t"
+      "ds_read_b128 %5, %9 offset:4096\n\t"
+      "ds_read_b128 %6, %9 offset:8192\n\t"
+      "ds_read_b128 %7, %9 offset:12288\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(A0), "=&v"(A1), "=&v"(A2), "=&v"(A3), "=&v"(B0), "=&v"(B1), "=&v"(B2), "=&v"(B3)
+      : "v"(xa), "v"(wa)
+      : "memory");
+  const bf16x8 A[4] = {A0, A1, A2, A3}, Bv[4] = {B0, B1, B2, B3};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i], Bv[j], acc[i][j], 0, 0, 0);
+}
+
+template <bool kR4>
+struct DmaRaw;
+template <>
+struct DmaRaw<true> {   // rows v*64 + tid/8, 16 sm bytes + 8 nibble bytes each
+  uint4 sm[2];
+  uint2 nb[2];
+};
+template <>
+struct DmaRaw<false> {  // rows v*32 + tid/16, 16 bytes each
+  uint4 w[4];
+};
+
+template <bool kR4>
+__device__ __forceinline__ void dma_wload(const GemmArgs& a, int32_t c0, int tid, int64_t n0,
+                                          uint32_t wo, uint32_t no, DmaRaw<kR4>& q) {
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+  if constexpr (kR4) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const uint8_t* bs = a.w + (n0 + v * 64) * a.k + c0;
+      const uint8_t* bn = a.nib + (n0 + v * 64) * (a.k >> 1) + (c0 >> 1);
+      q.sm[v] = z4;
+      q.nb[v] = make_uint2(0, 0);
+      if (n0 + v * 64 + (tid >> 3) < a.n) {
+        q.sm[v] = *reinterpret_cast<const uint4*>(bs + wo);
+        q.nb[v] = *reinterpret_cast<const uint2*>(bn + no);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint8_t* base = a.w + ((n0 + v * 32) * a.k + c0) * 2;
+      q.w[v] = z4;
+      if (n0 + v * 32 + (tid >> 4) < a.n) q.w[v] = *reinterpret_cast<const uint4*>(base + wo);
+    }
+  }
+}
+
+// One super-block of weights as this thread's 4 bf16 operand pieces
+// (rebuilt for R4: rows v*64 + tid/8, pieces 2q, 2q+1 of each; twin: rows
+// v*32 + tid/16, piece tid % 16).
+template <bool kR4>
+__device__ __forceinline__ void dma_wbuild(const GemmArgs& a, const Lut& L, int32_t c0, int tid,
+                                           int64_t n0, const DmaRaw<kR4>& q,
+                                           const EscTab (&tab)[2], int32_t tcol0,
+                                           uint4 (&wv)[4]) {
+  if constexpr (kR4) {
+    const int cc = 16 * (tid & 7);
+    uint32_t E[2][4];
+    uint32_t esc = 0;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      E[v][0] = lookup4(q.nb[v].x, L);
+      E[v][1] = lookup4(q.nb[v].x >> 4, L);
+      E[v][2] = lookup4(q.nb[v].y, L);
+      E[v][3] = lookup4(q.nb[v].y >> 4, L);
+      esc |= (0xEEEEEEEEu - q.nb[v].x) & q.nb[v].x & 0x88888888u;
+      esc |= (0xEEEEEEEEu - q.nb[v].y) & q.nb[v].y & 0x88888888u;
+    }
+    if (esc) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const int64_t n = n0 + v * 64 + (tid >> 3);
+        esc_patch_word(a, tab[v], n, c0 + cc, c0 + cc - tcol0, q.nb[v].x, E[v][0], E[v][1]);
+        esc_patch_word(a, tab[v], n, c0 + cc + 8, c0 + cc + 8 - tcol0, q.nb[v].y, E[v][2],
+                       E[v][3]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const uint2 p0 = bf16_pairs4(q.sm[v].x, E[v][0]), p1 = bf16_pairs4(q.sm[v].y, E[v][1]);
+      const uint2 p2 = bf16_pairs4(q.sm[v].z, E[v][2]), p3 = bf16_pairs4(q.sm[v].w, E[v][3]);
+      wv[2 * v] = make_uint4(p0.x, p0.y, p1.x, p1.y);
+      wv[2 * v + 1] = make_uint4(p2.x, p2.y, p3.x, p3.y);
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wv[v] = q.w[v];
+  }
+}
+
+template <bool kR4>
+__device__ __forceinline__ void dma_wstore(int tid, uint16_t* wt, const uint4 (&wv)[4]) {
+  if constexpr (kR4) {
+    const int qq = tid & 7;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int row = v * 64 + (tid >> 3);
+      *reinterpret_cast<uint4*>(wt + swz(row, 2 * qq)) = wv[2 * v];
+      *reinterpret_cast<uint4*>(wt + swz(row, 2 * qq + 1)) = wv[2 * v + 1];
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      *reinterpret_cast<uint4*>(wt + swz(v * 32 + (tid >> 4), tid & 15)) = wv[v];
+  }
+}
+
+template <bool kR4, bool kSplit>
+__global__ __launch_bounds__(kDmaThreads, 2) void gemm_dma_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t xt[2][kDmaBM * kSB];
+  __shared__ __attribute__((aligned(16))) uint16_t wt[kBN * kSB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(static_cast<int>(tid >> 6));
+  const int64_t tiles_n = (a.n + kBN - 1) / kBN, tiles_m = (a.m + kDmaBM - 1) / kDmaBM;
+  const int32_t S = a.slices;
+  const int64_t items = tiles_n * tiles_m * (kSplit ? S : 1);
+  const int64_t per = (items + kXcds - 1) / kXcds;
+  const int64_t item = static_cast<int64_t>(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (item >= items) return;
+  const int64_t tile = kSplit ? item / S : item;
+  const int32_t s_only = kSplit ? static_cast<int32_t>(item - tile * S) : 0;
+  const int64_t n0 = (tile / tiles_m) * kBN;
+  const int64_t m0 = (tile % tiles_m) * kDmaBM;
+  const int wm = (wave >> 1) * 64;
+  const int wn = (wave & 1) * 64;
+  uint32_t l0 = a.lut0, l1 = a.lut1, l2 = a.lut2, l3 = a.lut3;
+  asm volatile("" : "+v"(l0), "+v"(l1), "+v"(l2), "+v"(l3));
+  const Lut L{l0, l1, l2, l3};
+  const int r = lane & 15, g = lane >> 4;
+
+  floatx4 acc[4][4], tot[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tot[i][j] = acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int32_t nsb = a.k / kSB;
+  int32_t s = s_only, u_lo, s_hi;
+  slice_superblocks(a.k, S, s, u_lo, s_hi);
+  const int32_t u_first = u_lo;
+  const int32_t u_end = kSplit ? s_hi : nsb;
+  const bool with_tail = !kSplit || s_only == S - 1;
+
+  // X: this wave's 8 DMA pieces per super-block, rows (8 wave + q) * 4 +
+  // lane / 16 of the tile (rows past M read row M-1: never stored), each
+  // lane loading the piece that belongs at its slot
+  const uint8_t* xtile = reinterpret_cast<const uint8_t*>(a.x + m0 * a.ldx);
+  const int32_t xrows = static_cast<int32_t>(min(static_cast<int64_t>(kDmaBM), a.m - m0));
+  const int32_t ldx2 = static_cast<int32_t>(a.ldx) * 2;
+  // byte offset of DMA piece qd of this lane from the super-block's start
+  auto xoff = [&](int qd) -> uint32_t {
+    const int R = (8 * wave + qd) * 4 + (lane >> 4);
+    const int pc = (lane & 15) ^ (R & 7);
+    return static_cast<uint32_t>(min(R, xrows - 1) * ldx2 + 16 * pc);
+  };
+  const uint32_t wo = kR4 ? static_cast<uint32_t>((tid >> 3) * a.k + 16 * (tid & 7))
+                          : static_cast<uint32_t>(((tid >> 4) * a.k + 8 * (tid & 15)) * 2);
+  const uint32_t no = static_cast<uint32_t>((tid >> 3) * (a.k >> 1) + 8 * (tid & 7));
+
+  EscTab tab[2];
+  int32_t tcol0 = u_lo * kSB;
+  auto build_tabs = [&](int32_t c0) {
+    tcol0 = c0;
+    const int32_t c1 = min(a.k, (c0 / kEscRange + 1) * kEscRange);
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int64_t n = n0 + v * 64 + (tid >> 3);
+      if (n < a.n) {
+        esc_tab_build(a, n, c0, c1, tab[v]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tab[v].ent[i] = 0xFFFFu;
+        tab[v].over = 0;
+      }
+    }
+  };
+
+  if (u_lo < u_end) {
+    DmaRaw<kR4> q;
+    uint4 wv[4];
+    dma_wload<kR4>(a, u_lo * kSB, tid, n0, wo, no, q);
+#pragma unroll
+    for (int qd = 0; qd < 8; ++qd)
+      dma16(xtile + u_lo * kSB * 2 + xoff(qd), &xt[0][(8 * wave + qd) * 4 * kSB]);
+    if (kR4) build_tabs(u_lo * kSB);
+    for (int32_t u = u_lo; u < u_end; ++u) {
+      const int b = (u - u_first) & 1;
+      if (kR4 && u != u_first && (u * kSB) % kEscRange == 0) build_tabs(u * kSB);
+      dma_wait();
+      lds_barrier();   // compute of u-1 done everywhere; X(u) in LDS
+      if constexpr (kR4) {
+        // this super-block's weights, loaded during the previous products
+        dma_wbuild<kR4>(a, L, u * kSB, tid, n0, q, tab, tcol0, wv);
+        dma_wstore<kR4>(tid, wt, wv);
+      } else {
+        dma_wstore<kR4>(tid, wt, q.w);
+      }
+      if (u + 1 < u_end) {
+        dma_wload<kR4>(a, (u + 1) * kSB, tid, n0, wo, no, q);
+#pragma unroll
+        for (int qd = 0; qd < 8; ++qd)
+          dma16(xtile + (u + 1) * kSB * 2 + xoff(qd), &xt[b ^ 1][(8 * wave + qd) * 4 * kSB]);
+      }
+      lds_barrier();   // W(u) in LDS; the loads for u + 1 stay in flight
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dma_step_asm(lds_addr(xt[b] + swz(wm + r, 4 * g + j)),
+                     lds_addr(wt + swz(wn + r, 4 * g + j)), acc);
+      if (!kSplit && u + 1 == s_hi && s + 1 < S) {
+        fold<4>(s, acc, tot);
+        ++s;
+        slice_superblocks(a.k, S, s, u_lo, s_hi);
+      }
+    }
+  }
+  if (with_tail) {
+    // 32-column tail blocks: plain stores into the same swizzled tiles
+    for (int32_t c0 = nsb * kSB; c0 < a.k; c0 += 32) {
+      __syncthreads();
+      {
+        const int row = tid >> 1, p0 = 2 * (tid & 1);
+        const int64_t xm = min(m0 + row, a.m - 1);
+        const uint4* px = reinterpret_cast<const uint4*>(a.x + xm * a.ldx + c0 + 8 * p0);
+        *reinterpret_cast<uint4*>(&xt[0][swz(row, p0)]) = px[0];
+        *reinterpret_cast<uint4*>(&xt[0][swz(row, p0 + 1)]) = px[1];
+      }
+      {
+        const int row = tid >> 2, pc = tid & 3;
+        const int64_t wn_ = min(n0 + row, a.n - 1);
+        const int32_t c = c0 + 8 * pc;
+        uint4 v;
+        if constexpr (kR4)
+          v = rebuild8(a, L, *reinterpret_cast<const uint2*>(a.w + wn_ * a.k + c),
+                       *reinterpret_cast<const uint32_t*>(a.nib + wn_ * (a.k >> 1) + (c >> 1)),
+                       wn_, c);
+        else
+          v = *reinterpret_cast<const uint4*>(a.w + 2 * (wn_ * a.k + c));
+        *reinterpret_cast<uint4*>(&wt[swz(row, pc)]) = v;
+      }
+      __syncthreads();
+      dma_step(xt[0], wt, wm, wn, r, g, acc);
+    }
+  }
+
+  if (kSplit && S > 1) {
+    float* part = a.part + static_cast<int64_t>(s_only) * a.m * a.n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t on = n0 + wn + 16 * j + r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t om = m0 + wm + 16 * i + 4 * g + e;
+          if (om < a.m && on < a.n) part[om * a.n + on] = acc[i][j][e];
+        }
+      }
+    return;
+  }
+  if (!kSplit) fold<4>(s, acc, tot);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t on = n0 + wn + 16 * j + r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        store_out(a, m0 + wm + 16 * i + 4 * g + e, on, kSplit ? acc[i][j][e] : tot[i][j][e]);
+    }
+}
+
 // y[m][n] = ((p0 + p1) + p2) + ... over the S (<= 8) slice partials, in
 // slice order. Block (x, y): row y, columns 1024x .. 1024x+1023, four per
 // thread; every slice's load is issued before the adds.
@@ -1140,12 +1501,25 @@ void launch_large(const GemmArgs& a, bool split, int64_t blocks, hipStream_t str
     hipLaunchKernelGGL((gemm_large_kernel<kR4, BM, NJ, false>), grid, block, 0, stream, a);
 }
 
+// M above 128 runs the DMA-fed tiled kernel (256-row tiles) when its 32-bit
+// per-lane X offsets fit (255 rows of ldx elements).
+#ifndef BINADE_GEMM_DMA
+#define BINADE_GEMM_DMA 1
+#endif
+
 template <bool kR4>
 void launch_large_cfg(const GemmArgs& a, const Plan& p, hipStream_t stream) {
-  if (p.nj == 2)
+  if (p.nj == 2) {
     launch_large<kR4, 128, 2>(a, p.split, p.blocks, stream);
-  else
+  } else if (BINADE_GEMM_DMA && BINADE_GEMM_LARGE_BM == kDmaBM && a.ldx < (1 << 23)) {
+    const dim3 grid(static_cast<uint32_t>(p.blocks)), block(kDmaThreads);
+    if (p.split)
+      hipLaunchKernelGGL((gemm_dma_kernel<kR4, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_dma_kernel<kR4, false>), grid, block, 0, stream, a);
+  } else {
     launch_large<kR4, BINADE_GEMM_LARGE_BM, 4>(a, p.split, p.blocks, stream);
+  }
 }
 
 int32_t launch(GemmArgs a, bool r4, void* workspace, int64_t workspace_bytes,
