@@ -289,6 +289,40 @@ def test_gemm_random_twin_and_f64(mnk):
     assert np.array_equal(bits_np(Yb), oracle.f32_to_bf16(Y.numpy()))
 
 
+@pytest.mark.parametrize("m", [16, 30, 33, 300])
+def test_gemm_strided_x_and_y(m):
+    """X and Y wider than the product (ldx = K + 72, ldy = N + 8) through the
+    C ABI, on the streamed (M <= 32), tiled (33) and DMA-fed (300) kernels:
+    the same bits as the contiguous call, and Y's padding columns untouched."""
+    import ctypes
+    N, K = 136, 4160
+    W = synth.normal_bf16(spec(N, K, 0.015, m, 2e-3, 1e3))
+    X = synth.vector_bf16(K, m + 3, count=m)
+    _, r4 = to_r4(W)
+    Xd = X.to(DEV)
+    ref = B.r4_gemm(r4, Xd).cpu()
+    xw = torch.zeros(m, K + 72, dtype=torch.bfloat16, device=DEV)
+    xw[:, :K] = Xd
+    sentinel = -12345.0
+    for r4_side in (True, False):
+        yw = torch.full((m, N + 8), sentinel, dtype=torch.float32, device=DEV)
+        nb = B.gemm_workspace_bytes(m, N, K)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+        st = B._stream(None)
+        if r4_side:
+            d = r4.desc()
+            B._call("binade_r4_gemm", ctypes.byref(d), B._ptr(xw), m, xw.stride(0), B._ptr(yw),
+                    yw.stride(0), B.F32, B._ptr(ws), nb, st)
+        else:
+            wd = W.to(DEV)
+            B._call("binade_bf16_gemm", B._ptr(wd), N, K, B._ptr(xw), m, xw.stride(0),
+                    B._ptr(yw), yw.stride(0), B.F32, B._ptr(ws), nb, st)
+        torch.cuda.synchronize()
+        y = yw.cpu()
+        assert torch.equal(y[:, :N].contiguous().view(torch.int32), ref.view(torch.int32))
+        assert torch.all(y[:, N:] == sentinel)
+
+
 # ---------------------------------------------------------- batched launches
 def test_batched_decode_and_gemv_equal_single_calls():
     shapes = [(300, 3072), (64, 8192), (37, 96), (4100, 256), (5, 4160), (1024, 1024),
