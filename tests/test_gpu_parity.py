@@ -271,7 +271,8 @@ def test_gemm_small_integers_exact_and_twin(mnk):
 
 
 @pytest.mark.parametrize("mnk", [(16, 128, 3840), (32, 96, 15360), (130, 64, 3840),
-                                 (7, 33, 512), (24, 1000, 1024), (20, 300, 4160)])
+                                 (7, 33, 512), (24, 1000, 1024), (20, 300, 4160),
+                                 (260, 96, 8192), (520, 130, 4160)])
 def test_gemm_random_twin_and_f64(mnk):
     M, N, K = mnk
     W = synth.normal_bf16(spec(N, K, 0.015, M, 1e-3, 20.0))
