@@ -646,6 +646,9 @@ __device__ __forceinline__ uint32_t lds_address(const uint32_t* p) {
 __device__ __forceinline__ void lds_or(uint32_t addr, uint32_t v) {
   __hip_atomic_fetch_or((lds_u32*)addr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+__device__ __forceinline__ void lds_and(uint32_t addr, uint32_t v) {
+  __hip_atomic_fetch_and((lds_u32*)addr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
 // Nibbles of 8 weights in weight order (weight i at bits 4i) -> R4 order
 // (weight i in byte i % 4, high nibble for i >= 4).
@@ -716,7 +719,11 @@ __device__ __forceinline__ void byte_walk(const uint32_t (&x)[4], int32_t c, uin
         const uint32_t v = e[jj].x | static_cast<uint32_t>(min(max(t, 0), 15));
         // v << (sb % 32) over the word holding nibble sb / 4 and the next
         const uint64_t w = static_cast<uint64_t>(v) << (sb & 31u);
-        const uint32_t addr = nb + (__builtin_amdgcn_ubfe(sb, 5, 27) << 2);
+        // nb + 4 * (sb / 32), as two instructions
+        uint32_t addr;
+        asm("v_bfe_u32 %0, %1, 5, 27\n\tv_lshl_add_u32 %0, %0, 2, %2"
+            : "=&v"(addr)
+            : "v"(sb), "v"(nb));
         lds_or(addr, static_cast<uint32_t>(w));
         lds_or(addr + 4u, static_cast<uint32_t>(w >> 32));
       }
@@ -828,22 +835,15 @@ __device__ __forceinline__ void decode_job_bytes(const RiceArgs& a, const uint8_
   const uint32_t nw = (Brel + 31u) >> 5;                           // <= 255
   const uint32_t spl = (((nbits + 7u) >> 3) + 63u) >> 6;           // 1..16
 
-  // ---- stage the job's unary words (bits outside the job cleared, zeros
-  // up to word 259) and remainder words; clear the nibble buffer
+  // ---- stage the job's unary words (words past the job are already zero;
+  // the bits past its end in its last word are cleared; the bits before its
+  // first bit are never read), zeros up to word 259, and its remainder
+  // words; clear the nibble buffer
   {
-    const uint32_t i0 = 4u * lane;
-    const uint32_t last = nw - 1u;
-    const uint32_t keep_last = 0xFFFFFFFFu >> (31u - ((Brel - 1u) & 31u));
-    uint32_t v[4] = {f.w.x, f.w.y, f.w.z, f.w.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t i = i0 + q;
-      if (i >= nw) v[q] = 0u;
-      if (i == 0u) v[q] &= 0xFFFFFFFFu << uA;
-      if (i == last) v[q] &= keep_last;
-    }
-    reinterpret_cast<uint4*>(stage)[lane] = make_uint4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<uint4*>(stage)[lane] = f.w;
     if (lane < 4) stage[256 + lane] = 0u;
+    if (lane == 0)
+      lds_and(lds_address(stage + (nw - 1u)), 0xFFFFFFFFu >> (31u - ((Brel - 1u) & 31u)));
     remw[lane] = f.rw0;
     remw[64 + lane] = f.rw1;
     reinterpret_cast<uint4*>(nibw)[lane] = make_uint4(0u, 0u, 0u, 0u);
