@@ -105,30 +105,39 @@ static_assert(kByteNib % 4 == 0 && kWaveWords % 4 == 0, "16-byte aligned LDS reg
 // bit of each weight's nibble in R4 order (weight i -> byte i % 4, high
 // nibble for i >= 4).
 constexpr int32_t kNoCode = -(1 << 30);
-// The table entry of byte value b for Rice parameter k (words as above),
-// computed by each thread of a block for its own b (no table in memory).
-__device__ __forceinline__ uint4 byte_entry(uint32_t k, uint32_t b) {
-  uint32_t nib = 0, m = 0, first = 0, prev = 0;
-#pragma unroll
-  for (uint32_t i = 0; i < 8; ++i) {
-    if (((b >> i) & 1u) == 0u) continue;
-    if (m == 0)
-      first = i;
-    else
-      nib |= ((i - prev - 1u) << k) << (4u * m);
-    prev = i;
-    ++m;
+// Both tables for k = 1 (the byte-table path's k), built at compile time and
+// copied into each block's LDS at its start.
+struct ByteTables {
+  uint32_t lut[256][4];
+  uint32_t spread[256];
+};
+
+__host__ __device__ constexpr ByteTables make_byte_tables() {
+  constexpr uint32_t k = 1;
+  ByteTables t{};
+  for (uint32_t b = 0; b < 256; ++b) {
+    uint32_t nib = 0, m = 0, first = 0, prev = 0;
+    for (uint32_t i = 0; i < 8; ++i) {
+      if (((b >> i) & 1u) == 0u) continue;
+      if (m == 0)
+        first = i;
+      else
+        nib |= ((i - prev - 1u) << k) << (4u * m);
+      prev = i;
+      ++m;
+    }
+    t.lut[b][0] = nib;
+    t.lut[b][1] = m ? first << k : static_cast<uint32_t>(kNoCode);
+    t.lut[b][2] = 4u * m;
+    t.lut[b][3] = m ? (7u - prev) << k : 0x7FFFFFFFu;
+    uint32_t v = 0;
+    for (uint32_t i = 0; i < 8; ++i) v |= ((b >> i) & 1u) << (8u * (i & 3u) + 4u * (i >> 2));
+    t.spread[b] = v;
   }
-  return make_uint4(nib, m ? first << k : static_cast<uint32_t>(kNoCode), 4u * m,
-                    m ? (7u - prev) << k : 0x7FFFFFFFu);
+  return t;
 }
 
-__device__ __forceinline__ uint32_t spread_entry(uint32_t r) {
-  uint32_t v = 0;
-#pragma unroll
-  for (uint32_t i = 0; i < 8; ++i) v |= ((r >> i) & 1u) << (8u * (i & 3u) + 4u * (i >> 2));
-  return v;
-}
+__device__ const ByteTables kByteTables = make_byte_tables();
 
 struct RiceArgs {
   const uint32_t* unary;
@@ -999,12 +1008,12 @@ __device__ __forceinline__ void decode_job_bytes(const RiceArgs& a, const uint8_
   }
 }
 
-// The byte tables for Rice k = 1 (the byte-table path's k), computed, one entry per
-// thread of the 256-thread block.
+// The byte tables into LDS, one entry of each per thread of the 256-thread
+// block.
 __device__ __forceinline__ void load_byte_tables(uint4* lut, uint32_t* spread) {
   const uint32_t t = threadIdx.x;
-  lut[t] = byte_entry(1u, t);
-  spread[t] = spread_entry(t);
+  lut[t] = *reinterpret_cast<const uint4*>(kByteTables.lut[t]);
+  spread[t] = kByteTables.spread[t];
   __syncthreads();
 }
 
