@@ -309,7 +309,7 @@ def rice_to_r4(planes: RicePlanes, status: torch.Tensor | None = None,
 
 def rice_to_r4_batch(planes: list, status: torch.Tensor | None = None,
                      stream=None, outs: list | None = None) -> list:
-    """binade_rice_to_r4_batch: decode several tensors (up to 8 per launch)."""
+    """binade_rice_to_r4_batch: decode several tensors (up to 16 per launch)."""
     n = len(planes)
     if outs is None:
         outs = []

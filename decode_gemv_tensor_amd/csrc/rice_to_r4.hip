@@ -167,15 +167,11 @@ struct RiceArgs {
   uint32_t unit;            // distance between row-chunk starts in a job: 2048 or cols
   uint32_t unit_recip;      // ceil(2^32 / unit): i / unit = mulhi(i, unit_recip) for i <= 4096
   int64_t jobs;
-  uint32_t table[64];       // exp_of_rank, 4 bytes per word
+  // the exponents of ranks 15 .. n-1 (only escapes look them up) sit in
+  // the launch's argument pool; esc_tbl: byte offset of rank 15's, from the
+  // start of the launch's arguments
+  uint32_t esc_tbl;
 };
-
-// The rank -> exponent table of a kernel's tensor, read in place from the
-// kernel's argument segment (only escapes look it up).
-__device__ __forceinline__ const uint8_t* kernarg_table(size_t args_offset) {
-  return (const uint8_t*)__builtin_amdgcn_kernarg_segment_ptr() + args_offset +
-         offsetof(RiceArgs, table);
-}
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -1017,14 +1013,17 @@ __device__ __forceinline__ void load_byte_tables(uint4* lut, uint32_t* spread) {
   __syncthreads();
 }
 
-// Up to 8 tensors per launch: tensor i owns the launch's jobs
-// [first_job[i], first_job[i+1]).
-constexpr int kMaxDecodeBatch = 8;
+// Up to 16 tensors per launch: tensor i owns the launch's jobs
+// [first_job[i], first_job[i+1]). Their escape exponents share one pool.
+constexpr int kMaxDecodeBatch = 16;
+constexpr int kEscPool = 1024;
 struct RiceBatch {
   RiceArgs item[kMaxDecodeBatch];
   uint32_t first_job[kMaxDecodeBatch + 1];
   int32_t count;
+  uint8_t pool[kEscPool];
 };
+static_assert(sizeof(RiceBatch) <= 4096, "kernel arguments of one decode launch");
 
 // One wave per job (job g of the launch is wave g). The tensor's arguments
 // are read in place from the argument segment (an index into a by-value
@@ -1044,7 +1043,11 @@ __global__ __launch_bounds__(256, BINADE_DECODE_MIN_WAVES) void rice_to_r4_batch
     if (t < b.count && g >= b.first_job[t]) i = t;
   i = uniform(i);
   const size_t off = offsetof(RiceBatch, item) + static_cast<size_t>(i) * sizeof(RiceArgs);
-  const RiceArgs& a = *(const RiceArgs*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + off);
+  const char* kp = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+  const RiceArgs& a = *(const RiceArgs*)(kp + off);
+  // table[r] for 15 <= r < n (every lookup is of an escape whose rank was
+  // checked against n)
+  const uint8_t* table = (const uint8_t*)kp + a.esc_tbl - 15;
   Job job;
   JobLoads L;
   bool bytes = false;
@@ -1058,7 +1061,7 @@ __global__ __launch_bounds__(256, BINADE_DECODE_MIN_WAVES) void rice_to_r4_batch
   load_byte_tables(lut, spread);
   if (!live) return;
   if (bytes) {
-    decode_job_bytes<1>(a, kernarg_table(off), job, L, lane, lds[wave], lut, spread);
+    decode_job_bytes<1>(a, table, job, L, lane, lds[wave], lut, spread);
     return;
   }
   // general path: each run of the job
@@ -1068,7 +1071,7 @@ __global__ __launch_bounds__(256, BINADE_DECODE_MIN_WAVES) void rice_to_r4_batch
     Prefetch pf;
     prefetch_bounds(a, run, pf);
     prefetch_words(a, run, lane, pf);
-    decode_run(a, kernarg_table(off), run, pf, lane, lds[wave], lds[wave] + (kStageWords + 4),
+    decode_run(a, table, run, pf, lane, lds[wave], lds[wave] + (kStageWords + 4),
                lds[wave] + kGeneralWords + lane);
     wave_sync();   // the next run reuses the same LDS
   }
@@ -1151,10 +1154,6 @@ int64_t prepare_decode(const binade_rice* in, binade_r4* out, uint32_t* dev_stat
     a.unit_recip = in->cols > 1 ? recip(static_cast<uint64_t>(in->cols)) : 0u;
     a.jobs = (in->rows + 2 * G - 1) / (2 * G);
   }
-  for (int q = 0; q < 64; ++q)
-    a.table[q] = uint32_t(in->exp_of_rank[4 * q]) | (uint32_t(in->exp_of_rank[4 * q + 1]) << 8) |
-                 (uint32_t(in->exp_of_rank[4 * q + 2]) << 16) |
-                 (uint32_t(in->exp_of_rank[4 * q + 3]) << 24);
   return a.jobs;
 }
 
@@ -1186,12 +1185,16 @@ extern "C" int32_t binade_rice_to_r4_batch(const binade_rice* in, binade_r4* out
   RiceBatch b{};
   int n = 0;
   uint64_t jobs = 0;
+  uint32_t pool = 0;   // bytes of the escape pool in use
   for (int32_t i = 0; i < count; ++i) {
     RiceArgs a;
     const int64_t nj = prepare_decode(&in[i], &out[i], dev_status, a);
     if (nj < 0) return static_cast<int32_t>(nj);
-    // a launch holds up to 8 tensors and fewer than 2^31 jobs
-    if (n == kMaxDecodeBatch || jobs + static_cast<uint64_t>(nj) >= (1ull << 31)) {
+    const uint32_t esc_bytes = in[i].n > 15 ? in[i].n - 15 : 0;   // <= 241
+    // a launch holds up to 16 tensors, their escape exponents and fewer
+    // than 2^31 jobs
+    if (n == kMaxDecodeBatch || pool + esc_bytes > static_cast<uint32_t>(kEscPool) ||
+        jobs + static_cast<uint64_t>(nj) >= (1ull << 31)) {
       b.first_job[n] = static_cast<uint32_t>(jobs);
       b.count = n;
       const int32_t s = launch_batch(b, st);
@@ -1199,8 +1202,12 @@ extern "C" int32_t binade_rice_to_r4_batch(const binade_rice* in, binade_r4* out
       b = RiceBatch{};
       n = 0;
       jobs = 0;
+      pool = 0;
     }
     if (static_cast<uint64_t>(nj) >= (1ull << 31)) return BINADE_EUNSUPPORTED;
+    for (uint32_t r = 0; r < esc_bytes; ++r) b.pool[pool + r] = in[i].exp_of_rank[15 + r];
+    a.esc_tbl = static_cast<uint32_t>(offsetof(RiceBatch, pool)) + pool;
+    pool += esc_bytes;
     b.item[n] = a;
     b.first_job[n] = static_cast<uint32_t>(jobs);
     jobs += static_cast<uint64_t>(nj);

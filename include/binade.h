@@ -178,7 +178,7 @@ int32_t binade_pack_rice(const uint16_t *w, int64_t rows, int64_t cols,
 int32_t binade_rice_to_r4(const binade_rice *in, binade_r4 *out,
                           uint32_t *dev_status, void *stream);
 
-/* Format 2 -> R4 for count tensors, up to 8 per launch (a model's load-time
+/* Format 2 -> R4 for count tensors, up to 16 per launch (a model's load-time
  * decode): in[i] and out[i] as for binade_rice_to_r4; the same kernel and
  * results. The argument checks of every tensor run before its launch. */
 int32_t binade_rice_to_r4_batch(const binade_rice *in, binade_r4 *out,

@@ -1,5 +1,5 @@
 """GPU parity at the benchmark's full sizes, in the launch configurations the
-benchmark times (batched decode of up to 8 tensors per launch, batched
+benchmark times (batched decode of up to 16 tensors per launch, batched
 GEMV of up to 16, the prompt GEMM with its workspace).
 
 Whole-output checks need no oracle: R4 equals the oracle's R4 of the
@@ -48,7 +48,7 @@ def check_r4_against_oracle(name, wb: np.ndarray, r4) -> None:
 
 
 def decode_and_gemv(specs, sample_rows=48, seed=0):
-    """Decode the tensors in one batched call (8 per launch), multiply each by
+    """Decode the tensors in one batched call (16 per launch), multiply each by
     its own vector in one batched GEMV call (16 per launch), and check both
     at full size."""
     ws = [synth.normal_bf16(sp) for sp in specs]

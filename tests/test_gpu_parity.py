@@ -352,6 +352,39 @@ def test_batched_decode_and_gemv_equal_single_calls():
         assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), shapes[i]
 
 
+def test_batched_decode_splits_on_wide_tables():
+    """Tensors whose tables hold many exponents (their escape exponents fill
+    a launch's argument pool after a few tensors): the batched call splits
+    into several launches and still equals the single calls."""
+    def wide(rows, cols, seed, spread_frac):
+        # N(0, 0.02), with a fraction of the weights given exponents spread
+        # over 2^-100 .. 2^100
+        g = torch.Generator().manual_seed(seed)
+        w = torch.randn(rows, cols, generator=g) * 0.02
+        pick = torch.rand(rows, cols, generator=g) < spread_frac
+        e = torch.randint(-100, 100, (rows, cols), generator=g).to(torch.float32)
+        return torch.where(pick, w.sign() * torch.exp2(e), w).to(torch.bfloat16)
+
+    # Rice k = 1 (byte-table path) and k = 5 (general path) in turn
+    ws = [wide(64 + 16 * i, 512 + 1536 * (i % 2), 600 + i, 0.5 if i % 2 else 0.005)
+          for i in range(12)]
+    planes = [B.pack_rice(w).to(DEV) for w in ws]
+    assert min(p.table.n for p in planes) > 100
+    assert {p.k for p in planes} == {1, 5}
+    assert sum(p.table.n - 15 for p in planes) > 1024   # more than one launch's pool
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    outs = B.rice_to_r4_batch(planes, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for w, o in zip(ws, outs):
+        wn = bits_np(w)
+        ref = oracle.make_r4(wn, oracle.build_table(wn))
+        assert o.n_esc == ref["n_esc"] and o.n_esc > 0
+        assert np.array_equal(o.nib.cpu().numpy(), ref["nib"].reshape(-1))
+        assert np.array_equal(o.esc[: o.n_esc].cpu().numpy().view(np.uint32), ref["esc"])
+        assert np.array_equal(bits_np(B.unpack(o)), wn)
+
+
 @pytest.mark.parametrize("nk", [(200, 15360), (136, 8192), (72, 3840), (72, 4160), (40, 96)])
 def test_gemm_rows_do_not_depend_on_m(nk):
     """The GEMM order depends on K only: the same X row gives the same bits
