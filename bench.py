@@ -332,7 +332,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: "
-              "this build runs the single-GPU path only", file=sys.stderr)
+              "the library runs on a single GPU (no sharding across GPUs)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
