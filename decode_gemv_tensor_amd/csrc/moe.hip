@@ -16,9 +16,9 @@
 // in turn. A job finds with one ballot per 64 pairs the pairs that chose its
 // expert, loads its rows' escape metadata once (escape prefixes and
 // side-list entries, a lane each), and walks each row set once per pair:
-// lane tiles rebuilt with v_perm_b32 table lookups, escapes patched from
-// registers. A second pair of the same expert re-reads the rows the wave
-// has just read, from cache.
+// lane tiles rebuilt through an LDS table of exponent pairs (one lookup per
+// nibble byte), escapes patched from registers. A second pair of the same
+// expert re-reads the rows the wave has just read, from cache.
 //
 // A packed row's slots 32, 16, ... down to its group width hold no tile, so
 // the matvec's tree adds +0.0 to each of the group's slots at those levels;
@@ -74,18 +74,40 @@ __device__ __forceinline__ void store_out(const MoeArgs& a, int64_t i, float v) 
     static_cast<float*>(a.y)[i] = v;
 }
 
+// Exponent table of pairs in LDS: entry b, for a byte b of an R4 nibble
+// word (rank of weight i in its low nibble, of weight i + 4 in its high
+// nibble), holds the two rotated exponents, low byte first. One lookup per
+// byte replaces two 16-entry v_perm lookups (this kernel is bound by its
+// instruction issue).
+__device__ __forceinline__ void build_pair_table(const MoeArgs& a, uint16_t* pt) {
+  const uint32_t b = threadIdx.x;   // 256 threads, one entry each
+  const uint32_t t[4] = {a.lut0, a.lut1, a.lut2, a.lut3};
+  const uint32_t lo = (t[(b & 15) >> 2] >> (8 * (b & 3))) & 0xFFu;
+  const uint32_t hi = (t[b >> 6] >> (8 * ((b >> 4) & 3))) & 0xFFu;
+  pt[b] = static_cast<uint16_t>(lo | (hi << 8));
+}
+
+// The exponents of the 8 weights of nibble word P: lo for weights 0..3,
+// hi for 4..7 (bytes in weight order).
+__device__ __forceinline__ void pair_lookup8(uint32_t P, const uint16_t* pt, uint32_t& lo,
+                                             uint32_t& hi) {
+  const uint32_t A = pt[P & 0xFFu] | (static_cast<uint32_t>(pt[(P >> 8) & 0xFFu]) << 16);
+  const uint32_t B = pt[(P >> 16) & 0xFFu] | (static_cast<uint32_t>(pt[P >> 24]) << 16);
+  lo = __builtin_amdgcn_perm(B, A, 0x06040200u);   // A = e0 e4 e1 e5, B = e2 e6 e3 e7
+  hi = __builtin_amdgcn_perm(B, A, 0x07050301u);
+}
+
 // Exponent dwords of one lane tile of a packed wave: table lookups, then
 // every packed row's escapes (uniform loop per row; the lane holding the
 // entry's tile patches it).
-__device__ __forceinline__ void moe_tile_exponents(const MoeArgs& a, uint4 nb, const Lut& L,
+__device__ __forceinline__ void moe_tile_exponents(const MoeArgs& a, uint4 nb, const uint16_t* pt,
                                                    int64_t grow0, int64_t n_valid, int G,
                                                    int wl, int C, int j, int lane,
                                                    uint32_t (&E)[8]) {
   const uint32_t P[4] = {nb.x, nb.y, nb.z, nb.w};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    E[2 * q] = lookup4(P[q], L);
-    E[2 * q + 1] = lookup4(P[q] >> 4, L);
+    pair_lookup8(P[q], pt, E[2 * q], E[2 * q + 1]);
   }
   const int gi = lane >> wl;
   for (int r = 0; r < G; ++r) {
@@ -224,7 +246,7 @@ __device__ __forceinline__ void moe_load(const MoeArgs& a, int64_t grow, int t, 
 
 // One lane tile's 32 weights as fp32 (escapes patched for R4).
 template <bool kR4>
-__device__ __forceinline__ void moe_weights(const MoeArgs& a, const MoeRaw<kR4>& r, const Lut& L,
+__device__ __forceinline__ void moe_weights(const MoeArgs& a, const MoeRaw<kR4>& r, const uint16_t* pt,
                                             bool regs, uint32_t pre_lane, uint32_t ent_lane,
                                             uint32_t e0, int cbase, int64_t grow0,
                                             int64_t n_valid, int G, int wl, int C, int j,
@@ -235,13 +257,12 @@ __device__ __forceinline__ void moe_weights(const MoeArgs& a, const MoeRaw<kR4>&
       const uint32_t P[4] = {r.nb.x, r.nb.y, r.nb.z, r.nb.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        E[2 * q] = lookup4(P[q], L);
-        E[2 * q + 1] = lookup4(P[q] >> 4, L);
+        pair_lookup8(P[q], pt, E[2 * q], E[2 * q + 1]);
       }
       moe_patch_regs(pre_lane, ent_lane, e0, cbase, static_cast<int>(n_valid), C, j, wl, G, lane,
                      E);
     } else {
-      moe_tile_exponents(a, r.nb, L, grow0, n_valid, G, wl, C, j, lane, E);
+      moe_tile_exponents(a, r.nb, pt, grow0, n_valid, G, wl, C, j, lane, E);
     }
     const uint32_t S[8] = {r.s0.x, r.s0.y, r.s0.z, r.s0.w, r.s1.x, r.s1.y, r.s1.z, r.s1.w};
 #pragma unroll
@@ -273,7 +294,7 @@ __device__ __forceinline__ void moe_weights(const MoeArgs& a, const MoeRaw<kR4>&
 // register count (and so the waves per SIMD) where this latency-bound
 // kernel wants it.
 template <bool kR4>
-__device__ __forceinline__ void moe_rows(const MoeArgs& a, const Lut& L, int32_t e, int64_t row0,
+__device__ __forceinline__ void moe_rows(const MoeArgs& a, const uint16_t* pt, int32_t e, int64_t row0,
                                          int G, int gi, int ti, int wl, int J, int C, int lane,
                                          const int32_t* idx_s) {
   const int64_t left = a.n_rows - row0;
@@ -325,7 +346,7 @@ __device__ __forceinline__ void moe_rows(const MoeArgs& a, const Lut& L, int32_t
           MoeRaw<kR4> rj;
           moe_load<kR4>(a, grow, t, active, rj);
           float w[32];
-          moe_weights<kR4>(a, rj, L, regs, pre_lane, ent_lane, e0, cbase, grow0, n_valid, G, wl,
+          moe_weights<kR4>(a, rj, pt, regs, pre_lane, ent_lane, e0, cbase, grow0, n_valid, G, wl,
                            C, j, lane, w);
           if (!active) continue;
           const int64_t xrow = a.x_per_slot ? pp : pp / a.top_k;
@@ -359,6 +380,8 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(MoeArgs a) {
   __shared__ uint32_t before[kMaxExpertWords];
   __shared__ int32_t idx_s[kMaxPairsLds];
   __shared__ uint32_t n_chosen, any_bad;
+  __shared__ uint16_t pt[256];
+  if (kR4) build_pair_table(a, pt);   // visible after chosen_set's barriers
   chosen_set(a, present, before, idx_s, &n_chosen, &any_bad);
   const int lane = threadIdx.x & 63;
   const int wl = a.width_log2;
@@ -367,7 +390,6 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(MoeArgs a) {
   const int ti = lane & ((1 << wl) - 1);        // this lane's tile (packed)
   const int J = a.cols >> 5;
   const int C = (J + 63) >> 6;
-  const Lut L{a.lut0, a.lut1, a.lut2, a.lut3};
   const uint32_t U = uniform(n_chosen);
   const uint64_t jobs = static_cast<uint64_t>(U) * a.groups;
   const uint64_t W = static_cast<uint64_t>(gridDim.x) * (blockDim.x >> 6);
@@ -378,7 +400,7 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(MoeArgs a) {
     const int32_t e = uniform(chosen_expert(a, present, before, u));
     const int64_t row0 = static_cast<int64_t>(job - static_cast<uint64_t>(u) * a.groups) * G *
                          a.sets;
-    moe_rows<kR4>(a, L, e, row0, G, gi, ti, wl, J, C, lane, idx_s);
+    moe_rows<kR4>(a, pt, e, row0, G, gi, ti, wl, J, C, lane, idx_s);
   }
   if (uniform(any_bad) != 0u) {
     // out-of-range indices: flag once, and zero those pairs' rows (rows
