@@ -173,6 +173,12 @@ struct RiceArgs {
   uint32_t esc_tbl;
 };
 
+// v mod chunk_mod, chunk_mod being the row-chunk width (2048) or, for rows
+// shorter than a chunk, the row length: a mask in the first case.
+__device__ __forceinline__ uint32_t mod_chunk(uint32_t v, uint32_t chunk_mod) {
+  return chunk_mod == static_cast<uint32_t>(kChunk) ? (v & (kChunk - 1u)) : v % chunk_mod;
+}
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
@@ -327,7 +333,7 @@ __device__ bool decode_tile_exact(BitReader<kLds>& br, const RiceArgs& a,
     const uint32_t sh = 8u * ((i & 7) & 3) + 4u * ((i & 7) >> 2);
     out[i >> 3] |= (r < 15u ? r : 15u) << sh;
     if (r >= 15u) {
-      const uint32_t ent = (static_cast<uint32_t>(a_table[r & 0xFFu]) << 16) | ((run_off + i) % chunk_mod);
+      const uint32_t ent = (static_cast<uint32_t>(a_table[r & 0xFFu]) << 16) | mod_chunk(run_off + i, chunk_mod);
       if (emit)
         esc_at[n_esc_lane] = ent;
       else if (n_esc_lane < kEscSlots)
@@ -571,7 +577,7 @@ __device__ __forceinline__ void decode_run(const RiceArgs& a, const uint8_t* tab
           }
         }
         if (n15 == 1u) {
-          slots[0] = (static_cast<uint32_t>(table[rmax & 0xFFu]) << 16) | ((run_off + found) % chunk_mod);
+          slots[0] = (static_cast<uint32_t>(table[rmax & 0xFFu]) << 16) | mod_chunk(run_off + found, chunk_mod);
           n_esc_lane = 1;
         } else {
           exact = true;
@@ -712,7 +718,7 @@ __device__ __forceinline__ void byte_walk(const uint32_t (&x)[4], int32_t c, uin
         if (rank >= 15u) {
           if (kEmit) {
             if (rank < n)
-              dst[n_esc++] = (static_cast<uint32_t>(table[rank]) << 16) | (idx % chunk_mod);
+              dst[n_esc++] = (static_cast<uint32_t>(table[rank]) << 16) | mod_chunk(idx, chunk_mod);
           } else {
             const uint32_t pos = lds_add_rtn(ctr, rank < n ? 1u : kBadRank) & ~kBadRank;
             if (pos < static_cast<uint32_t>(kByteSlots)) slots[pos * 64] = (idx << 8) | rank;
@@ -993,7 +999,7 @@ __device__ __forceinline__ void decode_job_bytes(const RiceArgs& a, const uint8_
     if (n_esc_lane <= static_cast<uint32_t>(kByteSlots)) {
       for (uint32_t i = 0; i < n_esc_lane; ++i) {
         const uint32_t ent = slots[i * 64];
-        dst[i] = (static_cast<uint32_t>(table[ent & 0xFFu]) << 16) | ((ent >> 8) % chunk_mod);
+        dst[i] = (static_cast<uint32_t>(table[ent & 0xFFu]) << 16) | mod_chunk(ent >> 8, chunk_mod);
       }
     } else {
       // more escapes than slots: walk the bytes again, writing them out
