@@ -18,7 +18,9 @@
 // side-list entries, a lane each), and walks each row set once per pair:
 // lane tiles rebuilt through an LDS table of exponent pairs (one lookup per
 // nibble byte), escapes patched from registers. A second pair of the same
-// expert re-reads the rows the wave has just read, from cache.
+// expert re-reads the rows the wave has just read, from cache. Rows of
+// 64 < J <= 96 tiles (two chunks, the second on at most 32 lanes) are taken
+// two at a time, their second chunks in one pass on the wave's two halves.
 //
 // A packed row's slots 32, 16, ... down to its group width hold no tile, so
 // the matvec's tree adds +0.0 to each of the group's slots at those levels;
@@ -293,7 +295,7 @@ __device__ __forceinline__ void moe_weights(const MoeArgs& a, const MoeRaw<kR4>&
 // tiles are loaded per chunk inside each pass over a pair, which keeps the
 // register count (and so the waves per SIMD) where this latency-bound
 // kernel wants it.
-template <bool kR4>
+template <bool kR4, bool kMerge>
 __device__ __forceinline__ void moe_rows(const MoeArgs& a, const uint16_t* pt, int32_t e, int64_t row0,
                                          int G, int gi, int ti, int wl, int J, int C, int lane,
                                          const int32_t* idx_s) {
@@ -320,11 +322,86 @@ __device__ __forceinline__ void moe_rows(const MoeArgs& a, const uint16_t* pt, i
     }
   }
 
+  const bool merged =
+      kMerge && G == 1 && C == 2 && a.sets == 2 && J > 64 && J <= 96 && row0 + 1 < a.n_rows;
   for (int32_t base = 0; base < a.n_pairs; base += 64) {
     const int32_t p = base + lane;
     const int32_t v = p < a.n_pairs ? (p < kMaxPairsLds ? idx_s[p] : a.idx[p]) : 0;
     const uint64_t mine_all = __ballot(p < a.n_pairs && v == e);
     if (mine_all == 0) continue;
+    if (merged) {
+      // Two whole-wave rows of 64 < J <= 96 tiles: row A's and row B's first
+      // chunks in two passes, then both second chunks in one pass (row A on
+      // lanes 0..31, row B on lanes 32..63, its slot sums moved there and
+      // back unchanged). Each slot's chain and the slot tree are those of
+      // the passes below.
+      const int64_t growA = grow_w, growB = grow_w + 1;
+      uint64_t mine = mine_all;
+      while (mine != 0) {
+        const int b = __builtin_ctzll(mine);
+        mine &= mine - 1;
+        const int32_t pp = base + b;
+        const int64_t xrow = a.x_per_slot ? pp : pp / a.top_k;
+        const uint16_t* xr = a.x + xrow * a.cols;
+        float a0A = 0.0f, a1A = 0.0f, a0B = 0.0f, a1B = 0.0f;
+#pragma unroll 1
+        for (int h = 0; h < 2; ++h) {
+          MoeRaw<kR4> rj;
+          moe_load<kR4>(a, h ? growB : growA, lane, true, rj);
+          float w[32];
+          moe_weights<kR4>(a, rj, pt, regs, pre_lane, ent_lane, e0, 2 * h, h ? growB : growA, 1,
+                           1, 6, 2, 0, lane, w);
+          float xf[32];
+          load_x_tile(xr, lane, xf);
+          float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            s0 = __builtin_fmaf(w[2 * i], xf[2 * i], s0);
+            s1 = __builtin_fmaf(w[2 * i + 1], xf[2 * i + 1], s1);
+          }
+          if (h) {
+            a0B = s0;
+            a1B = s1;
+          } else {
+            a0A = s0;
+            a1A = s1;
+          }
+        }
+        const int half = lane >> 5;
+        const int t1 = 64 + (lane & 31);
+        const bool act = t1 < J;
+        const float m0 = __shfl(a0B, (lane - 32) & 63, 64);
+        const float m1 = __shfl(a1B, (lane - 32) & 63, 64);
+        float c0 = half ? m0 : a0A, c1 = half ? m1 : a1A;
+        {
+          MoeRaw<kR4> rj;
+          moe_load<kR4>(a, half ? growB : growA, t1, act, rj);
+          float w[32];
+          moe_weights<kR4>(a, rj, pt, regs, pre_lane, ent_lane, e0, 0, growA, 2, 2, 5, 2, 1, lane,
+                           w);
+          if (act) {
+            float xf[32];
+            load_x_tile(xr, t1, xf);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              c0 = __builtin_fmaf(w[2 * i], xf[2 * i], c0);
+              c1 = __builtin_fmaf(w[2 * i + 1], xf[2 * i + 1], c1);
+            }
+          }
+        }
+        const float sum = c0 + c1;
+        const float bsum = __shfl(sum, (lane + 32) & 63, 64);
+        float rA = half ? a0A + a1A : sum;
+        float rB = half ? a0B + a1B : bsum;
+        rA = slot_tree(rA);
+        rB = slot_tree(rB);
+        if (lane == 0) {
+          store_out(a, static_cast<int64_t>(pp) * a.n_rows + row0, rA);
+          store_out(a, static_cast<int64_t>(pp) * a.n_rows + row0 + 1, rB);
+        }
+      }
+      continue;
+    }
     for (int set = 0; set < a.sets; ++set) {
       const int64_t set0 = row0 + static_cast<int64_t>(set) * G;
       if (set0 >= a.n_rows) break;
@@ -374,7 +451,9 @@ __device__ __forceinline__ void moe_rows(const MoeArgs& a, const uint16_t* pt, i
 // Persistent blocks: the chosen set is found once per block; wave w then
 // takes the jobs w, w + W, ... (W waves in the grid), job = (u-th chosen
 // expert, row group) with a.groups row groups per expert.
-template <bool kR4>
+// kMerge: rows of 64 < J <= 96 lane tiles run the merged second pass (the
+// instantiation holds more registers, so other row widths use the other).
+template <bool kR4, bool kMerge>
 __global__ __launch_bounds__(256) void moe_gemv_kernel(MoeArgs a) {
   __shared__ uint32_t present[kMaxExpertWords];
   __shared__ uint32_t before[kMaxExpertWords];
@@ -400,7 +479,7 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(MoeArgs a) {
     const int32_t e = uniform(chosen_expert(a, present, before, u));
     const int64_t row0 = static_cast<int64_t>(job - static_cast<uint64_t>(u) * a.groups) * G *
                          a.sets;
-    moe_rows<kR4>(a, pt, e, row0, G, gi, ti, wl, J, C, lane, idx_s);
+    moe_rows<kR4, kMerge>(a, pt, e, row0, G, gi, ti, wl, J, C, lane, idx_s);
   }
   if (uniform(any_bad) != 0u) {
     // out-of-range indices: flag once, and zero those pairs' rows (rows
@@ -421,24 +500,25 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(MoeArgs a) {
 
 // Blocks of the persistent MoE kernel that fit on the current device at once
 // (queried once per device and kind).
-int32_t resident_blocks(bool r4, int64_t& blocks) {
-  static int64_t cached[2][64] = {};
+int32_t resident_blocks(bool r4, bool merge, int64_t& blocks) {
+  static int64_t cached[2][2][64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return launch_status();
-  if (dev < 64 && cached[r4][dev] > 0) {
-    blocks = cached[r4][dev];
+  if (dev < 64 && cached[r4][merge][dev] > 0) {
+    blocks = cached[r4][merge][dev];
     return BINADE_OK;
   }
   int per_cu = 0, cus = 0;
-  const hipError_t q = r4 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                                &per_cu, moe_gemv_kernel<true>, 256, 0)
-                          : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                                &per_cu, moe_gemv_kernel<false>, 256, 0);
+  const void* k = r4 ? (merge ? reinterpret_cast<const void*>(&moe_gemv_kernel<true, true>)
+                              : reinterpret_cast<const void*>(&moe_gemv_kernel<true, false>))
+                     : (merge ? reinterpret_cast<const void*>(&moe_gemv_kernel<false, true>)
+                              : reinterpret_cast<const void*>(&moe_gemv_kernel<false, false>));
+  const hipError_t q = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, 0);
   if (q != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return launch_status();
   blocks = static_cast<int64_t>(per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
-  if (dev < 64) cached[r4][dev] = blocks;
+  if (dev < 64) cached[r4][merge][dev] = blocks;
   return BINADE_OK;
 }
 
@@ -453,17 +533,20 @@ int32_t launch(MoeArgs a, bool r4, hipStream_t stream) {
   // at most min(experts, pairs) experts are chosen
   const int64_t chosen_max = a.n_experts < a.n_pairs ? a.n_experts : a.n_pairs;
   const int64_t waves = chosen_max * a.groups;
+  // rows of 64 < J <= 96 tiles: the instantiation with the merged second pass
+  const bool merge = J > 64 && J <= 96;
   int64_t resident = 0;
-  const int32_t st = resident_blocks(r4, resident);
+  const int32_t st = resident_blocks(r4, merge, resident);
   if (st != BINADE_OK) return st;
   const int64_t need = (waves + 3) / 4;
-  const int64_t blocks = need < resident ? (need > 0 ? need : 1) : resident;
-  if (r4)
-    hipLaunchKernelGGL(moe_gemv_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL(moe_gemv_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                       stream, a);
+  const dim3 grid(static_cast<uint32_t>(need < resident ? (need > 0 ? need : 1) : resident));
+  if (r4) {
+    if (merge) hipLaunchKernelGGL((moe_gemv_kernel<true, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((moe_gemv_kernel<true, false>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (merge) hipLaunchKernelGGL((moe_gemv_kernel<false, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((moe_gemv_kernel<false, false>), grid, dim3(256), 0, stream, a);
+  }
   return launch_status();
 }
 
