@@ -219,8 +219,10 @@ def _moe_case(E, N, K, n_tokens, top_k, seed, x_per_slot):
 
 
 @pytest.mark.parametrize("case", [(16, 40, 96, 3, 4, False), (128, 704, 2816, 8, 8, False),
-                                  (128, 2816, 704, 8, 8, True), (6, 33, 4160, 5, 2, True)],
-                         ids=["small", "gate_up", "down", "ragged"])
+                                  (128, 2816, 704, 8, 8, True), (6, 33, 4160, 5, 2, True),
+                                  (5, 37, 2240, 6, 3, False), (7, 9, 3072, 4, 5, True)],
+                         ids=["small", "gate_up", "down", "ragged", "paired_rows_odd",
+                              "paired_rows_96"])
 def test_moe_matches_oracle_and_twin(case):
     E, N, K, T, k, per_slot = case
     w, idx, x = _moe_case(E, N, K, T, k, 40 + E, per_slot)
