@@ -74,6 +74,11 @@ def _load():
             lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
             lib.oracle_f32_to_bf16_array.argtypes = [P, I64, P]
             lib.oracle_gemm_f64.argtypes = [P, I64, I64, P, I64, P]
+            lib.oracle_mfma_step.argtypes = [P, P, ctypes.c_float]
+            lib.oracle_mfma_step.restype = ctypes.c_float
+            lib.oracle_gemm_replay.argtypes = [P, I64, I64, P, I64, P]
+            lib.oracle_gemm_replay_entries.argtypes = [P, I64, I64, P, I64, P,
+                                                       P, I64, P]
             _lib = lib
     return _lib
 
@@ -259,9 +264,7 @@ def moe_replay(experts_bits, x_bits, idx, x_per_slot: bool) -> np.ndarray:
 
 
 def gemm_f64(w_bits, x_bits) -> np.ndarray:
-    """Y = X W^T summed in double (the prompt GEMM's plain definition). No
-    bit replay of the GEMM exists: its parity is unpinned beyond this bound,
-    exact-arithmetic inputs and the bf16-weight twin."""
+    """Y = X W^T summed in double (the prompt GEMM's plain definition)."""
     w = _u16(w_bits)
     x = _u16(x_bits)
     N, K = w.shape
@@ -269,6 +272,43 @@ def gemm_f64(w_bits, x_bits) -> np.ndarray:
     y = np.zeros((M, N), np.float64)
     _check("oracle_gemm_f64", _load().oracle_gemm_f64(_p(w), N, K, _p(x), M, _p(y)))
     return y
+
+
+def mfma_step(a_bits, b_bits, c: float) -> np.float32:
+    """One output of one bf16 matrix-core step, c + sum of 32 products, by the
+    reading stated above oracle_mfma_step in binade_oracle.c."""
+    a = _u16(a_bits).reshape(-1)
+    b = _u16(b_bits).reshape(-1)
+    assert a.size == 32 and b.size == 32
+    return np.float32(_load().oracle_mfma_step(_p(a), _p(b), ctypes.c_float(c)))
+
+
+def gemm_replay(w_bits, x_bits) -> np.ndarray:
+    """Y = X W^T in the prompt GEMM's documented order of matrix-core steps
+    and slices ("Binade" package page, "NVIDIA GPUs")."""
+    w = _u16(w_bits)
+    x = _u16(x_bits)
+    N, K = w.shape
+    M, K2 = x.shape
+    assert K == K2
+    y = np.zeros((M, N), np.float32)
+    _check("oracle_gemm_replay", _load().oracle_gemm_replay(_p(w), N, K, _p(x), M, _p(y)))
+    return y
+
+
+def gemm_replay_entries(w_bits, x_bits, mi, ni) -> np.ndarray:
+    """The replay of the entries Y[mi[i], ni[i]] only."""
+    w = _u16(w_bits)
+    x = _u16(x_bits)
+    N, K = w.shape
+    M = x.shape[0]
+    mi = np.ascontiguousarray(mi, np.int64)
+    ni = np.ascontiguousarray(ni, np.int64)
+    out = np.zeros(mi.size, np.float32)
+    _check("oracle_gemm_replay_entries",
+           _load().oracle_gemm_replay_entries(_p(w), N, K, _p(x), M, _p(mi),
+                                              _p(ni), mi.size, _p(out)))
+    return out
 
 
 def f32_to_bf16(y: np.ndarray) -> np.ndarray:

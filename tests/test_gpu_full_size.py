@@ -6,8 +6,9 @@ Whole-output checks need no oracle: R4 equals the oracle's R4 of the
 weights bit for bit (the oracle's conversion is plain C and fast), the
 unpacked bits equal the weights, and every product equals its bf16-weight
 twin bit for bit. Against the oracle's products, sampled outputs: rows of
-the matvec replayed in the fixed fp32 order (bit-exact), and GEMM entries
-within 1e-2 of the fp64 sum (relative to sum |w x|)."""
+the matvec and entries of the GEMM replayed in their fixed fp32 orders
+(bit-exact), and both within 1e-2 of the fp64 sum (relative to
+sum |w x|)."""
 import numpy as np
 import pytest
 import torch
@@ -116,7 +117,7 @@ def test_64m_embedding_decode_full_size():
 def test_prompt_gemm_full_size(nk):
     """Y = X W^T for M = 16, 32, 128, 2048 on the full FFN shapes: bit-equal
     to the bf16 twin everywhere, rows independent of M, sampled entries
-    within the fp64 bound."""
+    bit-equal to the oracle's replay and within the fp64 bound."""
     N, K = nk
     w = synth.normal_bf16(synth.TensorSpec("w", N, K, 0.015, 2000 + N))
     r4 = B.rice_to_r4(B.pack_rice(w).to(DEV))
@@ -143,5 +144,9 @@ def test_prompt_gemm_full_size(nk):
         xb = bits_np(X[rows])
         ref = oracle.gemm_f64(wb, xb)
         scale = oracle.gemm_f64(wb & 0x7FFF, xb & 0x7FFF)
-        got = y.cpu().numpy()[np.ix_(rows, cols)].astype(np.float64)
+        got32 = y.cpu().numpy()[np.ix_(rows, cols)]
+        mi, ni = np.meshgrid(rows, cols, indexing="ij")
+        rep = oracle.gemm_replay_entries(wb_all, bits_np(X[:m]), mi.reshape(-1), ni.reshape(-1))
+        assert same_f32(got32.reshape(-1), rep), m
+        got = got32.astype(np.float64)
         assert np.all(np.abs(got - ref) <= 1e-2 * scale), m
