@@ -28,6 +28,7 @@ EXPORTS = ["binade_status_str", "binade_last_hip_error", "binade_build_table",
            "binade_rice_to_r4_batch", "binade_unpack", "binade_r4_gemv",
            "binade_r4_gemv_batch", "binade_bf16_gemv", "binade_bf16_gemv_batch",
            "binade_r4_gemm", "binade_bf16_gemm", "binade_gemm_workspace_bytes",
+           "binade_r4_gemm_noalloc", "binade_gemm_scratch_bytes",
            "binade_r4_moe_gemv", "binade_bf16_moe_gemv"]
 
 
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
             L.binade_last_hip_error.restype = I32
             L.binade_gemm_workspace_bytes.argtypes = [I64, I64, I64]
             L.binade_gemm_workspace_bytes.restype = I64
+            L.binade_gemm_scratch_bytes.argtypes = []
+            L.binade_gemm_scratch_bytes.restype = I64
             sig = {
                 "binade_build_table": [P, I64, P],
                 "binade_sizes_of": [P, I64, I64, P],
@@ -107,6 +110,7 @@ def lib() -> ctypes.CDLL:
                 "binade_r4_gemv": [P, P, P, I32, P],
                 "binade_bf16_gemv": [P, I64, I64, P, P, I32, P],
                 "binade_r4_gemm": [P, P, I64, I64, P, I64, I32, P, I64, P],
+                "binade_r4_gemm_noalloc": [P, P, I64, I64, P, I64, I32, P],
                 "binade_bf16_gemm": [P, I64, I64, P, I64, I64, P, I64, I32, P, I64,
                                      P],
                 "binade_r4_moe_gemv": [P, I32, P, I32, P, I64, I32, P, I32, P, P],
@@ -436,6 +440,24 @@ def r4_gemm(w: R4Tensor, x: torch.Tensor, out_dtype=torch.float32,
     _call("binade_r4_gemm", ctypes.byref(d), _ptr(x), m, x.stride(0), _ptr(y),
           y.stride(0), code, _ptr(ws), nb, _stream(stream))
     return y
+
+
+def r4_gemm_noalloc(w: R4Tensor, x: torch.Tensor, out_dtype=torch.float32,
+                    y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = X W^T through binade_r4_gemm_noalloc (the library's fixed scratch,
+    no workspace). With y given, nothing is allocated here either."""
+    code = _dtype_code(out_dtype)
+    x = _bits16(x)
+    m = x.shape[0]
+    y = _y((m, w.rows), code, x.device, y)
+    d = w.desc()
+    _call("binade_r4_gemm_noalloc", ctypes.byref(d), _ptr(x), m, x.stride(0),
+          _ptr(y), y.stride(0), code, _stream(stream))
+    return y
+
+
+def gemm_scratch_bytes() -> int:
+    return int(lib().binade_gemm_scratch_bytes())
 
 
 def bf16_gemm(w: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32,

@@ -49,6 +49,13 @@
 #include "binade.h"
 #include "device_common.h"
 
+// Fixed device scratch of binade_r4_gemm_noalloc: the split slices' partial
+// sums (32 MiB). Every device the library runs on holds its own copy until
+// the process ends. In host code `scratch` names a host-side stand-in, never
+// the device memory: host code uses only the per-device address that
+// scratch_address() looks up.
+static __device__ __align__(256) uint8_t scratch[32ll << 20];
+
 namespace binade {
 namespace {
 
@@ -1582,6 +1589,78 @@ uint32_t pack4(const uint8_t* l) {
          (uint32_t(l[3]) << 24);
 }
 
+constexpr int64_t kScratchBytes = sizeof(scratch);
+constexpr int kMaxDevices = 64;
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current. nullptr (and *status set) when HIP reports an error.
+void* scratch_address(int32_t* status) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_last_hip_error(static_cast<int32_t>(e));
+    *status = BINADE_EHIP;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *status = BINADE_EUNSUPPORTED;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      set_last_hip_error(static_cast<int32_t>(e));
+      *status = BINADE_EHIP;
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+// Argument checks and kernel arguments of the R4 GEMM. *nothing is set when
+// the product is empty (M = 0 or N = 0).
+int32_t r4_gemm_args(const binade_r4* w, const uint16_t* x, int64_t m,
+                     int64_t ldx, void* y, int64_t ldy, int32_t y_dtype,
+                     GemmArgs* a, bool* nothing) {
+  *nothing = false;
+  if (w == nullptr || w->rows < 0 || w->cols <= 0) return BINADE_EINVAL;
+  int32_t s = check_xy(x, m, ldx, y, ldy, w->rows, w->cols, y_dtype);
+  if (s != BINADE_OK) return s;
+  if (m == 0 || w->rows == 0) {
+    *nothing = true;
+    return BINADE_OK;
+  }
+  if (w->sm == nullptr || w->nib == nullptr || w->esc_pre == nullptr ||
+      (w->n_esc > 0 && w->esc == nullptr))
+    return BINADE_EINVAL;
+  if (!aligned16(w->sm) || !aligned16(w->nib)) return BINADE_EUNSUPPORTED;
+  if (w->n_esc > 0xFFFFFFFFull) return BINADE_EUNSUPPORTED;
+  *a = GemmArgs{};
+  a->w = w->sm;
+  a->nib = w->nib;
+  a->esc_pre = w->esc_pre;
+  a->esc = w->esc;
+  a->n_esc = static_cast<uint32_t>(w->n_esc);
+  a->lut0 = rot_exponents4(pack4(w->lut));
+  a->lut1 = rot_exponents4(pack4(w->lut + 4));
+  a->lut2 = rot_exponents4(pack4(w->lut + 8));
+  a->lut3 = rot_exponents4(pack4(w->lut + 12));
+  a->x = x;
+  a->y = y;
+  a->m = m;
+  a->n = w->rows;
+  a->k = static_cast<int32_t>(w->cols);
+  a->ldx = ldx;
+  a->ldy = ldy;
+  a->y_bf16 = y_dtype == BINADE_BF16;
+  return BINADE_OK;
+}
+
 }  // namespace
 }  // namespace binade
 
@@ -1596,33 +1675,31 @@ extern "C" int32_t binade_r4_gemm(const binade_r4* w, const uint16_t* x,
                                   int64_t m, int64_t ldx, void* y, int64_t ldy,
                                   int32_t y_dtype, void* workspace,
                                   int64_t workspace_bytes, void* stream) {
-  if (w == nullptr || w->rows < 0 || w->cols <= 0) return BINADE_EINVAL;
-  int32_t s = check_xy(x, m, ldx, y, ldy, w->rows, w->cols, y_dtype);
-  if (s != BINADE_OK || m == 0 || w->rows == 0) return s;
-  if (w->sm == nullptr || w->nib == nullptr || w->esc_pre == nullptr ||
-      (w->n_esc > 0 && w->esc == nullptr))
-    return BINADE_EINVAL;
-  if (!aligned16(w->sm) || !aligned16(w->nib)) return BINADE_EUNSUPPORTED;
-  if (w->n_esc > 0xFFFFFFFFull) return BINADE_EUNSUPPORTED;
   GemmArgs a{};
-  a.w = w->sm;
-  a.nib = w->nib;
-  a.esc_pre = w->esc_pre;
-  a.esc = w->esc;
-  a.n_esc = static_cast<uint32_t>(w->n_esc);
-  a.lut0 = rot_exponents4(pack4(w->lut));
-  a.lut1 = rot_exponents4(pack4(w->lut + 4));
-  a.lut2 = rot_exponents4(pack4(w->lut + 8));
-  a.lut3 = rot_exponents4(pack4(w->lut + 12));
-  a.x = x;
-  a.y = y;
-  a.m = m;
-  a.n = w->rows;
-  a.k = static_cast<int32_t>(w->cols);
-  a.ldx = ldx;
-  a.ldy = ldy;
-  a.y_bf16 = y_dtype == BINADE_BF16;
+  bool nothing = false;
+  int32_t s = r4_gemm_args(w, x, m, ldx, y, ldy, y_dtype, &a, &nothing);
+  if (s != BINADE_OK || nothing) return s;
   return launch(a, true, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int64_t binade_gemm_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" int32_t binade_r4_gemm_noalloc(const binade_r4* w, const uint16_t* x,
+                                          int64_t m, int64_t ldx, void* y,
+                                          int64_t ldy, int32_t y_dtype,
+                                          void* stream) {
+  GemmArgs a{};
+  bool nothing = false;
+  int32_t s = r4_gemm_args(w, x, m, ldx, y, ldy, y_dtype, &a, &nothing);
+  if (s != BINADE_OK || nothing) return s;
+  const int64_t need = plan_for(a.m, a.n, a.k).part_bytes;
+  if (need > kScratchBytes) return BINADE_ENOSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_address(&s);
+    if (ws == nullptr) return s;
+  }
+  return launch(a, true, ws, need, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int32_t binade_bf16_gemm(const uint16_t* w, int64_t rows,

@@ -250,6 +250,25 @@ int32_t binade_bf16_gemm(const uint16_t *w, int64_t rows, int64_t cols,
                          int64_t ldy, int32_t y_dtype, void *workspace,
                          int64_t workspace_bytes, void *stream);
 
+/* binade_r4_gemm without a workspace argument and without allocating, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). The split slices'
+ * partial sums go to a fixed scratch array inside the library, one per
+ * device, of binade_gemm_scratch_bytes() bytes (32 MiB), held until the
+ * process ends. Same arguments, results and order as binade_r4_gemm (the
+ * same bits whether or not it splits). Returns BINADE_ENOSPACE, launching
+ * nothing, when the shape's partial sums (binade_gemm_workspace_bytes)
+ * exceed the scratch. Calls are stream-ordered but share the device's
+ * scratch: calls that overlap on one device (different streams or host
+ * threads) race and must not be issued. Nothing in the scratch is read before
+ * the same call writes it. */
+int32_t binade_r4_gemm_noalloc(const binade_r4 *w, const uint16_t *x,
+                               int64_t m, int64_t ldx, void *y, int64_t ldy,
+                               int32_t y_dtype, void *stream);
+
+/* Size in bytes of binade_r4_gemm_noalloc's per-device scratch. */
+int64_t binade_gemm_scratch_bytes(void);
+
 /* Workspace bytes with which binade_r4_gemm / binade_bf16_gemm split the
  * slices of an M x N x K product over blocks (0: that shape never splits;
  * also 0 for invalid sizes). Pure host function. */
