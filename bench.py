@@ -107,8 +107,115 @@ def spread(v) -> dict:
     return {"p10": at(0.1), "median": at(0.5), "p90": at(0.9)}
 
 
-def host_cores_used() -> int:
-    return 1
+def host_cpu() -> tuple[int, dict]:
+    """Threads the CPU baseline may use -- this process's CPU affinity, at
+    most 16 (one GPU's share of the host) -- and what the host reports."""
+    aff = len(os.sched_getaffinity(0))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return max(1, min(16, aff)), {"os_cpu_count": os.cpu_count(), "affinity_cpus": aff,
+                                  "model": model}
+
+
+def oracle_rate(items, fn, threads: int, min_s: float):
+    """Runs fn(item) over `items` (cycling) on `threads` host threads until
+    min_s seconds have passed; returns (sum of the values fn returns, seconds).
+    The oracle is a C library called through ctypes, which releases the GIL,
+    and it keeps no global state, so items run truly in parallel."""
+    import threading
+    lock = threading.Lock()
+    state = {"i": 0, "done": 0.0}
+    t0 = time.perf_counter()
+
+    def worker():
+        while time.perf_counter() - t0 < min_s:
+            with lock:
+                it = items[state["i"] % len(items)]
+                state["i"] += 1
+            v = fn(it)
+            with lock:
+                state["done"] += v
+
+    ts = [threading.Thread(target=worker) for _ in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    return state["done"], time.perf_counter() - t0
+
+
+def cpu_baseline(tensors, host_bits, xs, log_fn) -> dict:
+    """The oracle timed on this host: its fp32-order GEMV replay over the
+    stack tensors (the metric's unit, GB/s of the R4 GEMV's bytes) and its
+    format 2 -> R4 decode (bit-by-bit Rice decode, then the R4 layout) over
+    row blocks of one gate tensor, each on one thread and on every thread
+    this process may use. Results do not depend on the thread count: the
+    items are independent tensors or row blocks."""
+    import oracle  # test infrastructure: cpu baseline only
+    cores, host = host_cpu()
+    gemv_items = []
+    for t in tensors:
+        wn = host_bits[t["spec"].name].view(torch.int16).numpy().view(np.uint16)
+        xb = xs[t["spec"].cols].cpu().view(torch.int16).numpy().view(np.uint16)
+        gemv_items.append((wn, xb, gemv_bytes(t["r4"])))
+
+    def gemv_one(it):
+        oracle.gemv_replay(it[0], it[1])
+        return it[2]
+
+    gate = next(t for t in tensors if t["spec"].name.endswith(".gate"))
+    gw = host_bits[gate["spec"].name].view(torch.int16).numpy().view(np.uint16)
+    blocks = [np.ascontiguousarray(gw[r:r + 256]) for r in range(0, gw.shape[0], 256)]
+
+    def pack(b):
+        tab = oracle.build_table(b)
+        return tab, oracle.pack_rice(b, tab)
+
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        packed = list(ex.map(pack, blocks))
+
+    def dec_bytes_of(pk):
+        n = pk["rows"] * pk["cols"]
+        return (4 * ((pk["unary_bits"] + 31) // 32) + 4 * ((n * pk["k"] + 31) // 32)
+                + 12 * pk["anchor"].size + n // 2 + 4 * pk["n_esc"])
+
+    dec_items = [(tab, pk, pk["rows"] * pk["cols"], dec_bytes_of(pk)) for tab, pk in packed]
+
+    def dec_one(it):
+        bits = oracle.rice_decode(it[1])
+        oracle.make_r4(bits, it[0])
+        return it[2]
+
+    res = {}
+    for name, items, fn, secs in (("gemv", gemv_items, gemv_one, 5.0), ("decode", dec_items, dec_one, 4.0)):
+        for th in (1, cores):
+            done, el = oracle_rate(items, fn, th, secs)
+            res[(name, th)] = (done, el)
+            log_fn(f"cpu baseline {name} x{th}: {done / el / 1e9:.3f} G/s over {el:.1f}s")
+    g1, gn = res[("gemv", 1)], res[("gemv", cores)]
+    d1, dn = res[("decode", 1)], res[("decode", cores)]
+    sym_b = sum(it[3] for it in dec_items) / sum(it[2] for it in dec_items)   # bytes per symbol
+    return {"value": round(gn[0] / gn[1] / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": (f"oracle fp32-order GEMV replay (C, one tensor per thread) cycling over the "
+                       f"{len(gemv_items)} stack tensors for {gn[1]:.1f} s on {cores} threads; bytes "
+                       "counted as the R4 GEMV's"),
+            "single_thread_GBs": round(g1[0] / g1[1] / 1e9, 3),
+            "decode": {"kernel": "rice_to_r4",
+                       "gsym_per_s": round(dn[0] / dn[1] / 1e9, 4),
+                       "GBs": round(dn[0] * sym_b / dn[1] / 1e9, 4),
+                       "single_thread_gsym_per_s": round(d1[0] / d1[1] / 1e9, 4),
+                       "cores": cores,
+                       "sample": (f"oracle bit-by-bit Rice decode + R4 layout over {len(dec_items)} "
+                                  f"row blocks (256 x {gw.shape[1]}) of {gate['spec'].name}, "
+                                  f"{dn[1]:.1f} s on {cores} threads")},
+            "host": host}
 
 
 MFMA_BF16_PEAK_TFS = 2500.0   # MI355X dense bf16 matrix peak
@@ -278,6 +385,118 @@ def measure_gemm(dev, stream) -> dict:
     return out
 
 
+def planes_replica(p: B.RicePlanes, dev) -> B.RicePlanes:
+    """Device copies of a format 2 tensor's planes (the sm plane shared)."""
+    return B.RicePlanes(rows=p.rows, cols=p.cols, table=p.table, sm=p.sm, unary=p.unary.clone(),
+                        rem=None if p.rem is None else p.rem.clone(), anchor=p.anchor.clone(),
+                        esc_pre=p.esc_pre.clone(), unary_bits=p.unary_bits, n_esc=p.n_esc)
+
+
+def measure_configs(dev, stream) -> dict:
+    """The single 1024 x 1024 tensor (table, pack, decode, GEMV), and the
+    12B-class shapes: bulk decode of the 262144 x 256 tensor (67,108,864
+    symbols) and the batch-1 GEMV of 15360 x 3840 and 3840 x 15360. Each
+    timed HIP-graph replay works on copies whose total is >= 1 GiB (decode:
+    planes in, nibbles and escapes out; GEMV: weights), so no launch finds its
+    data in the last-level cache; medians of 15 replays, per launch."""
+    out = {}
+    # ---- single 1024 x 1024 tensor (launch-bound; reported, not a roofline)
+    sp = synth.single_1024()[0]
+    w = synth.normal_bf16(sp, device=dev)
+    wh = w.cpu()
+    t0 = time.perf_counter()
+    table = B.build_table(wh)
+    t1 = time.perf_counter()
+    planes = B.pack_rice(wh, table)
+    t2 = time.perf_counter()
+    dp = planes.to(dev)
+    r4 = B.rice_to_r4(dp)
+    x = synth.vector_bf16(sp.cols, 1, device=dev)
+    y = torch.empty(sp.rows, dtype=torch.float32, device=dev)
+    tdec = graph_time_ms(stream, lambda: B.rice_to_r4(dp, stream=stream, out=r4))
+    tgv = graph_time_ms(stream, lambda: B.r4_gemv(r4, x, y=y, stream=stream))
+    ttw = graph_time_ms(stream, lambda: B.bf16_gemv(w, x, y=y, stream=stream))
+    torch.cuda.synchronize()
+    if not torch.equal(B.unpack(r4).view(torch.int16), w.view(torch.int16)):
+        raise SystemExit("parity gate: 1024 x 1024 unpack differs")
+    out["single_1024x1024"] = {
+        "host_table_ms": round((t1 - t0) * 1e3, 3), "host_pack_ms": round((t2 - t1) * 1e3, 3),
+        "format2_bits_per_weight": round(planes.bits_per_weight(), 4),
+        "r4_bits_per_weight": round(r4.bits_per_weight(), 4),
+        "decode_us": round(tdec * 1e3, 2), "gemv_us": round(tgv * 1e3, 2),
+        "bf16_twin_gemv_us": round(ttw * 1e3, 2),
+        "note": "1.5 MB of weights: one launch is bound by launch and cache latency, not HBM"}
+    # ---- 64M-symbol bulk decode
+    sp = synth.embedding_64m()
+    w = synth.normal_bf16(sp, device=dev)
+    planes = B.pack_rice(w.cpu())
+    dp = planes.to(dev)
+    ref = B.rice_to_r4(dp)
+    per_copy = decode_bytes(dp) + dp.rows * dp.cols   # + the sm plane it leaves alone
+    n = max(2, -(-ROTATE_BYTES // per_copy))
+    copies = [dp] + [planes_replica(dp, dev) for _ in range(n - 1)]
+    outs = [ref] + [B.R4Tensor(dp.rows, dp.cols, bytes(16), dp.sm, torch.empty_like(ref.nib),
+                               dp.esc_pre, torch.empty_like(ref.esc), dp.n_esc) for _ in range(n - 1)]
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def dec_rot():
+        for p_, o_ in zip(copies, outs):
+            B.rice_to_r4(p_, status=status, stream=stream, out=o_)
+
+    v = spread(graph_replays_ms(stream, dec_rot))
+    torch.cuda.synchronize()
+    if int(status.item()) != 0 or not all(torch.equal(o_.nib, ref.nib) for o_ in outs):
+        raise SystemExit("parity gate: bulk decode copies differ")
+    if not torch.equal(B.unpack(ref).view(torch.int16), w.view(torch.int16)):
+        raise SystemExit("parity gate: bulk decode unpack differs")
+    t = v["median"] / n
+    syms = dp.rows * dp.cols
+    ach = decode_bytes(dp) / (t * 1e-3) / 1e9
+    out["bulk_decode_262144x256"] = {
+        "symbols": syms, "us_per_launch": round(t * 1e3, 2),
+        "us_spread": {k: round(x_ / n * 1e3, 2) for k, x_ in v.items()},
+        "gsym_per_s": round(syms / (t * 1e-3) / 1e9, 1), "GBs": round(ach, 1),
+        "frac_of_hbm_peak": round(ach / HBM_PEAK_GBS, 4), "copies": n,
+        "bytes_per_launch": decode_bytes(dp)}
+    del copies, outs, ref, dp, w
+    torch.cuda.empty_cache()
+    # ---- 12B FFN batch-1 GEMV
+    for sp in synth.gemma_12b_ffn()[1:]:
+        w = synth.normal_bf16(sp, device=dev)
+        r4 = B.rice_to_r4(B.pack_rice(w.cpu()).to(dev))
+        N, K = sp.rows, sp.cols
+        x = synth.vector_bf16(K, 700 + N, device=dev)
+        y = torch.empty(N, dtype=torch.float32, device=dev)
+        y2 = torch.empty_like(y)
+        n_r4 = -(-ROTATE_BYTES // r4.nbytes())
+        n_bf = -(-ROTATE_BYTES // (2 * N * K))
+        r4s = [r4] + [r4_replica(r4) for _ in range(n_r4 - 1)]
+        wts = [w] + [w.clone() for _ in range(n_bf - 1)]
+
+        def r4_rot():
+            for t_ in r4s:
+                B.r4_gemv(t_, x, y=y, stream=stream)
+
+        def bf_rot():
+            for t_ in wts:
+                B.bf16_gemv(t_, x, y=y2, stream=stream)
+
+        tr = spread(graph_replays_ms(stream, r4_rot))["median"] / len(r4s)
+        tt = spread(graph_replays_ms(stream, bf_rot))["median"] / len(wts)
+        torch.cuda.synchronize()
+        if not torch.equal(y.view(torch.int32), y2.view(torch.int32)):
+            raise SystemExit(f"parity gate: 12B GEMV differs from its twin ({N}x{K})")
+        gb = gemv_bytes(r4) / (tr * 1e-3) / 1e9
+        out[f"gemv_{N}x{K}"] = {
+            "us_per_launch": round(tr * 1e3, 2), "GBs": round(gb, 1),
+            "frac_of_hbm_peak": round(gb / HBM_PEAK_GBS, 4),
+            "bf16_twin_us": round(tt * 1e3, 2), "speedup_vs_twin": round(tt / tr, 3),
+            "copies": {"r4": len(r4s), "bf16": len(wts)}}
+        del w, r4, r4s, wts
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure_moe(dev, stream) -> dict:
     """One gathered MoE step: 8 tokens x top-8 of 128 experts through gate,
     up (shared token input) and down (per-slot input) in R4 and bf16."""
@@ -325,6 +544,7 @@ def main():
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-twin", action="store_true")
     ap.add_argument("--skip-gemm", action="store_true")
+    ap.add_argument("--skip-configs", action="store_true")
     ap.add_argument("--skip-moe", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy used to scale memory counters")
@@ -590,32 +810,14 @@ def main():
 
     # ------------------------------------------------------------ GEMM, MoE
     # (the other rows of the path, reported beside the step; not in `value`)
+    configs = None if args.skip_configs else measure_configs(dev, stream)
     gemm = None if args.skip_gemm else measure_gemm(dev, stream)
     moe = None if args.skip_moe else measure_moe(dev, stream)
 
     # ------------------------------------------------------------ CPU oracle
     cpu = None
     if not args.skip_cpu_baseline:
-        # whole passes over the stack until at least 10 s of CPU work
-        t0 = time.perf_counter()
-        done_b = 0
-        n_done = 0
-        while time.perf_counter() - t0 < 10.0 and n_done < 20 * len(tensors):
-            for t in tensors:
-                wn = host_bits[t["spec"].name].view(torch.int16).numpy().view(np.uint16)
-                xb = xs[t["spec"].cols].cpu().view(torch.int16).numpy().view(np.uint16)
-                oracle.gemv_replay(wn, xb)
-                done_b += gemv_bytes(t["r4"])
-                n_done += 1
-                if time.perf_counter() - t0 > 30.0:
-                    break
-        el = time.perf_counter() - t0
-        cpu = {"value": done_b / el / 1e9, "unit": "GB/s", "cores": host_cores_used(),
-               "kind": "oracle",
-               "sample": f"oracle fp32-order GEMV replay (single-threaded C), {n_done} tensor "
-                         f"products over the {len(tensors)} stack tensors' bf16 bits "
-                         f"({n_done / len(tensors):.2f} passes), {el:.1f} s; bytes counted as "
-                         f"the R4 GEMV's"}
+        cpu = cpu_baseline(tensors, host_bits, xs, log)
 
     dominant = "gemv" if gemv_kernel_ms >= dec_kernel_ms else "rice_to_r4"
     roof_g = {"kernel": "r4_gemv", "bound": "hbm", "achieved": round(gemv_ach, 1),
@@ -657,6 +859,7 @@ def main():
         "roofline_other": roof_d if dominant == "gemv" else roof_g,
         "bf16_twin": twin,
         "gemv_per_layer_schedule": sched,
+        "other_configs": configs,
         "prompt_gemm": gemm,
         "moe_gather": moe,
         "cpu_baseline": cpu,

@@ -9,6 +9,7 @@ implementation behind it.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import threading
 from dataclasses import dataclass, field
@@ -134,6 +135,23 @@ def _call(name: str, *args):
 
 def _ptr(t: torch.Tensor | None):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _on_stream(fn):
+    """Run a device binding with `stream` as torch's current stream, so the
+    temporaries it makes (contiguous copies, outputs, GEMM workspace) are
+    allocated and filled in the same stream order as the kernel that uses
+    them, and the caching allocator does not hand them to other streams while
+    that kernel runs."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, stream=None, **kw)
+        if not isinstance(stream, torch.cuda.Stream):
+            stream = torch.cuda.ExternalStream(int(stream))
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return wrapper
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -286,6 +304,7 @@ def r4_from_planes(rows, cols, lut, sm, nib, esc_pre, esc) -> R4Tensor:
                     int(esc.numel()))
 
 
+@_on_stream
 def rice_to_r4(planes: RicePlanes, status: torch.Tensor | None = None,
                stream=None, out: R4Tensor | None = None) -> R4Tensor:
     """binade_rice_to_r4 on device planes; allocates nib / esc unless `out`."""
@@ -311,6 +330,7 @@ def rice_to_r4(planes: RicePlanes, status: torch.Tensor | None = None,
                     planes.esc_pre, esc, planes.n_esc)
 
 
+@_on_stream
 def rice_to_r4_batch(planes: list, status: torch.Tensor | None = None,
                      stream=None, outs: list | None = None) -> list:
     """binade_rice_to_r4_batch: decode several tensors (up to 16 per launch)."""
@@ -335,6 +355,7 @@ def rice_to_r4_batch(planes: list, status: torch.Tensor | None = None,
     return outs
 
 
+@_on_stream
 def r4_gemv_batch(ws: list, xs: list, out_dtype=torch.float32,
                   ys: list | None = None, stream=None) -> list:
     """binade_r4_gemv_batch: several independent R4 GEMVs in one launch."""
@@ -349,6 +370,7 @@ def r4_gemv_batch(ws: list, xs: list, out_dtype=torch.float32,
     return ys
 
 
+@_on_stream
 def bf16_gemv_batch(ws: list, xs: list, out_dtype=torch.float32,
                     ys: list | None = None, stream=None) -> list:
     """binade_bf16_gemv_batch: the batched twin."""
@@ -381,6 +403,7 @@ def _dtype_code(out_dtype) -> int:
     raise ValueError(out_dtype)
 
 
+@_on_stream
 def r4_gemv(w: R4Tensor, x: torch.Tensor, out_dtype=torch.float32,
             y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     code = _dtype_code(out_dtype)
@@ -391,6 +414,7 @@ def r4_gemv(w: R4Tensor, x: torch.Tensor, out_dtype=torch.float32,
     return y
 
 
+@_on_stream
 def bf16_gemv(w: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32,
               y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     code = _dtype_code(out_dtype)
@@ -403,6 +427,7 @@ def bf16_gemv(w: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32,
     return y
 
 
+@_on_stream
 def unpack(w: R4Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     if out is None:
         out = torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device=w.nib.device)
@@ -426,6 +451,7 @@ def _workspace(m, n, k, device, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
+@_on_stream
 def r4_gemm(w: R4Tensor, x: torch.Tensor, out_dtype=torch.float32,
             y: torch.Tensor | None = None, stream=None,
             workspace: torch.Tensor | None = None) -> torch.Tensor:
@@ -442,6 +468,7 @@ def r4_gemm(w: R4Tensor, x: torch.Tensor, out_dtype=torch.float32,
     return y
 
 
+@_on_stream
 def r4_gemm_noalloc(w: R4Tensor, x: torch.Tensor, out_dtype=torch.float32,
                     y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Y = X W^T through binade_r4_gemm_noalloc (the library's fixed scratch,
@@ -460,6 +487,7 @@ def gemm_scratch_bytes() -> int:
     return int(lib().binade_gemm_scratch_bytes())
 
 
+@_on_stream
 def bf16_gemm(w: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32,
               y: torch.Tensor | None = None, stream=None,
               workspace: torch.Tensor | None = None) -> torch.Tensor:
@@ -475,6 +503,7 @@ def bf16_gemm(w: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32,
     return y
 
 
+@_on_stream
 def r4_moe_gemv(experts: R4Tensor, n_experts: int, x: torch.Tensor,
                 idx: torch.Tensor, x_per_slot: bool = False,
                 out_dtype=torch.float32, y: torch.Tensor | None = None,
@@ -492,6 +521,7 @@ def r4_moe_gemv(experts: R4Tensor, n_experts: int, x: torch.Tensor,
     return y
 
 
+@_on_stream
 def bf16_moe_gemv(experts: torch.Tensor, n_experts: int, x: torch.Tensor,
                   idx: torch.Tensor, x_per_slot: bool = False,
                   out_dtype=torch.float32, y: torch.Tensor | None = None,

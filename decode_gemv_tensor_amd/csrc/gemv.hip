@@ -348,14 +348,14 @@ GemvArgs args_from_r4(const binade_r4* w, bool rotated) {
 
 // Launch shape: rows per wave R and whether a wave prefetches its next
 // chunk. Neither changes the arithmetic. BINADE_GEMV_ROWS_PER_WAVE (1, 2, 4)
-// and BINADE_GEMV_PREFETCH (0, 1) override the defaults.
+// and BINADE_GEMV_PREFETCH (0, 1), read once at the first launch, override
+// the defaults.
 struct GemvShape {
   int rows_per_wave;
   bool prefetch;
 };
 
-GemvShape gemv_shape(int64_t rows) {
-  (void)rows;
+GemvShape read_gemv_shape() {
   GemvShape s{1, false};   // one row per wave measured fastest at every shape
   if (const char* env = getenv("BINADE_GEMV_ROWS_PER_WAVE")) {
     const int r = atoi(env);
@@ -363,6 +363,12 @@ GemvShape gemv_shape(int64_t rows) {
   }
   if (const char* env = getenv("BINADE_GEMV_PREFETCH")) s.prefetch = atoi(env) != 0;
   return s;
+}
+
+GemvShape gemv_shape(int64_t rows) {
+  (void)rows;
+  static const GemvShape shape = read_gemv_shape();
+  return shape;
 }
 
 int32_t launch_gemv(const GemvArgs& a, bool r4, hipStream_t stream) {

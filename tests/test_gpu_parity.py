@@ -113,16 +113,40 @@ def test_r4_gemv_matches_oracle_twin_and_f64(shape):
     assert np.array_equal(yb, oracle.f32_to_bf16(y_ref))
 
 
-@pytest.mark.parametrize("rpw", ["1", "2", "4"])
-def test_gemv_bits_do_not_depend_on_launch_shape(rpw, monkeypatch):
-    monkeypatch.setenv("BINADE_GEMV_ROWS_PER_WAVE", rpw)
+_SHAPE_CHILD = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+from decode_gemv_tensor_amd import binade as B
+w = torch.from_numpy(np.load(sys.argv[2]).view(np.int16)).view(torch.bfloat16)
+x = torch.from_numpy(np.load(sys.argv[3]).view(np.int16)).view(torch.bfloat16)
+r4 = B.rice_to_r4(B.pack_rice(w).to("cuda"))
+y = B.r4_gemv(r4, x.to("cuda")).cpu().numpy()
+np.save(sys.argv[4], y)
+"""
+
+
+def test_gemv_bits_do_not_depend_on_launch_shape(tmp_path):
+    """The launch-shape knobs are read once per process, so each variant runs
+    in a child process of its own (one at a time)."""
+    import subprocess
+    import sys
     w = synth.normal_bf16(spec(203, 3072, seed=9))
     x = synth.vector_bf16(3072, 10)
+    np.save(tmp_path / "w.npy", bits_np(w))
+    np.save(tmp_path / "x.npy", bits_np(x))
+    ref = oracle.gemv_replay(bits_np(w), bits_np(x))
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for env in ({"BINADE_GEMV_ROWS_PER_WAVE": "2"}, {"BINADE_GEMV_ROWS_PER_WAVE": "4"},
+                {"BINADE_GEMV_PREFETCH": "1"}):
+        out = tmp_path / "y.npy"
+        r = subprocess.run([sys.executable, "-c", _SHAPE_CHILD, root, str(tmp_path / "w.npy"),
+                            str(tmp_path / "x.npy"), str(out)],
+                           env={**os.environ, **env}, timeout=300, capture_output=True, text=True)
+        assert r.returncode == 0, (env, r.stderr[-2000:])
+        assert same_f32(np.load(out), ref), env
     _, r4 = to_r4(w)
-    y = B.r4_gemv(r4, x.to(DEV)).cpu().numpy()
-    assert same_f32(y, oracle.gemv_replay(bits_np(w), bits_np(x)))
-    y2 = B.bf16_gemv(w.to(DEV), x.to(DEV)).cpu().numpy()
-    assert same_f32(y2, y)
+    assert same_f32(B.r4_gemv(r4, x.to(DEV)).cpu().numpy(), ref)
+    assert same_f32(B.bf16_gemv(w.to(DEV), x.to(DEV)).cpu().numpy(), ref)
 
 
 def test_exhaustive_bit_patterns_through_the_device():
@@ -237,6 +261,34 @@ def test_moe_matches_oracle_and_twin(case):
     ref = oracle.moe_replay(bits_np(w).reshape(E, N, K), bits_np(x), idx.numpy(), per_slot)
     assert same_f32(y, ref)
     assert same_f32(y2, ref)
+
+
+def test_moe_paired_rows_with_many_escapes_and_bf16_output():
+    """Rows of 88 tiles (gate/up width 2816) run two per wave with a merged
+    second pass; exponents spread over 41 values put most weights in the side
+    list (hundreds of escapes per row pair, beyond what a wave keeps in
+    registers). Outputs in fp32 and bf16 against the oracle and the twin."""
+    E, N, K, T, k = 5, 9, 2816, 4, 3
+    rng = np.random.default_rng(123)
+    sign = rng.integers(0, 2, (E * N, K)).astype(np.uint16) << 15
+    expo = rng.integers(100, 141, (E * N, K)).astype(np.uint16) << 7
+    mant = rng.integers(0, 128, (E * N, K)).astype(np.uint16)
+    wb = sign | expo | mant
+    w = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16)
+    idx = synth.topk_indices(T, k, E, 9)
+    x = synth.vector_bf16(K, 10, count=T)
+    planes, r4 = to_r4(w)
+    assert planes.n_esc > 0.5 * E * N * K
+    ref = oracle.moe_replay(wb.reshape(E, N, K), bits_np(x), idx.numpy(), False)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    y = B.r4_moe_gemv(r4, E, x.to(DEV), idx.to(DEV), status=status).cpu().numpy()
+    yb = B.r4_moe_gemv(r4, E, x.to(DEV), idx.to(DEV), out_dtype=torch.bfloat16)
+    tb = B.bf16_moe_gemv(w.to(DEV), E, x.to(DEV), idx.to(DEV), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert same_f32(y, ref)
+    assert np.array_equal(bits_np(yb), oracle.f32_to_bf16(ref))
+    assert np.array_equal(bits_np(tb), oracle.f32_to_bf16(ref))
 
 
 def test_moe_shared_experts_and_bad_index():
