@@ -74,6 +74,10 @@ def _load():
             lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
             lib.oracle_f32_to_bf16_array.argtypes = [P, I64, P]
             lib.oracle_gemm_f64.argtypes = [P, I64, I64, P, I64, P]
+            lib.oracle_pack_f1.argtypes = [P, I64, I64, P, U32, P, P, P, I64, P, I64,
+                                           P, P, P, P, P]
+            lib.oracle_f1_decode.argtypes = [I64, I64, P, U32, P, P, P, ctypes.c_uint64,
+                                             P, I64, P, P, P, P]
             lib.oracle_mfma_step.argtypes = [P, P, ctypes.c_float]
             lib.oracle_mfma_step.restype = ctypes.c_float
             lib.oracle_gemm_replay.argtypes = [P, I64, I64, P, I64, P]
@@ -184,6 +188,59 @@ def rice_decode(pk: dict) -> np.ndarray:
                                       _p(np.ascontiguousarray(pk["anchor"])),
                                       _p(np.ascontiguousarray(pk["esc_pre"])),
                                       _p(out)))
+    return out
+
+
+# ---------------------------------------------------------------- format 1
+TILE = 128  # columns per format 1 tile (the oracle's own constant)
+
+
+def pack_f1(w_bits, table: dict) -> dict:
+    """Format 1: a code width per 128-column tile with escapes ("Binade"
+    package page, "How it works": the second file format)."""
+    w = _u16(w_bits)
+    rows, cols = w.shape
+    nsym = rows * cols
+    tpr = (cols + TILE - 1) // TILE
+    cpr = (cols + CHUNK - 1) // CHUNK
+    nchunks = rows * cpr
+    code_words = nsym * 8 // 32 + 2
+    sm = np.zeros(nsym, np.uint8)
+    width = np.zeros(rows * tpr, np.uint8)
+    codes = np.zeros(code_words, np.uint32)
+    esc = np.zeros(max(nsym, 1), np.uint8)
+    anchor = np.zeros(nchunks + 1, np.uint64)
+    f1_pre = np.zeros(nchunks + 1, np.uint32)
+    esc_pre = np.zeros(nchunks + 1, np.uint32)
+    bits = ctypes.c_uint64(0)
+    nf1 = ctypes.c_int64(0)
+    _check("oracle_pack_f1",
+           _load().oracle_pack_f1(_p(w), rows, cols, _p(table["exp_of_rank"]), table["n"],
+                                  _p(sm), _p(width), _p(codes), code_words, _p(esc), esc.size,
+                                  _p(anchor), _p(f1_pre), _p(esc_pre), ctypes.byref(bits),
+                                  ctypes.byref(nf1)))
+    cb = int(bits.value)
+    return {"rows": rows, "cols": cols, "n": table["n"],
+            "exp_of_rank": table["exp_of_rank"].copy(), "sm": sm.reshape(rows, cols),
+            "width": width.reshape(rows, tpr), "codes": codes[: (cb + 31) // 32].copy(),
+            "code_bits": cb, "esc": esc[: nf1.value].copy(), "n_f1esc": int(nf1.value),
+            "anchor": anchor, "f1_pre": f1_pre, "esc_pre": esc_pre,
+            "n_esc": int(esc_pre[-1])}
+
+
+def f1_decode(pk: dict) -> np.ndarray:
+    rows, cols = pk["rows"], pk["cols"]
+    out = np.zeros((rows, cols), np.uint16)
+    codes = np.concatenate([pk["codes"], np.zeros(1, np.uint32)])
+    esc = pk["esc"] if pk["esc"].size else np.zeros(1, np.uint8)
+    _check("oracle_f1_decode",
+           _load().oracle_f1_decode(rows, cols, _p(np.ascontiguousarray(pk["exp_of_rank"])),
+                                    pk["n"], _p(np.ascontiguousarray(pk["sm"])),
+                                    _p(np.ascontiguousarray(pk["width"])), _p(codes),
+                                    pk["code_bits"], _p(np.ascontiguousarray(esc)),
+                                    pk["n_f1esc"], _p(np.ascontiguousarray(pk["anchor"])),
+                                    _p(np.ascontiguousarray(pk["f1_pre"])),
+                                    _p(np.ascontiguousarray(pk["esc_pre"])), _p(out)))
     return out
 
 

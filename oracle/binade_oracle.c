@@ -26,6 +26,7 @@
  * Parity status by function:
  *   table, rice pack/decode, r4 make/unpack, gemv replay, gemv fp64,
  *   moe replay, bf16 rounding        -- pinned by tests/test_oracle_*.py
+ *   format 1 pack/decode             -- pinned by tests/test_oracle_format1.py
  *   gemm fp64                         -- pinned by tests/test_oracle_gemv.py
  *   matrix-core step, gemm replay     -- pinned by tests/test_oracle_gemm.py
  *                                        (hand-derived cases in
@@ -261,6 +262,174 @@ int oracle_rice_decode(int64_t rows, int64_t cols, int k,
   }
   if (pos != unary_bits || anchor[nchunks] != pos ||
       esc_pre[nchunks] != nesc)
+    return OR_ECORRUPT;
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Format 1 ([P1] "How it works": the second file format, a fixed code width
+ * per 128-weight tile with escapes, about 11.27 bits per weight). The pages
+ * give no byte layout. Readings:
+ *  - a tile is 128 consecutive columns of one row; a row's last tile may be
+ *    shorter;
+ *  - a tile has a width w in 0..8. For w >= 1 a rank r < 2^w - 1 is stored
+ *    as the w-bit code r, and a larger rank as the escape code 2^w - 1 with
+ *    the rank itself appended, as a byte, to an escape list in row-major
+ *    order. w = 0 stores nothing: every rank of the tile is 0;
+ *  - a tile takes the width with the fewest bits, len * w + 8 * escapes
+ *    (w = 0 only when every rank is 0); ties go to the smaller width;
+ *  - planes: a width byte per tile (row-major); the codes, tile after tile
+ *    in row-major order, code i of a tile at bits base + i * w, least
+ *    significant bit first in u32 words; the escape bytes;
+ *  - per row-chunk of OR_CHUNK columns (whose first column starts a tile):
+ *    anchor = bit position of the chunk's first code, f1_pre = format 1
+ *    escapes before the chunk, esc_pre = weights of rank >= 15 before the
+ *    chunk (R4's escapes, as in format 2); the entry after the last chunk
+ *    holds the totals. */
+#define OR_TILE 128
+
+static int64_t tiles_per_row(int64_t cols) { return (cols + OR_TILE - 1) / OR_TILE; }
+
+/* bits of a tile's codes and escapes at width w; -1 when w = 0 cannot hold
+ * the tile (some rank is not 0) */
+static int64_t f1_tile_bits(const int *ranks, int64_t len, int w) {
+  int64_t i, esc = 0;
+  if (w == 0) {
+    for (i = 0; i < len; ++i)
+      if (ranks[i] != 0) return -1;
+    return 0;
+  }
+  for (i = 0; i < len; ++i)
+    if (ranks[i] >= (1 << w) - 1) ++esc;
+  return len * w + 8 * esc;
+}
+
+static int f1_best_width(const int *ranks, int64_t len) {
+  int w, best = -1;
+  int64_t best_bits = 0;
+  for (w = 0; w <= 8; ++w) {
+    int64_t b = f1_tile_bits(ranks, len, w);
+    if (b < 0) continue;
+    if (best < 0 || b < best_bits) {
+      best = w;
+      best_bits = b;
+    }
+  }
+  return best;
+}
+
+int oracle_pack_f1(const uint16_t *w, int64_t rows, int64_t cols,
+                   const uint8_t *exp_of_rank, uint32_t n, uint8_t *sm,
+                   uint8_t *width, uint32_t *codes, int64_t code_words,
+                   uint8_t *esc, int64_t esc_cap, uint64_t *anchor,
+                   uint32_t *f1_pre, uint32_t *esc_pre, uint64_t *code_bits_out,
+                   int64_t *n_f1esc_out) {
+  int rank_of_exp[256];
+  int ranks[OR_TILE];
+  int64_t row, t, i, tpr, cpr, n_f1 = 0, n_r4 = 0;
+  uint64_t pos = 0;
+  uint32_t r;
+  if (!w || rows <= 0 || cols <= 0 || !exp_of_rank || n == 0 || n > 256 ||
+      !sm || !width || !codes || !anchor || !f1_pre || !esc_pre)
+    return OR_EINVAL;
+  for (r = 0; r < 256; ++r) rank_of_exp[r] = -1;
+  for (r = 0; r < n; ++r) rank_of_exp[exp_of_rank[r]] = (int)r;
+  memset(codes, 0, (size_t)code_words * 4);
+  tpr = tiles_per_row(cols);
+  cpr = chunks_per_row(cols);
+  for (row = 0; row < rows; ++row) {
+    for (t = 0; t < tpr; ++t) {
+      int64_t c0 = t * OR_TILE;
+      int64_t len = cols - c0 < OR_TILE ? cols - c0 : OR_TILE;
+      int wt;
+      if (c0 % OR_CHUNK == 0) {
+        int64_t c = row * cpr + c0 / OR_CHUNK;
+        anchor[c] = pos;
+        f1_pre[c] = (uint32_t)n_f1;
+        esc_pre[c] = (uint32_t)n_r4;
+      }
+      for (i = 0; i < len; ++i) {
+        uint16_t b = w[row * cols + c0 + i];
+        ranks[i] = rank_of_exp[exponent_field(b)];
+        if (ranks[i] < 0) return OR_EINVAL;
+        sm[row * cols + c0 + i] = sm_byte(b);
+        if (ranks[i] >= 15) ++n_r4;
+      }
+      wt = f1_best_width(ranks, len);
+      width[row * tpr + t] = (uint8_t)wt;
+      if (wt == 0) continue;
+      for (i = 0; i < len; ++i) {
+        int escape = (1 << wt) - 1;
+        int code = ranks[i] >= escape ? escape : ranks[i];
+        int j;
+        if (ranks[i] >= escape) {
+          if (n_f1 >= esc_cap) return OR_ENOSPACE;
+          esc[n_f1++] = (uint8_t)ranks[i];
+        }
+        for (j = 0; j < wt; ++j, ++pos) {
+          if ((int64_t)(pos >> 5) >= code_words) return OR_ENOSPACE;
+          if ((code >> j) & 1) set_bit(codes, pos);
+        }
+      }
+    }
+  }
+  anchor[rows * cpr] = pos;
+  f1_pre[rows * cpr] = (uint32_t)n_f1;
+  esc_pre[rows * cpr] = (uint32_t)n_r4;
+  if (code_bits_out) *code_bits_out = pos;
+  if (n_f1esc_out) *n_f1esc_out = n_f1;
+  return OR_OK;
+}
+
+/* Format 1 back to bf16, code by code. A width above 8, an escape rank
+ * below its escape code or not in the table, or any disagreement with the
+ * anchors and prefixes is ECORRUPT. */
+int oracle_f1_decode(int64_t rows, int64_t cols, const uint8_t *exp_of_rank,
+                     uint32_t n, const uint8_t *sm, const uint8_t *width,
+                     const uint32_t *codes, uint64_t code_bits,
+                     const uint8_t *esc, int64_t n_f1esc,
+                     const uint64_t *anchor, const uint32_t *f1_pre,
+                     const uint32_t *esc_pre, uint16_t *out) {
+  int64_t row, t, i, tpr, cpr, n_f1 = 0, n_r4 = 0;
+  uint64_t pos = 0;
+  if (rows <= 0 || cols <= 0 || !exp_of_rank || n == 0 || n > 256 || !sm ||
+      !width || !codes || !anchor || !f1_pre || !esc_pre || !out)
+    return OR_EINVAL;
+  tpr = tiles_per_row(cols);
+  cpr = chunks_per_row(cols);
+  for (row = 0; row < rows; ++row) {
+    for (t = 0; t < tpr; ++t) {
+      int64_t c0 = t * OR_TILE;
+      int64_t len = cols - c0 < OR_TILE ? cols - c0 : OR_TILE;
+      int wt = width[row * tpr + t];
+      if (c0 % OR_CHUNK == 0) {
+        int64_t c = row * cpr + c0 / OR_CHUNK;
+        if (anchor[c] != pos || f1_pre[c] != (uint32_t)n_f1 ||
+            esc_pre[c] != (uint32_t)n_r4)
+          return OR_ECORRUPT;
+      }
+      if (wt > 8) return OR_ECORRUPT;
+      for (i = 0; i < len; ++i) {
+        int rank = 0, j;
+        if (wt > 0) {
+          int escape = (1 << wt) - 1, code = 0;
+          if (pos + (uint64_t)wt > code_bits) return OR_ECORRUPT;
+          for (j = 0; j < wt; ++j, ++pos) code |= (int)get_bit(codes, pos) << j;
+          rank = code;
+          if (code == escape) {
+            if (n_f1 >= n_f1esc) return OR_ECORRUPT;
+            rank = esc[n_f1++];
+            if (rank < escape) return OR_ECORRUPT;
+          }
+        }
+        if (rank >= (int)n) return OR_ECORRUPT;
+        if (rank >= 15) ++n_r4;
+        out[row * cols + c0 + i] = bf16_from_parts(sm[row * cols + c0 + i], exp_of_rank[rank]);
+      }
+    }
+  }
+  if (pos != code_bits || n_f1 != n_f1esc || anchor[rows * cpr] != pos ||
+      f1_pre[rows * cpr] != (uint32_t)n_f1 || esc_pre[rows * cpr] != (uint32_t)n_r4)
     return OR_ECORRUPT;
   return OR_OK;
 }
