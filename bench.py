@@ -385,6 +385,15 @@ def measure_gemm(dev, stream) -> dict:
     return out
 
 
+def f1_decode_bytes(p: B.F1Planes) -> int:
+    """Algorithmic bytes of one format 1 -> R4 decode: codes, width bytes,
+    escape bytes and the per-chunk index (anchor, two prefixes) read;
+    nibbles and R4 side-list entries written. sm is not touched."""
+    n = p.rows * p.cols
+    return ((p.code_bits + 7) // 8 + p.width.numel() + p.n_f1esc + 16 * p.anchor.numel()
+            + n // 2 + 4 * p.n_esc)
+
+
 def planes_replica(p: B.RicePlanes, dev) -> B.RicePlanes:
     """Device copies of a format 2 tensor's planes (the sm plane shared)."""
     return B.RicePlanes(rows=p.rows, cols=p.cols, table=p.table, sm=p.sm, unary=p.unary.clone(),
@@ -460,6 +469,45 @@ def measure_configs(dev, stream) -> dict:
         "bytes_per_launch": decode_bytes(dp)}
     del copies, outs, ref, dp, w
     torch.cuda.empty_cache()
+    # ---- format 1 -> R4 (the second file format) on the 64M tensor and a
+    # 12B FFN weight
+    for sp in (synth.embedding_64m(), synth.gemma_12b_ffn()[1]):
+        w = synth.normal_bf16(sp, device=dev)
+        f1 = B.pack_f1(w.cpu())
+        dp = f1.to(dev)
+        ref = B.f1_to_r4(dp)
+        per_copy = f1_decode_bytes(dp) + dp.rows * dp.cols
+        n = max(2, -(-ROTATE_BYTES // per_copy))
+        copies = [dp] + [B.F1Planes(**{**dp.__dict__, "codes": dp.codes.clone(),
+                                       "width": dp.width.clone(), "esc_rank": dp.esc_rank.clone(),
+                                       "anchor": dp.anchor.clone(), "f1_pre": dp.f1_pre.clone()})
+                         for _ in range(n - 1)]
+        outs = [ref] + [B.R4Tensor(dp.rows, dp.cols, bytes(16), dp.sm, torch.empty_like(ref.nib),
+                                   dp.esc_pre, torch.empty_like(ref.esc), dp.n_esc) for _ in range(n - 1)]
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def f1_rot():
+            for p_, o_ in zip(copies, outs):
+                B.f1_to_r4(p_, status=status, stream=stream, out=o_)
+
+        v = spread(graph_replays_ms(stream, f1_rot))
+        torch.cuda.synchronize()
+        if int(status.item()) != 0 or not all(torch.equal(o_.nib, ref.nib) for o_ in outs):
+            raise SystemExit("parity gate: format 1 decode copies differ")
+        if not torch.equal(B.unpack(ref).view(torch.int16), w.view(torch.int16)):
+            raise SystemExit("parity gate: format 1 decode unpack differs")
+        t = v["median"] / n
+        syms = dp.rows * dp.cols
+        ach = f1_decode_bytes(dp) / (t * 1e-3) / 1e9
+        out[f"format1_decode_{dp.rows}x{dp.cols}"] = {
+            "symbols": syms, "format1_bits_per_weight": round(f1.bits_per_weight(), 4),
+            "us_per_launch": round(t * 1e3, 2),
+            "us_spread": {k: round(x_ / n * 1e3, 2) for k, x_ in v.items()},
+            "gsym_per_s": round(syms / (t * 1e-3) / 1e9, 1), "GBs": round(ach, 1),
+            "frac_of_hbm_peak": round(ach / HBM_PEAK_GBS, 4), "copies": n,
+            "bytes_per_launch": f1_decode_bytes(dp)}
+        del copies, outs, ref, dp, w, f1
+        torch.cuda.empty_cache()
     # ---- 12B FFN batch-1 GEMV
     for sp in synth.gemma_12b_ffn()[1:]:
         w = synth.normal_bf16(sp, device=dev)

@@ -26,6 +26,7 @@ DEV_CORRUPT_STREAM, DEV_BAD_INDEX, DEV_CORRUPT_ESC = 0x1, 0x2, 0x4
 
 EXPORTS = ["binade_status_str", "binade_last_hip_error", "binade_build_table",
            "binade_sizes_of", "binade_pack_rice", "binade_rice_to_r4",
+           "binade_f1_sizes_of", "binade_pack_f1", "binade_f1_to_r4",
            "binade_rice_to_r4_batch", "binade_unpack", "binade_r4_gemv",
            "binade_r4_gemv_batch", "binade_bf16_gemv", "binade_bf16_gemv_batch",
            "binade_r4_gemm", "binade_bf16_gemm", "binade_gemm_workspace_bytes",
@@ -55,6 +56,22 @@ class RiceDesc(ctypes.Structure):
                 ("rem", ctypes.c_void_p), ("rem_words", ctypes.c_uint64),
                 ("anchor", ctypes.c_void_p), ("esc_pre", ctypes.c_void_p),
                 ("n_esc", ctypes.c_uint64)]
+
+
+class F1Desc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("n", ctypes.c_uint32), ("exp_of_rank", ctypes.c_uint8 * 256),
+                ("sm", ctypes.c_void_p), ("width", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("code_bits", ctypes.c_uint64),
+                ("code_words", ctypes.c_uint64), ("esc_rank", ctypes.c_void_p),
+                ("n_f1esc", ctypes.c_uint64), ("esc_cap", ctypes.c_uint64),
+                ("anchor", ctypes.c_void_p), ("f1_pre", ctypes.c_void_p),
+                ("esc_pre", ctypes.c_void_p), ("n_esc", ctypes.c_uint64)]
+
+
+class F1Sizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in
+                ("n_weights", "n_tiles", "n_chunks", "code_words", "esc_cap")]
 
 
 class R4Desc(ctypes.Structure):
@@ -105,6 +122,9 @@ def lib() -> ctypes.CDLL:
                 "binade_pack_rice": [P, I64, I64, P, P],
                 "binade_rice_to_r4": [P, P, P, P],
                 "binade_rice_to_r4_batch": [P, P, I32, P, P],
+                "binade_f1_sizes_of": [I64, I64, P],
+                "binade_pack_f1": [P, I64, I64, P, P],
+                "binade_f1_to_r4": [P, P, P, P],
                 "binade_r4_gemv_batch": [P, P, P, I32, I32, P],
                 "binade_bf16_gemv_batch": [P, P, P, P, P, I32, I32, P],
                 "binade_unpack": [P, P, P],
@@ -261,6 +281,85 @@ def pack_rice(w: torch.Tensor, table: Table | None = None) -> RicePlanes:
     return planes
 
 
+@dataclass
+class F1Planes:
+    """Format 1 planes of one tensor (host or device tensors) + descriptor."""
+    rows: int
+    cols: int
+    table: Table
+    sm: torch.Tensor
+    width: torch.Tensor
+    codes: torch.Tensor
+    esc_rank: torch.Tensor
+    anchor: torch.Tensor
+    f1_pre: torch.Tensor
+    esc_pre: torch.Tensor
+    code_bits: int
+    n_f1esc: int
+    n_esc: int
+
+    def desc(self) -> F1Desc:
+        d = F1Desc()
+        d.rows, d.cols, d.n = self.rows, self.cols, self.table.n
+        ctypes.memmove(d.exp_of_rank, self.table.exp_of_rank, 256)
+        d.sm = self.sm.data_ptr()
+        d.width = self.width.data_ptr()
+        d.codes = self.codes.data_ptr()
+        d.code_bits = self.code_bits
+        d.code_words = self.codes.numel()
+        d.esc_rank = self.esc_rank.data_ptr()
+        d.n_f1esc = self.n_f1esc
+        d.esc_cap = self.esc_rank.numel()
+        d.anchor = self.anchor.data_ptr()
+        d.f1_pre = self.f1_pre.data_ptr()
+        d.esc_pre = self.esc_pre.data_ptr()
+        d.n_esc = self.n_esc
+        return d
+
+    def to(self, device) -> "F1Planes":
+        """The planes on `device`; the code and escape planes trimmed to what
+        the tensor uses (plus a padding word)."""
+        cw = (self.code_bits + 31) // 32 + 2
+        mv = lambda t: t.to(device, non_blocking=False)
+        return F1Planes(self.rows, self.cols, self.table, mv(self.sm), mv(self.width),
+                        mv(self.codes[:cw]), mv(self.esc_rank[: max(self.n_f1esc, 1)]),
+                        mv(self.anchor), mv(self.f1_pre), mv(self.esc_pre),
+                        self.code_bits, self.n_f1esc, self.n_esc)
+
+    def bits_per_weight(self) -> float:
+        """Format 1 as stored: sm byte, codes, escape bytes, a width byte per
+        tile and 16 index bytes per row-chunk."""
+        n = self.rows * self.cols
+        bits = (8 * n + self.code_bits + 8 * self.n_f1esc + 8 * self.width.numel()
+                + 128 * self.anchor.numel())
+        return bits / n
+
+
+def pack_f1(w: torch.Tensor, table: Table | None = None) -> F1Planes:
+    """binade_pack_f1: host bf16 [rows, cols] -> host format 1 planes."""
+    w = _bits16(w)
+    if w.is_cuda or w.dim() != 2:
+        raise ValueError("pack_f1 takes a 2-D host tensor")
+    rows, cols = w.shape
+    if table is None:
+        table = build_table(w)
+    s = F1Sizes()
+    _call("binade_f1_sizes_of", rows, cols, ctypes.byref(s))
+    planes = F1Planes(rows, cols, table, torch.empty(rows, cols, dtype=torch.uint8),
+                      torch.empty(int(s.n_tiles), dtype=torch.uint8),
+                      torch.empty(int(s.code_words), dtype=torch.int32),
+                      torch.empty(int(s.esc_cap), dtype=torch.uint8),
+                      torch.empty(int(s.n_chunks) + 1, dtype=torch.int64),
+                      torch.empty(int(s.n_chunks) + 1, dtype=torch.int32),
+                      torch.empty(int(s.n_chunks) + 1, dtype=torch.int32), 0, 0, 0)
+    d = planes.desc()
+    _call("binade_pack_f1", _ptr(w), rows, cols, ctypes.byref(table), ctypes.byref(d))
+    planes.code_bits = int(d.code_bits)
+    planes.n_f1esc = int(d.n_f1esc)
+    planes.n_esc = int(d.n_esc)
+    return planes
+
+
 # ------------------------------------------------------------------ device
 @dataclass
 class R4Tensor:
@@ -321,6 +420,32 @@ def rice_to_r4(planes: RicePlanes, status: torch.Tensor | None = None,
     d_out.nib = nib.data_ptr()
     d_out.esc = esc.data_ptr()
     _call("binade_rice_to_r4", ctypes.byref(d_in), ctypes.byref(d_out),
+          _ptr(status), _stream(stream))
+    lut = bytes(d_out.lut)
+    if out is not None:
+        out.lut = lut
+        return out
+    return R4Tensor(planes.rows, planes.cols, lut, planes.sm, nib,
+                    planes.esc_pre, esc, planes.n_esc)
+
+
+@_on_stream
+def f1_to_r4(planes: F1Planes, status: torch.Tensor | None = None,
+             stream=None, out: R4Tensor | None = None) -> R4Tensor:
+    """binade_f1_to_r4 on device planes; allocates nib / esc unless `out`."""
+    if not planes.sm.is_cuda:
+        raise ValueError("f1_to_r4 takes device planes (F1Planes.to('cuda'))")
+    dev = planes.sm.device
+    if out is None:
+        nib = torch.empty(planes.rows * planes.cols // 2, dtype=torch.uint8, device=dev)
+        esc = torch.empty(max(planes.n_esc, 1), dtype=torch.int32, device=dev)
+    else:
+        nib, esc = out.nib, out.esc
+    d_in = planes.desc()
+    d_out = R4Desc()
+    d_out.nib = nib.data_ptr()
+    d_out.esc = esc.data_ptr()
+    _call("binade_f1_to_r4", ctypes.byref(d_in), ctypes.byref(d_out),
           _ptr(status), _stream(stream))
     lut = bytes(d_out.lut)
     if out is not None:

@@ -206,6 +206,112 @@ extern "C" int32_t binade_pack_rice(const uint16_t* w, int64_t rows,
   return BINADE_OK;
 }
 
+// ---------------------------------------------------------------- format 1
+// "Binade" package page, "How it works": format 1 stores a fixed code width
+// per 128-weight tile, with escapes. The layout is the one binade.h states.
+
+namespace {
+
+constexpr int64_t kTile = 128;
+
+// The width of a tile of `len` ranks with the fewest code and escape bits,
+// len * w + 8 * (ranks >= 2^w - 1); width 0 only when every rank is 0; ties
+// to the smaller width. Ranks are counted once, by value.
+int tile_width(const uint16_t* ranks, int64_t len) {
+  std::array<int64_t, 257> at_least{};   // ranks >= v, for v = 0..256
+  for (int64_t i = 0; i < len; ++i) ++at_least[ranks[i]];
+  for (int v = 255; v >= 0; --v) at_least[v] += at_least[v + 1];
+  int best = at_least[1] == 0 ? 0 : -1;
+  int64_t best_bits = 0;
+  for (int w = 1; w <= 8; ++w) {
+    const int64_t bits = len * w + 8 * at_least[(1 << w) - 1];
+    if (best < 0 || bits < best_bits) {
+      best = w;
+      best_bits = bits;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+extern "C" int32_t binade_f1_sizes_of(int64_t rows, int64_t cols,
+                                      binade_f1_sizes* out) {
+  if (out == nullptr || rows <= 0 || cols <= 0) return BINADE_EINVAL;
+  const uint64_t nw = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols);
+  out->n_weights = nw;
+  out->n_tiles = static_cast<uint64_t>(rows) * static_cast<uint64_t>((cols + kTile - 1) / kTile);
+  out->n_chunks = static_cast<uint64_t>(rows) *
+                  static_cast<uint64_t>((cols + BINADE_CHUNK - 1) / BINADE_CHUNK);
+  out->code_words = nw * 8 / 32 + 2;
+  out->esc_cap = nw;
+  return BINADE_OK;
+}
+
+extern "C" int32_t binade_pack_f1(const uint16_t* w, int64_t rows, int64_t cols,
+                                  const binade_table* t, binade_f1* out) {
+  if (w == nullptr || t == nullptr || out == nullptr || rows <= 0 ||
+      cols <= 0 || t->n == 0 || t->n > 256)
+    return BINADE_EINVAL;
+  if (out->sm == nullptr || out->width == nullptr || out->codes == nullptr ||
+      out->anchor == nullptr || out->f1_pre == nullptr || out->esc_pre == nullptr ||
+      (out->esc_cap > 0 && out->esc_rank == nullptr))
+    return BINADE_EINVAL;
+  const int64_t tpr = (cols + kTile - 1) / kTile;
+  const int64_t cpr = (cols + BINADE_CHUNK - 1) / BINADE_CHUNK;
+  BitSink codes(out->codes, out->code_words);
+  uint64_t n_f1 = 0, n_r4 = 0;
+  uint16_t ranks[kTile];
+  for (int64_t row = 0; row < rows; ++row) {
+    const uint16_t* src = w + row * cols;
+    uint8_t* sm = out->sm + row * cols;
+    for (int64_t tile = 0; tile < tpr; ++tile) {
+      const int64_t c0 = tile * kTile;
+      const int64_t len = std::min<int64_t>(kTile, cols - c0);
+      if (c0 % BINADE_CHUNK == 0) {
+        const int64_t chunk = row * cpr + c0 / BINADE_CHUNK;
+        out->anchor[chunk] = codes.position();
+        out->f1_pre[chunk] = static_cast<uint32_t>(n_f1);
+        out->esc_pre[chunk] = static_cast<uint32_t>(n_r4);
+      }
+      for (int64_t i = 0; i < len; ++i) {
+        const uint16_t b = src[c0 + i];
+        const uint16_t r = t->rank_of_exp[exponent_of(b)];
+        if (r == 0xFFFF || r >= t->n) return BINADE_EINVAL;
+        ranks[i] = r;
+        sm[c0 + i] = static_cast<uint8_t>(((b >> 8) & 0x80u) | (b & 0x7Fu));
+        n_r4 += r >= 15;
+      }
+      const int wt = tile_width(ranks, len);
+      out->width[row * tpr + tile] = static_cast<uint8_t>(wt);
+      if (wt == 0) continue;
+      const uint32_t escape = (1u << wt) - 1u;
+      for (int64_t i = 0; i < len; ++i) {
+        if (ranks[i] >= escape) {
+          if (n_f1 >= out->esc_cap) return BINADE_ENOSPACE;
+          out->esc_rank[n_f1++] = static_cast<uint8_t>(ranks[i]);
+          if (!codes.put(escape, static_cast<uint32_t>(wt))) return BINADE_ENOSPACE;
+        } else if (!codes.put(ranks[i], static_cast<uint32_t>(wt))) {
+          return BINADE_ENOSPACE;
+        }
+      }
+    }
+  }
+  if (!codes.flush()) return BINADE_ENOSPACE;
+  const int64_t nchunks = rows * cpr;
+  out->anchor[nchunks] = codes.position();
+  out->f1_pre[nchunks] = static_cast<uint32_t>(n_f1);
+  out->esc_pre[nchunks] = static_cast<uint32_t>(n_r4);
+  out->rows = rows;
+  out->cols = cols;
+  out->n = t->n;
+  std::memcpy(out->exp_of_rank, t->exp_of_rank, sizeof(out->exp_of_rank));
+  out->code_bits = codes.position();
+  out->n_f1esc = n_f1;
+  out->n_esc = n_r4;
+  return BINADE_OK;
+}
+
 extern "C" const char* binade_status_str(int32_t s) {
   switch (s) {
     case BINADE_OK: return "ok";

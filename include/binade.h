@@ -134,6 +134,57 @@ typedef struct binade_r4 {
   uint64_t n_esc;
 } binade_r4;
 
+/* Format 1 descriptor ("Binade" package page, "How it works": a fixed code
+ * width per 128-weight tile with escapes). Layout (this library's reading;
+ * the pages give none): a tile is 128 consecutive columns of a row, a row's
+ * last tile may be shorter. Each tile has a width w in 0..8; for w >= 1 a
+ * rank r < 2^w - 1 is the w-bit code r and a larger rank is the escape code
+ * 2^w - 1 with the rank appended, as a byte, to the escape list (row-major);
+ * w = 0 stores nothing (every rank of the tile is 0). A tile takes the width
+ * with the fewest bits, len * w + 8 * escapes, ties to the smaller width.
+ *   sm       u8[rows*cols]     as in format 2 (the same plane)
+ *   width    u8[tiles]          per tile, row-major (tiles = rows *
+ *                               ceil(cols / 128))
+ *   codes    u32 words          the tiles' codes in row-major order, code i
+ *                               of a tile at bits base + i*w, least
+ *                               significant bit first
+ *   esc_rank u8[n_f1esc]        ranks of the escaped weights, row-major
+ *   anchor   u64[chunks+1]      code bit position of each row-chunk's first
+ *                               code; the last entry = total code bits
+ *   f1_pre   u32[chunks+1]      format 1 escapes before each row-chunk
+ *   esc_pre  u32[chunks+1]      weights of rank >= 15 before each row-chunk
+ *                               (R4's escape prefix, as in format 2)
+ * Pointers are host memory for binade_pack_f1, device memory for
+ * binade_f1_to_r4. */
+typedef struct binade_f1 {
+  int64_t rows, cols;
+  uint32_t n;
+  uint8_t exp_of_rank[256];
+  uint8_t *sm;
+  uint8_t *width;
+  uint32_t *codes;
+  uint64_t code_bits;
+  uint64_t code_words;    /* words the buffer holds */
+  uint8_t *esc_rank;
+  uint64_t n_f1esc;
+  uint64_t esc_cap;       /* entries the esc_rank buffer holds */
+  uint64_t *anchor;
+  uint32_t *f1_pre;
+  uint32_t *esc_pre;
+  uint64_t n_esc;         /* weights of rank >= 15 */
+} binade_f1;
+
+/* Buffer capacities a caller allocates for format 1 of a rows x cols
+ * tensor (widths depend on the data, so codes and escapes are bounded by
+ * 8 bits and one escape per weight). */
+typedef struct binade_f1_sizes {
+  uint64_t n_weights;     /* rows * cols */
+  uint64_t n_tiles;       /* rows * ceil(cols / 128) */
+  uint64_t n_chunks;      /* rows * ceil(cols / BINADE_CHUNK) */
+  uint64_t code_words;    /* u32 words: 8 bits per weight + 2 */
+  uint64_t esc_cap;       /* rows * cols */
+} binade_f1_sizes;
+
 /* Text for a status code (static storage). */
 const char *binade_status_str(int32_t status);
 /* The last HIP error code seen by a device call on this thread (0 if none). */
@@ -163,6 +214,20 @@ int32_t binade_sizes_of(const binade_table *t, int64_t rows, int64_t cols,
 int32_t binade_pack_rice(const uint16_t *w, int64_t rows, int64_t cols,
                          const binade_table *t, binade_rice *out);
 
+/* Capacities for format 1 of a rows x cols tensor (host). EINVAL: null out
+ * or rows/cols <= 0. */
+int32_t binade_f1_sizes_of(int64_t rows, int64_t cols, binade_f1_sizes *out);
+
+/* Format 1 pack of the bf16 matrix w [rows, cols] (host) under table t.
+ * out->sm, width, codes, esc_rank, anchor, f1_pre and esc_pre point at
+ * caller buffers of binade_f1_sizes_of() entries; out->code_words and
+ * out->esc_cap give the codes' and escapes' capacities. Fills the scalar
+ * fields; byte-identical to the oracle's pack. "Binade" package page, "How
+ * it works" (format 1). EINVAL: bad pointers or shape, or a weight whose
+ * exponent is not in t. ENOSPACE: a capacity is too small. */
+int32_t binade_pack_f1(const uint16_t *w, int64_t rows, int64_t cols,
+                       const binade_table *t, binade_f1 *out);
+
 /* -------------------------------------------------------------- device */
 
 /* Format 2 -> R4 on the GPU ("Binade" package page, "How it works": a GPU
@@ -184,6 +249,18 @@ int32_t binade_rice_to_r4(const binade_rice *in, binade_r4 *out,
 int32_t binade_rice_to_r4_batch(const binade_rice *in, binade_r4 *out,
                                 int32_t count, uint32_t *dev_status,
                                 void *stream);
+
+/* Format 1 -> R4 on the GPU ("Binade" package page, "How it works": at load
+ * a GPU kernel turns either file format into R4). in: device planes of a
+ * format 1 tensor as binade_pack_f1 leaves them (code_words and esc_cap the
+ * buffers' entries). out: as for binade_rice_to_r4 (rows, cols, sm, esc_pre
+ * set from in; lut filled; the kernel writes out->nib and out->esc, which
+ * the caller allocates). dev_status: device u32 or NULL; the kernel ORs
+ * BINADE_DEV_CORRUPT_* into it when a chunk's planes are inconsistent (its
+ * outputs are then unspecified). EUNSUPPORTED: cols % 32 != 0 or misaligned
+ * planes. The R4 result equals binade_rice_to_r4's on the same weights. */
+int32_t binade_f1_to_r4(const binade_f1 *in, binade_r4 *out,
+                        uint32_t *dev_status, void *stream);
 
 /* R4 -> bf16 bits [rows, cols] on the GPU (the rebuild path; "Binade"
  * package page, "Use": unpack restores the original BF16 bit for bit). */

@@ -169,3 +169,37 @@ def test_device_entry_points_validate_before_touching_the_gpu():
     # zero rows: a valid no-op that launches nothing
     d.rows, d.cols = 0, 64
     assert L.binade_r4_gemv(ctypes.byref(d), None, None, 0, None) == B.OK
+
+
+@pytest.mark.parametrize("case", ["llm", "all_patterns", "one_exponent", "wide", "short_rows", "ragged"])
+def test_format1_pack_matches_oracle_bytes(case):
+    """binade_pack_f1 (host C++) against the oracle's format 1 pack, plane by
+    plane, on the spreads the oracle's pins cover."""
+    rng = np.random.default_rng(21)
+    if case == "llm":
+        wn = _np(_tensor(40, 3072, sigma=0.02, seed=3, frac=1e-3, scale=20.0))
+    elif case == "all_patterns":
+        wn = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).reshape(256, 256)
+    elif case == "one_exponent":
+        wn = ((rng.integers(0, 2, (7, 4160)) << 15) | (125 << 7) | rng.integers(0, 128, (7, 4160))).astype(np.uint16)
+    elif case == "wide":
+        wn = ((rng.integers(0, 2, (9, 2080)) << 15) | (rng.integers(20, 220, (9, 2080)) << 7)
+              | rng.integers(0, 128, (9, 2080))).astype(np.uint16)
+    elif case == "short_rows":
+        wn = _np(_tensor(300, 96, sigma=0.02, seed=4, frac=0.0, scale=1.0))
+    else:   # columns not a multiple of 32 (host packing takes any width)
+        wn = _np(_tensor(5, 1000, sigma=0.02, seed=5, frac=1e-2, scale=1e3))
+    w = torch.from_numpy(wn.view(np.int16)).view(torch.bfloat16)
+    t = B.build_table(w)
+    p = B.pack_f1(w, t)
+    po = oracle.pack_f1(wn, oracle.build_table(wn))
+    assert p.code_bits == po["code_bits"] and p.n_f1esc == po["n_f1esc"] and p.n_esc == po["n_esc"]
+    assert np.array_equal(p.sm.numpy(), po["sm"])
+    assert np.array_equal(p.width.numpy(), po["width"].reshape(-1))
+    nc = po["codes"].size
+    assert np.array_equal(p.codes.numpy().view(np.uint32)[:nc], po["codes"])
+    assert not p.codes.numpy()[nc:].any()
+    assert np.array_equal(p.esc_rank.numpy()[: p.n_f1esc], po["esc"])
+    assert np.array_equal(p.anchor.numpy().view(np.uint64), po["anchor"])
+    assert np.array_equal(p.f1_pre.numpy().view(np.uint32), po["f1_pre"])
+    assert np.array_equal(p.esc_pre.numpy().view(np.uint32), po["esc_pre"])
