@@ -535,11 +535,43 @@ def measure_configs(dev, stream) -> dict:
         if not torch.equal(y.view(torch.int32), y2.view(torch.int32)):
             raise SystemExit(f"parity gate: 12B GEMV differs from its twin ({N}x{K})")
         gb = gemv_bytes(r4) / (tr * 1e-3) / 1e9
-        out[f"gemv_{N}x{K}"] = {
+        line = {
             "us_per_launch": round(tr * 1e3, 2), "GBs": round(gb, 1),
             "frac_of_hbm_peak": round(gb / HBM_PEAK_GBS, 4),
             "bf16_twin_us": round(tt * 1e3, 2), "speedup_vs_twin": round(tt / tr, 3),
             "copies": {"r4": len(r4s), "bf16": len(wts)}}
+        # the decode step of m sequences: one launch reads W once for m rows
+        small = {}
+        for m in (2, 4, 8):
+            xm = synth.vector_bf16(K, 800 + N + m, device=dev, count=m)
+            ym = torch.empty(m, N, dtype=torch.float32, device=dev)
+            ym2 = torch.empty_like(ym)
+
+            def r4_rows_rot():
+                for t_ in r4s:
+                    B.r4_gemv_rows(t_, xm, y=ym, stream=stream)
+
+            def bf_rows_rot():
+                for t_ in wts:
+                    B.bf16_gemv_rows(t_, xm, y=ym2, stream=stream)
+
+            trm = spread(graph_replays_ms(stream, r4_rows_rot))["median"] / len(r4s)
+            ttm = spread(graph_replays_ms(stream, bf_rows_rot))["median"] / len(wts)
+            torch.cuda.synchronize()
+            if not torch.equal(ym.view(torch.int32), ym2.view(torch.int32)):
+                raise SystemExit(f"parity gate: {m}-row GEMV differs from its twin ({N}x{K})")
+            if not torch.equal(ym[0].view(torch.int32),
+                               B.r4_gemv(r4, xm[0].contiguous()).view(torch.int32)):
+                raise SystemExit(f"parity gate: {m}-row GEMV row 0 differs from batch 1")
+            bm = gemv_bytes(r4) + (m - 1) * (2 * K + 4 * N)
+            gbm = bm / (trm * 1e-3) / 1e9
+            small[f"m{m}"] = {
+                "us_per_launch": round(trm * 1e3, 2), "GBs": round(gbm, 1),
+                "frac_of_hbm_peak": round(gbm / HBM_PEAK_GBS, 4),
+                "bf16_twin_us": round(ttm * 1e3, 2), "speedup_vs_twin": round(ttm / trm, 3),
+                "speedup_vs_m_batch1_launches": round(m * tr / trm, 3)}
+        line["small_batch_rows"] = small
+        out[f"gemv_{N}x{K}"] = line
         del w, r4, r4s, wts
         torch.cuda.empty_cache()
     return out
@@ -576,11 +608,43 @@ def measure_moe(dev, stream) -> dict:
     used = int(torch.unique(idx).numel())
     nbytes = sum(r4_bytes(r4) * used // E for r4 in r4s)
     nbytes += 2 * (xh.numel() * 2 + xf.numel()) + 4 * sum(y.numel() for y in ys)
+    # the whole layer with its epilogue: gate, up, silu*up (bf16), down on the
+    # per-slot activations, router-weighted combine
+    rw = synth.router_weights(T, k, 3103, device=dev).reshape(-1)
+    h = torch.empty(T * k, synth.MOE_FFN, dtype=torch.bfloat16, device=dev)
+    comb = torch.empty(T, synth.MOE_HIDDEN, dtype=torch.float32, device=dev)
+
+    reps = 20   # launches per replay: a lone small launch is dominated by the replay's own cost
+
+    def silu_only():
+        for _ in range(reps):
+            B.moe_silu_mul(ys[0], ys[1], h=h, stream=stream)
+
+    def combine_only():
+        for _ in range(reps):
+            B.moe_combine(ys[2], rw, k, out=comb, stream=stream)
+
+    def r4_layer():
+        B.r4_moe_gemv(r4s[0], E, xh, idx, y=ys[0], stream=stream)
+        B.r4_moe_gemv(r4s[1], E, xh, idx, y=ys[1], stream=stream)
+        B.moe_silu_mul(ys[0], ys[1], h=h, stream=stream)
+        B.r4_moe_gemv(r4s[2], E, h, idx, x_per_slot=True, y=ys[2], stream=stream)
+        B.moe_combine(ys[2], rw, k, out=comb, stream=stream)
+
+    t_silu = graph_time_ms(stream, silu_only) / reps
+    t_comb = graph_time_ms(stream, combine_only) / reps
+    t_layer = graph_time_ms(stream, r4_layer)
+    torch.cuda.synchronize()
     return {"workload": "128 experts, gate/up 704x2816 and down 2816x704; 8 tokens x top-8",
             "unique_experts": used, "r4_us_per_step": round(tr * 1e3, 2),
             "r4_GBs": round(nbytes / tr / 1e6, 1), "bf16_twin_us_per_step": round(tt * 1e3, 2),
             "speedup_vs_twin": round(tt / tr, 3),
-            "bytes": "unique experts' R4 bytes once + inputs + fp32 outputs"}
+            "bytes": "unique experts' R4 bytes once + inputs + fp32 outputs",
+            "epilogue": {"silu_mul_us": round(t_silu * 1e3, 2),
+                         "combine_us": round(t_comb * 1e3, 2),
+                         "r4_layer_us": round(t_layer * 1e3, 2),
+                         "layer": "gate, up, silu*up -> bf16, down per slot, weighted top-8 "
+                                  "combine; one HIP graph"}}
 
 
 def main():

@@ -31,7 +31,8 @@ EXPORTS = ["binade_status_str", "binade_last_hip_error", "binade_build_table",
            "binade_r4_gemv_batch", "binade_bf16_gemv", "binade_bf16_gemv_batch",
            "binade_r4_gemm", "binade_bf16_gemm", "binade_gemm_workspace_bytes",
            "binade_r4_gemm_noalloc", "binade_gemm_scratch_bytes",
-           "binade_r4_moe_gemv", "binade_bf16_moe_gemv"]
+           "binade_r4_moe_gemv", "binade_bf16_moe_gemv", "binade_r4_gemv_rows",
+           "binade_bf16_gemv_rows", "binade_moe_silu_mul", "binade_moe_combine"]
 
 
 class Table(ctypes.Structure):
@@ -130,6 +131,10 @@ def lib() -> ctypes.CDLL:
                 "binade_unpack": [P, P, P],
                 "binade_r4_gemv": [P, P, P, I32, P],
                 "binade_bf16_gemv": [P, I64, I64, P, P, I32, P],
+                "binade_r4_gemv_rows": [P, P, I64, I32, P, I64, I32, P],
+                "binade_bf16_gemv_rows": [P, I64, I64, P, I64, I32, P, I64, I32, P],
+                "binade_moe_silu_mul": [P, P, I64, P, I32, P],
+                "binade_moe_combine": [P, P, I64, I32, I64, P, I32, P],
                 "binade_r4_gemm": [P, P, I64, I64, P, I64, I32, P, I64, P],
                 "binade_r4_gemm_noalloc": [P, P, I64, I64, P, I64, I32, P],
                 "binade_bf16_gemm": [P, I64, I64, P, I64, I64, P, I64, I32, P, I64,
@@ -550,6 +555,70 @@ def bf16_gemv(w: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32,
     _call("binade_bf16_gemv", _ptr(w), rows, cols, _ptr(x), _ptr(y), code,
           _stream(stream))
     return y
+
+
+@_on_stream
+def r4_gemv_rows(w: R4Tensor, x: torch.Tensor, out_dtype=torch.float32,
+                 y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """binade_r4_gemv_rows: Y[b] = W x[b] for the 1..8 rows of x [m, K]; each
+    row bit-identical to r4_gemv of that row."""
+    code = _dtype_code(out_dtype)
+    x = _bits16(x)
+    m = x.shape[0]
+    y = _y((m, w.rows), code, x.device, y)
+    d = w.desc()
+    _call("binade_r4_gemv_rows", ctypes.byref(d), _ptr(x), x.shape[1], m, _ptr(y),
+          y.shape[1], code, _stream(stream))
+    return y
+
+
+@_on_stream
+def bf16_gemv_rows(w: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32,
+                   y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """binade_bf16_gemv_rows: the twin of r4_gemv_rows."""
+    code = _dtype_code(out_dtype)
+    w = _bits16(w)
+    x = _bits16(x)
+    rows, cols = w.shape
+    m = x.shape[0]
+    y = _y((m, rows), code, x.device, y)
+    _call("binade_bf16_gemv_rows", _ptr(w), rows, cols, _ptr(x), x.shape[1], m, _ptr(y),
+          y.shape[1], code, _stream(stream))
+    return y
+
+
+@_on_stream
+def moe_silu_mul(gate: torch.Tensor, up: torch.Tensor, out_dtype=torch.bfloat16,
+                 h: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """binade_moe_silu_mul: h = silu(gate) * up (fp64 inside, one rounding)."""
+    code = _dtype_code(out_dtype)
+    if gate.dtype != torch.float32 or up.dtype != torch.float32 or gate.shape != up.shape:
+        raise ValueError("gate and up: fp32 tensors of one shape")
+    gate = gate.contiguous()
+    up = up.contiguous()
+    h = _y(tuple(gate.shape), code, gate.device, h)
+    _call("binade_moe_silu_mul", _ptr(gate), _ptr(up), gate.numel(), _ptr(h), code,
+          _stream(stream))
+    return h
+
+
+@_on_stream
+def moe_combine(y: torch.Tensor, weights: torch.Tensor, top_k: int, out_dtype=torch.float32,
+                out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """binade_moe_combine: out[t] = sum over the token's top_k slots of
+    weight * y, an fp32 fma chain in slot order."""
+    code = _dtype_code(out_dtype)
+    if y.dtype != torch.float32 or weights.dtype != torch.float32:
+        raise ValueError("y and weights: fp32")
+    y = y.contiguous()
+    weights = weights.contiguous()
+    pairs, n = y.shape
+    if pairs % top_k or weights.numel() != pairs:
+        raise ValueError("y rows and weights must be n_tokens * top_k")
+    out = _y((pairs // top_k, n), code, y.device, out)
+    _call("binade_moe_combine", _ptr(y), _ptr(weights), pairs // top_k, top_k, n, _ptr(out),
+          code, _stream(stream))
+    return out
 
 
 @_on_stream

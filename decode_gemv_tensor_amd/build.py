@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["host_pack.cpp", "runtime.cpp", "gemv.hip", "rice_to_r4.hip",
-           "f1_to_r4.hip", "gemm.hip", "moe.hip"]
+           "f1_to_r4.hip", "gemm.hip", "moe.hip", "moe_epilogue.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",

@@ -267,6 +267,110 @@ __global__ __launch_bounds__(256) void bf16_gemv_kernel(GemvArgs a) {
   bf16_gemv_rows<R>(a, row0, lane);
 }
 
+// ---------------------------------------------------------------- 2..8 rows
+// The decode step of a few sequences at once: Y[b, :] = W x_b for b < m
+// (m <= 8), each output in exactly the batch-1 order above, so row b of Y is
+// bit-identical to the batch-1 product of x_b. A wave owns one weight row:
+// per lane tile it loads and rebuilds the 32 weights once and runs them
+// through the MB rows' two fma chains (x rows past m repeat row m-1 and are
+// not stored). Rows of x and y are ldx and ldy elements apart.
+struct GemvRowsArgs {
+  GemvArgs g;              // weights, table, rows, cols, y_bf16 (g.x, g.y: row 0)
+  int64_t ldx, ldy;
+  int32_t m;
+};
+
+template <int MB, bool kR4>
+__global__ __launch_bounds__(256) void gemv_rows_kernel(GemvRowsArgs ra) {
+  const GemvArgs& a = ra.g;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = uniform64(static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) +
+                                (threadIdx.x >> 6));
+  if (row >= a.rows) return;
+  const int J = a.cols >> 5;
+  const int C = (J + 63) >> 6;
+  const Lut Lr{a.lut0, a.lut1, a.lut2, a.lut3};
+  const uint16_t* xr[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) xr[b] = a.x + (b < ra.m ? b : ra.m - 1) * ra.ldx;
+  float acc0[MB], acc1[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) acc0[b] = acc1[b] = 0.0f;
+
+  for (int j = 0; j < C; ++j) {
+    const int t = j * 64 + lane;
+    if (t >= J) break;   // only in a ragged last chunk
+    float w[32];
+    if (kR4) {
+      const uint4* ps = reinterpret_cast<const uint4*>(a.sm + row * a.cols + 32 * t);
+      const uint4 s0 = ps[0], s1 = ps[1];
+      const uint4 nb = *reinterpret_cast<const uint4*>(a.nib + row * (a.cols >> 1) + 16 * t);
+      uint32_t E[8];
+      tile_exponents<true>(nb, Lr, a.esc_pre, a.esc, a.n_esc, row * C + j, lane, E);
+      const uint32_t S[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        uint32_t H, Lo;
+        split4_rot(S[d], E[d], H, Lo);
+        w[4 * d] = weight_f32<0>(H, Lo);
+        w[4 * d + 1] = weight_f32<1>(H, Lo);
+        w[4 * d + 2] = weight_f32<2>(H, Lo);
+        w[4 * d + 3] = weight_f32<3>(H, Lo);
+      }
+    } else {
+      const uint4* pw = reinterpret_cast<const uint4*>(
+          reinterpret_cast<const uint16_t*>(a.sm) + row * a.cols + 32 * t);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint4 q = pw[v];
+        const uint32_t d4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[8 * v + 2 * e] = bf16_lo(d4[e]);
+          w[8 * v + 2 * e + 1] = bf16_hi(d4[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      float xf[32];
+      load_x_tile(xr[b], t, xf);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc0[b] = __builtin_fmaf(w[2 * i], xf[2 * i], acc0[b]);
+        acc1[b] = __builtin_fmaf(w[2 * i + 1], xf[2 * i + 1], acc1[b]);
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    const float p = slot_tree(acc0[b] + acc1[b]);
+    if (lane == 0 && b < ra.m) {
+      const int64_t o = b * ra.ldy + row;
+      if (a.y_bf16)
+        static_cast<uint16_t*>(a.y)[o] = to_bf16_rne(p);
+      else
+        static_cast<float*>(a.y)[o] = p;
+    }
+  }
+}
+
+int32_t launch_gemv_rows(const GemvRowsArgs& ra, bool r4, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>((ra.g.rows + 3) / 4));
+  const dim3 block(256);
+  if (ra.m <= 2) {
+    if (r4) hipLaunchKernelGGL((gemv_rows_kernel<2, true>), grid, block, 0, stream, ra);
+    else hipLaunchKernelGGL((gemv_rows_kernel<2, false>), grid, block, 0, stream, ra);
+  } else if (ra.m <= 4) {
+    if (r4) hipLaunchKernelGGL((gemv_rows_kernel<4, true>), grid, block, 0, stream, ra);
+    else hipLaunchKernelGGL((gemv_rows_kernel<4, false>), grid, block, 0, stream, ra);
+  } else {
+    if (r4) hipLaunchKernelGGL((gemv_rows_kernel<8, true>), grid, block, 0, stream, ra);
+    else hipLaunchKernelGGL((gemv_rows_kernel<8, false>), grid, block, 0, stream, ra);
+  }
+  return launch_status();
+}
+
 // One wave per row-chunk; lane l rebuilds its tile's 32 bf16 patterns.
 __global__ __launch_bounds__(256) void r4_unpack_kernel(GemvArgs a,
                                                         uint16_t* out) {
@@ -545,4 +649,48 @@ extern "C" int32_t binade_unpack(const binade_r4* w, uint16_t* out,
   hipLaunchKernelGGL(r4_unpack_kernel, grid, dim3(256), 0,
                      static_cast<hipStream_t>(stream), a, out);
   return launch_status();
+}
+
+extern "C" int32_t binade_r4_gemv_rows(const binade_r4* w, const uint16_t* x, int64_t ldx,
+                                       int32_t m, void* y, int64_t ldy, int32_t y_dtype,
+                                       void* stream) {
+  int32_t s = check_r4(w);
+  if (s != BINADE_OK) return s;
+  if (y_dtype != BINADE_F32 && y_dtype != BINADE_BF16) return BINADE_EINVAL;
+  if (m < 1 || m > 8 || ldx < w->cols || ldy < w->rows) return BINADE_EINVAL;
+  if (w->rows == 0) return BINADE_OK;
+  if (x == nullptr || y == nullptr) return BINADE_EINVAL;
+  if (!aligned16(x) || ldx % 8 != 0) return BINADE_EUNSUPPORTED;
+  GemvRowsArgs ra{};
+  ra.g = args_from_r4(w, true);
+  ra.g.x = x;
+  ra.g.y = y;
+  ra.g.y_bf16 = y_dtype == BINADE_BF16;
+  ra.ldx = ldx;
+  ra.ldy = ldy;
+  ra.m = m;
+  return launch_gemv_rows(ra, true, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t binade_bf16_gemv_rows(const uint16_t* w, int64_t rows, int64_t cols,
+                                         const uint16_t* x, int64_t ldx, int32_t m, void* y,
+                                         int64_t ldy, int32_t y_dtype, void* stream) {
+  if (rows < 0 || cols <= 0) return BINADE_EINVAL;
+  if (cols % 32 != 0 || cols > (1 << 30)) return BINADE_EUNSUPPORTED;
+  if (y_dtype != BINADE_F32 && y_dtype != BINADE_BF16) return BINADE_EINVAL;
+  if (m < 1 || m > 8 || ldx < cols || ldy < rows) return BINADE_EINVAL;
+  if (rows == 0) return BINADE_OK;
+  if (w == nullptr || x == nullptr || y == nullptr) return BINADE_EINVAL;
+  if (!aligned16(w) || !aligned16(x) || ldx % 8 != 0) return BINADE_EUNSUPPORTED;
+  GemvRowsArgs ra{};
+  ra.g.sm = reinterpret_cast<const uint8_t*>(w);
+  ra.g.rows = rows;
+  ra.g.cols = static_cast<int32_t>(cols);
+  ra.g.x = x;
+  ra.g.y = y;
+  ra.g.y_bf16 = y_dtype == BINADE_BF16;
+  ra.ldx = ldx;
+  ra.ldy = ldy;
+  ra.m = m;
+  return launch_gemv_rows(ra, false, static_cast<hipStream_t>(stream));
 }

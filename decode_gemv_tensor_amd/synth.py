@@ -68,6 +68,15 @@ def topk_indices(n_tokens: int, top_k: int, n_experts: int, seed: int,
     return torch.argsort(keys, dim=1)[:, :top_k].to(torch.int32).contiguous()
 
 
+def router_weights(n_tokens: int, top_k: int, seed: int, device="cpu") -> torch.Tensor:
+    """fp32 [n_tokens, top_k] of positive weights summing to one per token (a
+    router's normalised top-k scores), from seeded N(0, 1) logits."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    logits = torch.randn(n_tokens, top_k, generator=g, device=device, dtype=torch.float32)
+    return torch.softmax(logits, dim=1).contiguous()
+
+
 def bits(t: torch.Tensor) -> torch.Tensor:
     """The raw 16-bit patterns of a bf16 tensor, as int16 (same storage)."""
     return t.view(torch.int16)

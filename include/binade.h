@@ -298,6 +298,24 @@ int32_t binade_bf16_gemv(const uint16_t *w, int64_t rows, int64_t cols,
                          const uint16_t *x, void *y, int32_t y_dtype,
                          void *stream);
 
+/* The decode step of 2..8 sequences: Y[b, :] = W x_b for b < m, m in 1..8
+ * ("Binade" package page, "Limitations": the fused kernels cover small dense
+ * products; "Results": the per-token matvec). Each row of Y is bit-identical
+ * to binade_r4_gemv of that row of X (the same order per output), and W is
+ * read once for all m rows. x: device bf16, row b at x + b*ldx (ldx >= K, a
+ * multiple of 8, x 16-byte aligned). y: device fp32 or bf16 per y_dtype,
+ * row b at y + b*ldy (ldy >= N). EINVAL: m outside 1..8, bad strides or
+ * pointers. */
+int32_t binade_r4_gemv_rows(const binade_r4 *w, const uint16_t *x, int64_t ldx,
+                            int32_t m, void *y, int64_t ldy, int32_t y_dtype,
+                            void *stream);
+
+/* The same with plain bf16 W [rows, cols] (device): the twin. */
+int32_t binade_bf16_gemv_rows(const uint16_t *w, int64_t rows, int64_t cols,
+                              const uint16_t *x, int64_t ldx, int32_t m,
+                              void *y, int64_t ldy, int32_t y_dtype,
+                              void *stream);
+
 /* Prompt GEMM Y[M,N] = X[M,K] W[N,K]^T with W in R4, tiles decoded into LDS
  * and multiplied on bf16 MFMA with fp32 accumulation ("Binade" package page,
  * "Results" and "Limitations": prompt processing with fused GEMM). X: device
@@ -375,6 +393,26 @@ int32_t binade_bf16_moe_gemv(const uint16_t *experts, int32_t n_experts,
                              const int32_t *idx, int64_t n_tokens,
                              int32_t top_k, void *y, int32_t y_dtype,
                              uint32_t *dev_status, void *stream);
+
+/* MoE epilogue, gate.up activation ("Binade" package page, "How it works"
+ * and "Limitations": the expert products of a MoE layer, whose gate and up
+ * outputs meet in an activation before the down product). h[i] = silu(g[i])
+ * * u[i] for i < n, silu(g) = g / (1 + exp(-g)), evaluated in fp64 from the
+ * fp32 inputs and rounded once to fp32 (then to bf16, nearest-even, when
+ * h_dtype is BF16). gate, up: device fp32[n]; h: device fp32 or bf16 [n].
+ * g = -inf gives NaN, as the formula does. */
+int32_t binade_moe_silu_mul(const float *gate, const float *up, int64_t n,
+                            void *h, int32_t h_dtype, void *stream);
+
+/* MoE epilogue, top-k weighted combine. y: device fp32 [n_tokens*top_k, N]
+ * (the down product per (token, slot) pair, as binade_r4_moe_gemv writes
+ * it); weights: device fp32 [n_tokens*top_k]. out[t, j] = acc after
+ * acc = +0.0; acc = fma(weights[t*top_k + s], y[t*top_k + s, j], acc) for
+ * s = 0 .. top_k-1, in fp32 (then bf16, nearest-even, when out_dtype is
+ * BF16). out: device [n_tokens, N]. EINVAL: top_k outside 1..64, sizes. */
+int32_t binade_moe_combine(const float *y, const float *weights,
+                           int64_t n_tokens, int32_t top_k, int64_t n,
+                           void *out, int32_t out_dtype, void *stream);
 
 #ifdef __cplusplus
 }

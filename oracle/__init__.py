@@ -48,8 +48,7 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_SO):
-                build()
+            build()   # compiles when the library is missing or older than its source
             lib = ctypes.CDLL(_SO)
             P = ctypes.c_void_p
             I64 = ctypes.c_int64
@@ -81,6 +80,9 @@ def _load():
             lib.oracle_mfma_step.argtypes = [P, P, ctypes.c_float]
             lib.oracle_mfma_step.restype = ctypes.c_float
             lib.oracle_gemm_replay.argtypes = [P, I64, I64, P, I64, P]
+            lib.oracle_silu_mul.argtypes = [P, P, I64, P]
+            lib.oracle_silu_mul.restype = None
+            lib.oracle_moe_combine.argtypes = [P, P, I64, I, I64, P]
             lib.oracle_gemm_replay_entries.argtypes = [P, I64, I64, P, I64, P,
                                                        P, I64, P]
             _lib = lib
@@ -318,6 +320,35 @@ def moe_replay(experts_bits, x_bits, idx, x_per_slot: bool) -> np.ndarray:
                                      1 if x_per_slot else 0, _p(idx),
                                      n_tokens, top_k, _p(y)))
     return y
+
+
+def gemv_rows_replay(w_bits, x_rows_bits) -> np.ndarray:
+    """Y[b] = W x_b for each row of X, each row in the matvec order: the
+    small-batch decode product's definition."""
+    x = _u16(x_rows_bits)
+    return np.stack([gemv_replay(w_bits, x[b]) for b in range(x.shape[0])])
+
+
+def silu_mul(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """MoE activation h = silu(gate) * up, in double, rounded once to fp32."""
+    g = np.ascontiguousarray(gate, np.float32)
+    u = np.ascontiguousarray(up, np.float32)
+    assert g.shape == u.shape
+    out = np.zeros(g.shape, np.float32)
+    _load().oracle_silu_mul(_p(g), _p(u), g.size, _p(out))
+    return out
+
+
+def moe_combine(y: np.ndarray, weights: np.ndarray, top_k: int) -> np.ndarray:
+    """out[t] = fp32 fma chain over the token's top_k slots, slot order."""
+    y = np.ascontiguousarray(y, np.float32)
+    w = np.ascontiguousarray(weights, np.float32).reshape(-1)
+    pairs, n = y.shape
+    assert pairs % top_k == 0 and w.size == pairs
+    out = np.zeros((pairs // top_k, n), np.float32)
+    _check("oracle_moe_combine",
+           _load().oracle_moe_combine(_p(y), _p(w), pairs // top_k, top_k, n, _p(out)))
+    return out
 
 
 def gemm_f64(w_bits, x_bits) -> np.ndarray:

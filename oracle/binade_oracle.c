@@ -27,6 +27,7 @@
  *   table, rice pack/decode, r4 make/unpack, gemv replay, gemv fp64,
  *   moe replay, bf16 rounding        -- pinned by tests/test_oracle_*.py
  *   format 1 pack/decode             -- pinned by tests/test_oracle_format1.py
+ *   moe silu*up, moe combine         -- pinned by tests/test_oracle_moe_epilogue.py
  *   gemm fp64                         -- pinned by tests/test_oracle_gemv.py
  *   matrix-core step, gemm replay     -- pinned by tests/test_oracle_gemm.py
  *                                        (hand-derived cases in
@@ -651,6 +652,39 @@ uint16_t oracle_f32_to_bf16(float f) {
 void oracle_f32_to_bf16_array(const float *in, int64_t n, uint16_t *out) {
   int64_t i;
   for (i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(in[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* MoE epilogue ([P1] "How it works" and "Limitations": a MoE layer's expert
+ * products; gate and up outputs meet in an activation before down, and a
+ * token's chosen experts' outputs are summed with the router's weights).
+ * Readings: the activation is SiLU, silu(g) = g / (1 + exp(-g)), applied to
+ * gate and multiplied by up, evaluated in double from the fp32 inputs and
+ * rounded once to fp32; the combine is an fp32 fused multiply-add chain over
+ * the token's slots in slot order, starting at +0.0. */
+void oracle_silu_mul(const float *gate, const float *up, int64_t n, float *out) {
+  int64_t i;
+  for (i = 0; i < n; ++i) {
+    double g = (double)gate[i];
+    double silu = g / (1.0 + exp(-g));
+    out[i] = (float)(silu * (double)up[i]);
+  }
+}
+
+int oracle_moe_combine(const float *y, const float *weights, int64_t n_tokens,
+                       int top_k, int64_t n, float *out) {
+  int64_t t, j;
+  int s;
+  if (!y || !weights || !out || n_tokens < 0 || n < 0 || top_k < 1) return OR_EINVAL;
+  for (t = 0; t < n_tokens; ++t) {
+    for (j = 0; j < n; ++j) {
+      float acc = 0.0f;
+      for (s = 0; s < top_k; ++s)
+        acc = fmaf(weights[t * top_k + s], y[(t * top_k + s) * n + j], acc);
+      out[t * n + j] = acc;
+    }
+  }
+  return OR_OK;
 }
 
 /* ------------------------------------------------------------------ */
