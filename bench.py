@@ -508,6 +508,57 @@ def measure_configs(dev, stream) -> dict:
             "bytes_per_launch": f1_decode_bytes(dp)}
         del copies, outs, ref, dp, w, f1
         torch.cuda.empty_cache()
+    # ---- the table and the format 2 pack on the device
+    for sp in [synth.gemma_12b_ffn()[0], synth.embedding_64m()]:
+        w = synth.normal_bf16(sp, device=dev)
+        rows, cols = sp.rows, sp.cols
+        n_copy = max(2, -(-ROTATE_BYTES // (2 * rows * cols)))
+        wcopies = [w] + [w.clone() for _ in range(n_copy - 1)]
+        ref = B.pack_rice_gpu(w)          # table on the device, planes, status-free run
+        table = ref.table
+        wsb = int(B.lib().binade_pack_gpu_workspace_bytes(rows, cols))
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        dtab = torch.empty(ctypes.sizeof(B.Table), dtype=torch.uint8, device=dev)
+        outp = B.RicePlanes(rows, cols, table, torch.empty_like(ref.sm), torch.empty_like(ref.unary),
+                            None if ref.rem is None else torch.empty_like(ref.rem),
+                            torch.empty_like(ref.anchor), torch.empty_like(ref.esc_pre), 0, 0)
+        d = outp.desc()
+        st = ctypes.c_void_p(stream.cuda_stream)
+
+        def table_rot():
+            for w_ in wcopies:
+                B._call("binade_build_table_gpu", B._ptr(w_), w_.numel(), B._ptr(ws), B._ptr(dtab), st)
+
+        def pack_rot():
+            for w_ in wcopies:
+                B._call("binade_pack_rice_gpu", B._ptr(w_), rows, cols, ctypes.byref(table),
+                        ctypes.byref(d), B._ptr(ws), None, st)
+
+        tt = spread(graph_replays_ms(stream, table_rot))["median"] / n_copy
+        tp = spread(graph_replays_ms(stream, pack_rot))["median"] / n_copy
+        torch.cuda.synchronize()
+        if not (torch.equal(outp.unary, ref.unary) and torch.equal(outp.sm, ref.sm)
+                and torch.equal(outp.anchor, ref.anchor)):
+            raise SystemExit("parity gate: device pack replays differ")
+        host = B.pack_rice(w.cpu())
+        if not (torch.equal(host.unary, ref.unary.cpu()) and torch.equal(host.sm, ref.sm.cpu())):
+            raise SystemExit("parity gate: device pack differs from the host pack")
+        t0 = time.perf_counter()
+        B.pack_rice(w.cpu())
+        host_ms = (time.perf_counter() - t0) * 1e3
+        planes_b = sum(ref.nbytes().values())
+        pack_b = 2 * rows * cols + planes_b        # bf16 read once + planes written
+        gbp = pack_b / (tp * 1e-3) / 1e9
+        out[f"gpu_table_and_pack_{rows}x{cols}"] = {
+            "table_us": round(tt * 1e3, 2), "pack_us": round(tp * 1e3, 2),
+            "table_GBs_read": round(2 * rows * cols / (tt * 1e-3) / 1e9, 1),
+            "pack_GBs": round(gbp, 1), "pack_frac_of_hbm_peak": round(gbp / HBM_PEAK_GBS, 4),
+            "bytes_per_pack": pack_b, "host_pack_ms_one_thread": round(host_ms, 1),
+            "speedup_vs_host_pack": round(host_ms / ((tt + tp)), 1), "copies": n_copy,
+            "note": "pack bytes: the bf16 weights read once plus the planes written; the kernels "
+                    "read the weights twice (count, then write)"}
+        del w, wcopies, ref, outp, ws
+        torch.cuda.empty_cache()
     # ---- 12B FFN batch-1 GEMV
     for sp in synth.gemma_12b_ffn()[1:]:
         w = synth.normal_bf16(sp, device=dev)

@@ -32,7 +32,8 @@ EXPORTS = ["binade_status_str", "binade_last_hip_error", "binade_build_table",
            "binade_r4_gemm", "binade_bf16_gemm", "binade_gemm_workspace_bytes",
            "binade_r4_gemm_noalloc", "binade_gemm_scratch_bytes",
            "binade_r4_moe_gemv", "binade_bf16_moe_gemv", "binade_r4_gemv_rows",
-           "binade_bf16_gemv_rows", "binade_moe_silu_mul", "binade_moe_combine"]
+           "binade_bf16_gemv_rows", "binade_moe_silu_mul", "binade_moe_combine",
+           "binade_build_table_gpu", "binade_pack_gpu_workspace_bytes", "binade_pack_rice_gpu"]
 
 
 class Table(ctypes.Structure):
@@ -117,6 +118,8 @@ def lib() -> ctypes.CDLL:
             L.binade_gemm_workspace_bytes.restype = I64
             L.binade_gemm_scratch_bytes.argtypes = []
             L.binade_gemm_scratch_bytes.restype = I64
+            L.binade_pack_gpu_workspace_bytes.argtypes = [I64, I64]
+            L.binade_pack_gpu_workspace_bytes.restype = I64
             sig = {
                 "binade_build_table": [P, I64, P],
                 "binade_sizes_of": [P, I64, I64, P],
@@ -135,6 +138,8 @@ def lib() -> ctypes.CDLL:
                 "binade_bf16_gemv_rows": [P, I64, I64, P, I64, I32, P, I64, I32, P],
                 "binade_moe_silu_mul": [P, P, I64, P, I32, P],
                 "binade_moe_combine": [P, P, I64, I32, I64, P, I32, P],
+                "binade_build_table_gpu": [P, I64, P, P, P],
+                "binade_pack_rice_gpu": [P, I64, I64, P, P, P, P, P],
                 "binade_r4_gemm": [P, P, I64, I64, P, I64, I32, P, I64, P],
                 "binade_r4_gemm_noalloc": [P, P, I64, I64, P, I64, I32, P],
                 "binade_bf16_gemm": [P, I64, I64, P, I64, I64, P, I64, I32, P, I64,
@@ -281,6 +286,59 @@ def pack_rice(w: torch.Tensor, table: Table | None = None) -> RicePlanes:
     planes = RicePlanes(rows, cols, table, sm, unary, rem, anchor, esc_pre, 0, 0)
     d = planes.desc()
     _call("binade_pack_rice", _ptr(w), rows, cols, ctypes.byref(table), ctypes.byref(d))
+    planes.unary_bits = int(d.unary_bits)
+    planes.n_esc = int(d.n_esc)
+    return planes
+
+
+def build_table_gpu(w: torch.Tensor, workspace: torch.Tensor | None = None,
+                    stream=None) -> Table:
+    """binade_build_table_gpu on a device bf16 tensor; the table is copied
+    back to the host (one synchronisation)."""
+    w = _bits16(w)
+    if not w.is_cuda:
+        raise ValueError("build_table_gpu takes a device tensor")
+    if workspace is None:
+        workspace = torch.empty(2048, dtype=torch.uint8, device=w.device)
+    dt = torch.empty(ctypes.sizeof(Table), dtype=torch.uint8, device=w.device)
+    s = torch.cuda.current_stream(w.device) if stream is None else stream
+    with torch.cuda.stream(s):
+        _call("binade_build_table_gpu", _ptr(w), w.numel(), _ptr(workspace), _ptr(dt),
+              _stream(s))
+        host = dt.cpu()
+    t = Table()
+    ctypes.memmove(ctypes.addressof(t), host.numpy().ctypes.data, ctypes.sizeof(Table))
+    return t
+
+
+def pack_rice_gpu(w: torch.Tensor, table: Table | None = None, status: torch.Tensor | None = None,
+                  stream=None) -> RicePlanes:
+    """binade_pack_rice_gpu: device bf16 [rows, cols] -> device format 2
+    planes, byte-identical to pack_rice; the table is built on the device
+    when not given."""
+    w = _bits16(w)
+    if not w.is_cuda or w.dim() != 2:
+        raise ValueError("pack_rice_gpu takes a 2-D device tensor")
+    rows, cols = w.shape
+    dev = w.device
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    ws_bytes = int(lib().binade_pack_gpu_workspace_bytes(rows, cols))
+    with torch.cuda.stream(s):
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        if table is None:
+            table = build_table_gpu(w, ws, stream=s)
+        sz = sizes_of(table, rows, cols)
+        sm = torch.empty(rows, cols, dtype=torch.uint8, device=dev)
+        unary = torch.empty(int(sz.unary_words), dtype=torch.int32, device=dev)
+        rem = (torch.empty(int(sz.rem_words), dtype=torch.int32, device=dev)
+               if table.k > 0 else None)
+        anchor = torch.empty(int(sz.n_chunks) + 1, dtype=torch.int64, device=dev)
+        esc_pre = torch.empty(int(sz.n_chunks) + 1, dtype=torch.int32, device=dev)
+        planes = RicePlanes(rows, cols, table, sm, unary, rem, anchor, esc_pre, 0, 0)
+        d = planes.desc()
+        _call("binade_pack_rice_gpu", _ptr(w), rows, cols, ctypes.byref(table), ctypes.byref(d),
+              _ptr(ws), _ptr(status), _stream(s))
+        ws.record_stream(s)
     planes.unary_bits = int(d.unary_bits)
     planes.n_esc = int(d.n_esc)
     return planes

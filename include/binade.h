@@ -230,6 +230,36 @@ int32_t binade_pack_f1(const uint16_t *w, int64_t rows, int64_t cols,
 
 /* -------------------------------------------------------------- device */
 
+/* The exponent table on the GPU: the same table binade_build_table makes
+ * ("Binade" package page, intro and "How it works": one table per tensor,
+ * exponents ranked by frequency; ties to the smaller exponent; the Rice k
+ * with the fewest bits, ties to the smaller k). w: device bf16[n], 16-byte
+ * aligned. workspace: device, >= 2048 bytes, 8-byte aligned (the histogram;
+ * cleared by the call). table: device binade_table, written by the call.
+ * Calls on one stream that share a workspace are ordered; calls that overlap
+ * on different streams need their own. */
+int32_t binade_build_table_gpu(const uint16_t *w, int64_t n, void *workspace,
+                               binade_table *table, void *stream);
+
+/* Workspace bytes binade_pack_rice_gpu needs for a rows x cols tensor
+ * (8 per row-chunk and 12 per 1024 chunks; at least the table's 2048). */
+int64_t binade_pack_gpu_workspace_bytes(int64_t rows, int64_t cols);
+
+/* Format 2 pack on the GPU: the same planes, byte for byte, as
+ * binade_pack_rice (padding words included). w: device bf16 [rows, cols],
+ * cols % 32 == 0. t: the tensor's table in HOST memory (binade_build_table,
+ * or binade_build_table_gpu copied back). out: device planes with host
+ * capacities as for binade_pack_rice; the scalar fields are filled from the
+ * table. dev_status (device u32 or NULL) gets BINADE_DEV_CORRUPT_STREAM when
+ * a weight's exponent is not in t or the bits disagree with t's counts (the
+ * planes are then unspecified; no write leaves the buffers).
+ * EUNSUPPORTED: cols % 32 != 0, misaligned pointers. ENOSPACE: capacities. */
+int32_t binade_pack_rice_gpu(const uint16_t *w, int64_t rows, int64_t cols,
+                             const binade_table *t, binade_rice *out,
+                             void *workspace, uint32_t *dev_status,
+                             void *stream);
+
+
 /* Format 2 -> R4 on the GPU ("Binade" package page, "How it works": a GPU
  * kernel turns the file format into R4 at load). in: device planes of a
  * format 2 tensor (all of in's fields filled as binade_pack_rice leaves
