@@ -80,6 +80,9 @@ def _load():
             lib.oracle_mfma_step.argtypes = [P, P, ctypes.c_float]
             lib.oracle_mfma_step.restype = ctypes.c_float
             lib.oracle_gemm_replay.argtypes = [P, I64, I64, P, I64, P]
+            lib.oracle_huff_lengths.argtypes = [P, P]
+            lib.oracle_huff_pack.argtypes = [P, I64, P, P, P, I64, P, P, P]
+            lib.oracle_huff_decode.argtypes = [I64, P, P, P, I64, P, P, P]
             lib.oracle_silu_mul.argtypes = [P, P, I64, P]
             lib.oracle_silu_mul.restype = None
             lib.oracle_moe_combine.argtypes = [P, P, I64, I, I64, P]
@@ -348,6 +351,62 @@ def moe_combine(y: np.ndarray, weights: np.ndarray, top_k: int) -> np.ndarray:
     out = np.zeros((pairs // top_k, n), np.float32)
     _check("oracle_moe_combine",
            _load().oracle_moe_combine(_p(y), _p(w), pairs // top_k, top_k, n, _p(out)))
+    return out
+
+
+HUFF_BLOCK, HUFF_GROUP, HUFF_MAXLEN = 64, 128, 31
+
+
+def exponent_counts(w_bits) -> np.ndarray:
+    """Count of each exponent byte (the Huffman codec's symbol counts)."""
+    w = _u16(w_bits).reshape(-1)
+    return np.bincount((w >> 7) & 0xFF, minlength=256).astype(np.uint64)
+
+
+def huff_lengths(counts) -> np.ndarray:
+    """Huffman code length of each exponent ("Lossless BF16 weight
+    compression" page: canonical Huffman over the exponent field)."""
+    c = np.ascontiguousarray(counts, np.uint64)
+    assert c.size == 256
+    ln = np.zeros(256, np.uint8)
+    _check("oracle_huff_lengths", _load().oracle_huff_lengths(_p(c), _p(ln)))
+    return ln
+
+
+def huff_pack(w_bits, lengths) -> dict:
+    """Blocks of 64 exponents in canonical Huffman codes, MSB-first, each
+    padded to a byte; 8-bit block lengths; a byte offset per 128 blocks."""
+    w = _u16(w_bits).reshape(-1)
+    ln = np.ascontiguousarray(lengths, np.uint8)
+    n = w.size
+    counts = exponent_counts(w)
+    nb = (n + HUFF_BLOCK - 1) // HUFF_BLOCK
+    cap = int((counts * ln.astype(np.uint64)).sum() + 7) // 8 + nb
+    sm = np.zeros(n, np.uint8)
+    stream = np.zeros(max(cap, 1), np.uint8)
+    block_len = np.zeros(nb, np.uint8)
+    group_off = np.zeros((nb + HUFF_GROUP - 1) // HUFF_GROUP + 1, np.uint64)
+    used = ctypes.c_uint64(0)
+    _check("oracle_huff_pack",
+           _load().oracle_huff_pack(_p(w), n, _p(ln), _p(sm), _p(stream), stream.size,
+                                    _p(block_len), _p(group_off), ctypes.byref(used)))
+    return {"n": n, "len": ln.copy(), "sm": sm, "stream": stream[: used.value].copy(),
+            "stream_bytes": int(used.value), "block_len": block_len, "group_off": group_off}
+
+
+def huff_decode(pk: dict) -> np.ndarray:
+    """The packed stream back to bf16 bits, code by code."""
+    n = pk["n"]
+    out = np.zeros(n, np.uint16)
+    stream = pk["stream"] if pk["stream"].size else np.zeros(1, np.uint8)
+    _check("oracle_huff_decode",
+           _load().oracle_huff_decode(n, _p(np.ascontiguousarray(pk["len"], np.uint8)),
+                                      _p(np.ascontiguousarray(pk["sm"], np.uint8)),
+                                      _p(np.ascontiguousarray(stream, np.uint8)),
+                                      pk["stream_bytes"],
+                                      _p(np.ascontiguousarray(pk["block_len"], np.uint8)),
+                                      _p(np.ascontiguousarray(pk["group_off"], np.uint64)),
+                                      _p(out)))
     return out
 
 

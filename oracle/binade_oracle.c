@@ -28,6 +28,7 @@
  *   moe replay, bf16 rounding        -- pinned by tests/test_oracle_*.py
  *   format 1 pack/decode             -- pinned by tests/test_oracle_format1.py
  *   moe silu*up, moe combine         -- pinned by tests/test_oracle_moe_epilogue.py
+ *   huffman lengths/pack/decode      -- pinned by tests/test_oracle_huffman.py
  *   gemm fp64                         -- pinned by tests/test_oracle_gemv.py
  *   matrix-core step, gemm replay     -- pinned by tests/test_oracle_gemm.py
  *                                        (hand-derived cases in
@@ -684,6 +685,176 @@ int oracle_moe_combine(const float *y, const float *weights, int64_t n_tokens,
       out[t * n + j] = acc;
     }
   }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Huffman comparison codec ([P5] "Lossless BF16 weight compression", intro:
+ * only the exponent field is entropy coded, sign and mantissa stay raw; "Best
+ * measured configuration": canonical Huffman, blocks of 64 symbols, 8-bit
+ * per-block lengths turned into offsets by a prefix sum, 128 blocks per
+ * thread block). Readings, where the page gives no layout:
+ *  - symbol = the exponent byte of each bf16 weight (row-major); sm bytes as
+ *    in format 2;
+ *  - code lengths by Huffman's construction: repeatedly merge the two nodes
+ *    of least (count, id), leaves having id = exponent and merged nodes
+ *    256, 257, ... in creation order; a single present exponent gets length
+ *    1; lengths above OR_HUFF_MAXLEN are refused (EUNSUPPORTED), which keeps
+ *    a block's bytes within 8 bits;
+ *  - canonical codes: exponents ordered by (length, exponent) take
+ *    consecutive values, the code growing by a left shift when the length
+ *    grows;
+ *  - each block of OR_HUFF_BLOCK symbols is written MSB-first (bit 7 of a
+ *    byte first) and padded with zero bits to a byte; block_len = its bytes;
+ *    group_off[g] = byte offset of block OR_HUFF_GROUP * g, the last entry
+ *    the total. */
+#define OR_HUFF_BLOCK 64
+#define OR_HUFF_GROUP 128
+#define OR_HUFF_MAXLEN 31
+
+int oracle_huff_lengths(const uint64_t *counts, uint8_t *len) {
+  uint64_t weight[511];
+  int parent[511], alive[511], nodes = 0, i, present = 0;
+  for (i = 0; i < 256; ++i) {
+    len[i] = 0;
+    weight[i] = counts[i];
+    alive[i] = counts[i] > 0;
+    parent[i] = -1;
+    present += alive[i];
+  }
+  if (present == 0) return OR_EINVAL;
+  if (present == 1) {
+    for (i = 0; i < 256; ++i)
+      if (counts[i]) len[i] = 1;
+    return OR_OK;
+  }
+  nodes = 256;
+  for (;;) {
+    int a = -1, b = -1;
+    for (i = 0; i < nodes; ++i) {
+      if (!alive[i]) continue;
+      if (a < 0 || weight[i] < weight[a]) { /* ids increase with i: ties keep the smaller id */
+        b = a;
+        a = i;
+      } else if (b < 0 || weight[i] < weight[b]) {
+        b = i;
+      }
+    }
+    if (b < 0) break; /* one node left: the root */
+    weight[nodes] = weight[a] + weight[b];
+    alive[nodes] = 1;
+    parent[nodes] = -1;
+    alive[a] = alive[b] = 0;
+    parent[a] = parent[b] = nodes;
+    ++nodes;
+  }
+  for (i = 0; i < 256; ++i) {
+    int d = 0, p;
+    if (!counts[i]) continue;
+    for (p = parent[i]; p >= 0; p = parent[p]) ++d;
+    if (d > OR_HUFF_MAXLEN) return OR_EUNSUPPORTED;
+    len[i] = (uint8_t)d;
+  }
+  return OR_OK;
+}
+
+/* canonical code of every exponent from the lengths */
+static void huff_codes(const uint8_t *len, uint32_t *code) {
+  uint32_t c = 0;
+  int prev = 0, l, e;
+  for (l = 1; l <= OR_HUFF_MAXLEN; ++l)
+    for (e = 0; e < 256; ++e) {
+      if (len[e] != l) continue;
+      if (prev) c <<= (l - prev);
+      code[e] = c++;
+      prev = l;
+    }
+}
+
+static void put_bit_msb(uint8_t *bytes, uint64_t p, unsigned bit) {
+  if (bit) bytes[p >> 3] |= (uint8_t)(0x80u >> (p & 7));
+}
+
+static unsigned get_bit_msb(const uint8_t *bytes, uint64_t p) {
+  return (bytes[p >> 3] >> (7 - (p & 7))) & 1u;
+}
+
+int oracle_huff_pack(const uint16_t *w, int64_t n, const uint8_t *len, uint8_t *sm,
+                     uint8_t *stream, int64_t cap, uint8_t *block_len, uint64_t *group_off,
+                     uint64_t *bytes_out) {
+  uint32_t code[256];
+  int64_t i, b, nb;
+  uint64_t pos = 0; /* bit position */
+  if (!w || n <= 0 || !len || !sm || !stream || !block_len || !group_off) return OR_EINVAL;
+  huff_codes(len, code);
+  memset(stream, 0, (size_t)cap);
+  nb = (n + OR_HUFF_BLOCK - 1) / OR_HUFF_BLOCK;
+  for (b = 0; b < nb; ++b) {
+    uint64_t start = pos;
+    if (b % OR_HUFF_GROUP == 0) group_off[b / OR_HUFF_GROUP] = pos >> 3;
+    for (i = b * OR_HUFF_BLOCK; i < n && i < (b + 1) * OR_HUFF_BLOCK; ++i) {
+      unsigned e = exponent_field(w[i]);
+      int l = len[e], j;
+      if (l == 0) return OR_EINVAL;
+      sm[i] = sm_byte(w[i]);
+      if ((int64_t)((pos + l + 7) >> 3) > cap) return OR_ENOSPACE;
+      for (j = l - 1; j >= 0; --j, ++pos) put_bit_msb(stream, pos, (code[e] >> j) & 1u);
+    }
+    pos = (pos + 7) & ~(uint64_t)7; /* pad the block to a byte */
+    block_len[b] = (uint8_t)((pos - start) >> 3);
+  }
+  group_off[(nb + OR_HUFF_GROUP - 1) / OR_HUFF_GROUP] = pos >> 3;
+  if (bytes_out) *bytes_out = pos >> 3;
+  return OR_OK;
+}
+
+/* Decode, code by code (the canonical first-code-per-length walk). Any block
+ * whose bytes or padding disagree with block_len, a group offset that
+ * disagrees with the blocks before it, or a bit string that is no code is
+ * ECORRUPT. */
+int oracle_huff_decode(int64_t n, const uint8_t *len, const uint8_t *sm,
+                       const uint8_t *stream, int64_t stream_bytes, const uint8_t *block_len,
+                       const uint64_t *group_off, uint16_t *out) {
+  uint32_t code[256], first[OR_HUFF_MAXLEN + 2], count[OR_HUFF_MAXLEN + 2];
+  int base[OR_HUFF_MAXLEN + 2], sorted[256], ns = 0, l, e;
+  int64_t i, b, nb;
+  uint64_t pos = 0;
+  if (n <= 0 || !len || !sm || !stream || !block_len || !group_off || !out) return OR_EINVAL;
+  huff_codes(len, code);
+  for (l = 0; l <= OR_HUFF_MAXLEN + 1; ++l) count[l] = 0, first[l] = 0, base[l] = 0;
+  for (l = 1; l <= OR_HUFF_MAXLEN; ++l) {
+    base[l] = ns;
+    for (e = 0; e < 256; ++e)
+      if (len[e] == l) {
+        if (count[l] == 0) first[l] = code[e];
+        sorted[ns++] = e;
+        ++count[l];
+      }
+  }
+  nb = (n + OR_HUFF_BLOCK - 1) / OR_HUFF_BLOCK;
+  for (b = 0; b < nb; ++b) {
+    uint64_t start = pos;
+    if (b % OR_HUFF_GROUP == 0 && group_off[b / OR_HUFF_GROUP] != (pos >> 3)) return OR_ECORRUPT;
+    for (i = b * OR_HUFF_BLOCK; i < n && i < (b + 1) * OR_HUFF_BLOCK; ++i) {
+      uint32_t c = 0;
+      int sym = -1;
+      for (l = 1; l <= OR_HUFF_MAXLEN; ++l) {
+        if ((int64_t)(pos >> 3) >= stream_bytes) return OR_ECORRUPT;
+        c = (c << 1) | get_bit_msb(stream, pos++);
+        if (count[l] && c >= first[l] && c - first[l] < count[l]) {
+          sym = sorted[base[l] + (int)(c - first[l])];
+          break;
+        }
+      }
+      if (sym < 0) return OR_ECORRUPT;
+      out[i] = bf16_from_parts(sm[i], (unsigned)sym);
+    }
+    pos = (pos + 7) & ~(uint64_t)7;
+    if (block_len[b] != (pos - start) >> 3) return OR_ECORRUPT;
+  }
+  if (group_off[(nb + OR_HUFF_GROUP - 1) / OR_HUFF_GROUP] != (pos >> 3) ||
+      (int64_t)(pos >> 3) != stream_bytes)
+    return OR_ECORRUPT;
   return OR_OK;
 }
 
