@@ -508,6 +508,44 @@ def measure_configs(dev, stream) -> dict:
             "bytes_per_launch": f1_decode_bytes(dp)}
         del copies, outs, ref, dp, w, f1
         torch.cuda.empty_cache()
+    # ---- the Huffman comparison decoder on the 64M-symbol tensor (the pages'
+    # own timing workload: an embedding-like 64M-symbol sample)
+    sp = synth.embedding_64m()
+    w = synth.normal_bf16(sp)
+    hp = B.pack_huff(w)
+    hd = hp.to(dev)
+    n_copy = max(2, -(-ROTATE_BYTES // (hp.n * 3)))
+    copies = [hd] + [B.HuffPlanes(hd.n, hd.len, hd.sm.clone(), hd.stream.clone(), hd.stream_bytes,
+                                  hd.block_len.clone(), hd.group_off.clone())
+                     for _ in range(n_copy - 1)]
+    hws = torch.empty(int(B.lib().binade_huff_workspace_bytes()), dtype=torch.uint8, device=dev)
+    houts = [torch.empty(hp.n, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    hstatus = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def huff_rot():
+        for i, c_ in enumerate(copies):
+            B.huff_decode(c_, out=houts[i & 1], status=hstatus, workspace=hws, stream=stream)
+
+    v = spread(graph_replays_ms(stream, huff_rot))
+    torch.cuda.synchronize()
+    if int(hstatus.item()) != 0 or not torch.equal(houts[0].cpu().view(torch.int16),
+                                                   w.reshape(-1).view(torch.int16)):
+        raise SystemExit("parity gate: Huffman decode differs from the weights")
+    t = v["median"] / n_copy
+    hbytes = hp.stream_bytes + hp.block_len.numel() + 8 * hp.group_off.numel() + hp.n + 2 * hp.n
+    gb = hbytes / (t * 1e-3) / 1e9
+    out["huffman_decode_262144x256"] = {
+        "symbols": hp.n, "huffman_bits_per_weight": round(hp.bits_per_weight(), 4),
+        "us_per_launch": round(t * 1e3, 2),
+        "us_spread": {k: round(x_ / n_copy * 1e3, 2) for k, x_ in v.items()},
+        "gsym_per_s": round(hp.n / (t * 1e-3) / 1e9, 1), "GBs": round(gb, 1),
+        "frac_of_hbm_peak": round(gb / HBM_PEAK_GBS, 4), "bytes_per_launch": hbytes,
+        "copies": n_copy,
+        "pages_context_ms": {"A100": 0.47, "RTX 4090": 0.19},
+        "note": "bytes: stream + 8-bit block lengths + group offsets + sm read, bf16 written "
+                "(the comparison decoder outputs whole bf16 weights; Rice->R4 writes 4-bit ranks)"}
+    del copies, hd, houts, w, hp
+    torch.cuda.empty_cache()
     # ---- the table and the format 2 pack on the device
     for sp in [synth.gemma_12b_ffn()[0], synth.embedding_64m()]:
         w = synth.normal_bf16(sp, device=dev)

@@ -33,7 +33,9 @@ EXPORTS = ["binade_status_str", "binade_last_hip_error", "binade_build_table",
            "binade_r4_gemm_noalloc", "binade_gemm_scratch_bytes",
            "binade_r4_moe_gemv", "binade_bf16_moe_gemv", "binade_r4_gemv_rows",
            "binade_bf16_gemv_rows", "binade_moe_silu_mul", "binade_moe_combine",
-           "binade_build_table_gpu", "binade_pack_gpu_workspace_bytes", "binade_pack_rice_gpu"]
+           "binade_build_table_gpu", "binade_pack_gpu_workspace_bytes", "binade_pack_rice_gpu",
+           "binade_huff_lengths", "binade_huff_pack", "binade_huff_workspace_bytes",
+           "binade_huff_decode"]
 
 
 class Table(ctypes.Structure):
@@ -41,6 +43,13 @@ class Table(ctypes.Structure):
                 ("exp_of_rank", ctypes.c_uint8 * 256),
                 ("rank_of_exp", ctypes.c_uint16 * 256),
                 ("count_of_rank", ctypes.c_uint64 * 256)]
+
+
+class HuffDesc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("len", ctypes.c_uint8 * 256),
+                ("sm", ctypes.c_void_p), ("stream", ctypes.c_void_p),
+                ("stream_bytes", ctypes.c_uint64), ("stream_cap", ctypes.c_uint64),
+                ("block_len", ctypes.c_void_p), ("group_off", ctypes.c_void_p)]
 
 
 class Sizes(ctypes.Structure):
@@ -120,6 +129,8 @@ def lib() -> ctypes.CDLL:
             L.binade_gemm_scratch_bytes.restype = I64
             L.binade_pack_gpu_workspace_bytes.argtypes = [I64, I64]
             L.binade_pack_gpu_workspace_bytes.restype = I64
+            L.binade_huff_workspace_bytes.argtypes = []
+            L.binade_huff_workspace_bytes.restype = I64
             sig = {
                 "binade_build_table": [P, I64, P],
                 "binade_sizes_of": [P, I64, I64, P],
@@ -139,6 +150,9 @@ def lib() -> ctypes.CDLL:
                 "binade_moe_silu_mul": [P, P, I64, P, I32, P],
                 "binade_moe_combine": [P, P, I64, I32, I64, P, I32, P],
                 "binade_build_table_gpu": [P, I64, P, P, P],
+                "binade_huff_lengths": [P, I64, P, P],
+                "binade_huff_pack": [P, P],
+                "binade_huff_decode": [P, P, P, P, P],
                 "binade_pack_rice_gpu": [P, I64, I64, P, P, P, P, P],
                 "binade_r4_gemm": [P, P, I64, I64, P, I64, I32, P, I64, P],
                 "binade_r4_gemm_noalloc": [P, P, I64, I64, P, I64, I32, P],
@@ -342,6 +356,74 @@ def pack_rice_gpu(w: torch.Tensor, table: Table | None = None, status: torch.Ten
     planes.unary_bits = int(d.unary_bits)
     planes.n_esc = int(d.n_esc)
     return planes
+
+
+@dataclass
+class HuffPlanes:
+    """Huffman comparison-codec planes (host or device tensors)."""
+    n: int
+    len: bytes
+    sm: torch.Tensor
+    stream: torch.Tensor
+    stream_bytes: int
+    block_len: torch.Tensor
+    group_off: torch.Tensor
+
+    def desc(self) -> HuffDesc:
+        d = HuffDesc()
+        d.n = self.n
+        ctypes.memmove(d.len, self.len, 256)
+        d.sm = self.sm.data_ptr()
+        d.stream = self.stream.data_ptr()
+        d.stream_bytes = self.stream_bytes
+        d.stream_cap = self.stream.numel()
+        d.block_len = self.block_len.data_ptr()
+        d.group_off = self.group_off.data_ptr()
+        return d
+
+    def to(self, device) -> "HuffPlanes":
+        return HuffPlanes(self.n, self.len, self.sm.to(device), self.stream.to(device),
+                          self.stream_bytes, self.block_len.to(device), self.group_off.to(device))
+
+    def bits_per_weight(self) -> float:
+        return (8 * self.n + 8 * self.stream_bytes + 8 * self.block_len.numel()
+                + 64 * self.group_off.numel()) / self.n
+
+
+def pack_huff(w: torch.Tensor) -> HuffPlanes:
+    """binade_huff_lengths + binade_huff_pack on a host bf16 tensor."""
+    w = _bits16(w).reshape(-1)
+    if w.is_cuda:
+        raise ValueError("pack_huff takes a host tensor")
+    n = w.numel()
+    ln = (ctypes.c_uint8 * 256)()
+    cap = ctypes.c_uint64(0)
+    _call("binade_huff_lengths", _ptr(w), n, ln, ctypes.byref(cap))
+    nb = (n + 63) // 64
+    planes = HuffPlanes(n, bytes(ln), torch.empty(n, dtype=torch.uint8),
+                        torch.empty(int(cap.value), dtype=torch.uint8), 0,
+                        torch.empty(nb, dtype=torch.uint8),
+                        torch.empty((nb + 127) // 128 + 1, dtype=torch.int64))
+    d = planes.desc()
+    _call("binade_huff_pack", _ptr(w), ctypes.byref(d))
+    planes.stream_bytes = int(d.stream_bytes)
+    return planes
+
+
+@_on_stream
+def huff_decode(p: HuffPlanes, out: torch.Tensor | None = None, status: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """binade_huff_decode: device planes -> bf16[n]."""
+    dev = p.sm.device
+    if out is None:
+        out = torch.empty(p.n, dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = torch.empty(int(lib().binade_huff_workspace_bytes()), dtype=torch.uint8,
+                                device=dev)
+    d = p.desc()
+    _call("binade_huff_decode", ctypes.byref(d), _ptr(out), _ptr(workspace), _ptr(status),
+          _stream(stream))
+    return out
 
 
 @dataclass

@@ -22,7 +22,7 @@ ARCH = "gfx950"
 
 SOURCES = ["host_pack.cpp", "runtime.cpp", "gemv.hip", "rice_to_r4.hip",
            "f1_to_r4.hip", "gemm.hip", "moe.hip", "moe_epilogue.hip",
-           "pack_gpu.hip"]
+           "pack_gpu.hip", "huff_decode.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",

@@ -13,6 +13,9 @@
 #include <array>
 #include <cstring>
 #include <numeric>
+#include <queue>
+#include <utility>
+#include <vector>
 
 #include "binade.h"
 #include "binade_internal.h"
@@ -309,6 +312,125 @@ extern "C" int32_t binade_pack_f1(const uint16_t* w, int64_t rows, int64_t cols,
   out->code_bits = codes.position();
   out->n_f1esc = n_f1;
   out->n_esc = n_r4;
+  return BINADE_OK;
+}
+
+// ---------------------------------------------------------------- Huffman
+// "Lossless BF16 weight compression" page, intro and "Best measured
+// configuration": the comparison codec. The layout is the one binade.h
+// states for binade_huff.
+
+namespace {
+
+constexpr int kHuffMaxLen = 31;
+
+// Code lengths by Huffman's construction: a min-heap of (weight, id), the
+// two lightest merged into node 256 + m at merge m.
+int32_t huff_lengths(const std::array<uint64_t, 256>& counts, uint8_t* len) {
+  using Node = std::pair<uint64_t, int>;
+  std::priority_queue<Node, std::vector<Node>, std::greater<Node>> heap;
+  std::array<int, 511> parent;
+  parent.fill(-1);
+  int present = 0;
+  for (int e = 0; e < 256; ++e) {
+    len[e] = 0;
+    if (counts[e]) {
+      heap.push({counts[e], e});
+      ++present;
+    }
+  }
+  if (present == 0) return BINADE_EINVAL;
+  if (present == 1) {
+    len[heap.top().second] = 1;
+    return BINADE_OK;
+  }
+  int next = 256;
+  while (heap.size() > 1) {
+    const Node a = heap.top();
+    heap.pop();
+    const Node b = heap.top();
+    heap.pop();
+    parent[a.second] = parent[b.second] = next;
+    heap.push({a.first + b.first, next++});
+  }
+  for (int e = 0; e < 256; ++e) {
+    if (!counts[e]) continue;
+    int d = 0;
+    for (int p = parent[e]; p >= 0; p = parent[p]) ++d;
+    if (d > kHuffMaxLen) return BINADE_EUNSUPPORTED;
+    len[e] = static_cast<uint8_t>(d);
+  }
+  return BINADE_OK;
+}
+
+// Canonical codes: exponents in (length, exponent) order take consecutive
+// values; a longer length shifts the running value left.
+std::array<uint32_t, 256> huff_codes(const uint8_t* len) {
+  std::array<uint32_t, 256> code{};
+  std::vector<std::pair<int, int>> order;   // (length, exponent)
+  for (int e = 0; e < 256; ++e)
+    if (len[e]) order.push_back({len[e], e});
+  std::sort(order.begin(), order.end());
+  uint32_t c = 0;
+  int prev = 0;
+  for (const auto& le : order) {
+    if (prev) c <<= (le.first - prev);
+    code[le.second] = c++;
+    prev = le.first;
+  }
+  return code;
+}
+
+std::array<uint64_t, 256> exponent_counts(const uint16_t* w, int64_t n) {
+  std::array<uint64_t, 256> c{};
+  for (int64_t i = 0; i < n; ++i) ++c[exponent_of(w[i])];
+  return c;
+}
+
+}  // namespace
+
+extern "C" int32_t binade_huff_lengths(const uint16_t* w, int64_t n, uint8_t* len,
+                                       uint64_t* stream_cap) {
+  if (w == nullptr || n <= 0 || len == nullptr) return BINADE_EINVAL;
+  const auto counts = exponent_counts(w, n);
+  const int32_t s = huff_lengths(counts, len);
+  if (s != BINADE_OK) return s;
+  if (stream_cap != nullptr) {
+    uint64_t bits = 0;
+    for (int e = 0; e < 256; ++e) bits += counts[e] * len[e];
+    const uint64_t blocks = (static_cast<uint64_t>(n) + BINADE_HUFF_BLOCK - 1) / BINADE_HUFF_BLOCK;
+    *stream_cap = (bits + 7) / 8 + blocks + 8;
+  }
+  return BINADE_OK;
+}
+
+extern "C" int32_t binade_huff_pack(const uint16_t* w, binade_huff* out) {
+  if (w == nullptr || out == nullptr || out->n <= 0 || out->sm == nullptr ||
+      out->stream == nullptr || out->block_len == nullptr || out->group_off == nullptr)
+    return BINADE_EINVAL;
+  const int64_t n = out->n;
+  const auto code = huff_codes(out->len);
+  std::memset(out->stream, 0, out->stream_cap);
+  uint64_t pos = 0;   // bit position, MSB-first within bytes
+  const int64_t blocks = (n + BINADE_HUFF_BLOCK - 1) / BINADE_HUFF_BLOCK;
+  for (int64_t b = 0; b < blocks; ++b) {
+    const uint64_t start = pos;
+    if (b % BINADE_HUFF_GROUP == 0) out->group_off[b / BINADE_HUFF_GROUP] = pos >> 3;
+    const int64_t i1 = std::min<int64_t>(n, (b + 1) * BINADE_HUFF_BLOCK);
+    for (int64_t i = b * BINADE_HUFF_BLOCK; i < i1; ++i) {
+      const uint32_t e = exponent_of(w[i]);
+      const int l = out->len[e];
+      if (l == 0 || l > kHuffMaxLen) return BINADE_EINVAL;
+      out->sm[i] = static_cast<uint8_t>(((w[i] >> 8) & 0x80u) | (w[i] & 0x7Fu));
+      if ((pos + l + 7) / 8 > out->stream_cap) return BINADE_ENOSPACE;
+      for (int j = l - 1; j >= 0; --j, ++pos)
+        if ((code[e] >> j) & 1u) out->stream[pos >> 3] |= static_cast<uint8_t>(0x80u >> (pos & 7));
+    }
+    pos = (pos + 7) & ~7ull;
+    out->block_len[b] = static_cast<uint8_t>((pos - start) >> 3);
+  }
+  out->group_off[(blocks + BINADE_HUFF_GROUP - 1) / BINADE_HUFF_GROUP] = pos >> 3;
+  out->stream_bytes = pos >> 3;
   return BINADE_OK;
 }
 

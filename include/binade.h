@@ -185,6 +185,38 @@ typedef struct binade_f1_sizes {
   uint64_t esc_cap;       /* rows * cols */
 } binade_f1_sizes;
 
+/* Huffman comparison codec ("Lossless BF16 weight compression" page, intro
+ * and "Best measured configuration": the exponent field in canonical Huffman
+ * codes, blocks of 64 symbols whose 8-bit byte lengths a prefix sum turns
+ * into offsets, sign and mantissa raw). Layout (this library's reading): the
+ * symbol is each weight's exponent byte, row-major; code lengths from
+ * Huffman's construction (merge the two nodes of least (count, id), leaves
+ * id = exponent, merged nodes 256, 257, ... in order; one present exponent
+ * gets length 1; lengths <= 31); canonical codes in (length, exponent)
+ * order; each block of BINADE_HUFF_BLOCK symbols MSB-first, padded to a
+ * byte.
+ *   sm         u8[n]                 as in format 2
+ *   stream     u8[stream_cap]        the blocks' codes (stream 4-byte
+ *                                    aligned for the decoder, stream_cap >=
+ *                                    stream_bytes + 8)
+ *   block_len  u8[ceil(n/64)]        bytes of each block
+ *   group_off  u64[ceil(n/8192)+1]   byte offset of every 128th block; the
+ *                                    last entry = stream_bytes
+ * Pointers are host memory for binade_huff_pack, device memory for
+ * binade_huff_decode. */
+#define BINADE_HUFF_BLOCK 64
+#define BINADE_HUFF_GROUP 128
+typedef struct binade_huff {
+  int64_t n;
+  uint8_t len[256];
+  uint8_t *sm;
+  uint8_t *stream;
+  uint64_t stream_bytes;
+  uint64_t stream_cap;
+  uint8_t *block_len;
+  uint64_t *group_off;
+} binade_huff;
+
 /* Text for a status code (static storage). */
 const char *binade_status_str(int32_t status);
 /* The last HIP error code seen by a device call on this thread (0 if none). */
@@ -227,6 +259,18 @@ int32_t binade_f1_sizes_of(int64_t rows, int64_t cols, binade_f1_sizes *out);
  * exponent is not in t. ENOSPACE: a capacity is too small. */
 int32_t binade_pack_f1(const uint16_t *w, int64_t rows, int64_t cols,
                        const binade_table *t, binade_f1 *out);
+
+/* Huffman code lengths of the exponents of w[n] (host) and the stream
+ * capacity a pack needs (its code bytes plus one byte per block and 8 bytes
+ * of look-ahead). EUNSUPPORTED: a code longer than 31 bits. */
+int32_t binade_huff_lengths(const uint16_t *w, int64_t n, uint8_t len[256],
+                            uint64_t *stream_cap);
+
+/* Huffman pack of w[out->n] (host) with the lengths in out->len; fills
+ * sm, stream (zero padded to stream_cap), block_len, group_off and
+ * stream_bytes; byte-identical to the oracle's pack. EINVAL: an exponent
+ * with no code, bad pointers. ENOSPACE: stream_cap too small. */
+int32_t binade_huff_pack(const uint16_t *w, binade_huff *out);
 
 /* -------------------------------------------------------------- device */
 
@@ -291,6 +335,23 @@ int32_t binade_rice_to_r4_batch(const binade_rice *in, binade_r4 *out,
  * planes. The R4 result equals binade_rice_to_r4's on the same weights. */
 int32_t binade_f1_to_r4(const binade_f1 *in, binade_r4 *out,
                         uint32_t *dev_status, void *stream);
+
+/* Workspace bytes binade_huff_decode needs (its decode tables). */
+int64_t binade_huff_workspace_bytes(void);
+
+/* Huffman stream -> bf16 weights on the GPU: the comparison decoder of the
+ * "Lossless BF16 weight compression" page ("Best measured configuration":
+ * one thread per block of 64 symbols, offsets from a prefix sum over the
+ * 8-bit block lengths of 128 blocks, a lookup table for the codes). in:
+ * device planes as binade_huff_pack leaves them. out: device bf16[n],
+ * 16-byte aligned. workspace: device, binade_huff_workspace_bytes(), 16-byte
+ * aligned (rebuilt by each call; calls overlapping on different streams need
+ * their own). dev_status: BINADE_DEV_CORRUPT_STREAM when a block's codes,
+ * padding or a group offset disagree with the index (outputs then
+ * unspecified). */
+int32_t binade_huff_decode(const binade_huff *in, uint16_t *out,
+                           void *workspace, uint32_t *dev_status,
+                           void *stream);
 
 /* R4 -> bf16 bits [rows, cols] on the GPU (the rebuild path; "Binade"
  * package page, "Use": unpack restores the original BF16 bit for bit). */

@@ -203,3 +203,47 @@ def test_format1_pack_matches_oracle_bytes(case):
     assert np.array_equal(p.anchor.numpy().view(np.uint64), po["anchor"])
     assert np.array_equal(p.f1_pre.numpy().view(np.uint32), po["f1_pre"])
     assert np.array_equal(p.esc_pre.numpy().view(np.uint32), po["esc_pre"])
+
+
+@pytest.mark.parametrize("case", ["llm", "all_patterns", "one_exponent", "ties", "groups"])
+def test_huffman_pack_matches_oracle_bytes(case):
+    """binade_huff_lengths / binade_huff_pack (host C++) against the oracle's
+    Huffman codec: the same lengths (tie rule included) and the same bytes."""
+    rng = np.random.default_rng(31)
+    if case == "llm":
+        wn = _np(_tensor(40, 3072, sigma=0.02, seed=6, frac=1e-3, scale=20.0))
+    elif case == "all_patterns":
+        wn = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).reshape(256, 256)
+    elif case == "one_exponent":
+        wn = ((rng.integers(0, 2, (7, 100)) << 15) | (125 << 7) | rng.integers(0, 128, (7, 100))).astype(np.uint16)
+    elif case == "ties":   # many equal counts: the merge order decides the lengths
+        e = np.repeat(np.arange(100, 124), 37)
+        rng.shuffle(e)
+        wn = ((e << 7) | rng.integers(0, 128, e.size)).astype(np.uint16).reshape(1, -1)
+    else:   # several groups of 128 blocks and a ragged block
+        wn = _np(_tensor(3, 9000, sigma=0.015, seed=7, frac=0.0, scale=1.0))
+    w = torch.from_numpy(np.ascontiguousarray(wn).view(np.int16)).view(torch.bfloat16)
+    p = B.pack_huff(w)
+    ln = oracle.huff_lengths(oracle.exponent_counts(wn))
+    assert bytes(p.len) == ln.tobytes()
+    po = oracle.huff_pack(wn, ln)
+    assert p.stream_bytes == po["stream_bytes"]
+    assert np.array_equal(p.sm.numpy(), po["sm"])
+    s = p.stream.numpy()
+    assert np.array_equal(s[: p.stream_bytes], po["stream"]) and not s[p.stream_bytes:].any()
+    assert s.size >= p.stream_bytes + 8
+    assert np.array_equal(p.block_len.numpy(), po["block_len"])
+    assert np.array_equal(p.group_off.numpy().view(np.uint64), po["group_off"])
+
+
+def test_huffman_deep_tree_refused():
+    # Fibonacci counts over 34 exponents make a chain: depth 33 > 31
+    f = [1, 1]
+    while len(f) < 34:
+        f.append(f[-1] + f[-2])
+    e = np.concatenate([np.full(c, i, np.uint16) for i, c in enumerate(f)])
+    wn = (e << 7).astype(np.uint16)
+    ln = (ctypes.c_uint8 * 256)()
+    cap = ctypes.c_uint64(0)
+    rc = B.lib().binade_huff_lengths(ctypes.c_void_p(wn.ctypes.data), wn.size, ln, ctypes.byref(cap))
+    assert rc == B.EUNSUPPORTED
