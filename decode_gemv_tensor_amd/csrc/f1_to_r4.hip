@@ -225,95 +225,112 @@ __device__ __forceinline__ void decode_checked(const uint32_t* g, uint32_t w, ui
   }
 }
 
-__global__ __launch_bounds__(64 * kF1Waves) void f1_to_r4_kernel(F1Args args) {
-  __shared__ __align__(16) uint32_t code_lds[kF1Waves][kCodeWords];
-  __shared__ __align__(16) uint32_t esc_lds[kF1Waves][kEscStage / 4];
-  __shared__ __align__(16) uint32_t nib_lds[kF1Waves][64 * 4];
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const char* kp = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
-  const F1Args& a = *(const F1Args*)kp;
-  const uint8_t* exp_of_rank = (const uint8_t*)kp + offsetof(F1Args, exp_of_rank);
-  const uint32_t j = blockIdx.x * kF1Waves + wave;
-  if (j >= static_cast<uint64_t>(a.jobs)) return;
-  uint32_t* words = code_lds[wave];
-  const uint8_t* escs = reinterpret_cast<const uint8_t*>(esc_lds[wave]);
-  const uint32_t T = a.tiles_per_row, C = a.chunks_per_row, n = a.n;
-  const uint32_t cols = static_cast<uint32_t>(a.cols);
+// One job's geometry, index entries and loads (issued, not yet waited for).
+struct F1Job {
+  uint64_t c0, fb, A, Bend;
+  uint32_t cnt, len, f0, f1end, e0, e1end, nw, n_escj;
+  bool bad, bad_esc, live, row_start;
+  __amdgpu_buffer_rsrc_t re;
+  u32x4 v0, v1;
+  uint32_t ev, w, row_local, col;
+  uint64_t row_anchor;
+  uint32_t row_f1, row_esc;
+};
 
+__device__ __forceinline__ void f1_load(const F1Args& a, uint32_t j, uint32_t lane, F1Job& J) {
+  const uint32_t T = a.tiles_per_row, C = a.chunks_per_row;
+  const uint32_t cols = static_cast<uint32_t>(a.cols);
   // ---- the job: chunks [c0, c0 + cnt), weights [fb, fb + len), tiles from t0
-  uint64_t c0, fb, t0;
-  uint32_t cnt, len, ntiles, q = 0;
+  uint64_t t0;
+  uint32_t ntiles;
   if (C > 1) {
     uint32_t row = __umulhi(j, a.chunk_recip);
     if (row * C > j) --row;
-    q = j - row * C;
-    c0 = j;
-    cnt = 1;
-    fb = static_cast<uint64_t>(row) * cols + q * kChunk;
-    len = min(static_cast<uint32_t>(kChunk), cols - q * kChunk);
+    const uint32_t q = j - row * C;
+    J.c0 = j;
+    J.cnt = 1;
+    J.fb = static_cast<uint64_t>(row) * cols + q * kChunk;
+    J.len = min(static_cast<uint32_t>(kChunk), cols - q * kChunk);
     t0 = static_cast<uint64_t>(row) * T + q * (kChunk / kF1Tile);
-    ntiles = (len + kF1Tile - 1) / kF1Tile;
+    ntiles = (J.len + kF1Tile - 1) / kF1Tile;
   } else {
     const uint64_t row0 = static_cast<uint64_t>(j) * a.job_rows;
-    cnt = static_cast<uint32_t>(min(static_cast<uint64_t>(a.job_rows), static_cast<uint64_t>(a.rows) - row0));
-    c0 = row0;
-    fb = row0 * cols;
-    len = cnt * cols;
+    J.cnt = static_cast<uint32_t>(min(static_cast<uint64_t>(a.job_rows), static_cast<uint64_t>(a.rows) - row0));
+    J.c0 = row0;
+    J.fb = row0 * cols;
+    J.len = J.cnt * cols;
     t0 = row0 * T;
-    ntiles = cnt * T;
+    ntiles = J.cnt * T;
   }
-  const uint64_t A = a.anchor[c0], Bend = a.anchor[c0 + cnt];
-  const uint32_t f0 = a.f1_pre[c0], f1end = a.f1_pre[c0 + cnt];
-  const uint32_t e0 = a.esc_pre[c0], e1end = a.esc_pre[c0 + cnt];
+  J.A = a.anchor[J.c0];
+  J.Bend = a.anchor[J.c0 + J.cnt];
+  J.f0 = a.f1_pre[J.c0];
+  J.f1end = a.f1_pre[J.c0 + J.cnt];
+  J.e0 = a.esc_pre[J.c0];
+  J.e1end = a.esc_pre[J.c0 + J.cnt];
   const bool first = j == 0, last = j + 1 == static_cast<uint64_t>(a.jobs);
   // codes start on a word, at most 8 bits per weight, inside the buffer;
   // escapes inside the list; the first job starts at zero, the last ends at
   // the totals
-  bool bad = (A & 31u) != 0 || Bend < A || Bend - A > 8ull * len || Bend > a.code_bits ||
-             (a.code_bits + 31) / 32 > a.code_words || f1end < f0 || f1end > a.n_f1esc ||
-             (first && (A != 0 || f0 != 0)) || (last && (Bend != a.code_bits || f1end != a.n_f1esc));
-  bool bad_esc = e1end < e0 || e1end > a.n_esc || (first && e0 != 0) || (last && e1end != a.n_esc);
+  J.bad = (J.A & 31u) != 0 || J.Bend < J.A || J.Bend - J.A > 8ull * J.len || J.Bend > a.code_bits ||
+          (a.code_bits + 31) / 32 > a.code_words || J.f1end < J.f0 || J.f1end > a.n_f1esc ||
+          (first && (J.A != 0 || J.f0 != 0)) ||
+          (last && (J.Bend != a.code_bits || J.f1end != a.n_f1esc));
+  J.bad_esc = J.e1end < J.e0 || J.e1end > a.n_esc || (first && J.e0 != 0) ||
+              (last && J.e1end != a.n_esc);
 
   // ---- 0. loads
-  const uint32_t nw = bad ? 0u : static_cast<uint32_t>((Bend - A) >> 5);   // <= 512
-  const __amdgpu_buffer_rsrc_t rc = span(a.codes + (A >> 5), 4u * nw);
-  const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rc, 16u * lane, 0, 0);
-  u32x4 v1 = {0u, 0u, 0u, 0u};
-  if (nw > 256u) v1 = __builtin_amdgcn_raw_buffer_load_b128(rc, 1024u + 16u * lane, 0, 0);
-  const uint32_t n_escj = bad ? 0u : f1end - f0;
-  const __amdgpu_buffer_rsrc_t re = span(a.esc_rank + f0, n_escj);
-  const uint32_t ev = load_u8(re, 4u * lane) | (load_u8(re, 4u * lane + 1u) << 8) |
-                      (load_u8(re, 4u * lane + 2u) << 16) | (load_u8(re, 4u * lane + 3u) << 24);
+  J.nw = J.bad ? 0u : static_cast<uint32_t>((J.Bend - J.A) >> 5);   // <= 512
+  const __amdgpu_buffer_rsrc_t rc = span(a.codes + (J.A >> 5), 4u * J.nw);
+  J.v0 = __builtin_amdgcn_raw_buffer_load_b128(rc, 16u * lane, 0, 0);
+  J.v1 = u32x4{0u, 0u, 0u, 0u};
+  if (J.nw > 256u) J.v1 = __builtin_amdgcn_raw_buffer_load_b128(rc, 1024u + 16u * lane, 0, 0);
+  J.n_escj = J.bad ? 0u : J.f1end - J.f0;
+  J.re = span(a.esc_rank + J.f0, J.n_escj);
+  J.ev = load_u8(J.re, 4u * lane) | (load_u8(J.re, 4u * lane + 1u) << 8) |
+         (load_u8(J.re, 4u * lane + 2u) << 16) | (load_u8(J.re, 4u * lane + 3u) << 24);
   const uint32_t o = 32u * lane;   // the lane's first weight in the job
-  const bool live = o < len;
-  uint32_t row_local = 0, col = o, tile = lane >> 2;
+  J.live = o < J.len;
+  J.row_local = 0;
+  J.col = o;
+  uint32_t tile = lane >> 2;
   if (C == 1) {
-    row_local = __umulhi(o, a.col_recip);
-    col = o - row_local * cols;
-    tile = row_local * T + (col >> 7);
+    J.row_local = __umulhi(o, a.col_recip);
+    J.col = o - J.row_local * cols;
+    tile = J.row_local * T + (J.col >> 7);
   }
-  uint32_t w = load_u8(span(a.width + t0, bad ? 0u : ntiles), tile);
-  if (!live) w = 0;
+  J.w = load_u8(span(a.width + t0, J.bad ? 0u : ntiles), tile);
+  if (!J.live) J.w = 0;
   // rows that start inside the job (short rows): their index entries
-  uint64_t row_anchor = 0;
-  uint32_t row_f1 = 0, row_esc = 0;
-  const bool row_start = C == 1 && live && lane > 0 && col == 0;
+  J.row_anchor = 0;
+  J.row_f1 = 0;
+  J.row_esc = 0;
+  J.row_start = C == 1 && J.live && lane > 0 && J.col == 0;
   if (C == 1) {
-    const uint64_t r = c0 + min(row_local, cnt - 1u);
-    row_anchor = a.anchor[r];
-    row_f1 = a.f1_pre[r];
-    row_esc = a.esc_pre[r];
+    const uint64_t r = J.c0 + min(J.row_local, J.cnt - 1u);
+    J.row_anchor = a.anchor[r];
+    J.row_f1 = a.f1_pre[r];
+    J.row_esc = a.esc_pre[r];
   }
-  *reinterpret_cast<u32x4*>(words + 4u * lane) = v0;
-  if (nw > 256u) *reinterpret_cast<u32x4*>(words + 256u + 4u * lane) = v1;
-  esc_lds[wave][lane] = ev;
+}
+
+// Decode a loaded job and write its nibbles and side-list entries.
+__device__ __forceinline__ void f1_finish(const F1Args& a, const uint8_t* exp_of_rank, F1Job& J,
+                                          uint32_t lane, uint32_t* words, uint32_t* esc_words,
+                                          uint32_t* nib_words) {
+  const uint32_t C = a.chunks_per_row, n = a.n;
+  const uint8_t* escs = reinterpret_cast<const uint8_t*>(esc_words);
+  wave_sync_lds();   // the previous job of this wave is done with the LDS
+  *reinterpret_cast<u32x4*>(words + 4u * lane) = J.v0;
+  if (J.nw > 256u) *reinterpret_cast<u32x4*>(words + 256u + 4u * lane) = J.v1;
+  esc_words[lane] = J.ev;
 
   // ---- 1. the lane's first word
+  const uint32_t w = J.w;
   const uint32_t w_incl = f1_scan(w);
   const uint32_t lw = w_incl - w;
-  bad = bad || w > 8u || (static_cast<uint64_t>(f1_lane63(w_incl)) << 5) != Bend - A;
-  if (row_start) bad = bad || row_anchor != A + (static_cast<uint64_t>(lw) << 5);
+  bool bad = J.bad || w > 8u || (static_cast<uint64_t>(f1_lane63(w_incl)) << 5) != J.Bend - J.A;
+  if (J.row_start) bad = bad || J.row_anchor != J.A + (static_cast<uint64_t>(lw) << 5);
   if (__any(bad)) {
     f1_flag(a.status, BINADE_DEV_CORRUPT_STREAM, lane);
     return;
@@ -334,28 +351,28 @@ __global__ __launch_bounds__(64 * kF1Waves) void f1_to_r4_kernel(F1Args args) {
     decode_w4(g, out, esc);
   else if (w != 0u)
     decode_checked(g, w, n, out, esc, big, bad);
-  uint32_t* nb = nib_lds[wave] + 4u * lane;
+  uint32_t* nb = nib_words + 4u * lane;
   *reinterpret_cast<u32x4*>(nb) = u32x4{out[0], out[1], out[2], out[3]};
 
   // ---- 3. escapes: place in the escape bytes, patch the nibbles
   const uint32_t ne = __popc(esc);
   const uint32_t e_incl = f1_scan(ne);
   const uint32_t e_before = e_incl - ne;
-  bad = bad || f1_lane63(e_incl) != n_escj;
-  if (row_start) bad = bad || row_f1 != f0 + e_before;
+  bad = bad || f1_lane63(e_incl) != J.n_escj;
+  if (J.row_start) bad = bad || J.row_f1 != J.f0 + e_before;
   if (__any(bad)) {
     f1_flag(a.status, BINADE_DEV_CORRUPT_STREAM, lane);
     return;
   }
   const uint32_t esc_code = (1u << w) - 1u, esc_nib = min(esc_code, 15u);
-  const bool staged = n_escj <= static_cast<uint32_t>(kEscStage);
+  const bool staged = J.n_escj <= static_cast<uint32_t>(kEscStage);
   uint32_t side = big;   // weights whose rank is >= 15, in weight order
   {
     uint32_t m = esc, k = e_before;
     while (m) {
       const uint32_t i = __builtin_ctz(m);
       m &= m - 1u;
-      const uint32_t rank = staged ? static_cast<uint32_t>(escs[k]) : load_u8(re, k);
+      const uint32_t rank = staged ? static_cast<uint32_t>(escs[k]) : load_u8(J.re, k);
       ++k;
       bad = bad || rank < esc_code || rank >= n;
       side |= (rank >= 15u ? 1u : 0u) << i;
@@ -371,20 +388,20 @@ __global__ __launch_bounds__(64 * kF1Waves) void f1_to_r4_kernel(F1Args args) {
   const uint32_t nr = __popc(side);
   const uint32_t r_incl = f1_scan(nr);
   const uint32_t r_before = r_incl - nr;
-  bad_esc = bad_esc || e1end - e0 != f1_lane63(r_incl);
-  if (row_start) bad_esc = bad_esc || row_esc != e0 + r_before;
+  bool bad_esc = J.bad_esc || J.e1end - J.e0 != f1_lane63(r_incl);
+  if (J.row_start) bad_esc = bad_esc || J.row_esc != J.e0 + r_before;
   if (__any(bad_esc)) {
     f1_flag(a.status, BINADE_DEV_CORRUPT_ESC, lane);
-  } else if (e1end != e0) {
-    uint32_t m = side, k = e0 + r_before;
-    const uint32_t col_base = C > 1 ? o : col;
+  } else if (J.e1end != J.e0) {
+    uint32_t m = side, k = J.e0 + r_before;
+    const uint32_t col_base = C > 1 ? 32u * lane : J.col;
     while (m) {
       const uint32_t i = __builtin_ctz(m);
       m &= m - 1u;
       uint32_t rank;
       if ((esc >> i) & 1u) {
         const uint32_t e = e_before + __popc(esc & ((1u << i) - 1u));
-        rank = staged ? static_cast<uint32_t>(escs[e]) : load_u8(re, e);
+        rank = staged ? static_cast<uint32_t>(escs[e]) : load_u8(J.re, e);
       } else {
         rank = code_at(g, w, i);
       }
@@ -393,8 +410,33 @@ __global__ __launch_bounds__(64 * kF1Waves) void f1_to_r4_kernel(F1Args args) {
   }
 
   // ---- 4. the lane's 16 nibble bytes
-  if (live)
-    *reinterpret_cast<u32x4*>(a.nib + (fb >> 1) + 16u * lane) = *reinterpret_cast<const u32x4*>(nb);
+  if (J.live)
+    *reinterpret_cast<u32x4*>(a.nib + (J.fb >> 1) + 16u * lane) = *reinterpret_cast<const u32x4*>(nb);
+}
+
+// kJobs consecutive jobs per wave, every job's loads issued before the first
+// is decoded. One job per wave is what runs: two and four measured 3% and
+// 35-40% slower (the loads of later jobs gained nothing, the registers they
+// hold cost waves).
+template <int kJobs>
+__global__ __launch_bounds__(64 * kF1Waves) void f1_to_r4_kernel(F1Args args) {
+  __shared__ __align__(16) uint32_t code_lds[kF1Waves][kCodeWords];
+  __shared__ __align__(16) uint32_t esc_lds[kF1Waves][kEscStage / 4];
+  __shared__ __align__(16) uint32_t nib_lds[kF1Waves][64 * 4];
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const char* kp = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+  const F1Args& a = *(const F1Args*)kp;
+  const uint8_t* exp_of_rank = (const uint8_t*)kp + offsetof(F1Args, exp_of_rank);
+  const uint32_t j0 = (blockIdx.x * kF1Waves + wave) * kJobs;
+  F1Job J[kJobs];
+#pragma unroll
+  for (int i = 0; i < kJobs; ++i)
+    if (j0 + i < static_cast<uint64_t>(a.jobs)) f1_load(a, j0 + i, lane, J[i]);
+#pragma unroll
+  for (int i = 0; i < kJobs; ++i)
+    if (j0 + i < static_cast<uint64_t>(a.jobs))
+      f1_finish(a, exp_of_rank, J[i], lane, code_lds[wave], esc_lds[wave], nib_lds[wave]);
 }
 
 }  // namespace
@@ -460,7 +502,7 @@ extern "C" int32_t binade_f1_to_r4(const binade_f1* in, binade_r4* out,
   for (int r = 0; r < 256; ++r) a.exp_of_rank[r] = in->exp_of_rank[r];
   const int64_t blocks = (a.jobs + kF1Waves - 1) / kF1Waves;
   if (blocks > 0x7FFFFFFFll) return BINADE_EUNSUPPORTED;
-  hipLaunchKernelGGL(f1_to_r4_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(64 * kF1Waves), 0,
-                     static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(f1_to_r4_kernel<1>, dim3(static_cast<uint32_t>(blocks)), dim3(64 * kF1Waves),
+                     0, static_cast<hipStream_t>(stream), a);
   return launch_status();
 }
