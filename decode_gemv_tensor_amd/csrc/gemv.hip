@@ -270,104 +270,167 @@ __global__ __launch_bounds__(256) void bf16_gemv_kernel(GemvArgs a) {
 // ---------------------------------------------------------------- 2..8 rows
 // The decode step of a few sequences at once: Y[b, :] = W x_b for b < m
 // (m <= 8), each output in exactly the batch-1 order above, so row b of Y is
-// bit-identical to the batch-1 product of x_b. A wave owns one weight row:
-// per lane tile it loads and rebuilds the 32 weights once and runs them
-// through the MB rows' two fma chains (x rows past m repeat row m-1 and are
-// not stored). Rows of x and y are ldx and ldy elements apart.
+// bit-identical to the batch-1 product of x_b. Per lane tile a wave loads and
+// rebuilds its weights once and runs them through the MB rows' two fma
+// chains (x rows past m repeat row m-1 and are not stored). Rows of x and y
+// are ldx and ldy elements apart.
 struct GemvRowsArgs {
   GemvArgs g;              // weights, table, rows, cols, y_bf16 (g.x, g.y: row 0)
   int64_t ldx, ldy;
   int32_t m;
 };
 
-template <int MB, bool kR4>
-__global__ __launch_bounds__(256) void gemv_rows_kernel(GemvRowsArgs ra) {
+// The x rows are staged in LDS: a block of kRowsWaves waves (R weight rows
+// each) copies each row-chunk's 2048 columns of the MB x rows into LDS once,
+// and every wave reads its lanes' 32 columns from there, so the vector
+// memory path carries the weights and one copy of x per block instead of one
+// per wave (8 rows at 15360 x 3840: 73 -> 50 us).
+constexpr int kRowsWaves = 8;
+
+template <int MB, bool kR4, int R>
+__global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows_lds_kernel(GemvRowsArgs ra) {
+  __shared__ __align__(16) uint32_t xs[MB][kChunk / 2];   // bf16 pairs
   const GemvArgs& a = ra.g;
   const int lane = threadIdx.x & 63;
-  const int64_t row = uniform64(static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) +
-                                (threadIdx.x >> 6));
-  if (row >= a.rows) return;
+  // R weight rows per wave: each converted x value feeds R rows' chains
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * kRowsWaves +
+                        uniform(static_cast<uint32_t>(threadIdx.x >> 6))) * R;
+  int64_t rr[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) rr[i] = row0 + i < a.rows ? row0 + i : a.rows - 1;
   const int J = a.cols >> 5;
   const int C = (J + 63) >> 6;
   const Lut Lr{a.lut0, a.lut1, a.lut2, a.lut3};
-  const uint16_t* xr[MB];
+  float acc0[R][MB], acc1[R][MB];
 #pragma unroll
-  for (int b = 0; b < MB; ++b) xr[b] = a.x + (b < ra.m ? b : ra.m - 1) * ra.ldx;
-  float acc0[MB], acc1[MB];
+  for (int i = 0; i < R; ++i)
 #pragma unroll
-  for (int b = 0; b < MB; ++b) acc0[b] = acc1[b] = 0.0f;
+    for (int b = 0; b < MB; ++b) acc0[i][b] = acc1[i][b] = 0.0f;
 
   for (int j = 0; j < C; ++j) {
     const int t = j * 64 + lane;
-    if (t >= J) break;   // only in a ragged last chunk
-    float w[32];
-    if (kR4) {
-      const uint4* ps = reinterpret_cast<const uint4*>(a.sm + row * a.cols + 32 * t);
-      const uint4 s0 = ps[0], s1 = ps[1];
-      const uint4 nb = *reinterpret_cast<const uint4*>(a.nib + row * (a.cols >> 1) + 16 * t);
-      uint32_t E[8];
-      tile_exponents<true>(nb, Lr, a.esc_pre, a.esc, a.n_esc, row * C + j, lane, E);
-      const uint32_t S[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    const bool active = t < J;
+    // this wave's weight loads first
+    uint4 s0[R], s1[R], nb[R], q[R][4];
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        uint32_t H, Lo;
-        split4_rot(S[d], E[d], H, Lo);
-        w[4 * d] = weight_f32<0>(H, Lo);
-        w[4 * d + 1] = weight_f32<1>(H, Lo);
-        w[4 * d + 2] = weight_f32<2>(H, Lo);
-        w[4 * d + 3] = weight_f32<3>(H, Lo);
+    for (int i = 0; i < R; ++i) {
+      s0[i] = s1[i] = nb[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) q[i][v] = s0[i];
+      if (active) {
+        if (kR4) {
+          const uint4* ps = reinterpret_cast<const uint4*>(a.sm + rr[i] * a.cols + 32 * t);
+          s0[i] = ps[0];
+          s1[i] = ps[1];
+          nb[i] = *reinterpret_cast<const uint4*>(a.nib + rr[i] * (a.cols >> 1) + 16 * t);
+        } else {
+          const uint4* pw = reinterpret_cast<const uint4*>(
+              reinterpret_cast<const uint16_t*>(a.sm) + rr[i] * a.cols + 32 * t);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) q[i][v] = pw[v];
+        }
       }
-    } else {
-      const uint4* pw = reinterpret_cast<const uint4*>(
-          reinterpret_cast<const uint16_t*>(a.sm) + row * a.cols + 32 * t);
+    }
+    // the chunk's x columns of the MB rows (16 bytes per thread per pass)
+    __syncthreads();   // the previous chunk's x is no longer read
+    const int cols_here = min(kChunk, a.cols - j * kChunk);
+    for (int i = threadIdx.x; i < MB * (kChunk / 8); i += 64 * kRowsWaves) {
+      const int b = i / (kChunk / 8), piece = i % (kChunk / 8);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (8 * piece < cols_here) {
+        const int bb = b < ra.m ? b : ra.m - 1;
+        v = *reinterpret_cast<const uint4*>(a.x + bb * ra.ldx + j * kChunk + 8 * piece);
+      }
+      reinterpret_cast<uint4*>(xs[b])[piece] = v;
+    }
+    __syncthreads();
+    if (!active) continue;
+    float w[R][32];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint4 q = pw[v];
-        const uint32_t d4[4] = {q.x, q.y, q.z, q.w};
+    for (int i = 0; i < R; ++i) {
+      if (kR4) {
+        uint32_t E[8];
+        tile_exponents<true>(nb[i], Lr, a.esc_pre, a.esc, a.n_esc, rr[i] * C + j, lane, E);
+        const uint32_t S[8] = {s0[i].x, s0[i].y, s0[i].z, s0[i].w,
+                               s1[i].x, s1[i].y, s1[i].z, s1[i].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[8 * v + 2 * e] = bf16_lo(d4[e]);
-          w[8 * v + 2 * e + 1] = bf16_hi(d4[e]);
+        for (int d = 0; d < 8; ++d) {
+          uint32_t H, Lo;
+          split4_rot(S[d], E[d], H, Lo);
+          w[i][4 * d] = weight_f32<0>(H, Lo);
+          w[i][4 * d + 1] = weight_f32<1>(H, Lo);
+          w[i][4 * d + 2] = weight_f32<2>(H, Lo);
+          w[i][4 * d + 3] = weight_f32<3>(H, Lo);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t d4[4] = {q[i][v].x, q[i][v].y, q[i][v].z, q[i][v].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w[i][8 * v + 2 * e] = bf16_lo(d4[e]);
+            w[i][8 * v + 2 * e + 1] = bf16_hi(d4[e]);
+          }
         }
       }
     }
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
-      float xf[32];
-      load_x_tile(xr[b], t, xf);
+      const uint4* px = reinterpret_cast<const uint4*>(xs[b]) + 4 * lane;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        acc0[b] = __builtin_fmaf(w[2 * i], xf[2 * i], acc0[b]);
-        acc1[b] = __builtin_fmaf(w[2 * i + 1], xf[2 * i + 1], acc1[b]);
+      for (int v = 0; v < 4; ++v) {
+        const uint4 xq = px[v];
+        const uint32_t d4[4] = {xq.x, xq.y, xq.z, xq.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = bf16_lo(d4[e]), x1 = bf16_hi(d4[e]);
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            acc0[i][b] = __builtin_fmaf(w[i][8 * v + 2 * e], x0, acc0[i][b]);
+            acc1[i][b] = __builtin_fmaf(w[i][8 * v + 2 * e + 1], x1, acc1[i][b]);
+          }
+        }
       }
     }
   }
 #pragma unroll
-  for (int b = 0; b < MB; ++b) {
-    const float p = slot_tree(acc0[b] + acc1[b]);
-    if (lane == 0 && b < ra.m) {
-      const int64_t o = b * ra.ldy + row;
-      if (a.y_bf16)
-        static_cast<uint16_t*>(a.y)[o] = to_bf16_rne(p);
-      else
-        static_cast<float*>(a.y)[o] = p;
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      const float p = slot_tree(acc0[i][b] + acc1[i][b]);
+      if (lane == 0 && row0 + i < a.rows && b < ra.m) {
+        const int64_t o = b * ra.ldy + row0 + i;
+        if (a.y_bf16)
+          static_cast<uint16_t*>(a.y)[o] = to_bf16_rne(p);
+        else
+          static_cast<float*>(a.y)[o] = p;
+      }
     }
-  }
 }
 
 int32_t launch_gemv_rows(const GemvRowsArgs& ra, bool r4, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>((ra.g.rows + 3) / 4));
-  const dim3 block(256);
-  if (ra.m <= 2) {
-    if (r4) hipLaunchKernelGGL((gemv_rows_kernel<2, true>), grid, block, 0, stream, ra);
-    else hipLaunchKernelGGL((gemv_rows_kernel<2, false>), grid, block, 0, stream, ra);
-  } else if (ra.m <= 4) {
-    if (r4) hipLaunchKernelGGL((gemv_rows_kernel<4, true>), grid, block, 0, stream, ra);
-    else hipLaunchKernelGGL((gemv_rows_kernel<4, false>), grid, block, 0, stream, ra);
-  } else {
-    if (r4) hipLaunchKernelGGL((gemv_rows_kernel<8, true>), grid, block, 0, stream, ra);
-    else hipLaunchKernelGGL((gemv_rows_kernel<8, false>), grid, block, 0, stream, ra);
+  // two weight rows per wave halve the x conversions (8 rows of x); only
+  // where the blocks still fill the chip (measured: 15360 rows 50 -> 42 us,
+  // 3840 rows slower)
+  const int R = (ra.m > 4 && ra.g.rows >= 8192) ? 2 : 1;
+  const dim3 sgrid(static_cast<uint32_t>((ra.g.rows + kRowsWaves * R - 1) / (kRowsWaves * R)));
+  const dim3 sblock(64 * kRowsWaves);
+#define BINADE_ROWS_LAUNCH(MB)                                                              \
+  if (R == 2) {                                                                             \
+    if (r4) hipLaunchKernelGGL((gemv_rows_lds_kernel<MB, true, 2>), sgrid, sblock, 0, stream, ra);   \
+    else hipLaunchKernelGGL((gemv_rows_lds_kernel<MB, false, 2>), sgrid, sblock, 0, stream, ra);     \
+  } else {                                                                                  \
+    if (r4) hipLaunchKernelGGL((gemv_rows_lds_kernel<MB, true, 1>), sgrid, sblock, 0, stream, ra);   \
+    else hipLaunchKernelGGL((gemv_rows_lds_kernel<MB, false, 1>), sgrid, sblock, 0, stream, ra);     \
   }
+  if (ra.m <= 2) {
+    BINADE_ROWS_LAUNCH(2)
+  } else if (ra.m <= 4) {
+    BINADE_ROWS_LAUNCH(4)
+  } else {
+    BINADE_ROWS_LAUNCH(8)
+  }
+#undef BINADE_ROWS_LAUNCH
   return launch_status();
 }
 
