@@ -247,3 +247,88 @@ def test_huffman_deep_tree_refused():
     cap = ctypes.c_uint64(0)
     rc = B.lib().binade_huff_lengths(ctypes.c_void_p(wn.ctypes.data), wn.size, ln, ctypes.byref(cap))
     assert rc == B.EUNSUPPORTED
+
+
+def test_struct_layouts_match_the_c_compiler(tmp_path):
+    """The ctypes mirrors have the sizes and field offsets gcc gives the
+    header's structs."""
+    import subprocess
+    src = tmp_path / "sizes.c"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    src.write_text("""#include <stdio.h>
+#include <stddef.h>
+#include "binade.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(binade_table), sizeof(binade_rice),
+         sizeof(binade_r4), sizeof(binade_f1), sizeof(binade_huff),
+         offsetof(binade_f1, sm), offsetof(binade_huff, sm), offsetof(binade_f1, n_esc));
+  return 0;
+}
+""")
+    exe = tmp_path / "sizes"
+    subprocess.run(["gcc", "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert got == [ctypes.sizeof(B.Table), ctypes.sizeof(B.RiceDesc), ctypes.sizeof(B.R4Desc),
+                   ctypes.sizeof(B.F1Desc), ctypes.sizeof(B.HuffDesc), B.F1Desc.sm.offset,
+                   B.HuffDesc.sm.offset, B.F1Desc.n_esc.offset]
+
+
+def test_new_device_entry_points_validate_before_touching_the_gpu():
+    """The format 1, small-batch, MoE epilogue, device pack and Huffman entry
+    points refuse bad arguments on the host, before any HIP call."""
+    L = B.lib()
+    P = ctypes.c_void_p
+    # format 1
+    f = B.F1Desc()
+    r = B.R4Desc()
+    assert L.binade_f1_to_r4(None, ctypes.byref(r), None, None) == B.EINVAL
+    f.rows, f.cols, f.n = 4, 48, 5
+    assert L.binade_f1_to_r4(ctypes.byref(f), ctypes.byref(r), None, None) == B.EUNSUPPORTED
+    f.cols = 64
+    assert L.binade_f1_to_r4(ctypes.byref(f), ctypes.byref(r), None, None) == B.EINVAL   # null planes
+    # small-batch product: m outside 1..8, short strides
+    d = B.R4Desc()
+    d.rows, d.cols = 4, 64
+    d.sm = d.nib = d.esc_pre = 16
+    for m, ldx, ldy in [(0, 64, 4), (9, 64, 4), (2, 32, 4), (2, 64, 3)]:
+        assert L.binade_r4_gemv_rows(ctypes.byref(d), P(16), ldx, m, P(16), ldy, B.F32, None) == B.EINVAL
+    assert L.binade_r4_gemv_rows(ctypes.byref(d), P(8), 64, 2, P(16), 4, B.F32, None) == B.EUNSUPPORTED
+    assert L.binade_r4_gemv_rows(ctypes.byref(d), P(16), 68, 2, P(16), 4, B.F32, None) == B.EUNSUPPORTED
+    assert L.binade_bf16_gemv_rows(P(16), 4, 48, P(16), 64, 2, P(16), 4, B.F32, None) == B.EUNSUPPORTED
+    # MoE epilogue
+    assert L.binade_moe_silu_mul(None, None, -1, None, B.BF16, None) == B.EINVAL
+    assert L.binade_moe_silu_mul(None, None, 10, None, 7, None) == B.EINVAL
+    assert L.binade_moe_silu_mul(None, None, 0, None, B.BF16, None) == B.OK      # empty: no launch
+    assert L.binade_moe_silu_mul(None, P(16), 10, P(16), B.BF16, None) == B.EINVAL
+    for k in (0, 65):
+        assert L.binade_moe_combine(P(16), P(16), 2, k, 8, P(16), B.F32, None) == B.EINVAL
+    assert L.binade_moe_combine(P(16), P(16), 0, 8, 8, P(16), B.F32, None) == B.OK
+    # device table and pack
+    t = B.Table()
+    assert L.binade_build_table_gpu(None, 10, P(16), P(16), None) == B.EINVAL
+    assert L.binade_build_table_gpu(P(8), 10, P(16), P(16), None) == B.EUNSUPPORTED
+    assert B.lib().binade_pack_gpu_workspace_bytes(0, 64) == 0
+    assert B.lib().binade_pack_gpu_workspace_bytes(4, 64) >= 2048
+    rd = B.RiceDesc()
+    assert L.binade_pack_rice_gpu(P(16), 4, 48, ctypes.byref(t), ctypes.byref(rd), P(16), None,
+                                  None) == B.EUNSUPPORTED
+    t.n, t.k = 1, 0
+    t.count_of_rank[0] = 4 * 64
+    assert L.binade_pack_rice_gpu(P(16), 4, 64, ctypes.byref(t), ctypes.byref(rd), P(16), None,
+                                  None) == B.EINVAL      # null planes
+    rd.sm, rd.unary, rd.anchor, rd.esc_pre = 16, 16, 16, 16
+    rd.unary_words = 1
+    assert L.binade_pack_rice_gpu(P(16), 4, 64, ctypes.byref(t), ctypes.byref(rd), P(16), None,
+                                  None) == B.ENOSPACE
+    # Huffman decode
+    h = B.HuffDesc()
+    assert L.binade_huff_decode(None, P(16), P(16), None, None) == B.EINVAL
+    h.n = 100
+    h.sm, h.stream, h.block_len, h.group_off = 16, 16, 16, 16
+    h.stream_bytes, h.stream_cap = 100, 104       # needs 8 bytes of look-ahead
+    assert L.binade_huff_decode(ctypes.byref(h), P(16), P(16), None, None) == B.EUNSUPPORTED
+    h.stream_cap = 108
+    h.len[3] = 32
+    assert L.binade_huff_decode(ctypes.byref(h), P(16), P(16), None, None) == B.EINVAL
+    assert B.lib().binade_huff_workspace_bytes() > 4096
