@@ -32,7 +32,14 @@ constexpr int kLutBits = 11;
 constexpr int kLut = 1 << kLutBits;
 constexpr int kMaxLen = 31;
 constexpr int kHuffThreads = BINADE_HUFF_GROUP;   // one thread per block of a group
-constexpr int kStageWords = 2048;                  // 8 KiB of a group's stream in LDS
+// A group's stream words staged in LDS (4 KiB: up to 4 bits per symbol on
+// average; a longer group reads its words from memory)
+constexpr int kStageWords = 1024;
+// Words past the staged ones that a block's reads can reach: a block of 64
+// codes of at most 31 bits spans at most 62 words beyond its first two, so
+// the top-up read stays inside the array even on a corrupt stream (where
+// the extra words are stale and the block is flagged by its length check).
+constexpr int kStagePad = 64;
 
 // Workspace layout (bytes)
 constexpr int kWsLut = 0;                        // u16[2048]: symbol | length << 8 (0: longer)
@@ -125,12 +132,96 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t v) {   // inclusive, 64 l
   return v;
 }
 
+// The decode tables and the group's staged words in LDS.
+struct HuffLds {
+  const uint16_t* lut;
+  const uint32_t* first;
+  const uint32_t* count;
+  const uint32_t* base;
+  const uint8_t* sorted;
+  const uint32_t* stage;
+};
+
+// One block's cnt codes from the bit buffer at word wi0 (skip bits in):
+// each code is one table lookup (a rare longer code walks the canonical
+// table, behind a wave-uniform test); the buffer tops up from the next word
+// without a branch when fewer than 32 bits are left. kStaged: words from
+// LDS, else from memory. kFull: every block of the wave holds 64 codes (no
+// per-code test of the count).
+template <bool kStaged, bool kFull>
+__device__ __forceinline__ void decode_block(const HuffLds& L, __amdgpu_buffer_rsrc_t rs, uint32_t w0,
+                                             uint32_t wi0, uint32_t skip, int cnt,
+                                             const uint32_t (&smw)[16], uint16_t* po,
+                                             uint32_t& used, bool& bad) {
+  auto word = [&](uint32_t i) -> uint32_t {
+    return kStaged ? L.stage[i] : bswap32(__builtin_amdgcn_raw_buffer_load_b32(rs, 4u * (w0 + i), 0, 0));
+  };
+  uint32_t wi = wi0;
+  uint64_t buf = ((static_cast<uint64_t>(word(wi)) << 32) | word(wi + 1)) << skip;
+  uint32_t avail = 64u - skip;
+  wi += 2;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = 8 * q + k;
+      if (kFull || i < cnt) {
+        const uint32_t ent = L.lut[static_cast<uint32_t>(buf >> (64 - kLutBits))];
+        uint32_t l = ent >> 8, sym = ent & 0xFFu;
+        if (__any(l == 0u)) {
+          if (l == 0u) {   // a code longer than the table: the canonical walk
+            bool found = false;
+            for (uint32_t ll = kLutBits + 1; ll <= kMaxLen; ++ll) {
+              const uint32_t c = static_cast<uint32_t>(buf >> (64 - ll));
+              if (L.count[ll] && c - L.first[ll] < L.count[ll]) {
+                sym = L.sorted[L.base[ll] + c - L.first[ll]];
+                l = ll;
+                found = true;
+                break;
+              }
+            }
+            if (!found) {
+              bad = true;
+              l = 1;
+            }
+          }
+        }
+        buf <<= l;
+        avail -= l;
+        used += l;
+        if (kStaged) {
+          // top up from the next word when fewer than 32 bits are left
+          const uint32_t nw = L.stage[wi];
+          const bool need = avail < 32u;
+          buf |= need ? static_cast<uint64_t>(nw) << (32u - avail) : 0ull;
+          wi += need ? 1u : 0u;
+          avail += need ? 32u : 0u;
+        } else if (avail < 32u) {
+          buf |= static_cast<uint64_t>(word(wi++)) << (32u - avail);
+          avail += 32u;
+        }
+        const uint32_t sm = (smw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        const uint32_t bf = ((sm & 0x80u) << 8) | (sym << 7) | (sm & 0x7Fu);
+        o[k >> 1] |= bf << (16 * (k & 1));
+      }
+    }
+    if (kFull || cnt == BINADE_HUFF_BLOCK) {
+      reinterpret_cast<uint4*>(po)[q] = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (8 * q + k < cnt) po[8 * q + k] = static_cast<uint16_t>(o[k >> 1] >> (16 * (k & 1)));
+    }
+  }
+}
+
 __global__ __launch_bounds__(kHuffThreads) void huff_decode_kernel(HuffArgs a) {
   __shared__ uint16_t lut[kLut];
   __shared__ uint32_t first[32], count[32], base[32];
   __shared__ uint8_t sorted[256];
-  __shared__ uint32_t stage[kStageWords];
-  __shared__ uint32_t wave0_total, group_total;
+  __shared__ uint32_t stage[kStageWords + kStagePad];
+  __shared__ uint32_t wave_total[2];
   const uint32_t tid = threadIdx.x;
   for (int i = tid; i < kLut / 2; i += kHuffThreads)
     reinterpret_cast<uint32_t*>(lut)[i] = reinterpret_cast<const uint32_t*>(a.ws + kWsLut)[i];
@@ -145,36 +236,27 @@ __global__ __launch_bounds__(kHuffThreads) void huff_decode_kernel(HuffArgs a) {
 
   for (int64_t g = blockIdx.x; g < a.groups; g += gridDim.x) {
     __syncthreads();   // tables ready; the previous group's stage is consumed
+    // Every load of the group is issued before any is waited on: the block
+    // lengths, the group's stream words (located by the group offsets alone,
+    // checked against the lengths' sum below) and the sign/mantissa bytes.
+    const uint64_t A = a.group_off[g], Aend = a.group_off[g + 1];
     const int64_t b = g * kHuffThreads + tid;
     const uint32_t blen = b < a.blocks ? a.block_len[b] : 0u;
-    uint32_t incl = wave_scan(blen);
-    if (tid == 63) wave0_total = incl;
-    const uint64_t A = a.group_off[g], Aend = a.group_off[g + 1];
-    __syncthreads();
-    if (tid >= 64) incl += wave0_total;
-    const uint32_t off = incl - blen;
-    if (tid == kHuffThreads - 1) group_total = incl;   // the group's bytes
-    __syncthreads();
-    const uint32_t gbytes = group_total;
-    bool bad = Aend < A || Aend - A != gbytes || Aend + 8 > 4ull * a.stream_words;
-    if (bad) {
-      if (tid == 0 && a.status) atomicOr(a.status, BINADE_DEV_CORRUPT_STREAM);
-      continue;
-    }
+    const bool span_ok = Aend >= A && Aend + 8 <= 4ull * a.stream_words;
     // the group's stream words, from the word holding its first byte, plus
     // two words of look-ahead
     const uint32_t w0 = static_cast<uint32_t>(A >> 2);
-    const uint32_t nwords = static_cast<uint32_t>(((A + gbytes + 3) >> 2) - w0) + 2u;
-    const bool staged = nwords <= static_cast<uint32_t>(kStageWords);
-    if (staged)
-      for (uint32_t i = tid; i < nwords; i += kHuffThreads)
-        stage[i] = bswap32(__builtin_amdgcn_raw_buffer_load_b32(rs, 4u * (w0 + i), 0, 0));
-    __syncthreads();
-    if (b >= a.blocks) continue;
-
+    const uint64_t nwords = span_ok ? ((Aend + 3) >> 2) - w0 + 2u : 0u;
+    const bool staged = nwords <= static_cast<uint64_t>(kStageWords);
+    uint32_t sw[kStageWords / kHuffThreads];
+#pragma unroll
+    for (int j = 0; j < kStageWords / kHuffThreads; ++j) {
+      const uint32_t i = tid + kHuffThreads * j;
+      sw[j] = staged && i < nwords ? __builtin_amdgcn_raw_buffer_load_b32(rs, 4u * (w0 + i), 0, 0) : 0u;
+    }
     const int64_t sym0 = b * BINADE_HUFF_BLOCK;
     const int64_t left = a.n - sym0;
-    const int cnt = left < BINADE_HUFF_BLOCK ? static_cast<int>(left) : BINADE_HUFF_BLOCK;
+    const int cnt = left <= 0 ? 0 : left < BINADE_HUFF_BLOCK ? static_cast<int>(left) : BINADE_HUFF_BLOCK;
     // the block's 64 sign/mantissa bytes
     uint32_t smw[16];
     if (cnt == BINADE_HUFF_BLOCK) {
@@ -191,69 +273,47 @@ __global__ __launch_bounds__(kHuffThreads) void huff_decode_kernel(HuffArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         uint32_t v = 0;
+        if (cnt > 0) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          v |= __builtin_amdgcn_raw_buffer_load_b8(rsm, static_cast<uint32_t>(sym0) + 4 * i + k, 0, 0)
-               << (8 * k);
+          for (int k = 0; k < 4; ++k)
+            v |= __builtin_amdgcn_raw_buffer_load_b8(rsm, static_cast<uint32_t>(sym0) + 4 * i + k, 0, 0)
+                 << (8 * k);
+        }
         smw[i] = v;
       }
     }
+    // block offsets within the group: a scan of the lengths over the two waves
+    uint32_t incl = wave_scan(blen);
+    if ((tid & 63) == 63) wave_total[tid >> 6] = incl;
+#pragma unroll
+    for (int j = 0; j < kStageWords / kHuffThreads; ++j) {
+      const uint32_t i = tid + kHuffThreads * j;
+      if (staged && i < nwords) stage[i] = bswap32(sw[j]);
+    }
+    __syncthreads();
+    if (tid >= 64) incl += wave_total[0];
+    const uint32_t off = incl - blen;
+    const uint32_t gbytes = wave_total[0] + wave_total[1];   // the group's bytes
+    bool bad = !span_ok || Aend - A != gbytes;
+    if (bad) {
+      if (tid == 0 && a.status) atomicOr(a.status, BINADE_DEV_CORRUPT_STREAM);
+      continue;
+    }
+    if (cnt == 0) continue;
     // bit buffer: the next bits at the top of a 64-bit value
     const uint64_t p = A + off;   // the block's first byte
-    uint32_t wi = static_cast<uint32_t>(p >> 2) - w0;
-    auto word = [&](uint32_t i) -> uint32_t {
-      return staged ? stage[i] : bswap32(__builtin_amdgcn_raw_buffer_load_b32(rs, 4u * (w0 + i), 0, 0));
-    };
+    const uint32_t wi0 = static_cast<uint32_t>(p >> 2) - w0;
     const uint32_t skip = static_cast<uint32_t>(p & 3u) * 8u;
-    uint64_t buf = ((static_cast<uint64_t>(word(wi)) << 32) | word(wi + 1)) << skip;
-    uint32_t avail = 64u - skip;
-    wi += 2;
     uint32_t used = 0;
     uint16_t* po = a.out + sym0;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      uint32_t o[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int i = 8 * q + k;
-        if (i < cnt) {
-          const uint32_t ent = lut[static_cast<uint32_t>(buf >> (64 - kLutBits))];
-          uint32_t l = ent >> 8, sym = ent & 0xFFu;
-          if (l == 0) {   // a code longer than the table: the canonical walk
-            bool found = false;
-            for (uint32_t ll = kLutBits + 1; ll <= kMaxLen; ++ll) {
-              const uint32_t c = static_cast<uint32_t>(buf >> (64 - ll));
-              if (count[ll] && c - first[ll] < count[ll]) {
-                sym = sorted[base[ll] + c - first[ll]];
-                l = ll;
-                found = true;
-                break;
-              }
-            }
-            if (!found) {
-              bad = true;
-              l = 1;
-            }
-          }
-          buf <<= l;
-          avail -= l;
-          used += l;
-          if (avail < 32u) {
-            buf |= static_cast<uint64_t>(word(wi++)) << (32u - avail);
-            avail += 32u;
-          }
-          const uint32_t s = (smw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-          const uint32_t bf = ((s & 0x80u) << 8) | (sym << 7) | (s & 0x7Fu);
-          o[k >> 1] |= bf << (16 * (k & 1));
-        }
-      }
-      if (cnt == BINADE_HUFF_BLOCK) {
-        reinterpret_cast<uint4*>(po)[q] = make_uint4(o[0], o[1], o[2], o[3]);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (8 * q + k < cnt) po[8 * q + k] = static_cast<uint16_t>(o[k >> 1] >> (16 * (k & 1)));
-      }
+    const HuffLds L{lut, first, count, base, sorted, stage};
+    if (staged) {
+      if (__all(cnt == BINADE_HUFF_BLOCK))
+        decode_block<true, true>(L, rs, w0, wi0, skip, cnt, smw, po, used, bad);
+      else
+        decode_block<true, false>(L, rs, w0, wi0, skip, cnt, smw, po, used, bad);
+    } else {
+      decode_block<false, false>(L, rs, w0, wi0, skip, cnt, smw, po, used, bad);
     }
     if (bad || (used + 7u) / 8u != blen) {
       if (a.status) atomicOr(a.status, BINADE_DEV_CORRUPT_STREAM);
@@ -302,7 +362,8 @@ extern "C" int32_t binade_huff_decode(const binade_huff* in, uint16_t* out, void
   a.blocks = (in->n + BINADE_HUFF_BLOCK - 1) / BINADE_HUFF_BLOCK;
   a.groups = (a.blocks + BINADE_HUFF_GROUP - 1) / BINADE_HUFF_GROUP;
   a.stream_words = static_cast<uint32_t>(in->stream_cap / 4);
-  const int64_t grid = a.groups < 4096 ? a.groups : 4096;
+  // one workgroup per group (the loop covers grids past the launch limit)
+  const int64_t grid = a.groups < (1ll << 30) ? a.groups : (1ll << 30);
   hipLaunchKernelGGL(huff_decode_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kHuffThreads), 0,
                      s, a);
   return launch_status();
