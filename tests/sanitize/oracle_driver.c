@@ -1,5 +1,6 @@
-/* Runs every oracle function on many shapes with buffers of exactly the
- * sizes its callers use, including corrupt streams. Built with
+/* Runs every oracle function (table, both file formats, R4, the GEMV, GEMM
+ * and MoE replays, the MoE epilogue, the Huffman codec) on many shapes with
+ * buffers of exactly the sizes its callers use, including corrupt streams. Built with
  * AddressSanitizer and UndefinedBehaviorSanitizer by
  * tests/test_host_sanitizers.py; any out-of-bounds access, leak or undefined
  * operation aborts the run. */
@@ -26,6 +27,21 @@ int oracle_gemm_replay(const uint16_t *w, int64_t N, int64_t K, const uint16_t *
 int oracle_moe_replay(const uint16_t *experts, int64_t n_experts, int64_t N, int64_t K, const uint16_t *x,
                       int x_per_slot, const int32_t *idx, int64_t n_tokens, int64_t top_k, float *y);
 float oracle_mfma_step(const uint16_t *a, const uint16_t *b, float c);
+int oracle_pack_f1(const uint16_t *w, int64_t rows, int64_t cols, const uint8_t *exp_of_rank, uint32_t n,
+                   uint8_t *sm, uint8_t *width, uint32_t *codes, int64_t code_words, uint8_t *esc, int64_t esc_cap,
+                   uint64_t *anchor, uint32_t *f1_pre, uint32_t *esc_pre, uint64_t *code_bits_out,
+                   int64_t *n_f1esc_out);
+int oracle_f1_decode(int64_t rows, int64_t cols, const uint8_t *exp_of_rank, uint32_t n, const uint8_t *sm,
+                     const uint8_t *width, const uint32_t *codes, uint64_t code_bits, const uint8_t *esc,
+                     int64_t n_f1esc, const uint64_t *anchor, const uint32_t *f1_pre, const uint32_t *esc_pre,
+                     uint16_t *out);
+void oracle_silu_mul(const float *gate, const float *up, int64_t n, float *out);
+int oracle_moe_combine(const float *y, const float *weights, int64_t n_tokens, int top_k, int64_t n, float *out);
+int oracle_huff_lengths(const uint64_t *counts, uint8_t *len);
+int oracle_huff_pack(const uint16_t *w, int64_t n, const uint8_t *len, uint8_t *sm, uint8_t *stream, int64_t cap,
+                     uint8_t *block_len, uint64_t *group_off, uint64_t *bytes_out);
+int oracle_huff_decode(int64_t n, const uint8_t *len, const uint8_t *sm, const uint8_t *stream,
+                       int64_t stream_bytes, const uint8_t *block_len, const uint64_t *group_off, uint16_t *out);
 
 static uint64_t state = 88172645463325252ull;
 static uint64_t next(void) { state ^= state << 13; state ^= state >> 7; state ^= state << 17; return state; }
@@ -86,6 +102,62 @@ static int check(int64_t rows, int64_t cols, int dist) {
     if (rc) bad = 1;
     free(nib); free(sm); free(epre); free(esc); free(x); free(y);
   }
+  {
+    /* format 1: pack into the capacities its callers use, then decode from
+     * exactly the words and escapes the pack wrote (plus the one word of
+     * look-ahead its callers append) */
+    int64_t tpr = (cols + 127) / 128, cw = n * 8 / 32 + 2, nf1 = 0, used;
+    uint64_t cbits = 0;
+    uint8_t *sm = malloc(n), *width = malloc(rows * tpr), *esc = malloc(n ? n : 1);
+    uint32_t *codes = malloc(cw * 4), *f1p = malloc((nch + 1) * 4), *epre = malloc((nch + 1) * 4);
+    uint64_t *anchor = malloc((nch + 1) * 8);
+    rc = oracle_pack_f1(w, rows, cols, eor, np, sm, width, codes, cw, esc, n, anchor, f1p, epre, &cbits, &nf1);
+    if (rc) bad = 1;
+    used = (int64_t)((cbits + 31) / 32) + 1;
+    {
+      uint32_t *c2 = malloc(used * 4);
+      uint8_t *e2 = malloc(nf1 ? nf1 : 1);
+      memcpy(c2, codes, (used - 1) * 4);
+      c2[used - 1] = 0;
+      memcpy(e2, esc, nf1);
+      if (!rc && (oracle_f1_decode(rows, cols, eor, np, sm, width, c2, cbits, e2, nf1, anchor, f1p, epre, back) ||
+                  memcmp(back, w, n * 2)))
+        bad = 1;
+      /* corrupt: a width above 8 must be reported */
+      if (rows * tpr > 0) {
+        width[0] = 9;
+        if (oracle_f1_decode(rows, cols, eor, np, sm, width, c2, cbits, e2, nf1, anchor, f1p, epre, back) == 0)
+          bad = 1;
+      }
+      free(c2); free(e2);
+    }
+    free(sm); free(width); free(esc); free(codes); free(f1p); free(epre); free(anchor);
+  }
+  {
+    /* Huffman: lengths, a pack into the stream bytes the codes need plus
+     * one per block (its callers' capacity), a decode from exactly the
+     * bytes written, and a corrupt block length */
+    uint64_t cnt[256], bits = 0, sb = 0;
+    uint8_t len[256];
+    int64_t nb = (n + 63) / 64, ng = (nb + 127) / 128, cap;
+    memset(cnt, 0, sizeof cnt);
+    for (i = 0; i < n; ++i) ++cnt[(w[i] >> 7) & 0xFF];
+    if (n > 0) {
+      rc = oracle_huff_lengths(cnt, len);
+      for (i = 0; i < 256; ++i) bits += cnt[i] * len[i];
+      cap = (int64_t)((bits + 7) / 8) + nb;
+      {
+        uint8_t *sm = malloc(n), *stream = malloc(cap), *bl = malloc(nb);
+        uint64_t *go = malloc((ng + 1) * 8);
+        rc |= oracle_huff_pack(w, n, len, sm, stream, cap, bl, go, &sb);
+        if (rc || oracle_huff_decode(n, len, sm, stream, (int64_t)sb, bl, go, back) || memcmp(back, w, n * 2))
+          bad = 1;
+        bl[0] ^= 1u;
+        if (oracle_huff_decode(n, len, sm, stream, (int64_t)sb, bl, go, back) == 0) bad = 1;
+        free(sm); free(stream); free(bl); free(go);
+      }
+    }
+  }
   free(w); free(back);
   if (bad) fprintf(stderr, "oracle failed at %lldx%lld dist %d\n", (long long)rows, (long long)cols, dist);
   return bad;
@@ -109,6 +181,22 @@ int main(void) {
     if (((cu >> 23) & 0xFF) == 0xFF) cu &= 0xBFFFFFFFu;
     memcpy(&c, &cu, 4);
     (void)oracle_mfma_step(a, b, c);
+  }
+  {
+    /* MoE epilogue: activation and combine over exact-size buffers */
+    float g[257], u[257], h[257], yv[3 * 4 * 33], wt[3 * 4], out[3 * 33];
+    int j;
+    for (j = 0; j < 257; ++j) {
+      uint32_t bits = (uint32_t)next();
+      if (((bits >> 23) & 0xFF) == 0xFF) bits &= 0xBFFFFFFFu;   /* finite */
+      memcpy(&g[j], &bits, 4);
+      u[j] = (float)((int)(next() % 2001) - 1000) / 7.0f;
+    }
+    oracle_silu_mul(g, u, 257, h);
+    for (j = 0; j < 3 * 4 * 33; ++j) yv[j] = (float)((int)(next() % 2001) - 1000) / 3.0f;
+    for (j = 0; j < 12; ++j) wt[j] = (float)(next() % 1000) / 1000.0f;
+    if (oracle_moe_combine(yv, wt, 3, 4, 33, out)) bad = 1;
+    if (oracle_moe_combine(yv, wt, 3, 0, 33, out) == 0) bad = 1;   /* top_k 0: EINVAL */
   }
   printf(bad ? "oracle: FAILED\n" : "oracle: ok\n");
   return bad;
