@@ -38,7 +38,7 @@ using namespace dev;
 constexpr int kPackWaves = 4;
 constexpr int kScanBlock = 1024;       // chunks per scan block
 constexpr int kStreamWords = 2048;     // LDS words per wave for a job's unary bits
-constexpr int kHistCopies = 16;        // histogram copies per block
+constexpr int kHistCopies = 64;        // histogram copies per block (one per lane)
 
 __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, uint64_t words) {
   const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
@@ -51,25 +51,33 @@ __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, uint64_t w
 __global__ __launch_bounds__(256) void hist_kernel(const uint16_t* w, int64_t n,
                                                    unsigned long long* counts) {
   // kHistCopies counts per bin, lane l adding into copy l % kHistCopies:
-  // lanes that hit the same bin mostly hit different words, in different
-  // banks (bin e, copy k at word e * (kHistCopies + 1) + k)
+  // the lanes of one instruction never hit the same word, and lanes that hit
+  // the same bin fall in different banks (bin e, copy k at word
+  // e * (kHistCopies + 1) + k). Two 16-byte loads per thread are in flight
+  // before their counts are added.
   constexpr int kStride = kHistCopies + 1;
   __shared__ uint32_t h[256 * kStride];
   uint32_t* mine = h + threadIdx.x % kHistCopies;
   for (int e = threadIdx.x; e < 256 * kStride; e += blockDim.x) h[e] = 0u;
   __syncthreads();
-  const int64_t groups = n >> 3;   // 8 weights per 16-byte load
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < groups;
-       g += stride) {
-    const uint4 v = reinterpret_cast<const uint4*>(w)[g];
+  auto add8 = [&](const uint4 v) {
     const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       atomicAdd(&mine[((d[i] >> 7) & 0xFFu) * kStride], 1u);
       atomicAdd(&mine[((d[i] >> 23) & 0xFFu) * kStride], 1u);
     }
+  };
+  const int64_t groups = n >> 3;   // 8 weights per 16-byte load
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const uint4* w4 = reinterpret_cast<const uint4*>(w);
+  int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; g + stride < groups; g += 2 * stride) {
+    const uint4 v0 = w4[g], v1 = w4[g + stride];
+    add8(v0);
+    add8(v1);
   }
+  if (g < groups) add8(w4[g]);
   if (blockIdx.x == 0)
     for (int64_t i = (groups << 3) + threadIdx.x; i < n; i += blockDim.x)
       atomicAdd(&mine[((w[i] >> 7) & 0xFFu) * kStride], 1u);
