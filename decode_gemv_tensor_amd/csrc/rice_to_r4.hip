@@ -925,6 +925,12 @@ __device__ __forceinline__ void decode_job_bytes(const RiceArgs& a, const uint8_
   else if (spl <= 8u)
     byte_walk<K, 8, false>(x, c_in, sb0, lut, remw, a.n, nb, ctr, slots, limit, table, chunk_mod,
                            nullptr, unused);
+  else if (spl <= 10u)
+    byte_walk<K, 10, false>(x, c_in, sb0, lut, remw, a.n, nb, ctr, slots, limit, table,
+                            chunk_mod, nullptr, unused);
+  else if (spl <= 11u)   // 3072-weight jobs at k = 1 (≈ 650 bytes)
+    byte_walk<K, 11, false>(x, c_in, sb0, lut, remw, a.n, nb, ctr, slots, limit, table,
+                            chunk_mod, nullptr, unused);
   else if (spl <= 12u)
     byte_walk<K, 12, false>(x, c_in, sb0, lut, remw, a.n, nb, ctr, slots, limit, table,
                             chunk_mod, nullptr, unused);
