@@ -55,12 +55,28 @@ struct HuffTables {
 
 __global__ __launch_bounds__(256) void huff_tables_kernel(HuffTables t, uint8_t* ws) {
   __shared__ uint32_t count[kMaxLen + 2], first[kMaxLen + 2], base[kMaxLen + 2];
+  __shared__ uint32_t wave_count[4][kMaxLen + 1];   // exponents of each length per wave
   __shared__ uint8_t sorted[256];
   const int e = threadIdx.x;
+  const int lane = e & 63, wave = e >> 6;
   if (e < kMaxLen + 2) count[e] = 0;
-  __syncthreads();
+  if (e < 4 * (kMaxLen + 1)) (&wave_count[0][0])[e] = 0;
   const uint32_t le = t.len[e];
-  if (le) atomicAdd(&count[le], 1u);
+  // the lanes of this wave with the same length as this lane (a ballot per
+  // bit of the 5-bit length)
+  uint64_t same = ~0ull;
+#pragma unroll
+  for (int b = 0; b < 5; ++b) {
+    const uint64_t m = __ballot((le >> b) & 1u);
+    same &= ((le >> b) & 1u) ? m : ~m;
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  const uint32_t in_wave = static_cast<uint32_t>(__popcll(same & below));
+  __syncthreads();
+  if (le) {
+    atomicAdd(&count[le], 1u);
+    if (in_wave == 0) wave_count[wave][le] = static_cast<uint32_t>(__popcll(same));
+  }
   __syncthreads();
   if (e == 0) {
     uint32_t code = 0, idx = 0;
@@ -73,22 +89,35 @@ __global__ __launch_bounds__(256) void huff_tables_kernel(HuffTables t, uint8_t*
   }
   __syncthreads();
   if (le) {
-    uint32_t before = 0;
-    for (int o = 0; o < e; ++o) before += t.len[o] == le ? 1u : 0u;
+    // exponents of the same length before e: earlier waves', then this one's
+    uint32_t before = in_wave;
+    for (int w = 0; w < wave; ++w) before += wave_count[w][le];
     sorted[base[le] + before] = static_cast<uint8_t>(e);
   }
   __syncthreads();
   uint16_t* lut = reinterpret_cast<uint16_t*>(ws + kWsLut);
-  for (int x = e; x < kLut; x += 256) {
-    uint16_t ent = 0;
-    for (int l = 1; l <= kLutBits; ++l) {
-      const uint32_t c = static_cast<uint32_t>(x) >> (kLutBits - l);
-      if (count[l] && c - first[l] < count[l]) {
-        ent = static_cast<uint16_t>(sorted[base[l] + c - first[l]] | (l << 8));
-        break;
+  // the table's lengths' counts and first codes, read once (wave-uniform)
+  uint32_t cnt_l[kLutBits + 1], fst_l[kLutBits + 1], bas_l[kLutBits + 1];
+#pragma unroll
+  for (int l = 1; l <= kLutBits; ++l) {
+    cnt_l[l] = count[l];
+    fst_l[l] = first[l];
+    bas_l[l] = base[l];
+  }
+#pragma unroll
+  for (int q = 0; q < kLut / 256; ++q) {
+    const uint32_t x = static_cast<uint32_t>(e + 256 * q);
+    // the shortest length whose codes hold x's prefix (none: a longer code)
+    uint32_t idx = 0, len = 0;
+#pragma unroll
+    for (int l = kLutBits; l >= 1; --l) {
+      const uint32_t d = (x >> (kLutBits - l)) - fst_l[l];
+      if (d < cnt_l[l]) {
+        idx = bas_l[l] + d;
+        len = static_cast<uint32_t>(l);
       }
     }
-    lut[x] = ent;
+    lut[x] = len ? static_cast<uint16_t>(sorted[idx] | (len << 8)) : static_cast<uint16_t>(0);
   }
   if (e < 32) {
     reinterpret_cast<uint32_t*>(ws + kWsFirst)[e] = e <= kMaxLen ? first[e] : 0u;

@@ -91,22 +91,31 @@ __global__ __launch_bounds__(256) void hist_kernel(const uint16_t* w, int64_t n,
 
 __global__ __launch_bounds__(256) void table_kernel(const unsigned long long* counts,
                                                     binade_table* t) {
-  __shared__ unsigned long long c[256];
+  __shared__ unsigned long long pc[256];   // counts of the present exponents (any order)
+  __shared__ uint32_t pe[256];             // and those exponents
   __shared__ unsigned long long by_rank[256];
   __shared__ unsigned long long bits_k[8];
   __shared__ uint32_t n_present;
   const int e = threadIdx.x;
-  c[e] = counts[e];
+  const unsigned long long ce = counts[e];
   by_rank[e] = 0ull;
   if (e == 0) n_present = 0u;
   __syncthreads();
-  const unsigned long long ce = c[e];
-  uint32_t rank = 0;
-  for (int o = 0; o < 256; ++o) rank += (c[o] > ce || (c[o] == ce && o < e)) ? 1u : 0u;
   if (ce) {
-    atomicAdd(&n_present, 1u);
-    by_rank[rank] = ce;
+    const uint32_t slot = atomicAdd(&n_present, 1u);
+    pc[slot] = ce;
+    pe[slot] = static_cast<uint32_t>(e);
   }
+  __syncthreads();
+  const uint32_t np = n_present;
+  // rank = present exponents before e in (count desc, exponent asc) order;
+  // it depends only on the counts, not on the slots' order
+  uint32_t rank = 0;
+  for (uint32_t o = 0; o < np; ++o) {
+    const unsigned long long co = pc[o];
+    rank += (co > ce || (co == ce && pe[o] < static_cast<uint32_t>(e))) ? 1u : 0u;
+  }
+  if (ce) by_rank[rank] = ce;
   __syncthreads();
   const uint32_t n = n_present;
   t->rank_of_exp[e] = ce ? static_cast<uint16_t>(rank) : static_cast<uint16_t>(0xFFFF);
