@@ -48,8 +48,14 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build()   # compiles when the library is missing or older than its source
-            lib = ctypes.CDLL(_SO)
+            # BINADE_ORACLE_LIB: a copy of the oracle built elsewhere (the
+            # planted-mistake test runs the pins against deliberately broken
+            # copies); otherwise the library beside this file
+            path = os.environ.get("BINADE_ORACLE_LIB")
+            if not path:
+                build()   # compiles when the library is missing or older than its source
+                path = _SO
+            lib = ctypes.CDLL(path)
             P = ctypes.c_void_p
             I64 = ctypes.c_int64
             U32 = ctypes.c_uint32

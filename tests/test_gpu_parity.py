@@ -231,6 +231,10 @@ def test_order_pins_hold_on_the_device():
     _, r4 = to_r4(w)
     y = B.r4_gemv(r4, x.to(DEV)).cpu()
     assert y.view(torch.int32).tolist() == [0, 0, 0]
+    # one rounding per chain step: 2^-149 then a 2^-150 product, fused,
+    # is a tie that goes to the even 2^-148 (the oracle's pin of the fma)
+    t = 2.0 ** -148
+    assert _pin(32, [(0, 2.0 ** -74, 2.0 ** -75), (2, 2.0 ** -75, 2.0 ** -75)]) == (t, t)
 
 
 # ---------------------------------------------------------- MoE

@@ -44,6 +44,27 @@ def test_hand_derived_format1():
     assert np.array_equal(oracle.f1_decode(pk), w)
 
 
+def test_width_ties_go_to_the_smaller_width():
+    """A 128-weight tile with 8 ranks of 1, 8 of 2 and 112 of 0 costs
+    128 * 1 + 8 * 16 = 256 bits at width 1 (escape code 1: the 16 ranks
+    escape) and 128 * 2 = 256 bits at width 2 (escape code 3: none do);
+    width 3 costs 384. The tie goes to width 1: 128 code bits, all ones at
+    the 16 escapes, and the escape list holds their ranks in order."""
+    exps = np.full(128, 120, np.uint16)
+    exps[5:13] = 121          # rank 1 (count 8, the smaller exponent of the tie)
+    exps[40:48] = 125         # rank 2 (count 8)
+    w = ((exps << 7) | (np.arange(128, dtype=np.uint16) % 128)).reshape(1, 128)
+    tab = oracle.build_table(w)
+    assert list(tab["exp_of_rank"][: tab["n"]]) == [120, 121, 125]
+    pk = oracle.pack_f1(w, tab)
+    assert pk["width"].reshape(-1).tolist() == [1]
+    assert pk["code_bits"] == 128
+    ones = [p for p in range(128) if (int(pk["codes"][p >> 5]) >> (p & 31)) & 1]
+    assert ones == list(range(5, 13)) + list(range(40, 48))
+    assert pk["esc"].tolist() == [1] * 8 + [2] * 8
+    assert np.array_equal(oracle.f1_decode(pk), w)
+
+
 def _ranks(w, tab):
     rank_of = {int(e): r for r, e in enumerate(tab["exp_of_rank"][: tab["n"]])}
     return np.vectorize(lambda b: rank_of[(int(b) >> 7) & 0xFF])(w)

@@ -44,6 +44,22 @@ def test_one_hot_input_selects_a_column(K):
         assert np.array_equal(y, f32(W[:, j]))
 
 
+def test_each_chain_step_rounds_once():
+    """A chain step is one fused multiply-add: a product that falls between
+    two fp32 subnormals is rounded together with the running sum. Slot 0's
+    even chain takes 2^-74 * 2^-75 = 2^-149 (the smallest subnormal), then
+    2^-75 * 2^-75 = 2^-150: fused, 2^-149 + 2^-150 lies halfway between
+    2^-149 and 2^-148 and goes to the even 2^-148. A product rounded on its
+    own would be a tie between 0 and 2^-149, go to 0, and leave 2^-149."""
+    K = 32
+    w = np.zeros(K, np.float32)
+    x = np.zeros(K, np.float32)
+    w[0], x[0] = 2.0 ** -74, 2.0 ** -75   # columns 0 and 2: the even chain, in order
+    w[2], x[2] = 2.0 ** -75, 2.0 ** -75
+    y = oracle.gemv_replay(bf16(w).reshape(1, K), bf16(x))
+    assert y[0] == np.float32(2.0 ** -148)
+
+
 @pytest.mark.parametrize("K", [64, 3072, 8192])
 def test_small_integers_are_exact_in_any_order(K):
     rng = np.random.default_rng(K)

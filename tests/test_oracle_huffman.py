@@ -45,6 +45,19 @@ def test_hand_derived_case():
     assert np.array_equal(oracle.huff_decode(pk), w)
 
 
+def test_merge_ties_go_to_the_smaller_id():
+    """Equal weights merge the smaller id first (an exponent is its own id,
+    merged nodes take 256, 257, ...). Counts 1, 1, 2, 2 for exponents 10,
+    11, 12, 13: 10 and 11 make node 256 of weight 2; the nodes of weight 2
+    are then 12, 13 and 256, so 12 and 13 make 257, and 256 with 257 the
+    root: every length is 2. Taking the larger id first would merge 256
+    with 13 and give lengths 3, 3, 1, 2."""
+    counts = np.zeros(256, np.uint64)
+    counts[[10, 11, 12, 13]] = [1, 1, 2, 2]
+    ln = oracle.huff_lengths(counts)
+    assert {int(e): int(ln[e]) for e in np.nonzero(ln)[0]} == {10: 2, 11: 2, 12: 2, 13: 2}
+
+
 def canonical(ln):
     code, c, prev = {}, 0, 0
     for l in range(1, 32):
