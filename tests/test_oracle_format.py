@@ -303,3 +303,17 @@ def test_r4_unpack_rejects_corruption():
 def test_build_table_rejects_empty():
     with pytest.raises(oracle.OracleError):
         oracle.build_table(np.zeros(0, np.uint16))
+
+
+def test_decode_rejects_a_rank_outside_the_table():
+    """A stream whose codes are consistent with its anchors and prefixes but
+    holds a rank the table does not have (the table given to the decoder is
+    one rank short) is rejected, not decoded through a stale entry."""
+    exps = np.array([120] * 40 + [121] * 20 + [122] * 4, np.uint16)
+    w = ((exps << 7) | np.arange(64, dtype=np.uint16)).reshape(1, 64)
+    tab = oracle.build_table(w)
+    pk = oracle.pack_rice(w, tab)
+    assert np.array_equal(oracle.rice_decode(pk), w)
+    short = dict(pk, n=pk["n"] - 1)
+    with pytest.raises(oracle.OracleError):
+        oracle.rice_decode(short)

@@ -139,6 +139,26 @@ def test_corrupt_planes_are_rejected():
         oracle.f1_decode(bad)
 
 
+def test_self_consistent_streams_outside_the_format_are_rejected():
+    """Planes whose counts, anchors and prefixes all agree but which break
+    the format: a width above 8 (128 codes of 9 zero bits) and an escape
+    whose listed rank is below its escape code (width 1, escape rank 0)."""
+    exps = np.full(128, 120, np.uint16)
+    exps[7] = 121
+    w = ((exps << 7) | np.arange(128, dtype=np.uint16)).reshape(1, 128)
+    tab = oracle.build_table(w)
+    good = oracle.pack_f1(w, tab)
+    assert good["width"].reshape(-1).tolist() == [1] and good["n_f1esc"] == 1
+    wide = dict(good, width=np.array([[9]], np.uint8), codes=np.zeros(36, np.uint32),
+                code_bits=128 * 9, esc=np.zeros(0, np.uint8), n_f1esc=0,
+                anchor=np.array([0, 1152], np.uint64), f1_pre=np.array([0, 0], np.uint32))
+    with pytest.raises(oracle.OracleError):
+        oracle.f1_decode(wide)
+    low = dict(good, esc=np.array([0], np.uint8))   # code 1 at column 7 lists rank 0
+    with pytest.raises(oracle.OracleError):
+        oracle.f1_decode(low)
+
+
 def test_bits_per_weight_near_the_pages_figure():
     """About 11.27 bits per weight on the pages' models; LLM-like synthetic
     tensors land within 0.15 of it (the index adds 0.06 bits per weight)."""

@@ -117,6 +117,28 @@ MUTANTS = {
     "combine without a fused multiply-add": [
         ("acc = fmaf(weights[t * top_k + s], y[(t * top_k + s) * n + j], acc);",
          "acc = weights[t * top_k + s] * y[(t * top_k + s) * n + j] + acc;")],
+    # decoders and their checks
+    "rice decode reads the remainder most significant bit first": [
+        ("        remainder |= get_bit(rem, (uint64_t)i * (uint64_t)k + (uint64_t)j)\n                     << j;",
+         "        remainder |= get_bit(rem, (uint64_t)i * (uint64_t)k + (uint64_t)j)\n                     << (k - 1 - j);")],
+    "rice decode accepts ranks outside the table": [
+        ("      rank = (q << k) | remainder;\n      if (rank >= n) return OR_ECORRUPT;",
+         "      rank = (q << k) | remainder;")],
+    "rice decode skips the anchor check": [
+        ("        if (anchor[c] != pos || esc_pre[c] != nesc) return OR_ECORRUPT;", ";")],
+    "r4 unpack skips the escape column check": [
+        ("        if ((esc[next] & 0xFFFFu) != (uint32_t)(col % OR_CHUNK)) return OR_ECORRUPT;", ";")],
+    "r4 unpack takes the side list for nibble 14": [
+        ("      if (v < 15) {\n        e = lut16[v];", "      if (v < 14) {\n        e = lut16[v];")],
+    "format 1 decode accepts widths above 8": [
+        ("      if (wt > 8) return OR_ECORRUPT;", ";")],
+    "format 1 decode accepts escapes below the escape code": [
+        ("            if (rank < escape) return OR_ECORRUPT;", ";")],
+    "huffman decode skips the block length check": [
+        ("    if (block_len[b] != (pos - start) >> 3) return OR_ECORRUPT;", ";")],
+    "huffman decode skips the group offset check": [
+        ("    if (b % OR_HUFF_GROUP == 0 && group_off[b / OR_HUFF_GROUP] != (pos >> 3)) return OR_ECORRUPT;",
+         ";")],
     # the matrix-core step and the GEMM order
     "step window 25 bits": [("cut = Ep - 24 + OR_W_BIAS;", "cut = Ep - 25 + OR_W_BIAS;")],
     "step window 23 bits": [("cut = Ep - 24 + OR_W_BIAS;", "cut = Ep - 23 + OR_W_BIAS;")],
