@@ -127,3 +127,29 @@ def test_f1_corrupt_planes_set_status():
     bad = B.F1Planes(**{**good.__dict__, "esc_pre": good.esc_pre.clone()})
     bad.esc_pre[-1] += 1                               # R4's escape total disagrees
     assert run(bad) & B.DEV_CORRUPT_ESC
+
+
+def test_f1_self_consistent_planes_outside_the_format_set_status():
+    """Planes whose counts, anchors and prefixes all agree but which break
+    the format: a width of 9 (128 codes of 9 zero bits) and an escape whose
+    listed rank is below its escape code (width 1, rank 0 listed)."""
+    exps = np.full(128, 120, np.uint16)
+    exps[7] = 121
+    wn = ((exps << 7) | np.arange(128, dtype=np.uint16)).reshape(1, 128)
+    good = B.pack_f1(as_bf16(wn))
+    assert good.width.tolist() == [1] and good.n_f1esc == 1
+
+    def run(planes):
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        B.f1_to_r4(planes.to(DEV), status=status)
+        torch.cuda.synchronize()
+        return int(status.item())
+
+    assert run(good) == 0
+    wide = B.F1Planes(**{**good.__dict__, "width": torch.tensor([9], dtype=torch.uint8),
+                         "codes": torch.zeros(38, dtype=good.codes.dtype), "code_bits": 128 * 9,
+                         "n_f1esc": 0, "anchor": torch.tensor([0, 1152], dtype=good.anchor.dtype),
+                         "f1_pre": torch.zeros(2, dtype=good.f1_pre.dtype)})
+    assert run(wide) & B.DEV_CORRUPT_STREAM
+    low = B.F1Planes(**{**good.__dict__, "esc_rank": torch.zeros_like(good.esc_rank)})
+    assert run(low) & B.DEV_CORRUPT_STREAM

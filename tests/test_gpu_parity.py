@@ -205,6 +205,34 @@ def test_corrupt_stream_sets_status():
     assert int(status.item()) & B.DEV_CORRUPT_ESC
 
 
+def test_rank_outside_the_table_sets_status():
+    """Planes whose codes agree with their anchors and prefixes, decoded with
+    a table one rank short: the weights of the missing rank are flagged, not
+    decoded through a stale entry. A 1 x 64 tensor over three exponents (the
+    per-weight walk) and a 64 x 2080 tensor with outliers (the byte walk of
+    tables of 15 ranks or more)."""
+    exps = np.array([120] * 40 + [121] * 20 + [122] * 4, np.uint16)
+    small = torch.from_numpy((((exps << 7) | np.arange(64, dtype=np.uint16))
+                              .reshape(1, 64)).view(np.int16)).view(torch.bfloat16)
+    wide = synth.normal_bf16(synth.TensorSpec("t", 64, 2080, 0.02, 21, outlier_frac=1e-3,
+                                              outlier_scale=20.0))
+    for name, w in (("1x64", small), ("64x2080", wide)):
+        planes = B.pack_rice(w)
+        print("rank outside the table", name, "n =", planes.table.n, "k =", planes.table.k, flush=True)
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        B.rice_to_r4(planes.to(DEV), status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, name
+        short = B.Table.from_buffer_copy(planes.table)
+        short.n -= 1
+        bad = B.RicePlanes(planes.rows, planes.cols, short, planes.sm, planes.unary,
+                           planes.rem, planes.anchor, planes.esc_pre, planes.unary_bits,
+                           planes.n_esc).to(DEV)
+        B.rice_to_r4(bad, status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) & B.DEV_CORRUPT_STREAM, name
+
+
 # ---------------------------------------------------------- order pins on GPU
 BIG = 4096.0
 
