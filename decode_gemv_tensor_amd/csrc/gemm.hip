@@ -1323,6 +1323,220 @@ __global__ __launch_bounds__(kDmaThreads, 2) void gemm_dma_kernel(GemmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- R4, M <= 128, split
+// One block of 4 waves per (group of 64*NT weight rows, slice). Each wave
+// streams NT tiles of 16 R4 weight rows through registers in the MFMA
+// operand layout of the streamed kernel (lane (r, g): row r of a tile,
+// columns 32g .. 32g+31 of a super-block), rebuilt one step at a time while
+// the previous step's products run on the matrix cores. The X rows (16*MT
+// of them; rows past M repeat row M-1, never stored) go global -> LDS by
+// DMA one super-block ahead into two swizzled buffers. LDS carries X only,
+// and each X operand read feeds NT products: a super-block costs 4 KiB of
+// LDS reads per m-tile per wave, against twice that per weight row in the
+// tiled kernel, which also stages the rebuilt weights. The bf16 twin keeps
+// the tiled kernel, the faster of the two for plain weights (the same bits
+// either way: the order depends on K only).
+constexpr int kWregWaves = 4;
+
+// The MT X operands of one step (m-tiles 16 rows = 4096 bytes apart from
+// LDS byte address xa), read in one batch that completes inside the asm
+// (see dma_step_asm).
+template <int MT>
+__device__ __forceinline__ void x_read_asm(uint32_t xa, bf16x8 (&A)[MT]) {
+  static_assert(MT == 2 || MT == 4 || MT == 8, "m-tiles per block");
+  if constexpr (MT == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %2 offset:4096\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(A[0]), "=&v"(A[1])
+        : "v"(xa)
+        : "memory");
+  } else if constexpr (MT == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:4096\n\t"
+        "ds_read_b128 %2, %4 offset:8192\n\t"
+        "ds_read_b128 %3, %4 offset:12288\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(A[0]), "=&v"(A[1]), "=&v"(A[2]), "=&v"(A[3])
+        : "v"(xa)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:4096\n\t"
+        "ds_read_b128 %2, %8 offset:8192\n\t"
+        "ds_read_b128 %3, %8 offset:12288\n\t"
+        "ds_read_b128 %4, %8 offset:16384\n\t"
+        "ds_read_b128 %5, %8 offset:20480\n\t"
+        "ds_read_b128 %6, %8 offset:24576\n\t"
+        "ds_read_b128 %7, %8 offset:28672\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(A[0]), "=&v"(A[1]), "=&v"(A[2]), "=&v"(A[3]), "=&v"(A[4]), "=&v"(A[5]),
+          "=&v"(A[6]), "=&v"(A[7])
+        : "v"(xa)
+        : "memory");
+  }
+}
+
+template <int NT, int MT>
+__global__ __launch_bounds__(64 * kWregWaves, 2) void gemm_wreg_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t xt[2][16 * MT * kSB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(static_cast<int>(tid >> 6));
+  constexpr int kRows = 16 * NT * kWregWaves;   // weight rows per block
+  const int32_t S = a.slices;
+  const int64_t items = ((a.n + kRows - 1) / kRows) * S;
+  const int64_t per = (items + kXcds - 1) / kXcds;
+  const int64_t item = static_cast<int64_t>(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (item >= items) return;
+  const int64_t grp = item / S;
+  const int32_t s = static_cast<int32_t>(item - grp * S);
+  int32_t u_lo, u_hi;
+  slice_superblocks(a.k, S, s, u_lo, u_hi);
+  const int32_t nsb = a.k / kSB;
+  const int32_t tails = s == S - 1 ? (a.k - nsb * kSB) / 32 : 0;
+  uint32_t l0 = a.lut0, l1 = a.lut1, l2 = a.lut2, l3 = a.lut3;
+  asm volatile("" : "+v"(l0), "+v"(l1), "+v"(l2), "+v"(l3));
+  const Lut L{l0, l1, l2, l3};
+  const int r = lane & 15, g = lane >> 4;
+
+  // this lane's weight rows (rows past N read row N-1; never stored)
+  int64_t wrow[NT];
+  const uint8_t* ps[NT];
+  const uint8_t* pn[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    wrow[nt] = min(grp * kRows + (wave * NT + nt) * 16 + r, a.n - 1);
+    ps[nt] = a.w + wrow[nt] * a.k;
+    pn[nt] = a.nib + wrow[nt] * (a.k >> 1);
+  }
+  // X: this wave's kDma DMA pieces per super-block, rows (kDma wave + qd) * 4
+  // + lane / 16, each lane loading the piece that belongs at its slot
+  constexpr int kDma = 4 * MT / kWregWaves;
+  static_assert(kDma >= 1 && kDma * kWregWaves == 4 * MT, "X pieces per wave");
+  const int32_t xrows = static_cast<int32_t>(min(static_cast<int64_t>(16 * MT), a.m));
+  const int32_t ldx2 = static_cast<int32_t>(a.ldx) * 2;
+  const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(a.x);
+  auto x_dma = [&](int32_t u, int b) {
+    const uint8_t* src = xsrc + static_cast<int64_t>(u) * (kSB * 2);
+#pragma unroll
+    for (int qd = 0; qd < kDma; ++qd) {
+      const int R = (kDma * wave + qd) * 4 + (lane >> 4);
+      const int pc = (lane & 15) ^ (R & 7);
+      dma16(src + (min(R, xrows - 1) * ldx2 + 16 * pc), &xt[b][(kDma * wave + qd) * 4 * kSB]);
+    }
+  };
+  // two sets of weight words, used in turn (the loop is unrolled by two so
+  // that no register copy ties the sets together)
+  StreamRaw<true> qa[NT], qb[NT];
+  auto w_load = [&](int32_t u, StreamRaw<true>(&q)[NT]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) stream_load<true>(ps[nt], pn[nt], u * kSB + 32 * g, q[nt]);
+  };
+  EscTab tab[NT];
+  int32_t tcol0 = u_lo * kSB;
+  auto build_tabs = [&](int32_t c0) {
+    tcol0 = c0;
+    const int32_t c1 = min(a.k, (c0 / kEscRange + 1) * kEscRange);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) esc_tab_build(a, wrow[nt], c0, c1, tab[nt]);
+  };
+  // the weights of step j (columns c + 8j .. c + 8j + 7) of each tile
+  auto operands = [&](const StreamRaw<true>(&q)[NT], int32_t c, int j, bf16x8(&Bj)[NT]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t S[8] = {q[nt].s0.x, q[nt].s0.y, q[nt].s0.z, q[nt].s0.w,
+                             q[nt].s1.x, q[nt].s1.y, q[nt].s1.z, q[nt].s1.w};
+      const uint32_t P[4] = {q[nt].nb.x, q[nt].nb.y, q[nt].nb.z, q[nt].nb.w};
+      Bj[nt] = as_bf16x8(rebuild8_tab(a, L, make_uint2(S[2 * j], S[2 * j + 1]), P[j], wrow[nt],
+                                      c + 8 * j, tab[nt], c + 8 * j - tcol0));
+    }
+  };
+
+  floatx4 acc[MT][NT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[t][nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Super-block u from weight words qc; the next one's loads go to qn. The
+  // weights of step j + 1 are rebuilt while the products of step j run.
+  auto superblock = [&](int32_t u, const StreamRaw<true>(&qc)[NT], StreamRaw<true>(&qn)[NT]) {
+    const int b = (u - u_lo) & 1;
+    if (u != u_lo && (u * kSB) % kEscRange == 0) build_tabs(u * kSB);
+    dma_wait();      // this wave's X(u) pieces and W(u) words have landed
+    lds_barrier();   // every wave's X(u); every wave is done reading X(u-1)
+    const int32_t c = u * kSB + 32 * g;
+    bf16x8 B0[NT], B1[NT], B2[NT], B3[NT];
+    operands(qc, c, 0, B0);
+    if (u + 1 < u_hi) {   // the next super-block, in flight during the products
+      x_dma(u + 1, b ^ 1);
+      w_load(u + 1, qn);
+    }
+    auto products = [&](int j, const bf16x8(&Bj)[NT]) {
+      bf16x8 A[MT];
+      x_read_asm<MT>(lds_addr(xt[b] + swz(r, 4 * g + j)), A);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t], Bj[nt], acc[t][nt], 0, 0, 0);
+    };
+    products(0, B0);
+    operands(qc, c, 1, B1);
+    products(1, B1);
+    operands(qc, c, 2, B2);
+    products(2, B2);
+    operands(qc, c, 3, B3);
+    products(3, B3);
+  };
+
+  if (u_lo < u_hi) {
+    x_dma(u_lo, 0);
+    w_load(u_lo, qa);
+    build_tabs(u_lo * kSB);
+    int32_t u = u_lo;
+    for (; u + 1 < u_hi; u += 2) {
+      superblock(u, qa, qb);
+      superblock(u + 1, qb, qa);
+    }
+    if (u < u_hi) superblock(u, qa, qb);
+  }
+  // 32-column tail blocks (last slice): operands straight from memory
+  for (int32_t tb = 0; tb < tails; ++tb) {
+    const int32_t c0 = nsb * kSB + 32 * tb + 8 * g;
+    bf16x8 Bt[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      Bt[nt] = as_bf16x8(rebuild8(a, L, *reinterpret_cast<const uint2*>(ps[nt] + c0),
+                                  *reinterpret_cast<const uint32_t*>(pn[nt] + (c0 >> 1)),
+                                  wrow[nt], c0));
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int64_t xm = min(static_cast<int64_t>(16 * t + r), a.m - 1);
+      const bf16x8 A = as_bf16x8(*reinterpret_cast<const uint4*>(a.x + xm * a.ldx + c0));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bt[nt], acc[t][nt], 0, 0, 0);
+    }
+  }
+
+  float* part = a.part + static_cast<int64_t>(s) * a.m * a.n;
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int64_t on = grp * kRows + (wave * NT + nt) * 16 + r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t om = 16 * t + 4 * g + e;
+        if (om < a.m && on < a.n) part[om * a.n + on] = acc[t][nt][e];
+      }
+    }
+}
+
 // y[m][n] = ((p0 + p1) + p2) + ... over the S (<= 8) slice partials, in
 // slice order. Block (x, y): row y, columns 1024x .. 1024x+1023, four per
 // thread; every slice's load is issued before the adds.
@@ -1431,16 +1645,30 @@ struct Plan {
   int bm = 0;        // tiled kernel: X rows per tile
   int nj = 0;        // tiled kernel: 16-row MFMA tiles per wave along N
   bool split = false;
+  int wreg = 0;      // split with M <= 128: weight-row tiles per wave of the
+                     // register-W kernel (0: the tiled kernel)
   int64_t blocks = 0;
   int64_t part_bytes = 0;   // workspace the split needs
 };
+
+// The register-W kernel for split shapes with M <= 128 (0: the tiled kernel).
+#ifndef BINADE_GEMM_WREG
+#define BINADE_GEMM_WREG 1
+#endif
+constexpr int64_t kWregTwoTilesFrom = 384;
+
+int64_t wreg_blocks(int64_t n, int nt, int32_t S) {
+  const int64_t rows = 16 * kWregWaves * nt;   // weight rows per block
+  const int64_t items = ((n + rows - 1) / rows) * S;
+  return ((items + kXcds - 1) / kXcds) * kXcds;
+}
 
 int64_t large_blocks(int64_t m, int64_t n, int bm, int64_t per_tile) {
   const int64_t items = ((n + kBN - 1) / kBN) * ((m + bm - 1) / bm) * per_tile;
   return ((items + kXcds - 1) / kXcds) * kXcds;
 }
 
-Plan plan_for(int64_t m, int64_t n, int64_t k) {
+Plan plan_for(int64_t m, int64_t n, int64_t k, bool r4) {
   Plan p;
   const int32_t S = slices_for(k);
   if (m <= kStreamMaxM && k >= kSB) {
@@ -1475,6 +1703,11 @@ Plan plan_for(int64_t m, int64_t n, int64_t k) {
   p.split = S > 1 && tiles < kSplitBelow && m <= kSplitMaxM;
   p.blocks = large_blocks(m, n, p.bm, p.split ? S : 1);
   p.part_bytes = p.split ? static_cast<int64_t>(S) * m * n * 4 : 0;
+  if (r4 && p.split && p.bm == 128 && BINADE_GEMM_WREG) {
+    // two weight-row tiles per wave when that still gives 1.5 blocks per CU
+    p.wreg = ((n + 127) / 128) * S >= kWregTwoTilesFrom ? 2 : 1;
+    p.blocks = wreg_blocks(n, p.wreg, S);
+  }
   return p;
 }
 
@@ -1514,8 +1747,25 @@ void launch_large(const GemmArgs& a, bool split, int64_t blocks, hipStream_t str
 #define BINADE_GEMM_DMA 1
 #endif
 
+template <int NT>
+void launch_wreg(const GemmArgs& a, int64_t blocks, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>(blocks)), block(64 * kWregWaves);
+  if (a.m <= 32)
+    hipLaunchKernelGGL((gemm_wreg_kernel<NT, 2>), grid, block, 0, stream, a);
+  else if (a.m <= 64)
+    hipLaunchKernelGGL((gemm_wreg_kernel<NT, 4>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_wreg_kernel<NT, 8>), grid, block, 0, stream, a);
+}
+
 template <bool kR4>
 void launch_large_cfg(const GemmArgs& a, const Plan& p, hipStream_t stream) {
+  if constexpr (kR4) {
+    if (p.wreg != 0) {
+      p.wreg == 2 ? launch_wreg<2>(a, p.blocks, stream) : launch_wreg<1>(a, p.blocks, stream);
+      return;
+    }
+  }
   if (p.nj == 2) {
     launch_large<kR4, 128, 2>(a, p.split, p.blocks, stream);
   } else if (BINADE_GEMM_DMA && BINADE_GEMM_LARGE_BM == kDmaBM && a.ldx < (1 << 23)) {
@@ -1532,7 +1782,7 @@ void launch_large_cfg(const GemmArgs& a, const Plan& p, hipStream_t stream) {
 int32_t launch(GemmArgs a, bool r4, void* workspace, int64_t workspace_bytes,
                hipStream_t stream) {
   a.slices = slices_for(a.k);
-  Plan p = plan_for(a.m, a.n, a.k);
+  Plan p = plan_for(a.m, a.n, a.k, r4);
   if (p.blocks > 0x7FFFFFFFll) return BINADE_EUNSUPPORTED;
   if (p.smt != 0) {
     if (p.part_bytes == 0 ||
@@ -1573,7 +1823,12 @@ int32_t launch(GemmArgs a, bool r4, void* workspace, int64_t workspace_bytes,
                   !aligned16(workspace))) {
     // no room for the partials: run every slice in one block (same bits)
     p.split = false;
+    p.wreg = 0;
     p.blocks = large_blocks(a.m, a.n, p.bm, 1);
+  }
+  if (p.wreg != 0 && a.ldx >= (1 << 23)) {   // its DMA offsets are 32-bit
+    p.wreg = 0;
+    p.blocks = large_blocks(a.m, a.n, p.bm, a.slices);
   }
   a.part = p.split ? static_cast<float*>(workspace) : nullptr;
   r4 ? launch_large_cfg<true>(a, p, stream) : launch_large_cfg<false>(a, p, stream);
@@ -1668,7 +1923,7 @@ using namespace binade;
 
 extern "C" int64_t binade_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0 || k % 32 != 0 || k > (1 << 30)) return 0;
-  return plan_for(m, n, k).part_bytes;
+  return plan_for(m, n, k, true).part_bytes;   // the same for the twin
 }
 
 extern "C" int32_t binade_r4_gemm(const binade_r4* w, const uint16_t* x,
@@ -1692,7 +1947,7 @@ extern "C" int32_t binade_r4_gemm_noalloc(const binade_r4* w, const uint16_t* x,
   bool nothing = false;
   int32_t s = r4_gemm_args(w, x, m, ldx, y, ldy, y_dtype, &a, &nothing);
   if (s != BINADE_OK || nothing) return s;
-  const int64_t need = plan_for(a.m, a.n, a.k).part_bytes;
+  const int64_t need = plan_for(a.m, a.n, a.k, true).part_bytes;
   if (need > kScratchBytes) return BINADE_ENOSPACE;
   void* ws = nullptr;
   if (need > 0) {

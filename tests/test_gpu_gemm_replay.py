@@ -2,8 +2,9 @@
 bit, through the C ABI (binade_r4_gemm and its bf16-weight twin).
 
 - Whole outputs on shapes that span one step, tail blocks, one to eight
-  slices, ragged M and N, both with the split workspace and without it, fp32
-  and bf16 outputs.
+  slices, ragged M and N, every kernel the M and the workspace select
+  (streamed, small, tiled, register-W with 2, 4 and 8 X tiles, DMA-fed),
+  both with the split workspace and without it, fp32 and bf16 outputs.
 - The hand-derived step and order cases of tests/golden, run on the device.
 - Special bf16 values (all 65,536 weight patterns, subnormal and signed-zero
   activations): R4 equals its twin bit for bit, NaN positions included.
@@ -65,7 +66,8 @@ def inputs(M, N, K, dist, seed):
 
 SHAPES = [(1, 64, 32), (16, 48, 96), (17, 64, 128), (32, 80, 160), (64, 64, 1024),
           (130, 96, 1056), (128, 64, 3840), (256, 40, 4128), (16, 64, 15360),
-          (300, 40, 2080), (520, 24, 9216)]
+          (300, 40, 2080), (520, 24, 9216), (48, 200, 2080), (100, 136, 3104),
+          (20, 40, 24576)]
 
 
 @pytest.mark.parametrize("mnk", SHAPES, ids=["x".join(map(str, s)) for s in SHAPES])
