@@ -1089,6 +1089,595 @@ __global__ __launch_bounds__(256, BINADE_DECODE_MIN_WAVES) void rice_to_r4_batch
   }
 }
 
+
+// ------------------------------------------------------------ streamed path
+// The byte table walked over long spans. One wave decodes a span of
+// consecutive row-chunks, which the format keeps contiguous in weights, in
+// unary bits and in escapes, in rounds of 64 * 8 * kSpl unary bits: lane l
+// takes the round's bits [8 kSpl l, 8 kSpl (l + 1)), requested one round
+// ahead; a wave prefix sum of their one bits places its codes and a wave
+// prefix maximum of the last one bits gives the zeros carried into it; the
+// byte walk then ORs the nibbles into an LDS buffer that holds the codes not
+// yet written. Whole batches of 64 tiles leave the buffer in R4 order with
+// their remainder bits; the unfinished tiles move to its front. The span's
+// bounds, escape count and setup are paid once per span instead of once per
+// 4096 weights. Every row-chunk start inside the span is checked in the round
+// that holds its previous weight's code: the lane holding that code's one
+// bit gets the start as its limit (its escapes before it are counted), and a
+// scalar pass compares the one bit's position with the chunk's anchor and
+// the escapes before it with the chunk's escape prefix.
+#ifndef BINADE_STREAM_SPL
+#define BINADE_STREAM_SPL 8
+#endif
+constexpr int kSpl = BINADE_STREAM_SPL;            // unary bytes per lane and round
+constexpr int kSplWords = kSpl / 4;
+constexpr uint32_t kRoundBits = 64u * 8u * kSpl;   // unary bits per round
+#ifndef BINADE_STREAM_WAVES
+#define BINADE_STREAM_WAVES 4
+#endif
+constexpr int kStreamWaves = BINADE_STREAM_WAVES;  // waves per block
+// LDS per wave (words): the nibble buffer (the unfinished tile, then up to
+// one code per bit of a round, and the 64-bit OR's spill word), two escape
+// counters and the escape slots of each lane, and the remainder words of the
+// round's codes (a rare escape reads its bit there)
+constexpr int kSNibWords = 4 + static_cast<int>(kRoundBits / 8) + 4;
+constexpr int kSCtr = kSNibWords;
+constexpr int kSSlots = kSCtr + 128;
+constexpr int kSRemWords = static_cast<int>(kRoundBits / 32) + 64;
+constexpr int kSRem = kSSlots + kByteSlots * 64;
+constexpr int kSWaveWords = kSRem + kSRemWords;
+constexpr int kRemRegs = kSRemWords / 64;          // remainder words per lane and round
+constexpr int kFlushRegs = static_cast<int>(kRoundBits / 32 / 64);   // tile batches per round
+static_assert(kSpl == 8 || kSpl == 16, "two or four unary words per lane and round");
+static_assert(kSNibWords % 4 == 0, "16-byte aligned LDS regions");
+static_assert(kSRemWords % 64 == 0 && kSRemWords >= kRoundBits / 32 + 1, "remainder stage");
+static_assert(kStreamWaves * kSWaveWords * 4 + 256 * 20 <= 64 * 1024, "LDS per block");
+
+struct StreamArgs {
+  const uint32_t* unary;
+  const uint32_t* rem;
+  const uint64_t* anchor;
+  const uint32_t* esc_pre;
+  uint8_t* nib;
+  uint32_t* esc;
+  uint32_t* status;
+  uint64_t unary_words;
+  uint32_t n_esc;         // side-list entries (< 2^32)
+  uint32_t total;         // rows * cols (< 2^31)
+  uint32_t cols;          // >= 128
+  uint32_t C;             // row-chunks per row
+  uint32_t n_chunks;      // rows * C
+  uint32_t cols_recip;    // ceil(2^32 / cols)
+  uint32_t span_chunks;   // row-chunks per span
+  uint32_t n;             // ranks in the table
+  uint32_t esc_tbl;       // byte offset of rank 15's exponent from the arguments
+};
+
+// A buffer resource over bytes [base, base + bytes): loads beyond it return
+// zero and access nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_span(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// Which check of the streamed path set the status word (a debugging build
+// only; BINADE_STREAM_DEBUG adds bit 8 + site).
+__device__ __forceinline__ uint32_t stream_site(int site) {
+#ifdef BINADE_STREAM_DEBUG
+  return 1u << (8 + site);
+#else
+  (void)site;
+  return 0u;
+#endif
+}
+
+// w / cols for w < 2^31: the reciprocal's quotient is exact or one too large.
+__device__ __forceinline__ uint32_t div_cols(uint32_t w, const StreamArgs& a) {
+  uint32_t q = __umulhi(w, a.cols_recip);
+  if (q * a.cols > w) --q;
+  return q;
+}
+
+// Column of weight w inside its row-chunk.
+__device__ __forceinline__ uint32_t col_in_chunk(uint32_t w, const StreamArgs& a) {
+  return (w - div_cols(w, a) * a.cols) & (kChunk - 1u);
+}
+
+// Weight index of row-chunk c's first weight (c <= n_chunks).
+__device__ __forceinline__ uint32_t chunk_weight(uint32_t c, const StreamArgs& a) {
+  if (c >= a.n_chunks) return a.total;
+  const uint32_t row = c / a.C;
+  return row * a.cols + (c - row * a.C) * static_cast<uint32_t>(kChunk);
+}
+
+// The row-chunk starts of a span, one after the other (uniform).
+struct ChunkCursor {
+  uint32_t w;      // weight index of the start
+  uint32_t c;      // its row-chunk
+  uint32_t col;    // its column in its row
+};
+__device__ __forceinline__ void next_chunk(ChunkCursor& k, const StreamArgs& a) {
+  k.c += 1u;
+  const uint32_t step = min(static_cast<uint32_t>(kChunk), a.cols - k.col);
+  k.w += step;
+  k.col += step;
+  if (k.col == a.cols) k.col = 0u;
+}
+
+// The byte walk of one lane over its kSpl bytes (x: bit 0 first). As
+// byte_walk with k = 1, the codes indexed from the nibble buffer's start;
+// a rare escape reads its remainder bit from the staged words remw, code
+// idx's word being remw[idx / 32 + roff].
+template <bool kEmit>
+__device__ __forceinline__ void stream_walk(const uint32_t (&x)[kSplWords], int32_t c,
+                                            uint32_t sb, const uint4* lut, const uint32_t* remw,
+                                            int32_t roff, uint32_t n, uint32_t nb,
+                                            uint32_t* ctr, uint32_t* slots, uint32_t limit,
+                                            const uint8_t* table, const StreamArgs& a,
+                                            uint32_t wbase, uint32_t* dst, uint32_t& n_esc) {
+  constexpr int kGroup = 4;
+#pragma unroll
+  for (int j0 = 0; j0 < kSpl; j0 += kGroup) {
+    uint4 e[kGroup];
+#pragma unroll
+    for (int jj = 0; jj < kGroup; ++jj) {
+      const int j = j0 + jj;
+      e[jj] = lut[__builtin_amdgcn_ubfe(x[j >> 2], 8 * (j & 3), 8)];
+    }
+#pragma unroll
+    for (int jj = 0; jj < kGroup; ++jj) {
+      const int32_t t = static_cast<int32_t>(e[jj].y) + c;     // first code's q << 1
+      if (t >= 14) {
+        // rare: the first code may be an escape
+        const uint32_t idx = sb >> 2;
+        const uint32_t rb = (remw[static_cast<int32_t>(idx >> 5) + roff] >> (idx & 31u)) & 1u;
+        const uint32_t rank = static_cast<uint32_t>(t) | rb;
+        if (rank >= 15u) {
+          if (kEmit) {
+            if (rank < n)
+              dst[n_esc++] =
+                  (static_cast<uint32_t>(table[rank]) << 16) | col_in_chunk(wbase + idx, a);
+          } else {
+            const uint32_t pos = lds_add_rtn(ctr, rank < n ? 1u : kBadRank) & ~kBadRank;
+            if (pos < static_cast<uint32_t>(kByteSlots)) slots[pos * 64] = (idx << 8) | (rank & 0xFFu);
+            if (idx < limit) lds_add_rtn(ctr + 64, 1u);
+          }
+        }
+      }
+      if (!kEmit) {
+        const uint32_t v = e[jj].x | static_cast<uint32_t>(min(max(t, 0), 15));
+        const uint64_t w = static_cast<uint64_t>(v) << (sb & 31u);
+        uint32_t addr;
+        asm("v_bfe_u32 %0, %1, 5, 27\n\tv_lshl_add_u32 %0, %0, 2, %2"
+            : "=&v"(addr)
+            : "v"(sb), "v"(nb));
+        lds_or(addr, static_cast<uint32_t>(w));
+        lds_or(addr + 4u, static_cast<uint32_t>(w >> 32));
+      }
+      c = min(c + 16, static_cast<int32_t>(e[jj].w));
+      sb += e[jj].z;
+    }
+  }
+}
+
+// Nibbles of 8 weights in weight order -> R4 order (weight i in byte i % 4,
+// high nibble for i >= 4): the low nibbles come from bytes 0, 1 of n and of
+// n >> 4, the high ones from bytes 1, 2 of n >> 4 and 2, 3 of n.
+__device__ __forceinline__ uint32_t r4_order(uint32_t n) {
+  const uint32_t r = n >> 4;
+  const uint32_t lo = __builtin_amdgcn_perm(r, n, 0x05010400u);
+  const uint32_t hi = __builtin_amdgcn_perm(r, n, 0x03060205u);
+  return (lo & 0x0F0F0F0Fu) | (hi & 0xF0F0F0F0u);
+}
+
+// One tile of the nibble buffer in R4 order with its remainder word.
+__device__ __forceinline__ uint4 r4_tile(uint4 nn, uint32_t rw, const uint32_t* spread) {
+  uint4 o;
+  o.x = r4_order(nn.x) | spread[rw & 0xFFu];
+  o.y = r4_order(nn.y) | spread[(rw >> 8) & 0xFFu];
+  o.z = r4_order(nn.z) | spread[(rw >> 16) & 0xFFu];
+  o.w = r4_order(nn.w) | spread[rw >> 24];
+  return o;
+}
+
+// The uniform facts of a span.
+struct Span {
+  uint64_t A, B;        // its unary bits [A, B)
+  uint64_t R0;          // A rounded down to 64 bits: the first round's first bit
+  uint32_t W0, W1;      // its weights [W0, W1)
+  uint32_t E0, E1;      // its escapes [E0, E1)
+  uint32_t ntiles;      // (W1 - W0) / 32
+  uint32_t c0;          // its first row-chunk
+};
+
+// The state a span's rounds carry (uniform).
+struct SpanState {
+  uint32_t r;           // the round's first bit, from R0
+  int32_t prev_last;    // last one bit before the round, from the round's first bit
+  uint32_t last_one;    // one past the last one bit seen, from R0 (0: none)
+  uint32_t P;           // codes before the round
+  uint32_t T;           // first tile not yet written
+  uint32_t esc_done;    // escapes written
+  ChunkCursor next;     // the next row-chunk start to check
+};
+
+// Resources of a span: its unary words from R0 on and its remainder words.
+struct SpanRes {
+  __amdgpu_buffer_rsrc_t unary;
+  __amdgpu_buffer_rsrc_t rem;
+  uint64_t anchor;      // lane i: anchor of row-chunk c0 + i (i < span_chunks <= 64)
+  uint32_t esc_pre;     // lane i: its escape prefix
+};
+
+// The lane's two unary words of the round starting r bits after R0 (zero
+// past the span's words). The offset goes in the range-checked operand.
+__device__ __forceinline__ void round_words(const SpanRes& rs, uint32_t r, uint32_t lane_off,
+                                            uint32_t (&x)[kSplWords]) {
+  if (kSplWords == 2) {
+    const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                  rs.unary, lane_off + (r >> 3), 0, 0));
+    x[0] = v.x;
+    x[kSplWords - 1] = v.y;
+  } else {
+    const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rs.unary, lane_off + (r >> 3), 0, 0));
+    x[0] = v.x;
+    x[1] = v.y;
+    x[2 % kSplWords] = v.z;
+    x[3 % kSplWords] = v.w;
+  }
+}
+
+// The remainder word of span tile t (zero past the span).
+__device__ __forceinline__ uint32_t tile_rem(const SpanRes& rs, uint32_t t) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rs.rem, 4u * t, 0, 0);
+}
+
+// The remainder words of span tiles t0 + 64 q + lane.
+__device__ __forceinline__ void round_rems(const SpanRes& rs, uint32_t t0, uint32_t lane,
+                                           uint32_t (&r)[kRemRegs]) {
+#pragma unroll
+  for (int q = 0; q < kRemRegs; ++q) r[q] = tile_rem(rs, t0 + 64u * q + lane);
+}
+
+// Round status: go on, the span's last round is done, or corrupt planes
+// (the status word is set).
+enum : int { kRoundNext = 0, kRoundLast = 1, kRoundBad = 2 };
+
+// One round of a span. xr, rr: this round's unary and remainder words
+// (already requested); the next round's are requested into xn, rn.
+__device__ __forceinline__ int stream_round(const StreamArgs& a, const Span& sp, const SpanRes& rs,
+                                            SpanState& st, const uint32_t (&xr)[kSplWords],
+                                            uint32_t (&xn)[kSplWords],
+                                            const uint32_t (&rr)[kRemRegs],
+                                            uint32_t (&rn)[kRemRegs], const uint8_t* table,
+                                            int lane, uint32_t* lds, const uint4* lut,
+                                            const uint32_t* spread) {
+  uint32_t* nibw = lds;
+  uint32_t* ctr = lds + kSCtr + lane;
+  uint32_t* slots = lds + kSSlots + lane;
+  uint32_t* remw = lds + kSRem;
+  const uint32_t r = st.r;
+  const uint32_t T = st.T;
+  const uint32_t P = st.P;
+  const uint64_t R = sp.R0 + r;
+  const uint32_t lane_u = static_cast<uint32_t>(lane);
+  // the remainder words of the tiles written at the end of this round
+  // (requested before the next round's words, which may stay in flight)
+  uint32_t rwf[kFlushRegs];
+#pragma unroll
+  for (int q = 0; q < kFlushRegs; ++q) rwf[q] = tile_rem(rs, T + 64u * q + lane_u);
+  // the remainder words of the round's codes: span tiles P / 32 + i at remw[i]
+#pragma unroll
+  for (int q = 0; q < kRemRegs; ++q) remw[64 * q + lane] = rr[q];
+  ctr[0] = 0u;
+  ctr[64] = 0u;
+  uint32_t x[kSplWords];
+#pragma unroll
+  for (int q = 0; q < kSplWords; ++q) x[q] = xr[q];
+  const int32_t lbit = static_cast<int32_t>(8 * kSpl) * lane;   // lane's first bit, from R
+  if (R < sp.A && lane == 0) {
+    // the span's first bits sit in lane 0's words
+    const uint32_t skip = static_cast<uint32_t>(sp.A - R);        // < 64
+    x[0] &= skip >= 32u ? 0u : 0xFFFFFFFFu << skip;
+    x[1] &= skip <= 32u ? 0xFFFFFFFFu : 0xFFFFFFFFu << (skip - 32u);   // skip < 64
+  }
+  const bool last_round = R + kRoundBits >= sp.B;
+  if (last_round) {
+    // the span ends in this round: clear the bits from B on
+    const int32_t keep = static_cast<int32_t>(sp.B - R) - lbit;   // lane bits inside the span
+#pragma unroll
+    for (int q = 0; q < kSplWords; ++q) {
+      const int32_t k = keep - 32 * q;
+      x[q] &= k <= 0 ? 0u : (k >= 32 ? 0xFFFFFFFFu : (1u << k) - 1u);
+    }
+  }
+  uint32_t pc = 0;
+#pragma unroll
+  for (int q = 0; q < kSplWords; ++q) pc += __popc(x[q]);
+  // the next round's words
+  round_words(rs, r + kRoundBits, 4u * kSplWords * lane_u, xn);
+
+  // ---- where the lane's codes go and the zeros carried into it
+  const uint32_t incl = wave_inclusive_sum(pc);
+  const uint32_t n_round = lane63(incl);
+  const uint32_t s_first = P + incl - pc;          // span index of the lane's first code
+  int32_t top = 0;
+#pragma unroll
+  for (int q = 0; q < kSplWords; ++q)
+    if (x[q]) top = 32 * q + 31 - static_cast<int32_t>(__clz(x[q]));
+  const int32_t last = pc ? lbit + top : st.prev_last;
+  const int32_t mx = wave_inclusive_max(last);
+  const int32_t prev = wave_shift_up(mx, st.prev_last);
+  const int32_t c_in = (lbit - prev - 1) << 1;
+  const int32_t round_last = static_cast<int32_t>(lane63(static_cast<uint32_t>(mx)));
+  // the next round's remainder words
+  round_rems(rs, (P + n_round) >> 5, lane_u, rn);
+
+  // ---- row-chunk starts X whose previous code X - 1 ends in this round:
+  // the lane holding that code counts its escapes before X
+  uint32_t limit = 0;
+  {
+    ChunkCursor k = st.next;
+    while (k.w < sp.W1 && k.w - sp.W0 <= P + n_round) {
+      const uint32_t X = k.w - sp.W0;
+      const uint32_t L = __popcll(__ballot(incl <= X - 1u - P));   // lane holding code X - 1
+      if (lane_u == L) limit = X;
+      next_chunk(k, a);
+    }
+  }
+
+  // ---- the walk
+  const uint32_t base = 32u * T;                   // span index of the buffer's first code
+  const int32_t roff = static_cast<int32_t>(T) - static_cast<int32_t>(P >> 5);
+  const uint32_t nb = lds_address(nibw);
+  uint32_t unused = 0;
+  wave_sync();
+  // lanes without a one bit (past the span's end in its last round) would
+  // all OR into one word: they skip the walk
+  if (pc != 0u)
+    stream_walk<false>(x, c_in, 4u * (s_first - base), lut, remw, roff, a.n, nb, ctr, slots,
+                       limit != 0u ? limit - base : 0u, table, a, sp.W0 + base, nullptr, unused);
+  const uint32_t cw = ctr[0];
+  const uint32_t n_esc_lane = cw & ~kBadRank;
+  if (__any((cw & kBadRank) != 0u) || P + n_round > sp.W1 - sp.W0) {
+    flag(a.status, BINADE_DEV_CORRUPT_STREAM | stream_site(1), lane);
+    return kRoundBad;
+  }
+
+  // ---- escapes: their places in the side list
+  uint32_t before, total;
+  if (__ballot(n_esc_lane > 1u) == 0) {
+    const uint64_t has = __ballot(n_esc_lane != 0u);
+    before = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(has >> 32),
+                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(has), 0u));
+    total = __popcll(has);
+  } else {
+    const uint32_t esc_incl = wave_inclusive_sum(n_esc_lane);
+    before = esc_incl - n_esc_lane;
+    total = lane63(esc_incl);
+  }
+  if (sp.E1 - sp.E0 - st.esc_done < total) {
+    flag(a.status, BINADE_DEV_CORRUPT_ESC | stream_site(2), lane);
+    return kRoundBad;
+  }
+
+  // ---- the chunk starts of this round against their anchors and escape
+  // prefixes (scalar, from the lane holding each start's previous code)
+  {
+    const uint32_t n_before = ctr[64];
+    uint32_t bad = 0;
+    ChunkCursor k = st.next;
+    while (k.w < sp.W1 && k.w - sp.W0 <= P + n_round) {
+      const uint32_t X = k.w - sp.W0;
+      const uint32_t L = __popcll(__ballot(incl <= X - 1u - P));
+      // (readlane returns an int: widen through uint32_t)
+      const uint32_t sl = static_cast<uint32_t>(__builtin_amdgcn_readlane(s_first, L));
+      const uint32_t el = static_cast<uint32_t>(__builtin_amdgcn_readlane(before, L)) +
+                          static_cast<uint32_t>(__builtin_amdgcn_readlane(n_before, L));
+      const uint32_t ci = k.c - sp.c0;   // < span_chunks
+      const uint64_t ia =
+          (static_cast<uint64_t>(static_cast<uint32_t>(
+               __builtin_amdgcn_readlane(static_cast<uint32_t>(rs.anchor >> 32), ci))) << 32) |
+          static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<uint32_t>(rs.anchor), ci));
+      const uint32_t ie = static_cast<uint32_t>(__builtin_amdgcn_readlane(rs.esc_pre, ci));
+      // the one bit ending code X - 1: bit p of lane L's bits, with X - 1 - sl
+      // one bits below it
+      const uint64_t p = ia - 1u - (R + 8u * kSpl * L);
+      bool ok = p < 8u * kSpl;
+      uint32_t below = 0;
+#pragma unroll
+      for (int q = 0; q < kSplWords; ++q) {
+        const uint32_t wq = static_cast<uint32_t>(__builtin_amdgcn_readlane(x[q], L));
+        const uint64_t lo = 32u * q;
+        if (p >= lo + 32u) {
+          below += __popc(wq);
+        } else if (p >= lo) {
+          const uint32_t b = static_cast<uint32_t>(p - lo);
+          ok = ok && ((wq >> b) & 1u) != 0u;
+          below += __popc(wq & ((1u << b) - 1u));
+        }
+      }
+      if (!ok || below != X - 1u - sl)
+        bad |= BINADE_DEV_CORRUPT_STREAM | stream_site(12);
+      if (ie != sp.E0 + st.esc_done + el) bad |= BINADE_DEV_CORRUPT_ESC;
+      next_chunk(k, a);
+    }
+    st.next = k;
+    if (bad != 0u) {
+      flag(a.status, bad | stream_site(3), lane);
+      return kRoundBad;
+    }
+  }
+
+  if (n_esc_lane > 0u) {
+    uint32_t* dst = a.esc + (sp.E0 + st.esc_done + before);
+    if (n_esc_lane <= static_cast<uint32_t>(kByteSlots)) {
+      for (uint32_t i = 0; i < n_esc_lane; ++i) {
+        const uint32_t ent = slots[i * 64];
+        dst[i] = (static_cast<uint32_t>(table[ent & 0xFFu]) << 16) |
+                 col_in_chunk(sp.W0 + base + (ent >> 8), a);
+      }
+    } else {
+      uint32_t n2 = 0;
+      stream_walk<true>(x, c_in, 4u * (s_first - base), lut, remw, roff, a.n, 0u, nullptr,
+                        nullptr, 0u, table, a, sp.W0 + base, dst, n2);
+    }
+  }
+  st.esc_done += total;
+  st.P = P + n_round;
+  if (n_round > 0u) st.last_one = r + static_cast<uint32_t>(round_last) + 1u;
+  st.prev_last = round_last - static_cast<int32_t>(kRoundBits);
+  st.r = r + kRoundBits;
+  wave_sync();
+
+  // ---- the finished tiles to R4 (at most kRoundBits / 32: a round adds at
+  // most one code per bit to an unfinished tile); the unfinished one to the
+  // front
+  const uint32_t done = (st.P >> 5) - T;
+  uint8_t* out = a.nib + (sp.W0 >> 1) + 16ull * T;
+#pragma unroll
+  for (int q = 0; q < kFlushRegs; ++q) {
+    if (64u * q >= done) break;   // uniform
+    if (64u * q + lane_u < done)
+      *reinterpret_cast<uint4*>(out + 16u * (64u * q + lane_u)) =
+          r4_tile(reinterpret_cast<const uint4*>(nibw)[64 * q + lane], rwf[q], spread);
+  }
+  st.T = T + done;
+  const uint4 cv = reinterpret_cast<const uint4*>(nibw)[done];
+  wave_sync();
+  // the next round ORs into zeros past the unfinished tile
+  if (lane == 0) reinterpret_cast<uint4*>(nibw)[0] = cv;
+#pragma unroll
+  for (int q = 0; q < (kSNibWords / 4 - 1 + 63) / 64; ++q)
+    if (1 + q * 64 + lane < kSNibWords / 4)
+      reinterpret_cast<uint4*>(nibw)[1 + q * 64 + lane] = make_uint4(0u, 0u, 0u, 0u);
+  wave_sync();
+  return last_round ? kRoundLast : kRoundNext;
+}
+
+__device__ void stream_span(const StreamArgs& a, const uint8_t* table, const Span& sp,
+                            int lane, uint32_t* lds, const uint4* lut,
+                            const uint32_t* spread) {
+  const uint32_t nw = sp.W1 - sp.W0;                 // codes of the span, a multiple of 32
+  // a valid code has at most 128 bits (rank <= 255 at k = 1)
+  if (sp.B < sp.A + nw || sp.B > a.unary_words * 32ull || sp.B - sp.A > 128ull * nw) {
+    flag(a.status, BINADE_DEV_CORRUPT_STREAM | stream_site(4), lane);
+    return;
+  }
+  if (sp.E1 < sp.E0 || sp.E1 > a.n_esc) {
+    flag(a.status, BINADE_DEV_CORRUPT_ESC | stream_site(5), lane);
+    return;
+  }
+  uint32_t* nibw = lds;
+#pragma unroll
+  for (int q = 0; q < (kSNibWords / 4 + 63) / 64; ++q)
+    if (q * 64 + lane < kSNibWords / 4)
+      reinterpret_cast<uint4*>(nibw)[q * 64 + lane] = make_uint4(0u, 0u, 0u, 0u);
+
+  SpanRes rs;
+  const uint64_t wR = sp.R0 >> 5;
+  rs.unary = buffer_span(a.unary + wR, static_cast<uint32_t>(4u * (((sp.B + 31u) >> 5) - wR)));
+  rs.rem = buffer_span(a.rem + (sp.W0 >> 5), 4u * sp.ntiles);
+  {
+    const uint32_t i = min(static_cast<uint32_t>(lane), a.span_chunks - 1u);
+    const uint32_t c = min(sp.c0 + i, a.n_chunks);
+    rs.anchor = a.anchor[c];
+    rs.esc_pre = a.esc_pre[c];
+  }
+  SpanState st;
+  st.r = 0;
+  st.prev_last = static_cast<int32_t>(sp.A - sp.R0) - 1;   // the bit before the span
+  st.last_one = 0;
+  st.P = 0;
+  st.T = 0;
+  st.esc_done = 0;
+  st.next.c = sp.c0;
+  st.next.w = sp.W0;
+  st.next.col = sp.W0 - div_cols(sp.W0, a) * a.cols;
+  next_chunk(st.next, a);
+  // two sets of word registers in turn: a round reads one while the next
+  // round's words arrive in the other (no copy of a register in flight)
+  const uint32_t lane_u = static_cast<uint32_t>(lane);
+  uint32_t xa[kSplWords], xb[kSplWords], ra[kRemRegs], rb[kRemRegs];
+  round_words(rs, 0u, 4u * kSplWords * lane_u, xa);
+  round_rems(rs, 0u, lane_u, ra);
+  int s;
+  while (true) {
+    s = stream_round(a, sp, rs, st, xa, xb, ra, rb, table, lane, lds, lut, spread);
+    if (s != kRoundNext) break;
+    s = stream_round(a, sp, rs, st, xb, xa, rb, ra, table, lane, lds, lut, spread);
+    if (s != kRoundNext) break;
+  }
+  if (s == kRoundBad) return;
+  if (st.P != nw || sp.R0 + st.last_one != sp.B) {
+    flag(a.status, BINADE_DEV_CORRUPT_STREAM | stream_site(6), lane);
+    return;
+  }
+  if (st.esc_done != sp.E1 - sp.E0) {
+    flag(a.status, BINADE_DEV_CORRUPT_ESC | stream_site(7), lane);
+    return;
+  }
+  // the last tiles (fewer than 64)
+  const uint32_t t = st.T + lane_u;
+  if (t < sp.ntiles) {
+    const uint32_t rw = tile_rem(rs, t);
+    *reinterpret_cast<uint4*>(a.nib + (sp.W0 >> 1) + 16ull * t) =
+        r4_tile(reinterpret_cast<const uint4*>(nibw)[lane], rw, spread);
+  }
+}
+
+struct StreamBatch {
+  StreamArgs item[kMaxDecodeBatch];
+  uint32_t first_job[kMaxDecodeBatch + 1];
+  int32_t count;
+  uint8_t pool[kEscPool];
+};
+static_assert(sizeof(StreamBatch) <= 4096, "kernel arguments of one streamed launch");
+
+// One wave per span (span s of tensor i is wave first_job[i] + s).
+__global__ __launch_bounds__(64 * kStreamWaves) void rice_stream_kernel(StreamBatch b) {
+  __shared__ __align__(16) uint32_t lds[kStreamWaves][kSWaveWords];
+  __shared__ uint4 lut[256];
+  __shared__ uint32_t spread[256];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t g = uniform(blockIdx.x * kStreamWaves + static_cast<uint32_t>(wave));
+  const bool live = g < b.first_job[b.count];
+  int i = 0;
+#pragma unroll
+  for (int t = 1; t < kMaxDecodeBatch; ++t)
+    if (t < b.count && g >= b.first_job[t]) i = t;
+  i = uniform(i);
+  const size_t off = offsetof(StreamBatch, item) + static_cast<size_t>(i) * sizeof(StreamArgs);
+  const char* kp = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+  const StreamArgs a = *(const StreamArgs*)(kp + off);   // uniform: held in SGPRs
+  const uint8_t* table = (const uint8_t*)kp + a.esc_tbl - 15;
+  Span sp{};
+  if (live) {
+    const uint32_t c0 = (g - b.first_job[i]) * a.span_chunks;
+    const uint32_t c1 = min(c0 + a.span_chunks, a.n_chunks);
+    sp.A = uniform64(static_cast<int64_t>(a.anchor[c0]));
+    sp.B = uniform64(static_cast<int64_t>(a.anchor[c1]));
+    sp.E0 = uniform(a.esc_pre[c0]);
+    sp.E1 = uniform(a.esc_pre[c1]);
+    sp.R0 = sp.A & ~63ull;
+    sp.W0 = chunk_weight(c0, a);
+    sp.W1 = chunk_weight(c1, a);
+    sp.ntiles = (sp.W1 - sp.W0) >> 5;
+    sp.c0 = c0;
+  }
+  for (uint32_t t = threadIdx.x; t < 512u; t += 64u * kStreamWaves) {
+    if (t < 256u)
+      lut[t] = *reinterpret_cast<const uint4*>(kByteTables.lut[t]);
+    else
+      spread[t - 256u] = kByteTables.spread[t - 256u];
+  }
+  __syncthreads();
+  if (!live) return;
+  stream_span(a, table, sp, lane, lds[wave], lut, spread);
+}
+
 }  // namespace
 }  // namespace binade
 
@@ -1182,6 +1771,54 @@ int32_t launch_batch(const RiceBatch& b, hipStream_t stream) {
   return launch_status();
 }
 
+int32_t launch_stream(const StreamBatch& b, hipStream_t stream) {
+  const uint32_t total = b.first_job[b.count];
+  if (total == 0) return BINADE_OK;
+  const int64_t blocks = (static_cast<int64_t>(total) + kStreamWaves - 1) / kStreamWaves;
+  hipLaunchKernelGGL(rice_stream_kernel, dim3(static_cast<uint32_t>(blocks)),
+                     dim3(64 * kStreamWaves), 0, stream, b);
+  return launch_status();
+}
+
+#ifndef BINADE_STREAM_SPAN
+#define BINADE_STREAM_SPAN 16384
+#endif
+
+// The streamed path takes tensors of the byte-table kind (Rice k = 1, a table
+// of at least 15 ranks) whose row-chunk starts are at least 128 weights apart
+// and whose weight indices fit 31 bits. Fills its arguments from a checked
+// request and returns the span count.
+int64_t prepare_stream(const binade_rice* in, const RiceArgs& r, StreamArgs& s) {
+#ifdef BINADE_NO_STREAM
+  return 0;
+#endif
+  // rows shorter than 1024 weights start a chunk every few hundred codes,
+  // which the per-job kernel checks more cheaply
+  if (in->k != 1 || in->n < 15 || in->cols < 1024) return 0;
+  const int64_t tail = in->cols % BINADE_CHUNK;
+  if (tail != 0 && tail < 128) return 0;
+  if (in->rows * in->cols >= (1ll << 31) || in->unary_words < 1) return 0;
+  s = StreamArgs{};
+  s.unary = r.unary;
+  s.rem = r.rem;
+  s.anchor = r.anchor;
+  s.esc_pre = r.esc_pre;
+  s.nib = r.nib;
+  s.esc = r.esc;
+  s.status = r.status;
+  s.unary_words = r.unary_words;
+  s.n_esc = static_cast<uint32_t>(r.n_esc);
+  s.total = static_cast<uint32_t>(in->rows * in->cols);
+  s.cols = static_cast<uint32_t>(in->cols);
+  s.C = r.chunks_per_row;
+  s.n_chunks = static_cast<uint32_t>(r.n_chunks);
+  s.cols_recip = static_cast<uint32_t>(((1ull << 32) + s.cols - 1) / s.cols);
+  const int64_t per = s.C > 1 ? BINADE_STREAM_SPAN / BINADE_CHUNK : BINADE_STREAM_SPAN / in->cols;
+  s.span_chunks = static_cast<uint32_t>(per > 64 ? 64 : per > 1 ? per : 1);
+  s.n = r.n;
+  return (r.n_chunks + s.span_chunks - 1) / s.span_chunks;
+}
+
 }  // namespace
 
 extern "C" int32_t binade_rice_to_r4(const binade_rice* in, binade_r4* out,
@@ -1194,17 +1831,43 @@ extern "C" int32_t binade_rice_to_r4_batch(const binade_rice* in, binade_r4* out
                                            void* stream) {
   if (count < 0 || (count > 0 && (in == nullptr || out == nullptr))) return BINADE_EINVAL;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  // two launches fill side by side: the streamed kernel's tensors and the
+  // job kernel's; each launch holds up to 16 tensors, their escape exponents
+  // and fewer than 2^31 waves
   RiceBatch b{};
-  int n = 0;
-  uint64_t jobs = 0;
-  uint32_t pool = 0;   // bytes of the escape pool in use
+  StreamBatch sbat{};
+  int n = 0, sn = 0;
+  uint64_t jobs = 0, spans = 0;
+  uint32_t pool = 0, spool = 0;   // bytes of the escape pools in use
   for (int32_t i = 0; i < count; ++i) {
     RiceArgs a;
     const int64_t nj = prepare_decode(&in[i], &out[i], dev_status, a);
     if (nj < 0) return static_cast<int32_t>(nj);
     const uint32_t esc_bytes = in[i].n > 15 ? in[i].n - 15 : 0;   // <= 241
-    // a launch holds up to 16 tensors, their escape exponents and fewer
-    // than 2^31 jobs
+    StreamArgs sa;
+    const int64_t ns = prepare_stream(&in[i], a, sa);
+    if (ns > 0) {
+      if (sn == kMaxDecodeBatch || spool + esc_bytes > static_cast<uint32_t>(kEscPool) ||
+          spans + static_cast<uint64_t>(ns) >= (1ull << 31)) {
+        sbat.first_job[sn] = static_cast<uint32_t>(spans);
+        sbat.count = sn;
+        const int32_t s = launch_stream(sbat, st);
+        if (s != BINADE_OK) return s;
+        sbat = StreamBatch{};
+        sn = 0;
+        spans = 0;
+        spool = 0;
+      }
+      if (static_cast<uint64_t>(ns) >= (1ull << 31)) return BINADE_EUNSUPPORTED;
+      for (uint32_t r = 0; r < esc_bytes; ++r) sbat.pool[spool + r] = in[i].exp_of_rank[15 + r];
+      sa.esc_tbl = static_cast<uint32_t>(offsetof(StreamBatch, pool)) + spool;
+      spool += esc_bytes;
+      sbat.item[sn] = sa;
+      sbat.first_job[sn] = static_cast<uint32_t>(spans);
+      spans += static_cast<uint64_t>(ns);
+      ++sn;
+      continue;
+    }
     if (n == kMaxDecodeBatch || pool + esc_bytes > static_cast<uint32_t>(kEscPool) ||
         jobs + static_cast<uint64_t>(nj) >= (1ull << 31)) {
       b.first_job[n] = static_cast<uint32_t>(jobs);
@@ -1228,7 +1891,13 @@ extern "C" int32_t binade_rice_to_r4_batch(const binade_rice* in, binade_r4* out
   if (n > 0) {
     b.first_job[n] = static_cast<uint32_t>(jobs);
     b.count = n;
-    return launch_batch(b, st);
+    const int32_t s = launch_batch(b, st);
+    if (s != BINADE_OK) return s;
+  }
+  if (sn > 0) {
+    sbat.first_job[sn] = static_cast<uint32_t>(spans);
+    sbat.count = sn;
+    return launch_stream(sbat, st);
   }
   return BINADE_OK;
 }

@@ -233,6 +233,77 @@ def test_rank_outside_the_table_sets_status():
         assert int(status.item()) & B.DEV_CORRUPT_STREAM, name
 
 
+def _wide_exponents(rows, cols, seed, spread_frac):
+    """N(0, 0.02) with a fraction of the weights given exponents spread over
+    2^-100 .. 2^100 (a table of about 200 ranks, many escapes)."""
+    g = torch.Generator().manual_seed(seed)
+    w = torch.randn(rows, cols, generator=g) * 0.02
+    pick = torch.rand(rows, cols, generator=g) < spread_frac
+    e = torch.randint(-100, 100, (rows, cols), generator=g).to(torch.float32)
+    return torch.where(pick, w.sign() * torch.exp2(e), w).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("rows,cols", [(64, 3072), (96, 256), (23, 15360)])
+def test_streamed_decode_with_dense_escapes(rows, cols):
+    """Rice k = 1 with 2% of the weights far from the bulk: codes of up to 100
+    unary bits cross lane and round boundaries, and many 64-bit lane windows
+    hold three or more escapes (written by a second walk)."""
+    w = _wide_exponents(rows, cols, 31 + cols, 0.02)
+    wn = bits_np(w)
+    planes = B.pack_rice(w)
+    assert planes.k == 1 and planes.table.n >= 15
+    ref = oracle.make_r4(wn, oracle.build_table(wn))
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    r4 = B.rice_to_r4(planes.to(DEV), status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert r4.n_esc == ref["n_esc"]
+    assert np.array_equal(r4.nib.cpu().numpy(), ref["nib"].reshape(-1))
+    assert np.array_equal(r4.esc[: r4.n_esc].cpu().numpy().view(np.uint32), ref["esc"])
+    assert np.array_equal(bits_np(B.unpack(r4)), wn)
+
+
+def _replace(planes, **kw):
+    f = dict(rows=planes.rows, cols=planes.cols, table=planes.table, sm=planes.sm,
+             unary=planes.unary, rem=planes.rem, anchor=planes.anchor, esc_pre=planes.esc_pre,
+             unary_bits=planes.unary_bits, n_esc=planes.n_esc)
+    f.update(kw)
+    return B.RicePlanes(f["rows"], f["cols"], f["table"], f["sm"], f["unary"], f["rem"],
+                        f["anchor"], f["esc_pre"], f["unary_bits"], f["n_esc"])
+
+
+@pytest.mark.parametrize("chunk", [1, 4, 9])
+def test_streamed_decode_checks_every_chunk_start(chunk):
+    """A 64 x 3072 tensor (two row-chunks per row, several per decode span):
+    an escape prefix one too large, an anchor one bit late and a flipped
+    unary bit, at a chunk inside a span (1, 9) and at a span's first chunk
+    (4), each set the status word."""
+    w = _wide_exponents(64, 3072, 77, 0.005)
+    planes = B.pack_rice(w)
+    assert planes.k == 1 and planes.table.n >= 15
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.rice_to_r4(planes.to(DEV), status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    esc_pre = planes.esc_pre.clone()
+    esc_pre[chunk:] += 1
+    n_esc = planes.n_esc + 1
+    cases = {"escape prefix": _replace(planes, esc_pre=esc_pre, n_esc=n_esc)}
+    anchor = planes.anchor.clone()
+    anchor[chunk] += 1
+    cases["anchor"] = _replace(planes, anchor=anchor)
+    unary = planes.unary.clone()
+    word = int(planes.anchor[chunk].item()) // 32 + 3
+    unary[word] ^= 1 << 9
+    cases["unary bit"] = _replace(planes, unary=unary)
+    for name, bad in cases.items():
+        print("streamed decode corruption", name, "chunk", chunk, flush=True)
+        status.zero_()
+        r4 = B.rice_to_r4(bad.to(DEV), status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) & (B.DEV_CORRUPT_STREAM | B.DEV_CORRUPT_ESC), name
+
+
 # ---------------------------------------------------------- order pins on GPU
 BIG = 4096.0
 
