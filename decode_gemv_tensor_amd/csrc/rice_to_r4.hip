@@ -1123,14 +1123,14 @@ constexpr int kStreamWaves = BINADE_STREAM_WAVES;  // waves per block
 constexpr int kSNibWords = 4 + static_cast<int>(kRoundBits / 8) + 4;
 constexpr int kSCtr = kSNibWords;
 constexpr int kSSlots = kSCtr + 128;
-constexpr int kSRemWords = static_cast<int>(kRoundBits / 32) + 64;
+constexpr int kSRemWords = static_cast<int>(kRoundBits / 32) + 8;
 constexpr int kSRem = kSSlots + kByteSlots * 64;
 constexpr int kSWaveWords = kSRem + kSRemWords;
-constexpr int kRemRegs = kSRemWords / 64;          // remainder words per lane and round
+constexpr int kRemRegs = (kSRemWords + 63) / 64;   // remainder words per lane and round
 constexpr int kFlushRegs = static_cast<int>(kRoundBits / 32 / 64);   // tile batches per round
 static_assert(kSpl == 8 || kSpl == 16, "two or four unary words per lane and round");
 static_assert(kSNibWords % 4 == 0, "16-byte aligned LDS regions");
-static_assert(kSRemWords % 64 == 0 && kSRemWords >= kRoundBits / 32 + 1, "remainder stage");
+static_assert(kSRemWords % 8 == 0 && kSRemWords >= kRoundBits / 32 + 1, "remainder stage");
 static_assert(kStreamWaves * kSWaveWords * 4 + 256 * 20 <= 64 * 1024, "LDS per block");
 
 struct StreamArgs {
@@ -1362,14 +1362,13 @@ __device__ __forceinline__ int stream_round(const StreamArgs& a, const Span& sp,
   const uint32_t P = st.P;
   const uint64_t R = sp.R0 + r;
   const uint32_t lane_u = static_cast<uint32_t>(lane);
-  // the remainder words of the tiles written at the end of this round
-  // (requested before the next round's words, which may stay in flight)
-  uint32_t rwf[kFlushRegs];
+  // the remainder words of the round's codes: span tiles T + i at remw[i]
+  // (T = P / 32: only the unfinished tile is carried from round to round).
+  // A rare escape reads its bit there, and the tiles written at the end of
+  // the round take their remainder words from there.
 #pragma unroll
-  for (int q = 0; q < kFlushRegs; ++q) rwf[q] = tile_rem(rs, T + 64u * q + lane_u);
-  // the remainder words of the round's codes: span tiles P / 32 + i at remw[i]
-#pragma unroll
-  for (int q = 0; q < kRemRegs; ++q) remw[64 * q + lane] = rr[q];
+  for (int q = 0; q < kRemRegs; ++q)
+    if (64 * q + lane < kSRemWords) remw[64 * q + lane] = rr[q];
   ctr[0] = 0u;
   ctr[64] = 0u;
   uint32_t x[kSplWords];
@@ -1429,7 +1428,7 @@ __device__ __forceinline__ int stream_round(const StreamArgs& a, const Span& sp,
 
   // ---- the walk
   const uint32_t base = 32u * T;                   // span index of the buffer's first code
-  const int32_t roff = static_cast<int32_t>(T) - static_cast<int32_t>(P >> 5);
+  const int32_t roff = 0;   // T == P / 32
   const uint32_t nb = lds_address(nibw);
   uint32_t unused = 0;
   wave_sync();
@@ -1541,7 +1540,7 @@ __device__ __forceinline__ int stream_round(const StreamArgs& a, const Span& sp,
     if (64u * q >= done) break;   // uniform
     if (64u * q + lane_u < done)
       *reinterpret_cast<uint4*>(out + 16u * (64u * q + lane_u)) =
-          r4_tile(reinterpret_cast<const uint4*>(nibw)[64 * q + lane], rwf[q], spread);
+          r4_tile(reinterpret_cast<const uint4*>(nibw)[64 * q + lane], remw[64 * q + lane], spread);
   }
   st.T = T + done;
   const uint4 cv = reinterpret_cast<const uint4*>(nibw)[done];
