@@ -1788,9 +1788,6 @@ int32_t launch_stream(const StreamBatch& b, hipStream_t stream) {
 // and whose weight indices fit 31 bits. Fills its arguments from a checked
 // request and returns the span count.
 int64_t prepare_stream(const binade_rice* in, const RiceArgs& r, StreamArgs& s) {
-#ifdef BINADE_NO_STREAM
-  return 0;
-#endif
   // rows shorter than 1024 weights start a chunk every few hundred codes,
   // which the per-job kernel checks more cheaply
   if (in->k != 1 || in->n < 15 || in->cols < 1024) return 0;
