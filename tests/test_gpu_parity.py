@@ -61,11 +61,16 @@ GEMV_SHAPES = [(1024, 1024, 0.02, 0, 0.0, 1.0, 16, 50.0),   # single 1024 tensor
                (4100, 256, 0.015, 6, 0.0, 1.0, 0, 1.0)]       # short rows, many
 
 
-# Decode jobs: two row-chunks of a row, or 2 * (2048 / cols) short rows.
-# Edge cases of that mapping: rows of exactly one chunk, a 32-column second
-# chunk, an odd chunk count, 32 short rows per job (31 inner chunk starts),
-# one row per run, and rows too short for the byte-table path.
-DECODE_SHAPES = [(9, 2048, 0.02, 7, 1e-3, 20.0, 0, 1.0),
+# Decode jobs: two row-chunks of a row, or 2 * (2048 / cols) short rows;
+# streamed spans: 8 row-chunks (rows longer than a chunk) or 16384 / cols
+# rows. Edge cases of those mappings: a one-row tensor, rows of exactly one
+# chunk, a 32-column second chunk, an odd chunk count, spans that end inside
+# a row, 32 short rows per job (31 inner chunk starts), one row per run, and
+# rows too short for the byte-table path.
+DECODE_SHAPES = [(1, 1024, 0.02, 13, 1e-3, 20.0, 0, 1.0),      # one row: a span of one round
+                 (3, 1152, 0.02, 14, 5e-3, 1e3, 0, 1.0),      # rows of 1152: one chunk each
+                 (2, 17408, 0.015, 15, 1e-3, 20.0, 0, 1.0),   # 9 chunks per row, spans across rows
+                 (9, 2048, 0.02, 7, 1e-3, 20.0, 0, 1.0),
                  (7, 2080, 0.02, 8, 2e-3, 1e3, 0, 1.0),
                  (11, 6144, 0.02, 9, 1e-3, 20.0, 0, 1.0),
                  (130, 128, 0.02, 10, 5e-3, 1e3, 0, 1.0),
