@@ -86,6 +86,11 @@ class Timer:
         e1 = torch.cuda.Event(enable_timing=True)
         e1.record(self.stream)
         self.pairs.setdefault(key, []).append((e0, e1))
+        return e1
+
+    def add(self, key, e0, e1):
+        """Another interval between two events already recorded."""
+        self.pairs.setdefault(key, []).append((e0, e1))
 
     def total_ms(self, key):
         return sum(a.elapsed_time(b) for a, b in self.pairs.get(key, []))
@@ -902,22 +907,23 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     torch.cuda.synchronize()
+    # One event between consecutive launches: launch i's interval runs from
+    # the event before it to the event after it, so the intervals of a phase
+    # add up to the phase and no launch waits behind a second event.
     with torch.cuda.stream(stream):
         for _ in range(args.steps):
             s0 = timer.start()
-            p0 = timer.start()
+            e = s0
             for gi in range(len(dec_groups)):
-                e = timer.start()
                 decode(gi)
-                timer.stop("decode", e)
-            timer.stop("decode_phase", p0)
-            p1 = timer.start()
+                e = timer.stop("decode", e)
+            timer.add("decode_phase", s0, e)
+            p1 = e
             for gi in range(len(gemv_args)):
-                e = timer.start()
                 gemv(gi)
-                timer.stop("gemv", e)
-            timer.stop("gemv_phase", p1)
-            timer.stop("step", s0)
+                e = timer.stop("gemv", e)
+            timer.add("gemv_phase", p1, e)
+            timer.add("step", s0, e)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     assert int(status.item()) == 0
