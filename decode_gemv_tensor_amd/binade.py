@@ -35,7 +35,8 @@ EXPORTS = ["binade_status_str", "binade_last_hip_error", "binade_build_table",
            "binade_bf16_gemv_rows", "binade_moe_silu_mul", "binade_moe_combine",
            "binade_build_table_gpu", "binade_pack_gpu_workspace_bytes", "binade_pack_rice_gpu",
            "binade_huff_lengths", "binade_huff_pack", "binade_huff_workspace_bytes",
-           "binade_huff_decode"]
+           "binade_huff_decode", "binade_rice_plan_bytes", "binade_rice_to_r4_plan",
+           "binade_rice_to_r4_run"]
 
 
 class Table(ctypes.Structure):
@@ -131,12 +132,16 @@ def lib() -> ctypes.CDLL:
             L.binade_pack_gpu_workspace_bytes.restype = I64
             L.binade_huff_workspace_bytes.argtypes = []
             L.binade_huff_workspace_bytes.restype = I64
+            L.binade_rice_plan_bytes.argtypes = [I32]
+            L.binade_rice_plan_bytes.restype = I64
             sig = {
                 "binade_build_table": [P, I64, P],
                 "binade_sizes_of": [P, I64, I64, P],
                 "binade_pack_rice": [P, I64, I64, P, P],
                 "binade_rice_to_r4": [P, P, P, P],
                 "binade_rice_to_r4_batch": [P, P, I32, P, P],
+                "binade_rice_to_r4_plan": [P, P, I32, P, I64],
+                "binade_rice_to_r4_run": [P, P, P, P],
                 "binade_f1_sizes_of": [I64, I64, P],
                 "binade_pack_f1": [P, I64, I64, P, P],
                 "binade_f1_to_r4": [P, P, P, P],
@@ -600,20 +605,23 @@ def f1_to_r4(planes: F1Planes, status: torch.Tensor | None = None,
                     planes.esc_pre, esc, planes.n_esc)
 
 
+def _r4_out(p) -> "R4Tensor":
+    """Device buffers for the R4 form of format 2 tensor p."""
+    dev = p.sm.device
+    return R4Tensor(p.rows, p.cols, bytes(16), p.sm,
+                    torch.empty(p.rows * p.cols // 2, dtype=torch.uint8, device=dev),
+                    p.esc_pre,
+                    torch.empty(max(p.n_esc, 1), dtype=torch.int32, device=dev),
+                    p.n_esc)
+
+
 @_on_stream
 def rice_to_r4_batch(planes: list, status: torch.Tensor | None = None,
                      stream=None, outs: list | None = None) -> list:
     """binade_rice_to_r4_batch: decode several tensors (up to 16 per launch)."""
     n = len(planes)
     if outs is None:
-        outs = []
-        for p in planes:
-            dev = p.sm.device
-            outs.append(R4Tensor(p.rows, p.cols, bytes(16), p.sm,
-                                 torch.empty(p.rows * p.cols // 2, dtype=torch.uint8, device=dev),
-                                 p.esc_pre,
-                                 torch.empty(max(p.n_esc, 1), dtype=torch.int32, device=dev),
-                                 p.n_esc))
+        outs = [_r4_out(p) for p in planes]
     din = (RiceDesc * n)(*[p.desc() for p in planes])
     dout = (R4Desc * n)()
     for i, o in enumerate(outs):
@@ -623,6 +631,38 @@ def rice_to_r4_batch(planes: list, status: torch.Tensor | None = None,
     for i, o in enumerate(outs):
         o.lut = bytes(dout[i].lut)
     return outs
+
+
+class RicePlan:
+    """A decode plan over format 2 tensors (binade_rice_to_r4_plan): their R4
+    outputs, the plan's host bytes and its copy in device memory. run()
+    decodes every tensor in one launch (binade_rice_to_r4_run). The plan
+    keeps references to the planes and outputs whose addresses it holds."""
+
+    def __init__(self, planes: list, outs: list | None = None):
+        n = len(planes)
+        self.planes = list(planes)
+        self.outs = [_r4_out(p) for p in planes] if outs is None else list(outs)
+        din = (RiceDesc * n)(*[p.desc() for p in planes])
+        dout = (R4Desc * n)()
+        for i, o in enumerate(self.outs):
+            dout[i].nib = o.nib.data_ptr()
+            dout[i].esc = o.esc.data_ptr()
+        nbytes = lib().binade_rice_plan_bytes(n)
+        if nbytes < 0:
+            raise BinadeError("binade_rice_plan_bytes", int(nbytes), 0)
+        self.host = (ctypes.c_uint8 * nbytes)()
+        _call("binade_rice_to_r4_plan", din, dout, n, self.host, nbytes)
+        for i, o in enumerate(self.outs):
+            o.lut = bytes(dout[i].lut)
+        device = planes[0].sm.device if n else torch.device("cpu")   # an empty plan never launches
+        self.dev = torch.frombuffer(bytearray(self.host), dtype=torch.uint8).to(device)
+
+    @_on_stream
+    def run(self, status: torch.Tensor | None = None, stream=None) -> list:
+        _call("binade_rice_to_r4_run", self.host, ctypes.c_void_p(self.dev.data_ptr()),
+              _ptr(status), _stream(stream))
+        return self.outs
 
 
 @_on_stream

@@ -49,6 +49,8 @@
 //  lane with more escapes writes them in a second, exact pass.
 #include <hip/hip_runtime.h>
 
+#include <cstring>
+
 #include "binade.h"
 #include "device_common.h"
 
@@ -1634,27 +1636,17 @@ struct StreamBatch {
 };
 static_assert(sizeof(StreamBatch) <= 4096, "kernel arguments of one streamed launch");
 
-// One wave per span (span s of tensor i is wave first_job[i] + s).
-__global__ __launch_bounds__(64 * kStreamWaves) void rice_stream_kernel(StreamBatch b) {
-  __shared__ __align__(16) uint32_t lds[kStreamWaves][kSWaveWords];
-  __shared__ uint4 lut[256];
-  __shared__ uint32_t spread[256];
+// The work of one wave: span `span` of the tensor a (when live), after the
+// block has put the byte tables in LDS.
+__device__ __forceinline__ void stream_wave(const StreamArgs& a, const uint8_t* table,
+                                            uint32_t span, bool live,
+                                            uint32_t (&lds)[kStreamWaves][kSWaveWords],
+                                            uint4* lut, uint32_t* spread) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const uint32_t g = uniform(blockIdx.x * kStreamWaves + static_cast<uint32_t>(wave));
-  const bool live = g < b.first_job[b.count];
-  int i = 0;
-#pragma unroll
-  for (int t = 1; t < kMaxDecodeBatch; ++t)
-    if (t < b.count && g >= b.first_job[t]) i = t;
-  i = uniform(i);
-  const size_t off = offsetof(StreamBatch, item) + static_cast<size_t>(i) * sizeof(StreamArgs);
-  const char* kp = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
-  const StreamArgs a = *(const StreamArgs*)(kp + off);   // uniform: held in SGPRs
-  const uint8_t* table = (const uint8_t*)kp + a.esc_tbl - 15;
   Span sp{};
   if (live) {
-    const uint32_t c0 = (g - b.first_job[i]) * a.span_chunks;
+    const uint32_t c0 = span * a.span_chunks;
     const uint32_t c1 = min(c0 + a.span_chunks, a.n_chunks);
     sp.A = uniform64(static_cast<int64_t>(a.anchor[c0]));
     sp.B = uniform64(static_cast<int64_t>(a.anchor[c1]));
@@ -1675,6 +1667,61 @@ __global__ __launch_bounds__(64 * kStreamWaves) void rice_stream_kernel(StreamBa
   __syncthreads();
   if (!live) return;
   stream_span(a, table, sp, lane, lds[wave], lut, spread);
+}
+
+// One wave per span (span s of tensor i is wave first_job[i] + s).
+__global__ __launch_bounds__(64 * kStreamWaves) void rice_stream_kernel(StreamBatch b) {
+  __shared__ __align__(16) uint32_t lds[kStreamWaves][kSWaveWords];
+  __shared__ uint4 lut[256];
+  __shared__ uint32_t spread[256];
+  const uint32_t g = uniform(blockIdx.x * kStreamWaves + (threadIdx.x >> 6));
+  const bool live = g < b.first_job[b.count];
+  int i = 0;
+#pragma unroll
+  for (int t = 1; t < kMaxDecodeBatch; ++t)
+    if (t < b.count && g >= b.first_job[t]) i = t;
+  i = uniform(i);
+  const size_t off = offsetof(StreamBatch, item) + static_cast<size_t>(i) * sizeof(StreamArgs);
+  const char* kp = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+  const StreamArgs a = *(const StreamArgs*)(kp + off);   // uniform: held in SGPRs
+  const uint8_t* table = (const uint8_t*)kp + a.esc_tbl - 15;
+  stream_wave(a, table, g - b.first_job[i], live, lds, lut, spread);
+}
+
+// A decode plan in device memory: its tensors' spans in one launch. The
+// plan holds first_job[count + 1] at first_off, StreamArgs[count] at
+// items_off and the escape exponents their esc_tbl offsets point at; the
+// status word comes with the launch.
+struct PlanLaunch {
+  const uint8_t* plan;
+  uint32_t* status;
+  uint32_t count;       // >= 1
+  uint32_t spans;       // first_job[count]
+  uint32_t first_off;
+  uint32_t items_off;
+};
+
+// One wave per span of the plan; the wave finds its tensor by a binary
+// search of first_job (uniform scalar loads).
+__global__ __launch_bounds__(64 * kStreamWaves) void rice_plan_kernel(PlanLaunch p) {
+  __shared__ __align__(16) uint32_t lds[kStreamWaves][kSWaveWords];
+  __shared__ uint4 lut[256];
+  __shared__ uint32_t spread[256];
+  const uint32_t g = uniform(blockIdx.x * kStreamWaves + (threadIdx.x >> 6));
+  const bool live = g < p.spans;
+  const uint32_t* first = reinterpret_cast<const uint32_t*>(p.plan + p.first_off);
+  uint32_t lo = 0, hi = p.count;   // first[lo] <= g < first[hi] for a live wave
+  while (hi - lo > 1u) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (g >= uniform(first[mid])) lo = mid;
+    else hi = mid;
+  }
+  lo = uniform(lo);
+  StreamArgs a = *reinterpret_cast<const StreamArgs*>(p.plan + p.items_off +
+                                                      static_cast<size_t>(lo) * sizeof(StreamArgs));
+  a.status = p.status;
+  const uint8_t* table = p.plan + a.esc_tbl - 15;
+  stream_wave(a, table, g - uniform(first[lo]), live, lds, lut, spread);
 }
 
 }  // namespace
@@ -1770,6 +1817,43 @@ int32_t launch_batch(const RiceBatch& b, hipStream_t stream) {
   return launch_status();
 }
 
+// Decode plans: a 32-byte header (PlanHeader), first_job[count + 1], the
+// tensors' StreamArgs (status cleared), then their escape exponents.
+constexpr uint32_t kPlanMagic = 0x31505242u;   // "BRP1"
+constexpr int32_t kMaxPlanTensors = 1 << 16;
+struct PlanHeader {
+  uint32_t magic;
+  int32_t count;
+  uint32_t spans;
+  uint32_t first_off;
+  uint32_t items_off;
+  uint32_t pool_off;
+  uint32_t bytes;       // bytes written, escape exponents included
+  uint32_t reserved;
+};
+static_assert(sizeof(PlanHeader) == 32, "plan header");
+
+struct PlanLayout {
+  uint32_t first_off, items_off, pool_off, max_bytes;
+};
+
+PlanLayout plan_layout(int32_t count) {
+  PlanLayout l;
+  l.first_off = sizeof(PlanHeader);
+  l.items_off = (l.first_off + 4u * static_cast<uint32_t>(count + 1) + 7u) & ~7u;
+  l.pool_off = l.items_off + static_cast<uint32_t>(count) * static_cast<uint32_t>(sizeof(StreamArgs));
+  l.max_bytes = l.pool_off + 241u * static_cast<uint32_t>(count);
+  return l;
+}
+
+int32_t launch_plan(const PlanLaunch& p, hipStream_t stream) {
+  if (p.spans == 0) return BINADE_OK;
+  const int64_t blocks = (static_cast<int64_t>(p.spans) + kStreamWaves - 1) / kStreamWaves;
+  hipLaunchKernelGGL(rice_plan_kernel, dim3(static_cast<uint32_t>(blocks)),
+                     dim3(64 * kStreamWaves), 0, stream, p);
+  return launch_status();
+}
+
 int32_t launch_stream(const StreamBatch& b, hipStream_t stream) {
   const uint32_t total = b.first_job[b.count];
   if (total == 0) return BINADE_OK;
@@ -1779,15 +1863,22 @@ int32_t launch_stream(const StreamBatch& b, hipStream_t stream) {
   return launch_status();
 }
 
+// Weights per span: a launch of up to 16 tensors, and a plan's single
+// launch (whose waves follow each other for the whole model, so that longer
+// spans pay their setup less often with no launch tail after each group).
 #ifndef BINADE_STREAM_SPAN
 #define BINADE_STREAM_SPAN 16384
+#endif
+#ifndef BINADE_PLAN_SPAN
+#define BINADE_PLAN_SPAN 32768
 #endif
 
 // The streamed path takes tensors of the byte-table kind (Rice k = 1, a table
 // of at least 15 ranks) whose row-chunk starts are at least 128 weights apart
 // and whose weight indices fit 31 bits. Fills its arguments from a checked
 // request and returns the span count.
-int64_t prepare_stream(const binade_rice* in, const RiceArgs& r, StreamArgs& s) {
+int64_t prepare_stream(const binade_rice* in, const RiceArgs& r, StreamArgs& s,
+                       int64_t span_weights = BINADE_STREAM_SPAN) {
   // rows shorter than 1024 weights start a chunk every few hundred codes,
   // which the per-job kernel checks more cheaply
   if (in->k != 1 || in->n < 15 || in->cols < 1024) return 0;
@@ -1809,7 +1900,7 @@ int64_t prepare_stream(const binade_rice* in, const RiceArgs& r, StreamArgs& s) 
   s.C = r.chunks_per_row;
   s.n_chunks = static_cast<uint32_t>(r.n_chunks);
   s.cols_recip = static_cast<uint32_t>(((1ull << 32) + s.cols - 1) / s.cols);
-  const int64_t per = s.C > 1 ? BINADE_STREAM_SPAN / BINADE_CHUNK : BINADE_STREAM_SPAN / in->cols;
+  const int64_t per = s.C > 1 ? span_weights / BINADE_CHUNK : span_weights / in->cols;
   s.span_chunks = static_cast<uint32_t>(per > 64 ? 64 : per > 1 ? per : 1);
   s.n = r.n;
   return (r.n_chunks + s.span_chunks - 1) / s.span_chunks;
@@ -1896,4 +1987,72 @@ extern "C" int32_t binade_rice_to_r4_batch(const binade_rice* in, binade_r4* out
     return launch_stream(sbat, st);
   }
   return BINADE_OK;
+}
+
+extern "C" int64_t binade_rice_plan_bytes(int32_t count) {
+  if (count < 0 || count > kMaxPlanTensors) return BINADE_EINVAL;
+  return plan_layout(count).max_bytes;
+}
+
+extern "C" int32_t binade_rice_to_r4_plan(const binade_rice* in, binade_r4* out,
+                                          int32_t count, void* plan, int64_t plan_bytes) {
+  if (count < 0 || count > kMaxPlanTensors || plan == nullptr ||
+      (count > 0 && (in == nullptr || out == nullptr)))
+    return BINADE_EINVAL;
+  const PlanLayout l = plan_layout(count);
+  if (plan_bytes < static_cast<int64_t>(l.max_bytes)) return BINADE_EINVAL;
+  uint8_t* base = static_cast<uint8_t*>(plan);
+  std::memset(base, 0, l.pool_off);
+  uint32_t* first = reinterpret_cast<uint32_t*>(base + l.first_off);
+  uint64_t spans = 0;
+  uint32_t pool = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    RiceArgs a;
+    const int64_t nj = prepare_decode(&in[i], &out[i], nullptr, a);
+    if (nj < 0) return static_cast<int32_t>(nj);
+    StreamArgs sa;
+    const int64_t ns = prepare_stream(&in[i], a, sa, BINADE_PLAN_SPAN);
+    if (ns <= 0 || spans + static_cast<uint64_t>(ns) >= (1ull << 31)) return BINADE_EUNSUPPORTED;
+    const uint32_t esc_bytes = in[i].n > 15 ? in[i].n - 15 : 0;   // <= 241
+    std::memcpy(base + l.pool_off + pool, in[i].exp_of_rank + 15, esc_bytes);
+    sa.esc_tbl = l.pool_off + pool;
+    sa.status = nullptr;
+    pool += esc_bytes;
+    first[i] = static_cast<uint32_t>(spans);
+    std::memcpy(base + l.items_off + static_cast<size_t>(i) * sizeof(StreamArgs), &sa, sizeof sa);
+    spans += static_cast<uint64_t>(ns);
+  }
+  first[count] = static_cast<uint32_t>(spans);
+  PlanHeader h{};
+  h.magic = kPlanMagic;
+  h.count = count;
+  h.spans = static_cast<uint32_t>(spans);
+  h.first_off = l.first_off;
+  h.items_off = l.items_off;
+  h.pool_off = l.pool_off;
+  h.bytes = l.pool_off + pool;
+  std::memcpy(base, &h, sizeof h);
+  return BINADE_OK;
+}
+
+extern "C" int32_t binade_rice_to_r4_run(const void* host_plan, const void* dev_plan,
+                                         uint32_t* dev_status, void* stream) {
+  if (host_plan == nullptr) return BINADE_EINVAL;
+  PlanHeader h;
+  std::memcpy(&h, host_plan, sizeof h);
+  if (h.magic != kPlanMagic || h.count < 0 || h.count > kMaxPlanTensors) return BINADE_EINVAL;
+  const PlanLayout l = plan_layout(h.count);
+  if (h.first_off != l.first_off || h.items_off != l.items_off || h.pool_off != l.pool_off)
+    return BINADE_EINVAL;
+  if (h.count == 0 || h.spans == 0) return BINADE_OK;
+  if (dev_plan == nullptr || (reinterpret_cast<uintptr_t>(dev_plan) & 7u) != 0)
+    return BINADE_EINVAL;
+  PlanLaunch p;
+  p.plan = static_cast<const uint8_t*>(dev_plan);
+  p.status = dev_status;
+  p.count = static_cast<uint32_t>(h.count);
+  p.spans = h.spans;
+  p.first_off = h.first_off;
+  p.items_off = h.items_off;
+  return launch_plan(p, static_cast<hipStream_t>(stream));
 }

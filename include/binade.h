@@ -324,6 +324,38 @@ int32_t binade_rice_to_r4_batch(const binade_rice *in, binade_r4 *out,
                                 int32_t count, uint32_t *dev_status,
                                 void *stream);
 
+/* Format 2 -> R4 for a whole model in one launch ("Binade" package page,
+ * "How it works": at load a GPU kernel turns the file format into R4). A
+ * plan is written once on the host, copied to device memory by the caller
+ * and run any number of times; each run decodes every tensor of the plan in
+ * a single launch, with the results of binade_rice_to_r4 bit for bit.
+ *
+ * binade_rice_plan_bytes: bytes a plan of count tensors may take (count in
+ * 0 .. 65536; BINADE_EINVAL otherwise).
+ *
+ * binade_rice_to_r4_plan: checks in[i] and fills out[i]'s host-visible
+ * fields exactly as binade_rice_to_r4_batch does, and writes the plan into
+ * HOST memory plan (plan_bytes >= binade_rice_plan_bytes(count), else
+ * BINADE_EINVAL). The plan records the device addresses of in[i]'s planes
+ * and of out[i].nib / out[i].esc: those buffers must stay allocated while
+ * the plan is used. Every tensor must take the streamed decoder: Rice
+ * k = 1, a table of at least 15 ranks, at least 1024 columns, a last
+ * row-chunk of 0 or at least 128 columns and fewer than 2^31 weights
+ * (together fewer than 2^31 spans of 32768 weights); otherwise
+ * BINADE_EUNSUPPORTED and the plan is not usable (binade_rice_to_r4_batch
+ * takes any tensor).
+ *
+ * binade_rice_to_r4_run: host_plan is the plan as written (its header is
+ * read); dev_plan is a byte-for-byte copy of it in device memory, 8-byte
+ * aligned, which the launch reads (the caller owns it and keeps it until
+ * the launch has run). dev_status: device u32 or NULL, as for
+ * binade_rice_to_r4. BINADE_EINVAL for a header that is not a plan's. */
+int64_t binade_rice_plan_bytes(int32_t count);
+int32_t binade_rice_to_r4_plan(const binade_rice *in, binade_r4 *out,
+                               int32_t count, void *plan, int64_t plan_bytes);
+int32_t binade_rice_to_r4_run(const void *host_plan, const void *dev_plan,
+                              uint32_t *dev_status, void *stream);
+
 /* Format 1 -> R4 on the GPU ("Binade" package page, "How it works": at load
  * a GPU kernel turns either file format into R4). in: device planes of a
  * format 1 tensor as binade_pack_f1 leaves them (code_words and esc_cap the

@@ -547,6 +547,60 @@ def test_batched_decode_splits_on_wide_tables():
         assert np.array_equal(bits_np(B.unpack(o)), wn)
 
 
+def test_decode_plan_runs_every_tensor_in_one_launch():
+    """A plan of 20 tensors (more than one batched launch holds), wide tables
+    with dense escapes among them, run twice over outputs filled with junk:
+    every tensor's R4 equals the oracle's both times."""
+    shapes = [(300, 3072), (64, 8192), (1, 4096), (3, 1152), (2, 17408), (7, 2176),
+              (33, 1344), (9, 2048), (11, 6144), (19, 15360), (24, 3072), (4, 8192),
+              (5, 4352), (128, 2816), (1, 15360), (6, 5120), (40, 1024), (2, 3072)]
+    ws = [synth.normal_bf16(spec(n, k, 0.02, 700 + i, 1e-3, 20.0)) for i, (n, k) in enumerate(shapes)]
+    ws += [_wide_exponents(64, 3072, 731, 0.02), _wide_exponents(23, 15360, 732, 0.02)]
+    planes = [B.pack_rice(w).to(DEV) for w in ws]
+    assert all(p.k == 1 and p.table.n >= 15 for p in planes)
+    plan = B.RicePlan(planes)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    refs = []
+    for w in ws:
+        wn = bits_np(w)
+        refs.append(oracle.make_r4(wn, oracle.build_table(wn)))
+    for rep in range(2):
+        print("decode plan run", rep, flush=True)
+        for o in plan.outs:
+            o.nib.fill_(0xA5)
+            o.esc.fill_(-1)
+        outs = plan.run(status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        for i, (o, ref) in enumerate(zip(outs, refs)):
+            assert o.lut == bytes(ref["lut"]), i
+            assert o.n_esc == ref["n_esc"], i
+            assert np.array_equal(o.nib.cpu().numpy(), ref["nib"].reshape(-1)), i
+            if o.n_esc:
+                assert np.array_equal(o.esc[: o.n_esc].cpu().numpy().view(np.uint32), ref["esc"]), i
+    assert np.array_equal(bits_np(B.unpack(plan.outs[-1])), bits_np(ws[-1]))
+
+
+def test_decode_plan_flags_a_corrupt_tensor():
+    """One tensor of a plan with an anchor one bit late: the run sets the
+    status word; the same plan without it runs clean."""
+    ws = [synth.normal_bf16(spec(n, k, 0.02, 750 + i, 1e-3, 20.0))
+          for i, (n, k) in enumerate([(64, 3072), (16, 8192), (48, 3072)])]
+    planes = [B.pack_rice(w) for w in ws]
+    anchor = planes[1].anchor.clone()
+    anchor[5] += 1
+    bad = _replace(planes[1], anchor=anchor)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    good = B.RicePlan([p.to(DEV) for p in planes])
+    good.run(status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    plan = B.RicePlan([planes[0].to(DEV), bad.to(DEV), planes[2].to(DEV)])
+    plan.run(status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & (B.DEV_CORRUPT_STREAM | B.DEV_CORRUPT_ESC)
+
+
 @pytest.mark.parametrize("nk", [(200, 15360), (136, 8192), (72, 3840), (72, 4160), (40, 96)])
 def test_gemm_rows_do_not_depend_on_m(nk):
     """The GEMM order depends on K only: the same X row gives the same bits

@@ -332,3 +332,67 @@ def test_new_device_entry_points_validate_before_touching_the_gpu():
     h.len[3] = 32
     assert L.binade_huff_decode(ctypes.byref(h), P(16), P(16), None, None) == B.EINVAL
     assert B.lib().binade_huff_workspace_bytes() > 4096
+
+
+def _plan_header(plan):
+    raw = bytes(plan.host)
+    magic, count, spans, first_off, items_off, pool_off, nbytes, _ = np.frombuffer(
+        raw[:32], dtype=np.uint32)
+    first = np.frombuffer(raw[first_off:first_off + 4 * (int(count) + 1)], dtype=np.uint32)
+    return raw, int(magic), int(count), int(spans), first, int(pool_off), int(nbytes)
+
+
+def test_decode_plan_layout_and_checks():
+    """binade_rice_to_r4_plan on host planes (it records addresses and never
+    reads through them): one span per 32768 weights of row-chunks (16 chunks
+    of 2048 for long rows, 32768 / cols short rows), the escape exponents of
+    every table in order, the R4 tables the oracle gives, and the declared
+    status codes for sizes, headers and tensors the streamed decoder does
+    not take."""
+    L = B.lib()
+    assert L.binade_rice_plan_bytes(0) == 40
+    assert L.binade_rice_plan_bytes(-1) == B.EINVAL
+    assert L.binade_rice_plan_bytes(65537) == B.EINVAL
+    shapes = [(24, 3072), (8, 8192), (3, 1152)]
+    ws = [synth.normal_bf16(synth.TensorSpec("p", r, c, 0.02, 40 + i, outlier_frac=2e-3,
+                                             outlier_scale=1e3))
+          for i, (r, c) in enumerate(shapes)]
+    planes = [B.pack_rice(w) for w in ws]
+    plan = B.RicePlan(planes)
+    raw, magic, count, spans, first, pool_off, nbytes = _plan_header(plan)
+    assert magic == 0x31505242 and count == 3
+    assert first.tolist() == [0, 3, 5, 6] and spans == 6
+    pool = b"".join(bytes(bytearray(p.table.exp_of_rank))[15:p.table.n] for p in planes)
+    assert raw[pool_off:nbytes] == pool and len(pool) > 0
+    for w, o in zip(ws, plan.outs):
+        wn = w.contiguous().view(torch.int16).numpy().view(np.uint16)
+        assert o.lut == bytes(oracle.make_r4(wn, oracle.build_table(wn))["lut"])
+    # a buffer one byte short
+    n = len(planes)
+    din = (B.RiceDesc * n)(*[p.desc() for p in planes])
+    dout = (B.R4Desc * n)()
+    for i, o in enumerate(plan.outs):
+        dout[i].nib = o.nib.data_ptr()
+        dout[i].esc = o.esc.data_ptr()
+    short = (ctypes.c_uint8 * (L.binade_rice_plan_bytes(n) - 1))()
+    assert L.binade_rice_to_r4_plan(din, dout, n, short, len(short)) == B.EINVAL
+    # rows shorter than 1024 weights, a last row-chunk of 64 columns, and
+    # Rice k != 1 take the per-job kernel only
+    for w in (synth.normal_bf16(synth.TensorSpec("s", 50, 64, 0.02, 7)),
+              synth.normal_bf16(synth.TensorSpec("s", 5, 4160, 0.02, 8)),
+              (torch.randn(64, 2048, generator=torch.Generator().manual_seed(3)) *
+               torch.exp2(torch.randint(-60, 60, (64, 2048),
+                                        generator=torch.Generator().manual_seed(4)))
+               ).to(torch.bfloat16)):
+        p = B.pack_rice(w)
+        with pytest.raises(B.BinadeError) as e:
+            B.RicePlan([planes[0], p])
+        assert e.value.code == B.EUNSUPPORTED, (p.rows, p.cols, p.k)
+    # headers that are not a plan's; an empty plan launches nothing
+    assert L.binade_rice_to_r4_run(bytes(32), None, None, None) == B.EINVAL
+    bad = bytearray(raw)
+    bad[12] ^= 4   # first_job's offset
+    assert L.binade_rice_to_r4_run(bytes(bad), None, None, None) == B.EINVAL
+    assert L.binade_rice_to_r4_run(None, None, None, None) == B.EINVAL
+    empty = B.RicePlan([])
+    assert L.binade_rice_to_r4_run(empty.host, None, None, None) == B.OK
